@@ -1,0 +1,195 @@
+"""CPU oracle for the MX block-scaled NT GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package.  It wraps ``liboracle.so`` (plain C, ``mx_oracle.c``), which
+shares no code with the GPU library.
+
+What the oracle computes, and where it comes from, is stated at the top of
+``mx_oracle.c``: exact per-32 block dot products of table-decoded E2M1/E4M3
+elements, each scaled by 2^(sA+sB-254), summed over blocks in double.
+
+The acceptance rule lives here too:
+  FP32 output: |gpu - C| <= 1e-5 * T
+  BF16 output: |gpu - C| <= 1e-5 * T + ulp_bf16(C)
+where T = sum over k of |a_k * b_k| (scaled) and ulp_bf16(x) is the spacing
+of bfloat16 numbers in x's binade (2^(max(floor(log2|x|), -126) - 7)); for
+x = 0 it is the smallest subnormal spacing, 2^-133.  NaN results are not
+graded by this rule.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+FMT_E2M1 = 1
+FMT_E4M3 = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+REL_TOL = 1e-5
+
+
+def _bind(lib):
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.mxo_e2m1_value.restype = ctypes.c_double
+    lib.mxo_e2m1_value.argtypes = [ctypes.c_uint]
+    lib.mxo_e4m3_value.restype = ctypes.c_double
+    lib.mxo_e4m3_value.argtypes = [ctypes.c_uint]
+    lib.mxo_e8m0_value.restype = ctypes.c_double
+    lib.mxo_e8m0_value.argtypes = [ctypes.c_uint]
+    lib.mxo_tables.restype = None
+    lib.mxo_tables.argtypes = [dp, dp]
+    lib.mxo_block_contrib.restype = ctypes.c_double
+    lib.mxo_block_contrib.argtypes = [ctypes.c_int, i64, u8p, u8p, u8p, u8p,
+                                      i64, i64, i64, dp]
+    lib.mxo_gemm.restype = ctypes.c_int
+    lib.mxo_gemm.argtypes = [ctypes.c_int, i64, i64, i64, u8p, u8p, u8p, u8p,
+                             ctypes.POINTER(ctypes.c_int64), i64, dp, dp,
+                             ctypes.c_int]
+    return lib
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _check_shapes(fmt, A, As, B, Bs, K):
+    if fmt not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    rb = K // 2 if fmt == FMT_E2M1 else K
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != rb or B.shape[1] != rb:
+        raise ValueError("A and B must be 2-D with %d bytes per row" % rb)
+    if As.shape != (A.shape[0], K // 32) or Bs.shape != (B.shape[0], K // 32):
+        raise ValueError("scale arrays must be rows x K/32")
+
+
+class Oracle:
+    """The oracle's entry points, bound to one build of ``mx_oracle.c``."""
+
+    def __init__(self, path=LIB_PATH):
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                "%s is not built (run oracle/build.py or __graft_entry__.build())" % path)
+        self.lib = _bind(ctypes.CDLL(path))
+
+    def e2m1_value(self, code):
+        return self.lib.mxo_e2m1_value(int(code))
+
+    def e4m3_value(self, code):
+        return self.lib.mxo_e4m3_value(int(code))
+
+    def e8m0_value(self, byte):
+        return self.lib.mxo_e8m0_value(int(byte))
+
+    def tables(self):
+        """(e2m1[16], e4m3[256]) decode tables as float64 arrays."""
+        t4 = np.zeros(16, np.float64)
+        t8 = np.zeros(256, np.float64)
+        dp = ctypes.POINTER(ctypes.c_double)
+        self.lib.mxo_tables(t4.ctypes.data_as(dp), t8.ctypes.data_as(dp))
+        return t4, t8
+
+    def gemm(self, fmt, A, A_scale, B, B_scale, K, rows=None, threads=0):
+        """Return (C, T) as float64 arrays of shape (len(rows) or M, N).
+
+        A: uint8 M x (K/2 or K); B: uint8 N x (K/2 or K); scales uint8
+        rows x K/32.  ``rows`` selects a subset of A's rows; ``threads`` <= 0
+        lets OpenMP choose."""
+        A, pa = _u8(A)
+        As, pas = _u8(A_scale)
+        B, pb = _u8(B)
+        Bs, pbs = _u8(B_scale)
+        _check_shapes(fmt, A, As, B, Bs, K)
+        M, N = A.shape[0], B.shape[0]
+        if rows is None:
+            nrows, prow = M, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            nrows = rows_arr.shape[0]
+            prow = rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        C = np.zeros((nrows, N), np.float64)
+        T = np.zeros((nrows, N), np.float64)
+        dp = ctypes.POINTER(ctypes.c_double)
+        rc = self.lib.mxo_gemm(fmt, M, N, K, pa, pas, pb, pbs, prow, nrows,
+                               C.ctypes.data_as(dp), T.ctypes.data_as(dp),
+                               int(threads))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return C, T
+
+    def block_contrib(self, fmt, A, A_scale, B, B_scale, K, m, n, b):
+        """(contribution, magnitude) of block b to C[m][n]."""
+        A, pa = _u8(A)
+        As, pas = _u8(A_scale)
+        B, pb = _u8(B)
+        Bs, pbs = _u8(B_scale)
+        _check_shapes(fmt, A, As, B, Bs, K)
+        t = ctypes.c_double(0.0)
+        c = self.lib.mxo_block_contrib(fmt, K, pa, pas, pb, pbs, int(m), int(n),
+                                       int(b), ctypes.byref(t))
+        return c, t.value
+
+
+_default = None
+
+
+def default():
+    """The oracle built from this directory's ``mx_oracle.c``."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def gemm(*args, **kw):
+    return default().gemm(*args, **kw)
+
+
+def block_contrib(*args, **kw):
+    return default().block_contrib(*args, **kw)
+
+
+def tables():
+    return default().tables()
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 numbers in the binade of each |x| (float64 array)."""
+    x = np.abs(np.asarray(x, np.float64))
+    _, e = np.frexp(x)                       # x = f * 2^e, f in [0.5, 1)
+    expo = np.maximum(e - 1, -126)           # floor(log2 |x|), clamped
+    ulp = np.ldexp(1.0, expo - 7)
+    return np.where(x == 0, np.ldexp(1.0, -133), ulp)
+
+
+def bound(C, T, out_is_bf16):
+    """Allowed |gpu - C| per element."""
+    b = REL_TOL * np.asarray(T, np.float64)
+    if out_is_bf16:
+        b = b + bf16_ulp(C)
+    return b
+
+
+def compare(gpu, C, T, out_is_bf16):
+    """Per-element acceptance.  Returns a dict with the worst error/bound ratio,
+    the number of failing elements and the first failing index (or None)."""
+    g = np.asarray(gpu, np.float64)
+    C = np.asarray(C, np.float64)
+    if g.shape != C.shape:
+        raise ValueError("shape mismatch %s vs %s" % (g.shape, C.shape))
+    err = np.abs(g - C)
+    lim = bound(C, T, out_is_bf16)
+    # T == 0 with FP32 output demands an exact zero: err <= 0.
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(lim > 0, err / lim, np.where(err == 0, 0.0, np.inf))
+    bad = ~(err <= lim)
+    nbad = int(bad.sum())
+    first = None
+    if nbad:
+        first = tuple(int(i) for i in np.argwhere(bad)[0])
+    return {"max_ratio": float(np.max(ratio)) if ratio.size else 0.0,
+            "n_bad": nbad, "first_bad": first}

@@ -1,0 +1,208 @@
+/*
+ * mx_oracle.c -- plain, slow CPU reference for the MX block-scaled NT GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this file's library; the GPU library
+ * never links it, includes it or calls it, and the two share no code.
+ *
+ * What is computed.  The FlyDSL summary pages (yuxiaoba.github.io, "FlyDSL"
+ * article, section "API compatibility is not universal input coverage")
+ * define the MX scaled GEMM's input contract: operands in a fixed row/column
+ * layout, one E8M0 scale per 32 consecutive values along K, K a multiple of
+ * 128.  The AI-compiler digest of 2026-10-22 (item 1, "Accelerating PyTorch on
+ * AMD GPUs with FlyDSL") adds "BlockWise1x32, E8M0 scale, FP32 accumulation"
+ * and names the element formats MXFP4 and MXFP8.  The element encodings are
+ * those of the OCP Microscaling (MX) v1.0 specification: MXFP4 = E2M1,
+ * MXFP8 = E4M3 (no infinities, S.1111.111 is NaN), scale = E8M0.
+ *
+ * With A (M x K) and B (N x K) both stored K-contiguous, scale bytes
+ * sA[m][b], sB[n][b] for block b = K-values 32b .. 32b+31, and dec() the
+ * element decode:
+ *
+ *   C[m][n] = sum_b 2^(sA[m][b] + sB[n][b] - 254) * P(m,n,b)
+ *   P(m,n,b) = sum_{j<32} dec(A[m][32b+j]) * dec(B[n][32b+j])
+ *   T[m][n]  = sum_b 2^(sA+sB-254) * sum_{j<32} |dec(A) * dec(B)|
+ *
+ * T is the magnitude sum used as the tolerance denominator.
+ *
+ * Precision.  P is exact in double: E2M1 values are multiples of 1/2 with
+ * |v| <= 6, so a block sum is a multiple of 1/4 below 2^11; E4M3 values are
+ * multiples of 2^-9 with |v| <= 448, so a product is a multiple of 2^-18
+ * below 2^18 and a 32-term sum needs at most 41 significant bits.  Scaling by
+ * a power of two in [2^-254, 2^254] is exact.  The only rounding is the final
+ * double-precision sum over the K/32 blocks, taken in increasing b.
+ *
+ * Storage.  MXFP8 rows are K bytes, element k in byte k.  MXFP4 rows are K/2
+ * bytes, element 2i in the low nibble of byte i and element 2i+1 in the high
+ * nibble.  Scale rows are K/32 bytes.  Everything is row-major and dense.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define MXO_FMT_E2M1 1
+#define MXO_FMT_E4M3 2
+
+/* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.  Exponent
+ * field 0 is subnormal: m * 2^-1.  No Inf, no NaN (OCP MX v1.0, FP4). */
+double mxo_e2m1_value(unsigned code)
+{
+    unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* E4M3 ("FN"): sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+ * Exponent field 0 is subnormal: m/8 * 2^-6.  S.1111.111 is NaN, no Inf
+ * (OCP MX v1.0, FP8 E4M3). */
+double mxo_e4m3_value(unsigned code)
+{
+    unsigned s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* E8M0 scale: 2^(byte - 127); byte 255 is NaN (OCP MX v1.0, E8M0). */
+double mxo_e8m0_value(unsigned byte)
+{
+    if (byte == 255) return NAN;
+    return ldexp(1.0, (int)byte - 127);
+}
+
+/* Decode element k of one packed row into a double. */
+static double decode_elem(int fmt, const uint8_t *row, int64_t k,
+                          const double *t4, const double *t8)
+{
+    if (fmt == MXO_FMT_E4M3) return t8[row[k]];
+    uint8_t byte = row[k >> 1];
+    return t4[(k & 1) ? (byte >> 4) : (byte & 15u)];
+}
+
+static void make_tables(double t4[16], double t8[256], double pow2[509])
+{
+    for (unsigned c = 0; c < 16; ++c) t4[c] = mxo_e2m1_value(c);
+    for (unsigned c = 0; c < 256; ++c) t8[c] = mxo_e4m3_value(c);
+    /* pow2[i] = 2^(i - 254), i = sA + sB in 0..508: every entry is an exact
+     * double (normal range reaches 2^-1022). */
+    for (int i = 0; i < 509; ++i) pow2[i] = ldexp(1.0, i - 254);
+}
+
+static int64_t row_bytes(int fmt, int64_t K) { return fmt == MXO_FMT_E2M1 ? K / 2 : K; }
+
+/* Fill the caller's 16- and 256-entry arrays with the element decode tables. */
+void mxo_tables(double *e2m1_out16, double *e4m3_out256)
+{
+    double pow2[509];
+    make_tables(e2m1_out16, e4m3_out256, pow2);
+}
+
+/*
+ * One block's contribution 2^(sA[m][b]+sB[n][b]-254) * P(m,n,b), with its
+ * magnitude counterpart written to *t_out (may be NULL).  Returns NaN if
+ * either scale byte is 255 or an element decodes to NaN.
+ */
+double mxo_block_contrib(int fmt, int64_t K,
+                         const uint8_t *A, const uint8_t *A_scale,
+                         const uint8_t *B, const uint8_t *B_scale,
+                         int64_t m, int64_t n, int64_t b, double *t_out)
+{
+    double t4[16], t8[256], pow2[509];
+    make_tables(t4, t8, pow2);
+    const int64_t nb = K / 32, rb = row_bytes(fmt, K);
+    const uint8_t *arow = A + m * rb, *brow = B + n * rb;
+    unsigned sa = A_scale[m * nb + b], sb = B_scale[n * nb + b];
+    double p = 0.0, t = 0.0;
+    for (int64_t j = 0; j < 32; ++j) {
+        double x = decode_elem(fmt, arow, 32 * b + j, t4, t8);
+        double y = decode_elem(fmt, brow, 32 * b + j, t4, t8);
+        p += x * y;
+        t += fabs(x * y);
+    }
+    double w = (sa == 255 || sb == 255) ? NAN : pow2[sa + sb];
+    if (t_out) *t_out = t * w;
+    return p * w;
+}
+
+/*
+ * C[i][n] and T[i][n] for the rows m = rows[i] (i < nrows), all n < N.  rows
+ * may be NULL, meaning rows 0..nrows-1.  C and T are nrows x N doubles,
+ * row-major; T may be NULL.  nthreads <= 0 uses OpenMP's default.
+ * Returns 0, or -1 on an argument the definition does not cover.
+ */
+int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
+             const uint8_t *A, const uint8_t *A_scale,
+             const uint8_t *B, const uint8_t *B_scale,
+             const int64_t *rows, int64_t nrows,
+             double *C, double *T, int nthreads)
+{
+    if (fmt != MXO_FMT_E2M1 && fmt != MXO_FMT_E4M3) return -1;
+    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || nrows < 0) return -1;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return -1;
+    if (!rows && nrows > M) return -1;
+
+    double t4[16], t8[256], pow2[509];
+    make_tables(t4, t8, pow2);
+    const int64_t nb = K / 32, rb = row_bytes(fmt, K);
+    const int64_t chunk = 128;      /* decoded A rows held at once */
+    double *adec = (double *)malloc(sizeof(double) * (size_t)(chunk * K));
+    if (!adec) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+
+    for (int64_t i0 = 0; i0 < nrows; i0 += chunk) {
+        const int64_t ni = (nrows - i0 < chunk) ? nrows - i0 : chunk;
+        /* Step 1: decode the chunk's A rows by table. */
+        for (int64_t i = 0; i < ni; ++i) {
+            int64_t m = rows ? rows[i0 + i] : i0 + i;
+            for (int64_t k = 0; k < K; ++k)
+                adec[i * K + k] = decode_elem(fmt, A + m * rb, k, t4, t8);
+        }
+        int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+        {
+            double *bdec = (double *)malloc(sizeof(double) * (size_t)K);
+            if (!bdec) {
+#pragma omp atomic write
+                failed = 1;
+            }
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t n = 0; n < N; ++n) {
+                if (!bdec) continue;
+                /* Step 1 (B side): decode row n of B by table. */
+                for (int64_t k = 0; k < K; ++k)
+                    bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);
+                const uint8_t *sbrow = B_scale + n * nb;
+                for (int64_t i = 0; i < ni; ++i) {
+                    int64_t m = rows ? rows[i0 + i] : i0 + i;
+                    const uint8_t *sarow = A_scale + m * nb;
+                    const double *a = adec + i * K;
+                    double c = 0.0, t = 0.0;
+                    for (int64_t b = 0; b < nb; ++b) {
+                        /* Step 2: the exact block dot product P(m,n,b). */
+                        double p = 0.0, q = 0.0;
+                        for (int64_t j = 32 * b; j < 32 * b + 32; ++j) {
+                            double prod = a[j] * bdec[j];
+                            p += prod;
+                            q += fabs(prod);
+                        }
+                        /* Step 3: the block's power-of-two scale. */
+                        unsigned sa = sarow[b], sb = sbrow[b];
+                        double w = (sa == 255 || sb == 255) ? NAN : pow2[sa + sb];
+                        /* Step 4: accumulate blocks in increasing b. */
+                        c += p * w;
+                        t += q * w;
+                    }
+                    C[(i0 + i) * N + n] = c;
+                    if (T) T[(i0 + i) * N + n] = t;
+                }
+            }
+            free(bdec);
+        }
+        if (failed) { free(adec); return -1; }
+    }
+    free(adec);
+    return 0;
+}

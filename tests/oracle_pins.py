@@ -1,0 +1,300 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with:
+  * library routines: torch's float8_e4m3fn / float8_e8m0fnu decodings, and a
+    numpy float64 matmul of dequantized operands;
+  * hand-computed worked examples and the OCP E2M1 value list (tests/golden);
+  * exact rational arithmetic (fractions.Fraction) on tiny inputs;
+  * exact integer matmul when every scale is 2^0 and every element an integer;
+  * invariants: a scale byte +k multiplies exactly its block's contribution
+    by 2^k; swapping the operands transposes C bit for bit; zeros give zero;
+    NaN scales and NaN elements poison exactly the outputs they touch.
+The decode tables used here come from torch and the golden file, never from
+the oracle.  tests/test_oracle_mutants.py plants mistakes in copies of the
+oracle and checks that these pins catch each one.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import mxinputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+E2M1, E4M3 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3
+
+
+# --------------------------------------------------------------------------
+# Independent decode tables (not the oracle's).
+
+def golden_e2m1():
+    vals = np.zeros(16, np.float64)
+    with open(os.path.join(GOLDEN, "e2m1_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()
+                vals[int(c)] = float(v)
+    return vals
+
+
+def torch_e4m3():
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def torch_e8m0():
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+
+
+def decode_rows(fmt, packed):
+    """uint8 operand rows -> float64 values with the independent tables."""
+    if fmt == E2M1:
+        return golden_e2m1()[mxinputs.unpack_e2m1(packed)]
+    return torch_e4m3()[np.asarray(packed, np.uint8)]
+
+
+def dequant(fmt, packed, scales):
+    v = decode_rows(fmt, packed)
+    e = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    return np.ldexp(v, e)
+
+
+# --------------------------------------------------------------------------
+def _same(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return a.shape == b.shape and bool(np.all((a == b) | (np.isnan(a) & np.isnan(b))))
+
+
+def pin_e4m3_table(orc):
+    _, t8 = orc.tables()
+    assert _same(t8, torch_e4m3()), "E4M3 table differs from torch.float8_e4m3fn"
+    for c in (0x01, 0x38, 0x7E, 0x7F, 0xFE, 0x80):
+        v = orc.e4m3_value(c)
+        assert _same(v, torch_e4m3()[c])
+
+
+def pin_e2m1_table(orc):
+    t4, _ = orc.tables()
+    g = golden_e2m1()
+    assert np.array_equal(t4, g), "E2M1 table differs from the OCP value list"
+    assert all(np.signbit(t4[8:]))
+
+
+def pin_e8m0(orc):
+    ref = torch_e8m0()
+    got = np.array([orc.e8m0_value(b) for b in range(256)])
+    assert _same(got, ref), "E8M0 decode differs from torch.float8_e8m0fnu"
+
+
+def _parse_bytes(tokens):
+    out = []
+    for t in tokens:
+        if "*" in t:
+            v, n = t.split("*")
+            out += [int(v, 16)] * int(n)
+        else:
+            out.append(int(t, 16))
+    return np.array(out, np.uint8)
+
+
+def load_worked_example(name):
+    d = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                k, *v = line.split()
+                d[k] = v
+    fmt = {"e2m1": E2M1, "e4m3": E4M3}[d["fmt"][0]]
+    K = int(d["K"][0])
+    A = _parse_bytes(d["a_row"])[None, :]
+    B = _parse_bytes(d["b_row"])[None, :]
+    As = np.array([int(x) for x in d["a_scale"]], np.uint8)[None, :]
+    Bs = np.array([int(x) for x in d["b_scale"]], np.uint8)[None, :]
+    assert A.shape[1] == (K // 2 if fmt == E2M1 else K)
+    return fmt, K, A, As, B, Bs, Fraction(d["C"][0]), Fraction(d["T"][0])
+
+
+def pin_worked_examples(orc):
+    for name in ("worked_example_e2m1.txt", "worked_example_e4m3.txt"):
+        fmt, K, A, As, B, Bs, Cx, Tx = load_worked_example(name)
+        C, T = orc.gemm(fmt, A, As, B, Bs, K)
+        assert C[0, 0] == float(Cx), (name, C[0, 0], float(Cx))
+        assert T[0, 0] == float(Tx), (name, T[0, 0], float(Tx))
+
+
+def _exact(fmt, A, As, B, Bs, K):
+    """C and T as Fractions, from the definition, with independent tables."""
+    va, vb = decode_rows(fmt, A), decode_rows(fmt, B)
+    M, N, nb = A.shape[0], B.shape[0], K // 32
+    C = [[Fraction(0)] * N for _ in range(M)]
+    T = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            for b in range(nb):
+                w = Fraction(2) ** (int(As[m, b]) + int(Bs[n, b]) - 254)
+                p = sum(Fraction(float(va[m, j])) * Fraction(float(vb[n, j]))
+                        for j in range(32 * b, 32 * b + 32))
+                q = sum(abs(Fraction(float(va[m, j])) * Fraction(float(vb[n, j])))
+                        for j in range(32 * b, 32 * b + 32))
+                C[m][n] += w * p
+                T[m][n] += w * q
+    return C, T
+
+
+def pin_bruteforce(orc):
+    for fmt in (E2M1, E4M3):
+        for seed, (M, N, K) in enumerate([(2, 3, 128), (3, 2, 256), (1, 4, 128)]):
+            pool = range(8) if fmt == E2M1 else range(127)
+            A, _ = mxinputs.random_codes(fmt, M, K, seed, pool, tensor=0)
+            B, _ = mxinputs.random_codes(fmt, N, K, seed, pool, tensor=1)
+            r = np.random.default_rng([7, seed, fmt])
+            As = r.integers(100, 155, size=(M, K // 32)).astype(np.uint8)
+            Bs = r.integers(100, 155, size=(N, K // 32)).astype(np.uint8)
+            C, T = orc.gemm(fmt, A, As, B, Bs, K)
+            Cx, Tx = _exact(fmt, A, As, B, Bs, K)
+            nb = K // 32
+            for m in range(M):
+                for n in range(N):
+                    tol = nb * 2.0 ** -52 * float(Tx[m][n])
+                    assert abs(C[m, n] - float(Cx[m][n])) <= tol, (fmt, m, n)
+                    assert abs(T[m, n] - float(Tx[m][n])) <= tol, (fmt, m, n)
+
+
+def _integer_pool(fmt):
+    """Magnitude codes whose value is an integer (found from the independent
+    tables)."""
+    t = golden_e2m1()[:8] if fmt == E2M1 else torch_e4m3()[:127]
+    return [c for c in range(len(t)) if float(t[c]).is_integer()]
+
+
+def pin_integer_exact(orc):
+    for fmt, K in ((E2M1, 256), (E4M3, 384)):
+        pool = _integer_pool(fmt)
+        A, As = mxinputs.random_codes(fmt, 9, K, 11, pool, tensor=0)
+        B, Bs = mxinputs.random_codes(fmt, 7, K, 11, pool, tensor=1)
+        ia = decode_rows(fmt, A).astype(np.int64)
+        ib = decode_rows(fmt, B).astype(np.int64)
+        ref = ia @ ib.T
+        C, T = orc.gemm(fmt, A, As, B, Bs, K)
+        assert np.array_equal(C, ref.astype(np.float64)), fmt
+        assert np.array_equal(T, (np.abs(ia) @ np.abs(ib).T).astype(np.float64)), fmt
+
+
+def pin_scale_shift(orc):
+    for fmt in (E2M1, E4M3):
+        case = mxinputs.make_random(fmt, 3, 4, 256, seed=3)
+        A, As, B, Bs, K = case["A"], case["A_scale"], case["B"], case["B_scale"], 256
+        base = {(m, n, b): orc.block_contrib(fmt, A, As, B, Bs, K, m, n, b)
+                for m in range(3) for n in range(4) for b in range(K // 32)}
+        for (side, row, blk, k) in (("a", 1, 2, 5), ("b", 3, 7, -9), ("a", 0, 0, 1)):
+            As2, Bs2 = As.copy(), Bs.copy()
+            if side == "a":
+                As2[row, blk] = int(As2[row, blk]) + k
+            else:
+                Bs2[row, blk] = int(Bs2[row, blk]) + k
+            for key, (c0, t0) in base.items():
+                c1, t1 = orc.block_contrib(fmt, A, As2, B, Bs2, K, *key)
+                m, n, b = key
+                hit = b == blk and ((side == "a" and m == row) or (side == "b" and n == row))
+                f = 2.0 ** k if hit else 1.0
+                assert c1 == c0 * f and t1 == t0 * f, (fmt, side, key)
+            # The whole sum moves by exactly (2^k - 1) * that block's term, up to
+            # the final double rounding of the block sum.
+            C0, T0 = orc.gemm(fmt, A, As, B, Bs, K)
+            C1, _ = orc.gemm(fmt, A, As2, B, Bs2, K)
+            if side == "a":
+                delta = np.array([[base[(row, n, blk)][0] * (2.0 ** k - 1) for n in range(4)]])
+                got = C1[row:row + 1] - C0[row:row + 1]
+                tol = 1e-14 * (T0[row:row + 1] * max(1.0, 2.0 ** k))
+            else:
+                delta = np.array([[base[(m, row, blk)][0] * (2.0 ** k - 1)] for m in range(3)])
+                got = C1[:, row:row + 1] - C0[:, row:row + 1]
+                tol = 1e-14 * (T0[:, row:row + 1] * max(1.0, 2.0 ** k))
+            assert np.all(np.abs(got - delta) <= tol), (fmt, side)
+
+
+def pin_numpy_matmul(orc):
+    for fmt in (E2M1, E4M3):
+        case = mxinputs.make_random(fmt, 64, 48, 512, seed=5)
+        A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+        ref = dequant(fmt, A, As) @ dequant(fmt, B, Bs).T
+        C, T = orc.gemm(fmt, A, As, B, Bs, 512)
+        assert np.all(np.abs(C - ref) <= 1e-12 * T), fmt
+        tref = np.abs(dequant(fmt, A, As)) @ np.abs(dequant(fmt, B, Bs)).T
+        assert np.all(np.abs(T - tref) <= 1e-12 * T), fmt
+
+
+def pin_symmetry(orc):
+    for fmt in (E2M1, E4M3):
+        case = mxinputs.make_random(fmt, 5, 7, 256, seed=9, scale_lo=90, scale_hi=160)
+        A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+        C, T = orc.gemm(fmt, A, As, B, Bs, 256)
+        Ct, Tt = orc.gemm(fmt, B, Bs, A, As, 256)
+        assert np.array_equal(C, Ct.T) and np.array_equal(T, Tt.T), fmt
+
+
+def pin_zero_and_onehot(orc):
+    for fmt in (E2M1, E4M3):
+        K = 256
+        rb = K // 2 if fmt == E2M1 else K
+        A = np.zeros((2, rb), np.uint8)
+        B = np.zeros((3, rb), np.uint8)
+        As = np.full((2, K // 32), 140, np.uint8)
+        Bs = np.full((3, K // 32), 90, np.uint8)
+        C, T = orc.gemm(fmt, A, As, B, Bs, K)
+        assert not C.any() and not T.any()
+        # one nonzero element in A[1] and B[2] at the same k = 77 (block 2)
+        k = 77
+        if fmt == E2M1:
+            A[1, k // 2] = 0x7 << 4          # odd k -> high nibble, 6.0
+            B[2, k // 2] = 0xB << 4          # -1.5
+            va, vb = 6.0, -1.5
+        else:
+            A[1, k] = 0x7E                   # 448
+            B[2, k] = 0x81                   # -2^-9
+            va, vb = 448.0, -(2.0 ** -9)
+        As[1, 2], Bs[2, 2] = 150, 60
+        C, T = orc.gemm(fmt, A, As, B, Bs, K)
+        expect = np.zeros((2, 3))
+        expect[1, 2] = va * vb * 2.0 ** (150 + 60 - 254)
+        assert np.array_equal(C, expect), fmt
+        assert np.array_equal(T, np.abs(expect)), fmt
+
+
+def pin_nan(orc):
+    for fmt in (E2M1, E4M3):
+        case = mxinputs.make_random(fmt, 3, 3, 128, seed=2)
+        A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+        As = As.copy()
+        As[1, 3] = 255
+        C, _ = orc.gemm(fmt, A, As, B, Bs, 128)
+        assert np.all(np.isnan(C[1])) and not np.isnan(C[[0, 2]]).any(), fmt
+        c, t = orc.block_contrib(fmt, A, As, B, Bs, 128, 1, 0, 3)
+        assert np.isnan(c) and np.isnan(t), fmt
+        c, t = orc.block_contrib(fmt, A, As, B, Bs, 128, 1, 0, 2)
+        assert not np.isnan(c) and not np.isnan(t), fmt
+    A = np.zeros((2, 128), np.uint8)
+    A[0, 5] = 0x7F
+    B = np.full((2, 128), 0x38, np.uint8)
+    s = np.full((2, 4), 127, np.uint8)
+    C, _ = orc.gemm(E4M3, A, s, B, s, 128)
+    assert np.all(np.isnan(C[0])) and np.all(C[1] == 0)
+
+
+def pin_row_subset(orc):
+    case = mxinputs.make_random(E2M1, 40, 6, 128, seed=4)
+    A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+    C, T = orc.gemm(E2M1, A, As, B, Bs, 128)
+    rows = [39, 0, 17, 17]
+    Cs, Ts = orc.gemm(E2M1, A, As, B, Bs, 128, rows=rows)
+    assert np.array_equal(Cs, C[rows]) and np.array_equal(Ts, T[rows])
+
+
+ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
+            pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
+            pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset]

@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that the pins in oracle_pins.py catch every one of them."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mx_oracle.c")
+
+# (name, original text, planted mistake).  Swapping the nibble order inside
+# decode_elem is not listed: it permutes K within a 32-block identically for
+# A and B, which leaves every block dot product, and so C and T, unchanged.
+MUTANTS = [
+    ("b_pair_swap", "bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);",
+     "bdec[k] = decode_elem(fmt, B + n * rb, k ^ 1, t4, t8);"),
+    ("scale_bias", "pow2[i] = ldexp(1.0, i - 254)", "pow2[i] = ldexp(1.0, i - 253)"),
+    ("b_scale_from_a", "unsigned sa = sarow[b], sb = sbrow[b];",
+     "unsigned sa = sarow[b], sb = sarow[b];"),
+    ("scale_block_index", "unsigned sa = sarow[b], sb = sbrow[b];",
+     "unsigned sa = sarow[b], sb = sbrow[nb - 1 - b];"),
+    ("dropped_term", "j < 32 * b + 32; ++j)", "j < 32 * b + 31; ++j)"),
+    ("e4m3_bias", "ldexp(1.0 + (double)m / 8.0, (int)e - 7)",
+     "ldexp(1.0 + (double)m / 8.0, (int)e - 8)"),
+    ("e4m3_subnormal", "ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
+    ("e4m3_nan", "if (e == 15 && m == 7) return NAN;", ""),
+    ("e2m1_subnormal", "0.5 * (double)m : ldexp", "1.0 * (double)m : ldexp"),
+    ("e2m1_sign", "    return s ? -mag : mag;\n}\n\n/* E4M3",
+     "    return mag;\n}\n\n/* E4M3"),
+    ("e2m1_bias", "ldexp(1.0 + 0.5 * (double)m, (int)e - 1)",
+     "ldexp(1.0 + 0.5 * (double)m, (int)e)"),
+    ("magnitude_not_abs", "q += fabs(prod);", "q += prod;"),
+    ("scale_nan_ignored", "double w = (sa == 255 || sb == 255) ? NAN : pow2[sa + sb];",
+     "double w = pow2[sa + sb];"),
+    ("e8m0_bias", "return ldexp(1.0, (int)byte - 127);", "return ldexp(1.0, (int)byte - 128);"),
+    ("row_index", "int64_t m = rows ? rows[i0 + i] : i0 + i;\n                    const",
+     "int64_t m = rows ? rows[i0] : i0 + i;\n                    const"),
+    ("b_row_stride", "bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);",
+     "bdec[k] = decode_elem(fmt, B + n * (rb - 1), k, t4, t8);"),
+]
+
+
+def test_mutations_are_distinct_and_apply():
+    src = open(SRC).read()
+    for name, old, new in MUTANTS:
+        assert src.count(old) >= 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert old in src
+    mutated = src.replace(old, new)
+    c = tmp_path / "mut.c"
+    so = tmp_path / "libmut.so"
+    c.write_text(mutated)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    "-w", str(c), "-o", str(so), "-lm"], check=True)
+    mut = oracle.Oracle(str(so))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mut)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin caught mutant %s" % name
