@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the MX block-scaled NT GEMM on one MI355X.
+
+One step = one mx_gemm call (C = A * B^T, MX block-scaled) over a synthetic,
+already-quantized workload resident in HBM; quantization is outside the
+timed region, as in the measurements the FlyDSL article reports (section
+"Performance numbers need their baselines").  The default workload is the
+MXFP8 Llama-3.1-8B fused-QKV projection, M=2048, N=6144, K=4096, BF16 out.
+
+Prints one JSON line: whole-job TFLOP/s over exactly --steps timed steps,
+the dominant kernel's roofline position (achieved vs the MI355X dense MX
+MFMA peak, from HIP events around every launch on the launch stream), and
+the CPU oracle's rate on a bounded row sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mxinputs  # noqa: E402
+
+DEFAULT_WORKLOAD = "mxfp8_llama8b_qkv"
+METRIC = "MX GEMM TFLOPS and % of MI355X dense MXFP4/MXFP8 MFMA peak per shape"
+# MI355X published dense peaks: MXFP4 10.1 PFLOP/s, MXFP8 5.0 PFLOP/s; HBM3E 8 TB/s.
+PEAK_TFLOPS = {mxinputs.FMT_E2M1: 10100.0, mxinputs.FMT_E4M3: 5000.0}
+PEAK_HBM_GBS = 8000.0
+# Ridge points (FLOP per byte) above which the MFMA, not HBM, bounds a shape.
+RIDGE = {f: PEAK_TFLOPS[f] * 1e12 / (PEAK_HBM_GBS * 1e9) for f in PEAK_TFLOPS}
+KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "microscaled_block_scaled_amd", "csrc", "*")))
+
+
+def algorithmic_bytes(fmt, M, N, K, out):
+    """Compulsory HBM traffic: A, B and their scales read once, C written once."""
+    eb = K // 2 if fmt == mxinputs.FMT_E2M1 else K
+    return (M + N) * eb + (M + N) * (K // 32) + M * N * (4 if out == mxinputs.OUT_FP32 else 2)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(case, target_s=12.0):
+    """The CPU oracle on a row sample of the same workload (all N columns)."""
+    import numpy as np
+    import oracle
+    threads = cpu_threads()
+    M, N, K, fmt = case["M"], case["N"], case["K"], case["fmt"]
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.gemm(fmt, case["A"], case["A_scale"], case["B"], case["B_scale"], K,
+                    rows=rows, threads=threads)
+        return time.perf_counter() - t0
+
+    r0 = min(M, 4)
+    t0 = run(np.arange(r0))
+    nrows = int(max(r0, min(M, r0 * target_s / max(t0, 1e-6))))
+    rows = np.linspace(0, M - 1, nrows).astype(np.int64)
+    t = run(rows)
+    flops = 2.0 * nrows * N * K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d rows of A (all %d columns, K=%d), %.1f s on %d threads"
+                      % (nrows, M, N, K, t, threads)}
+
+
+def bench_one(name, steps, warmup, with_cpu):
+    import torch
+    import microscaled_block_scaled_amd as mxg
+
+    case = mxinputs.make_case(name)
+    fmt, M, N, K, out = case["fmt"], case["M"], case["N"], case["K"], case["out"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
+    C = torch.empty((M, N), dtype=torch.float32 if out == mxinputs.OUT_FP32 else torch.bfloat16,
+                    device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    args = (fmt, M, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
+            C.data_ptr(), out, sh)
+
+    def step():
+        rc = mxg.gemm_ptr(*args)
+        if rc != 0:
+            raise RuntimeError("mx_gemm failed: %s" % mxg.strerror(rc))
+
+    for _ in range(warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    flops = 2.0 * M * N * K
+    nbytes = algorithmic_bytes(fmt, M, N, K, out)
+    tflops = flops * steps / wall / 1e12
+    bound = "mfma" if flops / nbytes >= RIDGE[fmt] else "hbm"
+    traffic = measured_traffic(name)
+    if bound == "mfma":
+        achieved = flops / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[fmt],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[fmt], 4)}
+    else:
+        achieved = nbytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = traffic
+    roof["algorithmic_bytes"] = nbytes
+    roof["launch_us"] = round(avg_launch_s * 1e6, 2)
+    plan = mxg.plan(fmt, M, N, K, out)
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8_e4m3" if fmt == mxinputs.FMT_E4M3 else "mxfp4_e2m1",
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "N": N, "K": K,
+                   "format": mxinputs.fmt_name(fmt),
+                   "out": "fp32" if out == mxinputs.OUT_FP32 else "bf16",
+                   "accumulate": "fp32", "peak_frac": round(tflops / PEAK_TFLOPS[fmt], 4),
+                   "plan": "variant %d tile %dx%d split %d, %d workgroups" % (
+                       plan["variant"], plan["tile_m"], plan["tile_n"], plan["split_k"],
+                       plan["workgroups"]),
+                   "kernel_source_sha256": kernel_source_hash()},
+        "roofline": roof,
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(case)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(mxinputs.CONFIGS))
+    ap.add_argument("--all", action="store_true",
+                    help="one line per workload (no CPU baseline except the default one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
+                         "multi-GPU component (each GPU would run its own shard "
+                         "independently); use --gpus 1.\n")
+        sys.exit(2)
+    names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \
+        if a.all else [a.workload]
+    for name in names:
+        with_cpu = (not a.no_cpu_baseline) and name == a.workload
+        print(json.dumps(bench_one(name, a.steps, a.warmup, with_cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,123 @@
+/*
+ * mxgemm.h -- C ABI of the MI355X (gfx950) MX block-scaled NT GEMM.
+ *
+ * The operation (FlyDSL summary pages, section "API compatibility is not
+ * universal input coverage"; AI-compiler digest 2026-10-22, item 1
+ * "Accelerating PyTorch on AMD GPUs with FlyDSL": MXFP8 / MXFP4 scaled GEMM,
+ * BlockWise1x32, E8M0 scale, FP32 accumulation, K a multiple of 128):
+ *
+ *   C[m][n] = sum_b 2^(sA[m][b] + sB[n][b] - 254)
+ *                   * sum_{j<32} A[m][32b+j] * B[n][32b+j]
+ *
+ * for m < M, n < N, b < K/32, with A and B holding MXFP4 (E2M1) or MXFP8
+ * (E4M3) elements and sA, sB their E8M0 scale bytes.  Products and sums are
+ * accumulated in FP32; C is written as FP32 or as BF16 (round to nearest
+ * even).  The element and scale encodings are those of the OCP Microscaling
+ * (MX) v1.0 specification.
+ *
+ * Memory layout (all dense, row-major, device memory owned by the caller):
+ *   A        M x K   elements, K-contiguous.  E4M3: M x K bytes, element k in
+ *            byte k.  E2M1: M x K/2 bytes, element 2i in the low nibble of
+ *            byte i, element 2i+1 in the high nibble.
+ *   B        N x K   elements, K-contiguous, same encoding as A ("NT": C is
+ *            A times B transposed).
+ *   A_scale  M x K/32 bytes; byte [m][b] scales K-values 32b .. 32b+31 of row m.
+ *   B_scale  N x K/32 bytes; likewise for B.
+ *   C        M x N  float or bfloat16 (uint16 bit pattern), row pitch N.
+ * There are no stride arguments: callers with other layouts must copy.
+ *
+ * Errors.  Every argument check runs before any HIP call; a failed check
+ * returns a negative MX_ERR_* code and touches nothing.  Launch failures are
+ * reported as MX_ERR_LAUNCH.  No function aborts or throws.
+ *
+ * Asynchrony.  mx_gemm enqueues its kernels on `stream` (a hipStream_t;
+ * NULL means the device's null stream) and returns without synchronising:
+ * C is ready when the stream reaches that point.  Inputs must stay alive and
+ * unmodified until then.  C must not overlap any input.  Results are
+ * bit-for-bit deterministic for a given (M, N, K, formats, device).
+ *
+ * Thread safety.  Calls may be made concurrently from several host threads
+ * and streams; the library keeps only read-only per-device state, set up
+ * once per device on first use.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats (MXFP4 = E2M1, MXFP8 = E4M3). */
+enum { MX_FMT_E2M1 = 1, MX_FMT_E4M3 = 2 };
+
+/* Output element types. */
+enum { MX_OUT_FP32 = 1, MX_OUT_BF16 = 2 };
+
+/* Return codes. */
+enum {
+    MX_OK = 0,
+    MX_ERR_FORMAT = -1,     /* fmt is not MX_FMT_E2M1 / MX_FMT_E4M3          */
+    MX_ERR_OUT_DTYPE = -2,  /* out_dtype is not MX_OUT_FP32 / MX_OUT_BF16     */
+    MX_ERR_SHAPE = -3,      /* M < 1, N < 1, K < 128, K % 128 != 0, or a
+                               dimension above MX_MAX_DIM                      */
+    MX_ERR_NULL = -4,       /* a required pointer is NULL                     */
+    MX_ERR_ALIGN = -5,      /* A, B or C not 16-byte aligned, or a scale
+                               array not 4-byte aligned                        */
+    MX_ERR_NO_DEVICE = -6,  /* no HIP device is visible                       */
+    MX_ERR_ARCH = -7,       /* the current device is not gfx950               */
+    MX_ERR_ALLOC = -8,      /* workspace allocation failed                    */
+    MX_ERR_LAUNCH = -9      /* a kernel launch failed                         */
+};
+
+/* Largest M, N or K accepted (keeps every tile index in 32 bits). */
+#define MX_MAX_DIM ((int64_t)1 << 30)
+
+/*
+ * C = A * B^T with MX block scaling, enqueued on `stream`.
+ *   fmt        MX_FMT_E2M1 or MX_FMT_E4M3 (A and B share the format)
+ *   M, N, K    sizes; K a multiple of 128
+ *   A, B       packed elements (layout above), 16-byte aligned device pointers
+ *   A_scale,
+ *   B_scale    E8M0 scale bytes (layout above), 4-byte aligned
+ *   C          output, 16-byte aligned; float if out_dtype == MX_OUT_FP32,
+ *              bfloat16 bits if MX_OUT_BF16
+ *   stream     hipStream_t, or NULL
+ * Returns MX_OK or a negative MX_ERR_* code.
+ */
+int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
+            const void *A, const void *A_scale,
+            const void *B, const void *B_scale,
+            void *C, int out_dtype, void *stream);
+
+/* Static, NUL-terminated description of a return code. */
+const char *mx_strerror(int code);
+
+/* Kernel variants a plan can choose. */
+enum { MX_VARIANT_TILE = 1, MX_VARIANT_DECODE = 2 };
+
+/* How mx_gemm would run a problem (filled by mx_gemm_plan). */
+typedef struct {
+    int variant;            /* MX_VARIANT_*                                   */
+    int tile_m, tile_n;     /* output tile of one workgroup                   */
+    int split_k;            /* K slices reduced in a second pass (1 = none)   */
+    int threads;            /* threads per workgroup                          */
+    int lds_bytes;          /* dynamic LDS per workgroup                      */
+    int64_t workgroups;     /* workgroups in the main launch                  */
+    int64_t workspace_bytes;/* device scratch the call allocates (0 = none)   */
+} mx_plan_t;
+
+/*
+ * Fill *plan with the launch mx_gemm would make for these arguments.  Pure
+ * host logic: it makes no HIP call and does not need a device.  Returns
+ * MX_OK, or the same argument error mx_gemm would return.
+ */
+int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype,
+                 mx_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

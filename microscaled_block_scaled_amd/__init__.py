@@ -1,0 +1,162 @@
+"""Python binding of libmxgemm.so, the gfx950 MX block-scaled NT GEMM.
+
+Argument marshalling only: every step of the GEMM runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no
+fallback: if the library is missing, or the device is not a gfx950, calls
+raise.
+
+    C = mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=torch.bfloat16)
+
+a: (M, K/2) uint8 for MXFP4 (E2M1, two elements per byte, element 2i in the
+   low nibble), or (M, K) uint8 / float8_e4m3fn for MXFP8 (E4M3);
+b: (N, ...) likewise; a_scale: (M, K/32) uint8 E8M0; b_scale: (N, K/32).
+Returns C = A * B^T, (M, N), float32 or bfloat16.
+"""
+import ctypes
+import os
+
+FMT_E2M1 = 1
+FMT_E4M3 = 2
+OUT_FP32 = 1
+OUT_BF16 = 2
+VARIANT_TILE = 1
+VARIANT_DECODE = 2
+
+MX_OK = 0
+MX_ERR_FORMAT = -1
+MX_ERR_OUT_DTYPE = -2
+MX_ERR_SHAPE = -3
+MX_ERR_NULL = -4
+MX_ERR_ALIGN = -5
+MX_ERR_NO_DEVICE = -6
+MX_ERR_ARCH = -7
+MX_ERR_ALLOC = -8
+MX_ERR_LAUNCH = -9
+
+_VALUE_ERRORS = (MX_ERR_FORMAT, MX_ERR_OUT_DTYPE, MX_ERR_SHAPE, MX_ERR_NULL, MX_ERR_ALIGN)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxgemm.so")
+_lib = None
+
+
+class MxPlan(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("tile_m", ctypes.c_int),
+                ("tile_n", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+def lib():
+    """The loaded libmxgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libmxgemm.so is not built; run microscaled_block_scaled_amd/build.py "
+            "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    L.mx_gemm.restype = ctypes.c_int
+    L.mx_gemm.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp,
+                          ctypes.c_int, vp]
+    L.mx_strerror.restype = ctypes.c_char_p
+    L.mx_strerror.argtypes = [ctypes.c_int]
+    L.mx_gemm_plan.restype = ctypes.c_int
+    L.mx_gemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_int,
+                               ctypes.POINTER(MxPlan)]
+    _lib = L
+    return L
+
+
+def strerror(code):
+    return lib().mx_strerror(int(code)).decode()
+
+
+def _raise(code):
+    msg = "mx_gemm: %s (code %d)" % (strerror(code), code)
+    if code in _VALUE_ERRORS:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def plan(fmt, M, N, K, out_dtype=OUT_BF16):
+    """How the library would run this problem (a dict); host logic only."""
+    p = MxPlan()
+    rc = lib().mx_gemm_plan(int(fmt), int(M), int(N), int(K), int(out_dtype),
+                            ctypes.byref(p))
+    if rc != MX_OK:
+        _raise(rc)
+    return p.as_dict()
+
+
+def gemm_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0):
+    """Raw entry point: integer device addresses, returns the status code."""
+    return lib().mx_gemm(int(fmt), int(M), int(N), int(K), A, A_scale, B,
+                         B_scale, C, int(out_dtype), stream or None)
+
+
+def _out_code(out_dtype):
+    import torch
+    if out_dtype in (torch.float32, OUT_FP32):
+        return OUT_FP32, torch.float32
+    if out_dtype in (torch.bfloat16, OUT_BF16):
+        return OUT_BF16, torch.bfloat16
+    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _as_u8(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu,
+                       getattr(torch, "float4_e2m1fn_x2", torch.uint8)):
+        raise ValueError("%s must hold bytes (uint8 or an 8-bit float view), got %s"
+                         % (name, t.dtype))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (no stride arguments; copy first)" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    return t
+
+
+def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None):
+    """C = A * B^T for MX-quantized A (M x K) and B (N x K); see module doc."""
+    import torch
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if fmt not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    code, tdt = _out_code(out_dtype)
+    a, b = _as_u8(a, "a"), _as_u8(b, "b")
+    a_scale, b_scale = _as_u8(a_scale, "a_scale"), _as_u8(b_scale, "b_scale")
+    M, N = a.shape[0], b.shape[0]
+    per = 2 if fmt == FMT_E2M1 else 1
+    K = a.shape[1] * per
+    if b.shape[1] * per != K:
+        raise ValueError("a and b disagree on K")
+    if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (N, K // 32):
+        raise ValueError("scales must be (rows, K/32) = (%d, %d) and (%d, %d)"
+                         % (M, K // 32, N, K // 32))
+    dev = a.device
+    for t in (b, a_scale, b_scale):
+        if t.device != dev:
+            raise ValueError("all operands must be on the same device")
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=dev)
+    elif out.dtype != tdt or tuple(out.shape) != (M, N) or not out.is_contiguous() \
+            or out.device != dev:
+        raise ValueError("out must be a contiguous (M, N) %s tensor on %s" % (tdt, dev))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = gemm_ptr(fmt, M, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
+                      b_scale.data_ptr(), out.data_ptr(), code, stream)
+    if rc != MX_OK:
+        _raise(rc)
+    return out

@@ -1,0 +1,135 @@
+// mxgemm.hip -- host side of the C ABI declared in include/mxgemm.h:
+// argument checks (all before any HIP call), one-time per-device checks,
+// the launch plan, and the kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "mxgemm.h"
+#include "mx_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
+{
+    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3) return MX_ERR_FORMAT;
+    if (out_dtype != MX_OUT_FP32 && out_dtype != MX_OUT_BF16) return MX_ERR_OUT_DTYPE;
+    // K a multiple of 128 (FlyDSL article, "API compatibility is not
+    // universal input coverage").
+    if (M < 1 || N < 1 || K < 128 || K % 128 != 0) return MX_ERR_SHAPE;
+    if (M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
+    return MX_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Plan: which kernel, which tile, how many workgroups.
+int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)
+{
+    int rc = check_args(fmt, M, N, K, out_dtype);
+    if (rc != MX_OK) return rc;
+    memset(p, 0, sizeof(*p));
+    p->variant = MX_VARIANT_TILE;
+    p->tile_m = 128;
+    p->tile_n = 128;
+    p->split_k = 1;
+    p->threads = 256;
+    p->lds_bytes = 0;
+    p->workgroups = ((M + p->tile_m - 1) / p->tile_m) * ((N + p->tile_n - 1) / p->tile_n);
+    p->workspace_bytes = 0;
+    return MX_OK;
+}
+
+// Per-device one-time check: the device must be a gfx950.
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_status[kMaxDevices];
+
+int device_ready(int *dev_out)
+{
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) return MX_ERR_NO_DEVICE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MX_ERR_NO_DEVICE;
+    if (dev >= kMaxDevices) return MX_ERR_ARCH;
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            g_dev_status[dev] = MX_ERR_NO_DEVICE;
+            return;
+        }
+        g_dev_status[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? MX_OK : MX_ERR_ARCH;
+    });
+    *dev_out = dev;
+    return g_dev_status[dev];
+}
+
+template <int FMT, int OUT>
+void launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
+                 const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
+                 hipStream_t stream)
+{
+    const int tiles_n = (int)((N + p.tile_n - 1) / p.tile_n);
+    hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, 128, 128, 2, 2>),
+                       dim3((unsigned)p.workgroups), dim3(p.threads), 0, stream,
+                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
+                       (const uint8_t *)Bs, C, (int)M, (int)N, (int)K, tiles_n);
+}
+
+}  // namespace
+
+extern "C" const char *mx_strerror(int code)
+{
+    switch (code) {
+    case MX_OK: return "success";
+    case MX_ERR_FORMAT: return "unsupported element format (expected MX_FMT_E2M1 or MX_FMT_E4M3)";
+    case MX_ERR_OUT_DTYPE: return "unsupported output type (expected MX_OUT_FP32 or MX_OUT_BF16)";
+    case MX_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 128, K % 128 == 0, all <= 2^30)";
+    case MX_ERR_NULL: return "null pointer argument";
+    case MX_ERR_ALIGN: return "misaligned pointer (A, B, C need 16 bytes; scales need 4)";
+    case MX_ERR_NO_DEVICE: return "no HIP device available";
+    case MX_ERR_ARCH: return "current device is not gfx950";
+    case MX_ERR_ALLOC: return "workspace allocation failed";
+    case MX_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+    }
+}
+
+extern "C" int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype,
+                            mx_plan_t *plan)
+{
+    if (!plan) return MX_ERR_NULL;
+    return make_plan(fmt, M, N, K, out_dtype, plan);
+}
+
+extern "C" int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
+                       const void *A, const void *A_scale,
+                       const void *B, const void *B_scale,
+                       void *C, int out_dtype, void *stream)
+{
+    mx_plan_t plan;
+    int rc = make_plan(fmt, M, N, K, out_dtype, &plan);
+    if (rc != MX_OK) return rc;
+    if (!A || !A_scale || !B || !B_scale || !C) return MX_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
+        !aligned(A_scale, 4) || !aligned(B_scale, 4))
+        return MX_ERR_ALIGN;
+    int dev = -1;
+    rc = device_ready(&dev);
+    if (rc != MX_OK) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();  // clear any stale error so the check below is ours
+    if (fmt == MX_FMT_E2M1) {
+        if (out_dtype == MX_OUT_FP32) launch_tile<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+        else launch_tile<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+    } else {
+        if (out_dtype == MX_OUT_FP32) launch_tile<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+        else launch_tile<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+    }
+    if (hipGetLastError() != hipSuccess) return MX_ERR_LAUNCH;
+    return MX_OK;
+}

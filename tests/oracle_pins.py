@@ -295,6 +295,64 @@ def pin_row_subset(orc):
     assert np.array_equal(Cs, C[rows]) and np.array_equal(Ts, T[rows])
 
 
+def _group_bound_numpy(fmt, A, As, B, Bs, K):
+    """E recomputed from its definition with numpy and the independent
+    tables: per aligned group of 8 K-values, the scaled sum of |p| mod
+    2^(floor(log2 max|p|) - 12)."""
+    va, vb = decode_rows(fmt, A), decode_rows(fmt, B)
+    M, N = va.shape[0], vb.shape[0]
+    E = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            p = (va[m] * vb[n]).reshape(-1, 8)
+            w = np.repeat(np.ldexp(1.0, As[m].astype(np.int64) + Bs[n].astype(np.int64) - 254), 4)
+            mx = np.abs(p).max(axis=1)
+            tot = 0.0
+            for gi in range(p.shape[0]):
+                if mx[gi] == 0:
+                    continue
+                grid = 2.0 ** (math.floor(math.log2(mx[gi])) - 12)
+                tot += w[gi] * float(np.sum(np.fmod(np.abs(p[gi]), grid)))
+            E[m, n] = tot
+    return E
+
+
+def pin_group_bound(orc):
+    # Closed forms: products {2^8, 7 x 2^-6} in one group: grid 2^-4, each
+    # 2^-6 lies wholly below it -> E = 7 * 2^-6.  With every small product a
+    # multiple of the grid (2^-4), E = 0.  Scale 2^(sA+sB-254) multiplies E.
+    K = 128
+    A = np.zeros((1, K), np.uint8)
+    B = np.zeros((1, K), np.uint8)
+    A[0, 8] = 0x78                        # 2^8 (E4M3 e=15, m=0)
+    B[0, 8:16] = 0x38                     # 1.0
+    for code, val, expect_mult in ((0x08, 2.0 ** -6, 7), (0x18, 2.0 ** -4, 0)):
+        A[0, 9:16] = code                 # 0x08 = 2^-6, 0x18 = 2^-4
+        for sa, sb in ((127, 127), (130, 120)):
+            As = np.full((1, 4), sa, np.uint8)
+            Bs = np.full((1, 4), sb, np.uint8)
+            C, T, E = orc.gemm(E4M3, A, As, B, Bs, K, group_bound=True)
+            assert E[0, 0] == expect_mult * val * 2.0 ** (sa + sb - 254), (code, sa, sb, E[0, 0])
+    # E2M1: every product is a multiple of 1/4 and the grid is at most 2^-7.
+    case = mxinputs.make_random(E2M1, 6, 5, 512, seed=21)
+    _, _, E = orc.gemm(E2M1, case["A"], case["A_scale"], case["B"], case["B_scale"], 512,
+                       group_bound=True)
+    assert not E.any()
+    # Random E4M3 with wide exponents: equal to the numpy recomputation.
+    for seed in (1, 2):
+        pool = range(127)
+        A, _ = mxinputs.random_codes(E4M3, 3, 256, 40 + seed, pool, tensor=0)
+        B, _ = mxinputs.random_codes(E4M3, 4, 256, 40 + seed, pool, tensor=1)
+        r = np.random.default_rng([9, seed])
+        As = r.integers(110, 145, size=(3, 8)).astype(np.uint8)
+        Bs = r.integers(110, 145, size=(4, 8)).astype(np.uint8)
+        _, T, E = orc.gemm(E4M3, A, As, B, Bs, 256, group_bound=True)
+        ref = _group_bound_numpy(E4M3, A, As, B, Bs, 256)
+        assert np.all(np.abs(E - ref) <= 1e-12 * T), seed
+        assert E.any()
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
-            pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset]
+            pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
+            pin_group_bound]

@@ -1,0 +1,116 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import microscaled_block_scaled_amd as mxg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"mx_gemm", "mx_strerror", "mx_gemm_plan"} <= set(names)
+    L = mxg.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"\b(MX_[A-Z0-9_]+)\s*=\s*(-?\d+)", src))
+    for k, v in consts.items():
+        short = k[3:]
+        if hasattr(mxg, short):
+            assert getattr(mxg, short) == v, k
+        elif hasattr(mxg, k):
+            assert getattr(mxg, k) == v, k
+    assert consts["MX_FMT_E2M1"] == mxg.FMT_E2M1 and consts["MX_OUT_BF16"] == mxg.OUT_BF16
+
+
+def test_strerror_covers_codes():
+    for code in range(-9, 1):
+        s = mxg.strerror(code)
+        assert s and s != "unknown error code", code
+    assert mxg.strerror(5) == "unknown error code"
+
+
+@pytest.mark.parametrize("fmt,M,N,K,out,code", [
+    (0, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
+    (3, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
+    (1, 16, 16, 128, 0, mxg.MX_ERR_OUT_DTYPE),
+    (2, 16, 16, 128, 7, mxg.MX_ERR_OUT_DTYPE),
+    (1, 0, 16, 128, 1, mxg.MX_ERR_SHAPE),
+    (1, 16, 0, 128, 1, mxg.MX_ERR_SHAPE),
+    (1, 16, 16, 0, 1, mxg.MX_ERR_SHAPE),
+    (1, 16, 16, 64, 1, mxg.MX_ERR_SHAPE),
+    (2, 16, 16, 100, 1, mxg.MX_ERR_SHAPE),
+    (2, 16, 16, 192, 2, mxg.MX_ERR_SHAPE),
+    (2, 16, 16, -128, 2, mxg.MX_ERR_SHAPE),
+    (2, (1 << 30) + 1, 16, 128, 2, mxg.MX_ERR_SHAPE),
+])
+def test_argument_errors(fmt, M, N, K, out, code):
+    L = mxg.lib()
+    p = mxg.MxPlan()
+    assert L.mx_gemm_plan(fmt, M, N, K, out, ctypes.byref(p)) == code
+    # Same code from mx_gemm, before any pointer is looked at or HIP called.
+    assert L.mx_gemm(fmt, M, N, K, None, None, None, None, None, out, None) == code
+
+
+def test_null_and_alignment_errors():
+    L = mxg.lib()
+    good = 1 << 20            # never dereferenced: checks fail first
+    args = [good, good, good, good, good]
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert L.mx_gemm(1, 16, 16, 128, *a[:4], a[4], 1, None) == mxg.MX_ERR_NULL
+    for i, mis in ((0, 8), (2, 4), (4, 2), (1, 2), (3, 1)):
+        a = list(args)
+        a[i] = good + mis
+        assert L.mx_gemm(1, 16, 16, 128, *a[:4], a[4], 1, None) == mxg.MX_ERR_ALIGN, i
+    assert L.mx_gemm_plan(1, 16, 16, 128, 1, None) == mxg.MX_ERR_NULL
+
+
+def test_no_device_reported():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible here")
+    good = 1 << 20
+    rc = mxg.lib().mx_gemm(2, 16, 16, 128, good, good, good, good, good, 2, None)
+    assert rc == mxg.MX_ERR_NO_DEVICE
+
+
+def test_plan_shapes():
+    p = mxg.plan(mxg.FMT_E4M3, 2048, 6144, 4096, mxg.OUT_BF16)
+    assert p["workgroups"] >= 1 and p["threads"] % 64 == 0
+    assert p["tile_m"] % 16 == 0 and p["tile_n"] % 16 == 0
+    tiles = -(-2048 // p["tile_m"]) * -(-6144 // p["tile_n"]) * p["split_k"]
+    assert p["workgroups"] == tiles
+    with pytest.raises(ValueError):
+        mxg.plan(mxg.FMT_E4M3, 16, 16, 100)
+
+
+def test_python_shim_rejects_bad_tensors():
+    import torch
+    a = torch.zeros((16, 64), dtype=torch.uint8)
+    s = torch.zeros((16, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mxg.mx_gemm(a, s, a, s, fmt=7)
+    with pytest.raises(ValueError):          # not on the GPU
+        mxg.mx_gemm(a, s, a, s, fmt=mxg.FMT_E2M1)
+    with pytest.raises(ValueError):          # float32 is not a byte type
+        mxg.mx_gemm(a.float(), s, a, s, fmt=mxg.FMT_E2M1)
+    with pytest.raises(ValueError):          # non-contiguous
+        mxg.mx_gemm(torch.zeros((16, 128), dtype=torch.uint8)[:, ::2], s, a, s,
+                    fmt=mxg.FMT_E2M1)

@@ -31,7 +31,12 @@ MUTANTS = [
      "    return mag;\n}\n\n/* E4M3"),
     ("e2m1_bias", "ldexp(1.0 + 0.5 * (double)m, (int)e - 1)",
      "ldexp(1.0 + 0.5 * (double)m, (int)e)"),
-    ("magnitude_not_abs", "q += fabs(prod);", "q += prod;"),
+    ("magnitude_not_abs", "q += fabs(prod[j - 32 * b]);", "q += prod[j - 32 * b];"),
+    ("group_grid_fine", "double grid = ldexp(1.0, (e - 1) - 12);",
+     "double grid = ldexp(1.0, (e - 1) - 20);"),
+    ("group_size_16", "for (int gi = 0; gi < 4; ++gi) loss += group_loss(prod + 8 * gi);",
+     "for (int gi = 0; gi < 2; ++gi) loss += group_loss(prod + 16 * gi);"),
+    ("group_loss_unscaled", "el += loss * w;", "el += loss;"),
     ("scale_nan_ignored", "double w = (sa == 255 || sb == 255) ? NAN : pow2[sa + sb];",
      "double w = pow2[sa + sb];"),
     ("e8m0_bias", "return ldexp(1.0, (int)byte - 127);", "return ldexp(1.0, (int)byte - 128);"),
