@@ -68,93 +68,105 @@ __device__ __forceinline__ v4f mma(const v8i &a, const v8i &b, v4f acc, int sa, 
         a, b, acc, mfma_fmt<FMT>::sel, mfma_fmt<FMT>::sel, 0, sa, 0, sb);
 }
 
+// Direct HBM -> LDS copies (gfx950 global_load_lds): lane l of the wave
+// writes its `size` bytes to lds + l * size; `lds` must be wave-uniform.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void g2l_16(const void *src, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l_4(const void *src, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs (bid % 8).
+// Give each XCD a contiguous run of tiles, walked in groups of `gm` M-tiles,
+// so the workgroups sharing an XCD's L2 also share A and B panels.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int gm,
+                                        int &tm, int &tn)
+{
+    const int ntiles = tiles_m * tiles_n;
+    int t = bid;
+    if ((ntiles & 7) == 0) t = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    const int per_group = gm * tiles_n;
+    const int grp = t / per_group, first_m = grp * gm;
+    const int gsz = min(tiles_m - first_m, gm);
+    const int w = t - grp * per_group;
+    tm = first_m + w % gsz;
+    tn = w / gsz;
+}
+
 // --------------------------------------------------------------------------
-// Tiled kernel: one workgroup computes a BM x BN tile of C; WGM x WGN waves
-// each own a (BM/WGM) x (BN/WGN) sub-tile of 16x16 accumulator fragments.
-// K is walked in 128-byte row segments, staged HBM -> registers -> LDS with
-// two LDS buffers: the global loads of segment s+1 are in flight while the
-// waves run the MFMAs of segment s.
+// Tiled kernel: one workgroup computes a BM x BN tile of C with WGM x WGN
+// waves, each owning a (BM/WGM) x (BN/WGN) block of 16x16 FP32 accumulators.
+// K is walked in 128-byte row segments (128 E4M3 or 256 E2M1 K-values).
+// Each segment of A, B and their scale bytes is copied HBM -> LDS directly
+// (no register staging) into one of two LDS stages; the copy of segment s+1
+// is in flight while the waves run segment s's MFMAs.  Rows are swizzled in
+// LDS (chunk c of row r stored at chunk c ^ swz(r)); the swizzle is applied
+// on the global side, since each lane's LDS slot is fixed by its lane id.
 template <int FMT, int OUT, int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
-            void *__restrict__ C, int M, int N, int K, int tiles_n)
+            void *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n, int gm)
 {
-    constexpr int NT = WGM * WGN * 64;
+    constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
-    constexpr int KV = seg<FMT>::kvals, SBY = seg<FMT>::sbytes;
-    constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;        // 16-B chunks per thread
-    constexpr int SDW = SBY / 4;                              // scale dwords per row
-    constexpr int SQ = (BM + BN) * SDW;                       // scale dwords per segment
-    constexpr int SQT = (SQ + NT - 1) / NT;
-    static_assert(CA * NT == BM * 8 && CB * NT == BN * 8, "tile / thread mismatch");
+    constexpr int KV = seg<FMT>::kvals, SBY = seg<FMT>::sbytes, SDW = SBY / 4;
+    constexpr int DATA = (BM + BN) * 128;                  // element bytes per stage
+    constexpr int SCALE_DW = (BM + BN) * SDW;              // scale dwords per stage
+    // Scale copies write whole 64-lane instructions (256 bytes each).
+    constexpr int STAGE = DATA + (SCALE_DW + 63) / 64 * 256;
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "rows per copy instruction");
     static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be 16-aligned");
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * 128];
-    __shared__ __attribute__((aligned(16))) uint8_t sS[2][(BM + BN) * 8];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;
     const int sp = K / 32;
     const int nseg = (K + KV - 1) / KV;
 
-    v4i ra[CA], rbv[CB];
-    uint32_t rs[SQT];
+    // Per-lane constant parts of the copy addresses.
+    const int crow = lane >> 3, cpc = lane & 7;   // row within an 8-row copy, LDS chunk
 
-    auto gload = [&](int s) {
+    auto issue = [&](int s, int stage) {
+        uint8_t *base = smem + stage * STAGE;
         const int64_t koff = (int64_t)s * 128;
 #pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            int q = tid + i * NT, r = q >> 3, c = q & 7;
-            int row = min(m0 + r, M - 1);
-            int64_t off = koff + c * 16;
-            ra[i] = (off < rowb) ? *(const v4i *)(A + (int64_t)row * rowb + off) : v4i{0, 0, 0, 0};
+        for (int i = wave; i < BM / 8; i += NW) {
+            const int r = i * 8 + crow;
+            const int row = min(m0 + r, M - 1);
+            int64_t off = koff + ((cpc ^ swz(r)) << 4);
+            off = min(off, rowb - 16);                 // E2M1 half segment: unused data
+            g2l_16(A + (int64_t)row * rowb + off, base + i * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            int q = tid + i * NT, r = q >> 3, c = q & 7;
-            int row = min(n0 + r, N - 1);
-            int64_t off = koff + c * 16;
-            rbv[i] = (off < rowb) ? *(const v4i *)(B + (int64_t)row * rowb + off) : v4i{0, 0, 0, 0};
+        for (int i = wave; i < BN / 8; i += NW) {
+            const int r = i * 8 + crow;
+            const int row = min(n0 + r, N - 1);
+            int64_t off = koff + ((cpc ^ swz(r)) << 4);
+            off = min(off, rowb - 16);
+            g2l_16(B + (int64_t)row * rowb + off, base + BM * 128 + i * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < SQT; ++i) {
-            int q = tid + i * NT;
-            uint32_t v = 0x7f7f7f7fu;
-            if (q < SQ) {
-                int r = q / SDW, part = q % SDW;
-                int soff = s * SBY + part * 4;
-                if (soff < sp) {
-                    if (r < BM) v = *(const uint32_t *)(As + (int64_t)min(m0 + r, M - 1) * sp + soff);
-                    else v = *(const uint32_t *)(Bs + (int64_t)min(n0 + r - BM, N - 1) * sp + soff);
-                }
-            }
-            rs[i] = v;
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            int q = tid + i * NT, r = q >> 3, c = q & 7;
-            *(v4i *)(&sA[buf][r * 128 + ((c ^ swz(r)) << 4)]) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            int q = tid + i * NT, r = q >> 3, c = q & 7;
-            *(v4i *)(&sB[buf][r * 128 + ((c ^ swz(r)) << 4)]) = rbv[i];
-        }
-#pragma unroll
-        for (int i = 0; i < SQT; ++i) {
-            int q = tid + i * NT;
-            if (q < SQ) {
-                int r = q / SDW, part = q % SDW;
-                *(uint32_t *)(&sS[buf][r * 8 + part * 4]) = rs[i];
-            }
+        for (int i = wave; i < (SCALE_DW + 63) / 64; i += NW) {
+            const int q = min(i * 64 + lane, SCALE_DW - 1);
+            const int r = q / SDW, part = q % SDW;
+            const int soff = min(s * SBY + part * 4, sp - 4);
+            const uint8_t *src = (r < BM) ? As + (int64_t)min(m0 + r, M - 1) * sp + soff
+                                          : Bs + (int64_t)min(n0 + r - BM, N - 1) * sp + soff;
+            g2l_4(src, base + DATA + i * 256);
         }
     };
 
@@ -166,58 +178,57 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 
     const int lr = lane & 15, g = lane >> 4;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
+    issue(0, 0);
     for (int s = 0; s < nseg; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nseg) gload(s + 1);
+        const int stage = s & 1;
+        wait_vm0();            // this wave's copies of segment s have landed
+        __syncthreads();       // ... and everyone's; stage s+1 is no longer read
+        if (s + 1 < nseg) issue(s + 1, stage ^ 1);
+
+        const uint8_t *sA = smem + stage * STAGE;
+        const uint8_t *sB = sA + BM * 128;
+        const uint8_t *sS = sA + DATA;
         // E2M1 with K % 256 == 128: the last segment holds one instruction's worth.
         const int nh = (FMT == FP4 && (s + 1) * KV > K) ? 1 : seg<FMT>::mfmas;
-#pragma unroll
-        for (int h = 0; h < seg<FMT>::mfmas; ++h) {
-            if (h >= nh) break;
-            v8i af[FM], bf[FN];
-            int sa[FM], sb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                int r = wm * WTM + i * 16 + lr;
-                const uint8_t *rowp = &sA[buf][r * 128];
-                if (FMT == FP8) {
-                    v4i lo = *(const v4i *)(rowp + ((g ^ swz(r)) << 4));
-                    v4i hi = *(const v4i *)(rowp + (((4 + g) ^ swz(r)) << 4));
-                    af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    sa[i] = sS[buf][r * 8 + g];
-                } else {
-                    v4i v = *(const v4i *)(rowp + (((4 * h + g) ^ swz(r)) << 4));
-                    af[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-                    sa[i] = sS[buf][r * 8 + 4 * h + g];
-                }
-            }
+        // One pass per instruction-sized K slice; kept rolled so only one
+        // pass's fragments are live.
+#pragma unroll 1
+        for (int h = 0; h < nh; ++h) {
+            const int cl = (FMT == FP8) ? g : 4 * h + g;      // chunk (E4M3: also 4+g)
+            const int sbyte = (FMT == FP8) ? g : 4 * h + g;   // scale byte in the segment
+            v8i bf[FN];
+            int sb[FN];
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                int r = wn * WTN + j * 16 + lr;
-                const uint8_t *rowp = &sB[buf][r * 128];
+                const int r = wn * WTN + j * 16 + lr;
+                const uint8_t *rp = sB + r * 128;
+                const v4i lo = *(const v4i *)(rp + ((cl ^ swz(r)) << 4));
                 if (FMT == FP8) {
-                    v4i lo = *(const v4i *)(rowp + ((g ^ swz(r)) << 4));
-                    v4i hi = *(const v4i *)(rowp + (((4 + g) ^ swz(r)) << 4));
+                    const v4i hi = *(const v4i *)(rp + (((4 + g) ^ swz(r)) << 4));
                     bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    sb[j] = sS[buf][(BM + r) * 8 + g];
                 } else {
-                    v4i v = *(const v4i *)(rowp + (((4 * h + g) ^ swz(r)) << 4));
-                    bf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-                    sb[j] = sS[buf][(BM + r) * 8 + 4 * h + g];
+                    bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
                 }
+                sb[j] = sS[(BM + r) * SBY + sbyte];
             }
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 16 + lr;
+                const uint8_t *rp = sA + r * 128;
+                const v4i lo = *(const v4i *)(rp + ((cl ^ swz(r)) << 4));
+                v8i af;
+                if (FMT == FP8) {
+                    const v4i hi = *(const v4i *)(rp + (((4 + g) ^ swz(r)) << 4));
+                    af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                } else {
+                    af = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+                }
+                const int sa = sS[r * SBY + sbyte];
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mma<FMT>(af[i], bf[j], acc[i][j], sa[i], sb[j]);
+                    acc[i][j] = mma<FMT>(af, bf[j], acc[i][j], sa, sb[j]);
+            }
         }
-        if (s + 1 < nseg) lstore(buf ^ 1);
-        __syncthreads();
     }
 
     // Epilogue: lane (c, g) of fragment (i, j) holds rows 4g..4g+3, column c.

@@ -27,19 +27,49 @@ int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Tile shapes of the tiled kernel: {BM, BN, waves along M, waves along N}.
+struct TileCfg { int bm, bn, wgm, wgn; };
+constexpr TileCfg kTiles[] = {
+    {256, 256, 2, 2}, {256, 192, 2, 2}, {256, 160, 2, 2}, {256, 128, 2, 2},
+    {128, 128, 2, 2},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kCUs = 256;   // MI355X compute units: one 256-row tile per CU per wave
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Pick the tile whose grid fills whole waves of CUs best, weighting away the
+// padding in partial tiles; ties go to the larger tile (more reuse per byte).
+int choose_tile(int64_t M, int64_t N)
+{
+    int best = 0;
+    double best_eff = -1.0;
+    for (int t = 0; t < kNumTiles; ++t) {
+        const TileCfg &c = kTiles[t];
+        if (c.bm == 128 && M > 128) continue;      // 128-row tiles only for short M
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+        const double fill = (double)tiles / (double)(cdiv(tiles, kCUs) * kCUs);
+        const double useful = (double)(M * N) / (double)(tiles * c.bm * c.bn);
+        const double eff = fill * useful;
+        if (eff > best_eff + 1e-9) { best_eff = eff; best = t; }
+    }
+    return best;
+}
+
 // Plan: which kernel, which tile, how many workgroups.
 int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)
 {
     int rc = check_args(fmt, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
     memset(p, 0, sizeof(*p));
+    const TileCfg &c = kTiles[choose_tile(M, N)];
     p->variant = MX_VARIANT_TILE;
-    p->tile_m = 128;
-    p->tile_n = 128;
+    p->tile_m = c.bm;
+    p->tile_n = c.bn;
     p->split_k = 1;
-    p->threads = 256;
+    p->threads = c.wgm * c.wgn * 64;
     p->lds_bytes = 0;
-    p->workgroups = ((M + p->tile_m - 1) / p->tile_m) * ((N + p->tile_n - 1) / p->tile_n);
+    p->workgroups = cdiv(M, c.bm) * cdiv(N, c.bn);
     p->workspace_bytes = 0;
     return MX_OK;
 }
@@ -67,16 +97,34 @@ int device_ready(int *dev_out)
     return g_dev_status[dev];
 }
 
+template <int FMT, int OUT, int BM, int BN, int WGM, int WGN>
+void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
+                int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
+    const int gm = 4;
+    hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, BM, BN, WGM, WGN>),
+                       dim3((unsigned)(tiles_m * tiles_n)), dim3(WGM * WGN * 64), 0, stream,
+                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
+                       (const uint8_t *)Bs, C, (int)M, (int)N, (int)K, tiles_m, tiles_n, gm);
+}
+
 template <int FMT, int OUT>
 void launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
                  const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
                  hipStream_t stream)
 {
-    const int tiles_n = (int)((N + p.tile_n - 1) / p.tile_n);
-    hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, 128, 128, 2, 2>),
-                       dim3((unsigned)p.workgroups), dim3(p.threads), 0, stream,
-                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
-                       (const uint8_t *)Bs, C, (int)M, (int)N, (int)K, tiles_n);
+#define MX_CFG(BM_, BN_, WM_, WN_)                                                        \
+    if (p.tile_m == BM_ && p.tile_n == BN_) {                                            \
+        launch_cfg<FMT, OUT, BM_, BN_, WM_, WN_>(A, As, B, Bs, C, M, N, K, stream);       \
+        return;                                                                           \
+    }
+    MX_CFG(256, 256, 2, 2)
+    MX_CFG(256, 192, 2, 2)
+    MX_CFG(256, 160, 2, 2)
+    MX_CFG(256, 128, 2, 2)
+    MX_CFG(128, 128, 2, 2)
+#undef MX_CFG
 }
 
 }  // namespace

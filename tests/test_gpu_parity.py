@@ -174,3 +174,5 @@ def test_full_workload_sampled(name):
     res, *_ = check_against_oracle(case, case["out"], rows=rows)
     log("full workload %s: worst ratio %.3g" % (name, res["max_ratio"]))
     _assert_ok(res, name)
+    # The workloads themselves meet the plain 1e-5 * T bound (+ bf16 ulp).
+    assert res.get("n_plain_bad", 0) == 0, res
