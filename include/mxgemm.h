@@ -116,6 +116,25 @@ typedef struct {
 int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype,
                  mx_plan_t *plan);
 
+/*
+ * The output tile shapes the library has kernels for.  Writes up to
+ * max_pairs (tile_m, tile_n) pairs to pairs[2i], pairs[2i+1] (pairs may be
+ * NULL) and returns how many shapes there are.  Host logic only.
+ */
+int mx_tile_shapes(int *pairs, int max_pairs);
+
+/*
+ * mx_gemm with the output tile chosen by the caller instead of the plan:
+ * (tile_m, tile_n) must be one of the shapes mx_tile_shapes lists, else
+ * MX_ERR_SHAPE.  Everything else -- arguments, layouts, errors, results --
+ * is as for mx_gemm.  It exists so that every kernel configuration can be
+ * exercised (and timed) on any problem size.
+ */
+int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
+                 const void *A, const void *A_scale,
+                 const void *B, const void *B_scale,
+                 void *C, int out_dtype, int tile_m, int tile_n, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

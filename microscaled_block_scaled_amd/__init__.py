@@ -58,6 +58,10 @@ def lib():
         raise RuntimeError(
             "libmxgemm.so is not built; run microscaled_block_scaled_amd/build.py "
             "(or __graft_entry__.build())")
+    # torch ships its own HIP runtime.  Load it first, so the library's
+    # libamdhip64.so.7 dependency resolves to that same runtime: two HIP (and
+    # HSA) runtimes in one process would not share devices, streams or memory.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     L.mx_gemm.restype = ctypes.c_int
@@ -68,6 +72,11 @@ def lib():
     L.mx_gemm_plan.restype = ctypes.c_int
     L.mx_gemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_int,
                                ctypes.POINTER(MxPlan)]
+    L.mx_tile_shapes.restype = ctypes.c_int
+    L.mx_tile_shapes.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+    L.mx_gemm_tile.restype = ctypes.c_int
+    L.mx_gemm_tile.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -93,8 +102,21 @@ def plan(fmt, M, N, K, out_dtype=OUT_BF16):
     return p.as_dict()
 
 
-def gemm_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0):
-    """Raw entry point: integer device addresses, returns the status code."""
+def tile_shapes():
+    """[(tile_m, tile_n), ...] the library has kernels for."""
+    n = lib().mx_tile_shapes(None, 0)
+    buf = (ctypes.c_int * (2 * n))()
+    lib().mx_tile_shapes(buf, n)
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
+
+
+def gemm_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0, tile=None):
+    """Raw entry point: integer device addresses, returns the status code.
+    ``tile=(tile_m, tile_n)`` forces a tile shape (mx_gemm_tile)."""
+    if tile is not None:
+        return lib().mx_gemm_tile(int(fmt), int(M), int(N), int(K), A, A_scale, B,
+                                  B_scale, C, int(out_dtype), int(tile[0]), int(tile[1]),
+                                  stream or None)
     return lib().mx_gemm(int(fmt), int(M), int(N), int(K), A, A_scale, B,
                          B_scale, C, int(out_dtype), stream or None)
 
@@ -125,8 +147,10 @@ def _as_u8(t, name):
     return t
 
 
-def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None):
-    """C = A * B^T for MX-quantized A (M x K) and B (N x K); see module doc."""
+def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
+            tile=None):
+    """C = A * B^T for MX-quantized A (M x K) and B (N x K); see module doc.
+    ``tile=(tile_m, tile_n)`` forces one of ``tile_shapes()``."""
     import torch
     if out_dtype is None:
         out_dtype = torch.bfloat16
@@ -156,7 +180,7 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None):
         stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         rc = gemm_ptr(fmt, M, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
-                      b_scale.data_ptr(), out.data_ptr(), code, stream)
+                      b_scale.data_ptr(), out.data_ptr(), code, stream, tile)
     if rc != MX_OK:
         _raise(rc)
     return out

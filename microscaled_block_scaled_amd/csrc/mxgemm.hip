@@ -30,7 +30,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // Tile shapes of the tiled kernel: {BM, BN, waves along M, waves along N}.
 struct TileCfg { int bm, bn, wgm, wgn; };
 constexpr TileCfg kTiles[] = {
-    {256, 256, 2, 2}, {256, 192, 2, 2}, {256, 160, 2, 2}, {256, 128, 2, 2},
+    {256, 256, 2, 2}, {256, 192, 2, 2}, {256, 160, 4, 1}, {256, 128, 2, 2},
     {128, 128, 2, 2},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -56,13 +56,11 @@ int choose_tile(int64_t M, int64_t N)
     return best;
 }
 
-// Plan: which kernel, which tile, how many workgroups.
-int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)
+// Plan for tile t: which kernel, which tile, how many workgroups.
+void fill_plan(int t, int64_t M, int64_t N, mx_plan_t *p)
 {
-    int rc = check_args(fmt, M, N, K, out_dtype);
-    if (rc != MX_OK) return rc;
     memset(p, 0, sizeof(*p));
-    const TileCfg &c = kTiles[choose_tile(M, N)];
+    const TileCfg &c = kTiles[t];
     p->variant = MX_VARIANT_TILE;
     p->tile_m = c.bm;
     p->tile_n = c.bn;
@@ -71,7 +69,21 @@ int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t
     p->lds_bytes = 0;
     p->workgroups = cdiv(M, c.bm) * cdiv(N, c.bn);
     p->workspace_bytes = 0;
+}
+
+int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)
+{
+    int rc = check_args(fmt, M, N, K, out_dtype);
+    if (rc != MX_OK) return rc;
+    fill_plan(choose_tile(M, N), M, N, p);
     return MX_OK;
+}
+
+int find_tile(int tile_m, int tile_n)
+{
+    for (int t = 0; t < kNumTiles; ++t)
+        if (kTiles[t].bm == tile_m && kTiles[t].bn == tile_n) return t;
+    return -1;
 }
 
 // Per-device one-time check: the device must be a gfx950.
@@ -110,22 +122,52 @@ void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, vo
 }
 
 template <int FMT, int OUT>
-void launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
+bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
                  const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
                  hipStream_t stream)
 {
 #define MX_CFG(BM_, BN_, WM_, WN_)                                                        \
-    if (p.tile_m == BM_ && p.tile_n == BN_) {                                            \
+    if (p.tile_m == BM_ && p.tile_n == BN_ && p.threads == WM_ * WN_ * 64) {             \
         launch_cfg<FMT, OUT, BM_, BN_, WM_, WN_>(A, As, B, Bs, C, M, N, K, stream);       \
-        return;                                                                           \
+        return true;                                                                      \
     }
     MX_CFG(256, 256, 2, 2)
     MX_CFG(256, 192, 2, 2)
-    MX_CFG(256, 160, 2, 2)
+    MX_CFG(256, 160, 4, 1)
     MX_CFG(256, 128, 2, 2)
     MX_CFG(128, 128, 2, 2)
 #undef MX_CFG
+    return false;
 }
+
+// Checks that need no device, then the device check, then the launch.
+int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
+             const void *A, const void *A_scale, const void *B, const void *B_scale,
+             void *C, int out_dtype, void *stream)
+{
+    if (!A || !A_scale || !B || !B_scale || !C) return MX_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
+        !aligned(A_scale, 4) || !aligned(B_scale, 4))
+        return MX_ERR_ALIGN;
+    int dev = -1;
+    const int rc = device_ready(&dev);
+    if (rc != MX_OK) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();  // clear any stale error so the check below is ours
+    bool launched;
+    if (fmt == MX_FMT_E2M1)
+        launched = (out_dtype == MX_OUT_FP32)
+            ? launch_tile<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
+            : launch_tile<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+    else
+        launched = (out_dtype == MX_OUT_FP32)
+            ? launch_tile<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
+            : launch_tile<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+    if (!launched || hipGetLastError() != hipSuccess) return MX_ERR_LAUNCH;
+    return MX_OK;
+}
+
 
 }  // namespace
 
@@ -153,6 +195,16 @@ extern "C" int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dt
     return make_plan(fmt, M, N, K, out_dtype, plan);
 }
 
+extern "C" int mx_tile_shapes(int *pairs, int max_pairs)
+{
+    if (pairs)
+        for (int t = 0; t < kNumTiles && t < max_pairs; ++t) {
+            pairs[2 * t] = kTiles[t].bm;
+            pairs[2 * t + 1] = kTiles[t].bn;
+        }
+    return kNumTiles;
+}
+
 extern "C" int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
                        const void *A, const void *A_scale,
                        const void *B, const void *B_scale,
@@ -161,23 +213,20 @@ extern "C" int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
     mx_plan_t plan;
     int rc = make_plan(fmt, M, N, K, out_dtype, &plan);
     if (rc != MX_OK) return rc;
-    if (!A || !A_scale || !B || !B_scale || !C) return MX_ERR_NULL;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
-        !aligned(A_scale, 4) || !aligned(B_scale, 4))
-        return MX_ERR_ALIGN;
-    int dev = -1;
-    rc = device_ready(&dev);
-    if (rc != MX_OK) return rc;
-
-    hipStream_t s = (hipStream_t)stream;
-    (void)hipGetLastError();  // clear any stale error so the check below is ours
-    if (fmt == MX_FMT_E2M1) {
-        if (out_dtype == MX_OUT_FP32) launch_tile<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
-        else launch_tile<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
-    } else {
-        if (out_dtype == MX_OUT_FP32) launch_tile<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
-        else launch_tile<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
-    }
-    if (hipGetLastError() != hipSuccess) return MX_ERR_LAUNCH;
-    return MX_OK;
+    return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
+
+extern "C" int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
+                            const void *A, const void *A_scale,
+                            const void *B, const void *B_scale,
+                            void *C, int out_dtype, int tile_m, int tile_n, void *stream)
+{
+    int rc = check_args(fmt, M, N, K, out_dtype);
+    if (rc != MX_OK) return rc;
+    const int t = find_tile(tile_m, tile_n);
+    if (t < 0) return MX_ERR_SHAPE;
+    mx_plan_t plan;
+    fill_plan(t, M, N, &plan);
+    return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
+}
+

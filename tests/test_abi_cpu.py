@@ -91,6 +91,26 @@ def test_no_device_reported():
     assert rc == mxg.MX_ERR_NO_DEVICE
 
 
+def test_tile_shapes_and_forced_tile_errors():
+    shapes = mxg.tile_shapes()
+    assert (256, 192) in shapes and len(shapes) == len(set(shapes))
+    for bm, bn in shapes:
+        assert bm % 32 == 0 and bn % 32 == 0
+    p = mxg.plan(mxg.FMT_E4M3, 2048, 6144, 4096)
+    assert (p["tile_m"], p["tile_n"]) in shapes
+    L = mxg.lib()
+    good = 1 << 20
+    # An unknown tile, or a bad shape, is rejected before any HIP call.
+    assert L.mx_gemm_tile(2, 64, 64, 128, good, good, good, good, good, 2, 100, 64,
+                          None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_tile(2, 64, 64, 100, good, good, good, good, good, 2, 256, 192,
+                          None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_tile(9, 64, 64, 128, good, good, good, good, good, 2, 256, 192,
+                          None) == mxg.MX_ERR_FORMAT
+    assert L.mx_gemm_tile(2, 64, 64, 128, None, good, good, good, good, 2, 256, 192,
+                          None) == mxg.MX_ERR_NULL
+
+
 def test_plan_shapes():
     p = mxg.plan(mxg.FMT_E4M3, 2048, 6144, 4096, mxg.OUT_BF16)
     assert p["workgroups"] >= 1 and p["threads"] % 64 == 0

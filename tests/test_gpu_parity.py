@@ -49,6 +49,24 @@ def test_tails(fmt, out, M, N, K):
     _assert_ok(res, "tails")
 
 
+def _tile_ids():
+    return ["%dx%d" % t for t in mxg.tile_shapes()]
+
+
+@pytest.mark.parametrize("tile", mxg.tile_shapes(), ids=_tile_ids())
+@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
+def test_every_tile(tile, fmt, out):
+    """Each kernel configuration, forced, on a ragged problem two tiles high
+    and wide whose K walks several full main-loop trips and a partial one."""
+    M, N = tile[0] + 37, tile[1] + 19
+    K = 4736 if fmt == E2M1 else 2432           # 37 / 19 x 128
+    case = mxinputs.make_random(fmt, M, N, K, seed=tile[0] + tile[1] + fmt)
+    log("every tile %s fmt=%d out=%d M=%d N=%d K=%d" % (tile, fmt, out, M, N, K))
+    res, *_ = check_against_oracle(case, out, tile=tile)
+    _assert_ok(res, "tile %s" % (tile,))
+
+
 @pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
 def test_scale_extremes(fmt):
     # sa + sb - 254 spans [-100, 100]: every block result stays an FP32 normal.
