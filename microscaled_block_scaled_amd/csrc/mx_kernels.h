@@ -45,12 +45,15 @@ enum { OF32 = 1, OBF16 = 2 };   // equal to MX_OUT_FP32 / MX_OUT_BF16
 // Format selector of the scaled MFMA (cbsz for A, blgp for B).
 template <int FMT> struct mfma_fmt { static constexpr int sel = (FMT == FP4) ? 4 : 0; };
 
-// A slab is 64 bytes of every row of the A and B tiles: 128 E2M1 or 64 E4M3
-// K-values, i.e. two or one 64-K instruction steps, and their scale bytes
-// (4 or 2 per row).
+// A slab is SW = 128 bytes of every row of the A and B tiles: 256 E2M1 or
+// 128 E4M3 K-values, i.e. four or two 64-K instruction steps, and their
+// scale bytes (8 or 4 per row).  128-byte rows make every copy request a
+// whole 128-byte line.
+constexpr int SW = 128;
 template <int FMT> struct slab {
-    static constexpr int kvals = (FMT == FP4) ? 128 : 64;
-    static constexpr int steps = kvals / 64;         // 2 (E2M1) or 1 (E4M3)
+    static constexpr int kvals = (FMT == FP4) ? 2 * SW : SW;
+    static constexpr int steps = kvals / 64;         // 4 (E2M1) or 2 (E4M3)
+    static constexpr int sbytes = kvals / 32;        // 8 (E2M1) or 4 (E4M3)
 };
 
 // FP32 -> BF16 bits, round to nearest even; NaN stays a (quiet) NaN.
@@ -62,14 +65,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
-// LDS row swizzle for 64-byte rows: chunk c of row r lives at chunk
-// c ^ swz(r).  For any 8 aligned rows, the even rows get distinct values and
-// so do the odd rows (two rows share a 128-byte bank line); for any 16
-// aligned rows, the four rows of each residue mod 4 get distinct values (four
-// rows share a 256-byte line).  A 16-byte read of one chunk by consecutive
-// rows is then free of bank conflicts whether the LDS serves 8 or 16 lanes
-// per cycle.  swz depends on r mod 16 only.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// LDS row swizzle for 128-byte rows: chunk c of row r lives at chunk
+// c ^ swz(r).  Any 8 aligned rows get 8 distinct values, and so do the even
+// (or odd) rows of any 16 aligned rows, so a 16-byte read of one chunk by
+// consecutive rows is free of bank conflicts whether the LDS serves 8 or 16
+// lanes per cycle.  swz depends on r mod 16 only.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int FMT>
 __device__ __forceinline__ v16f mma(const v8i &a, const v8i &b, v16f acc, int sa, int sb)
@@ -146,17 +147,17 @@ __device__ __forceinline__ void interleave()
 // Tiled kernel: one workgroup computes a BM x BN tile of C with WGM x WGN
 // waves, each owning a (BM/WGM) x (BN/WGN) block of 32x32 FP32 accumulators.
 //
-// K is walked in slabs: 64 bytes of every A and B row.  The LDS holds a ring
-// of S = 4 slabs and two scale buffers:
+// K is walked in slabs: 128 bytes of every A and B row.  The LDS holds a
+// ring of S = 2 slabs and two scale buffers:
 //   * slab k+S-1 is copied HBM -> LDS directly (global_load_lds, no register
 //     staging) into the ring slot that slab k-1 has just vacated, so S-1
 //     slabs of copies are in flight while slab k is multiplied -- the
 //     consumed part of the LDS tile is refilled as soon as it is free;
 //   * scale bytes travel 16 per row at a time (a "period": 16 K-blocks, i.e.
-//     8 E4M3 or 4 E2M1 slabs), one period ahead, into the scale buffer the
+//     4 E4M3 or 2 E2M1 slabs), one period ahead, into the scale buffer the
 //     period before last has vacated.  Row scales are K/32 bytes apart in
 //     memory, so a per-slab copy would cost one memory request per row for
-//     2-4 bytes; per period it is one request per row for 16;
+//     4-8 bytes; per period it is one request per row for 16;
 //   * the operand fragments of step t+1 are read LDS -> registers (two
 //     register sets) while the MFMAs of step t run, the reads spread between
 //     the MFMAs;
@@ -176,23 +177,25 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int HS = slab<FMT>::steps;                   // MFMA steps per slab
-    constexpr int SBS = (FMT == FP4) ? 4 : 2;              // scale bytes per row per slab
+    constexpr int SBS = slab<FMT>::sbytes;                 // scale bytes per row per slab
     constexpr int PS = 16 / SBS;                           // slabs per scale period
     constexpr int NR = (FMT == FP8) ? 2 : 1;               // 16-byte reads per fragment
     constexpr int ROWS = BM + BN;
-    constexpr int DATA = ROWS * 64;                        // element bytes per slab
+    constexpr int DATA = ROWS * SW;                        // element bytes per slab
     constexpr int NSI = (ROWS + 63) / 64;                  // scale copy instructions
     constexpr int SBUF = NSI * 64 * 16;                    // one scale buffer
-    constexpr int S = 4;                                   // ring depth
+    constexpr int S = 2;                                   // ring depth
+    constexpr int RPC = 1024 / SW;                         // rows per copy instruction
     static_assert(S * DATA + 2 * SBUF <= 163840, "LDS budget");
     static_assert(PS % S == 0 || S % PS == 0, "trip alignment");
-    static_assert(BM % 16 == 0 && BN % 16 == 0, "rows per copy instruction");
+    static_assert(BM % RPC == 0 && BN % RPC == 0, "rows per copy instruction");
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be 32-aligned");
-    constexpr int CPA = (BM / 16 + NW - 1) / NW;           // A copies per wave per slab
-    constexpr int CPB = (BN / 16 + NW - 1) / NW;           // B copies per wave per slab
+    constexpr int CPA = (BM / RPC + NW - 1) / NW;          // A copies per wave per slab
+    constexpr int CPB = (BN / RPC + NW - 1) / NW;          // B copies per wave per slab
     constexpr int CPS = (NSI + NW - 1) / NW;               // scale copies per wave per period
     constexpr int NCOPY = CPA + CPB;
     static_assert(NCOPY * (S - 2) < 64, "vmcnt range");
+    static_assert(S == 2 || S == 4, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * DATA + 2 * SBUF];
     uint8_t *const sbase = smem + S * DATA;                // scale buffers
@@ -205,11 +208,11 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int m0 = tm * BM, n0 = tn * BN;
     const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;
     const int sp = K / 32;
-    const int nslab = (int)(rowb / 64);
+    const int nslab = (int)((rowb + SW - 1) / SW);          // E2M1: the last may be half
     const int nper = (sp + 15) / 16;                       // scale periods
     const int nsteps = K / 64;
 
-    const int crow = lane >> 2, cpc = lane & 3;   // row within a 16-row copy, LDS chunk
+    const int crow = lane / (SW / 16), cpc = lane % (SW / 16);   // row in a copy, LDS chunk
 
     // Copy slab k into ring slot `slot`.  Branch-free: every wave issues the
     // same NCOPY instructions (a surplus one repeats the last row block,
@@ -218,21 +221,24 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     auto issue = [&](int k, int slot) {
         k = min(k, nslab - 1);
         uint8_t *base = smem + slot * DATA;
-        const int64_t koff = (int64_t)k * 64;
+        const int64_t koff = (int64_t)k * SW;
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
-            const int i = min(wave + u * NW, BM / 16 - 1);
-            const int r = i * 16 + crow;
+            const int i = min(wave + u * NW, BM / RPC - 1);
+            const int r = i * RPC + crow;
             const int row = min(m0 + r, M - 1);
-            g2l_16(A + (int64_t)row * rowb + koff + ((cpc ^ swz(r)) << 4), base + i * 1024);
+            // E2M1 with K % 256 == 128: the last slab is half a row segment;
+            // its upper half is never read, so the copy stays inside the row.
+            const int64_t off = min(koff + ((cpc ^ swz(r)) << 4), rowb - 16);
+            g2l_16(A + (int64_t)row * rowb + off, base + i * 1024);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
-            const int i = min(wave + u * NW, BN / 16 - 1);
-            const int r = i * 16 + crow;
+            const int i = min(wave + u * NW, BN / RPC - 1);
+            const int r = i * RPC + crow;
             const int row = min(n0 + r, N - 1);
-            g2l_16(B + (int64_t)row * rowb + koff + ((cpc ^ swz(r)) << 4),
-                   base + BM * 64 + i * 1024);
+            const int64_t off = min(koff + ((cpc ^ swz(r)) << 4), rowb - 16);
+            g2l_16(B + (int64_t)row * rowb + off, base + BM * SW + i * 1024);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`.
@@ -256,10 +262,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int lr = lane & 31, g = lane >> 5;
     // Per-lane LDS offsets.  A fragment row r = wm*WTM + 32i + lr has
     // swz(r) = swz(lr) (WTM and 32i are multiples of 16), so fragment i is the
-    // lane's offset plus the constant 2048*i.
+    // lane's offset plus the constant 32*SW*i.
     const int swl = swz(lr);
-    const int a_off = (wm * WTM + lr) * 64;
-    const int b_off = BM * 64 + (wn * WTN + lr) * 64;
+    const int a_off = (wm * WTM + lr) * SW;
+    const int b_off = BM * SW + (wn * WTN + lr) * SW;
     const int sa_off = (wm * WTM + lr) * 16;
     const int sb_off = (BM + wn * WTN + lr) * 16;
 
@@ -276,12 +282,14 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     auto load = [&](int set, int slot, int p, int sbuf, int kp, int shift) {
         const uint8_t *base = smem + slot * DATA;
         const uint8_t *sc = sbase + sbuf * SBUF;
-        const int c0 = 2 * p + g;                                 // E4M3: p == 0
+        // Step p of a slab: E4M3 chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g;
+        // in both, scale block 2p+g of the slab.
+        const int c0 = (FMT == FP8) ? 4 * p + g : 2 * p + g;
         const int o0 = (c0 ^ swl) << 4, o1 = ((c0 + 2) ^ swl) << 4;
-        const int sbyte = kp * SBS + c0 + shift;
+        const int sbyte = kp * SBS + 2 * p + g + shift;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const uint8_t *rp = base + a_off + i * 2048;
+            const uint8_t *rp = base + a_off + i * 32 * SW;
             const v4i lo = *(const v4i *)(rp + o0);
             if (FMT == FP8) {
                 const v4i hi = *(const v4i *)(rp + o1);
@@ -293,7 +301,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const uint8_t *rp = base + b_off + j * 2048;
+            const uint8_t *rp = base + b_off + j * 32 * SW;
             const v4i lo = *(const v4i *)(rp + o0);
             if (FMT == FP8) {
                 const v4i hi = *(const v4i *)(rp + o1);
