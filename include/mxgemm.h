@@ -60,8 +60,8 @@ enum {
     MX_OK = 0,
     MX_ERR_FORMAT = -1,     /* fmt is not MX_FMT_E2M1 / MX_FMT_E4M3          */
     MX_ERR_OUT_DTYPE = -2,  /* out_dtype is not MX_OUT_FP32 / MX_OUT_BF16     */
-    MX_ERR_SHAPE = -3,      /* M < 1, N < 1, K < 128, K % 128 != 0, or a
-                               dimension above MX_MAX_DIM                      */
+    MX_ERR_SHAPE = -3,      /* M < 1, N < 1, K < 128, K % 128 != 0, M or N
+                               above MX_MAX_DIM, or K above MX_MAX_K           */
     MX_ERR_NULL = -4,       /* a required pointer is NULL                     */
     MX_ERR_ALIGN = -5,      /* A, B or C not 16-byte aligned, or a scale
                                array not 4-byte aligned                        */
@@ -71,13 +71,16 @@ enum {
     MX_ERR_LAUNCH = -9      /* a kernel launch failed                         */
 };
 
-/* Largest M, N or K accepted (keeps every tile index in 32 bits). */
+/* Largest M or N accepted (keeps every tile index in 32 bits). */
 #define MX_MAX_DIM ((int64_t)1 << 30)
+/* Largest K accepted (keeps a tile's per-lane copy offsets, up to 256 rows of
+ * one operand, within 32 bits). */
+#define MX_MAX_K ((int64_t)1 << 24)
 
 /*
  * C = A * B^T with MX block scaling, enqueued on `stream`.
  *   fmt        MX_FMT_E2M1 or MX_FMT_E4M3 (A and B share the format)
- *   M, N, K    sizes; K a multiple of 128
+ *   M, N, K    sizes; K a multiple of 128, at most MX_MAX_K
  *   A, B       packed elements (layout above), 16-byte aligned device pointers
  *   A_scale,
  *   B_scale    E8M0 scale bytes (layout above), 4-byte aligned

@@ -19,6 +19,8 @@ FMT_E2M1 = 1
 FMT_E4M3 = 2
 OUT_FP32 = 1
 OUT_BF16 = 2
+MAX_DIM = 1 << 30     # largest M or N
+MAX_K = 1 << 24       # largest K
 VARIANT_TILE = 1
 VARIANT_DECODE = 2
 

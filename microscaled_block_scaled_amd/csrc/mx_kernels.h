@@ -30,7 +30,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <utility>
 
 namespace mx {
 
@@ -122,25 +121,16 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
     tn = w / gsz;
 }
 
-// --------------------------------------------------------------------------
-// Instruction interleave: ask the scheduler for NMF MFMAs with the NDS LDS
-// reads spread evenly between them (one scheduling region).  One wave per
-// SIMD cannot hide LDS issue behind MFMAs if the reads come in one cluster.
-template <int C>
-__device__ __forceinline__ void ds_reads_group()
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
 {
-    if constexpr (C > 0) __builtin_amdgcn_sched_group_barrier(0x100, C, 0);
+    (f(std::integral_constant<int, I>{}), ...);
 }
-template <int NMF, int NDS, int... I>
-__device__ __forceinline__ void interleave_impl(std::integer_sequence<int, I...>)
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
 {
-    ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
-      ds_reads_group<(I + 1) * NDS / NMF - I * NDS / NMF>()), ...);
-}
-template <int NMF, int NDS>
-__device__ __forceinline__ void interleave()
-{
-    interleave_impl<NMF, NDS>(std::make_integer_sequence<int, NMF>{});
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // --------------------------------------------------------------------------
@@ -179,7 +169,6 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int HS = slab<FMT>::steps;                   // MFMA steps per slab
     constexpr int SBS = slab<FMT>::sbytes;                 // scale bytes per row per slab
     constexpr int PS = 16 / SBS;                           // slabs per scale period
-    constexpr int NR = (FMT == FP8) ? 2 : 1;               // 16-byte reads per fragment
     constexpr int ROWS = BM + BN;
     constexpr int DATA = ROWS * SW;                        // element bytes per slab
     constexpr int NSI = (ROWS + 63) / 64;                  // scale copy instructions
@@ -214,6 +203,23 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 
     const int crow = lane / (SW / 16), cpc = lane % (SW / 16);   // row in a copy, LDS chunk
 
+    // Copy addresses are a wave-uniform base (scalar registers) plus a 32-bit
+    // per-lane offset, which stays below 256 rows * rowb < 2^32 for K <= 2^24.
+    // Rows past the end of the matrix are clamped to its last row (their
+    // results are never stored).
+    static_assert(RPC == 8 && BM % 64 == 0, "copy geometry");
+    const uint8_t *const At = A + (int64_t)m0 * rowb, *const Bt = B + (int64_t)n0 * rowb;
+    const uint8_t *const Ast = As + (int64_t)m0 * sp, *const Bst = Bs + (int64_t)n0 * sp;
+    const int last_a = min(BM, M - m0) - 1, last_b = min(BN, N - n0) - 1;   // last row in the tile
+    const uint32_t rowb32 = (uint32_t)rowb, lane_row = (uint32_t)crow * rowb32;
+    // Global chunk this lane fetches: LDS chunk cpc of row r holds chunk
+    // cpc ^ swz(r), and swz(i*8 + crow) depends only on crow and i's parity.
+    const uint32_t ch0 = (uint32_t)(cpc ^ swz(crow)) << 4;
+    const uint32_t ch1 = (uint32_t)(cpc ^ swz(crow + RPC)) << 4;
+    auto row_off = [&](int r0, int last) -> uint32_t {       // r0: first row of the block
+        return (r0 + crow <= last) ? (uint32_t)r0 * rowb32 + lane_row : (uint32_t)last * rowb32;
+    };
+
     // Copy slab k into ring slot `slot`.  Branch-free: every wave issues the
     // same NCOPY instructions (a surplus one repeats the last row block,
     // writing the same bytes to the same place), and k is clamped to the
@@ -222,26 +228,26 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         k = min(k, nslab - 1);
         uint8_t *base = smem + slot * DATA;
         const int64_t koff = (int64_t)k * SW;
+        // E2M1 with K % 256 == 128: the last slab is half a row segment; its
+        // upper half is never read, and its chunks are clamped into the row.
+        const uint32_t cmax = (uint32_t)(rowb - 16 - koff);
+        const uint8_t *const Ak = At + koff, *const Bk = Bt + koff;
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPC - 1);
-            const int r = i * RPC + crow;
-            const int row = min(m0 + r, M - 1);
-            // E2M1 with K % 256 == 128: the last slab is half a row segment;
-            // its upper half is never read, so the copy stays inside the row.
-            const int64_t off = min(koff + ((cpc ^ swz(r)) << 4), rowb - 16);
-            g2l_16(A + (int64_t)row * rowb + off, base + i * 1024);
+            const uint32_t ch = min((i & 1) ? ch1 : ch0, cmax);
+            g2l_16(Ak + (row_off(i * RPC, last_a) + ch), base + i * 1024);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
             const int i = min(wave + u * NW, BN / RPC - 1);
-            const int r = i * RPC + crow;
-            const int row = min(n0 + r, N - 1);
-            const int64_t off = min(koff + ((cpc ^ swz(r)) << 4), rowb - 16);
-            g2l_16(B + (int64_t)row * rowb + off, base + BM * SW + i * 1024);
+            const uint32_t ch = min((i & 1) ? ch1 : ch0, cmax);
+            g2l_16(Bk + (row_off(i * RPC, last_b) + ch), base + BM * SW + i * 1024);
         }
     };
-    // Copy scale period p (16 bytes of every row) into scale buffer `buf`.
+    // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
+    // lane l of copy instruction i fetches row 64i + l of the A rows then the
+    // B rows (BM is a multiple of 64, so each instruction is all A or all B).
     // Needs rows of at least 16 scale bytes (K >= 512).  The last period of a
     // row may be short: its copy is shifted left to end at the row's end, and
     // readers shift their byte index to match.  Every byte read lies inside
@@ -252,10 +258,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 #pragma unroll
         for (int u = 0; u < CPS; ++u) {
             const int i = min(wave + u * NW, NSI - 1);
-            const int r = min(i * 64 + lane, ROWS - 1);
-            const uint8_t *src = (r < BM) ? As + (int64_t)min(m0 + r, M - 1) * sp
-                                          : Bs + (int64_t)min(n0 + r - BM, N - 1) * sp;
-            g2l_16(src + soff, sbase + buf * SBUF + i * 1024);
+            const bool in_a = i * 64 < BM;
+            const int row = min(i * 64 + lane - (in_a ? 0 : BM), in_a ? last_a : last_b);
+            const uint8_t *const src = (in_a ? Ast : Bst) + soff;
+            g2l_16(src + (uint32_t)row * (uint32_t)sp, sbase + buf * SBUF + i * 1024);
         }
     };
 
@@ -269,48 +275,52 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int sa_off = (wm * WTM + lr) * 16;
     const int sb_off = (BM + wn * WTN + lr) * 16;
 
-    // Operand registers: two sets (the step being multiplied, the next one).
-    v8i fa[2][FM], fb[2][FN];
-    int fsa[2][FM], fsb[2][FN];
+    // Operand registers.  The operand with more fragments per wave (the
+    // "rolled" one, R) has a single register set: each of its fragments is
+    // reloaded for the next step as soon as the last MFMA of this step that
+    // reads it has been issued.  The other operand (D) has two sets, the next
+    // step's read while this step's are multiplied.  This keeps 2 waves per
+    // SIMD within 256 registers.
+    constexpr bool ROLL_A = FM >= FN;
+    constexpr int FR = ROLL_A ? FM : FN, FD = ROLL_A ? FN : FM;
+    const int r_off = ROLL_A ? a_off : b_off, d_off = ROLL_A ? b_off : a_off;
+    const int rs_off = ROLL_A ? sa_off : sb_off, ds_off = ROLL_A ? sb_off : sa_off;
+    v8i fr[FR], fd[2][FD];
+    int fsr[FR], fsd[2][FD];
 
-    // Fragments of pass p of slab k (ring slot `slot`, scale buffer `sbuf`,
-    // slab `kp` within its period) into register set `set`.  `shift` moves
-    // the scale byte index when the period's copy was shifted (last period).
-    // Every call sits in fully unrolled code, so set, slot, pass and kp fold
-    // to constants and each data read is the lane's offset plus an immediate;
-    // the scale buffer (the period's parity) and shift are runtime values.
-    auto load = [&](int set, int slot, int p, int sbuf, int kp, int shift) {
-        const uint8_t *base = smem + slot * DATA;
-        const uint8_t *sc = sbase + sbuf * SBUF;
+    // Where one step's operands are: ring slot `slot`, pass p of the slab,
+    // scale buffer `sbuf`, slab `kp` within its scale period, and the scale
+    // byte shift of a short last period.  Data chunk offsets and the scale
+    // byte are per lane (they depend on the lane group g and the swizzle).
+    struct Src { int data, scale, o0, o1; };
+    auto src_of = [&](int slot, int p, int sbuf, int kp, int shift) {
         // Step p of a slab: E4M3 chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g;
         // in both, scale block 2p+g of the slab.
         const int c0 = (FMT == FP8) ? 4 * p + g : 2 * p + g;
-        const int o0 = (c0 ^ swl) << 4, o1 = ((c0 + 2) ^ swl) << 4;
-        const int sbyte = kp * SBS + 2 * p + g + shift;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const uint8_t *rp = base + a_off + i * 32 * SW;
-            const v4i lo = *(const v4i *)(rp + o0);
-            if (FMT == FP8) {
-                const v4i hi = *(const v4i *)(rp + o1);
-                fa[set][i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                fa[set][i] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-            }
-            fsa[set][i] = sc[sa_off + i * 32 * 16 + sbyte];
+        return Src{slot * DATA, S * DATA + sbuf * SBUF + kp * SBS + 2 * p + g + shift,
+                   (c0 ^ swl) << 4, ((c0 + 2) ^ swl) << 4};
+    };
+    auto sel = [](bool c, const Src &x, const Src &y) {
+        return Src{c ? x.data : y.data, c ? x.scale : y.scale, c ? x.o0 : y.o0, c ? x.o1 : y.o1};
+    };
+    // Fragment f of an operand whose lane rows start at LDS offset `off`
+    // (scale rows at `soff`): 16 (E2M1) or 32 (E4M3) bytes and a scale byte.
+    auto frag = [&](const Src &s, int off, int soff, int f, v8i &v, int &sv) {
+        const uint8_t *rp = smem + s.data + off + f * 32 * SW;
+        const v4i lo = *(const v4i *)(rp + s.o0);
+        if (FMT == FP8) {
+            const v4i hi = *(const v4i *)(rp + s.o1);
+            v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            v = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
         }
+        sv = smem[s.scale + soff + f * 32 * 16];
+    };
+    auto load_all = [&](const Src &s, int set) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const uint8_t *rp = base + b_off + j * 32 * SW;
-            const v4i lo = *(const v4i *)(rp + o0);
-            if (FMT == FP8) {
-                const v4i hi = *(const v4i *)(rp + o1);
-                fb[set][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                fb[set][j] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-            }
-            fsb[set][j] = sc[sb_off + j * 32 * 16 + sbyte];
-        }
+        for (int f = 0; f < FR; ++f) frag(s, r_off, rs_off, f, fr[f], fsr[f]);
+#pragma unroll
+        for (int f = 0; f < FD; ++f) frag(s, d_off, ds_off, f, fd[set][f], fsd[set][f]);
     };
 
     v16f acc[FM][FN];
@@ -321,14 +331,30 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    auto mfmas = [&](int set) {
+    // Multiply one step (operands fr and fd[cur]) and read the next step's
+    // operands from `nx`: rolled fragment o right after its FD MFMAs, and the
+    // D fragments spread over the FR groups.  The scheduling groups keep each
+    // rolled reload behind the MFMAs that read the old value.
+    auto step = [&](int cur, const Src &nx) {
+        static_for<FR>([&](auto oc) {
+            constexpr int o = decltype(oc)::value;
+            constexpr int d0 = o * FD / FR, d1 = (o + 1) * FD / FR;
+            constexpr int NRD = (FMT == FP8) ? 3 : 2;           // LDS reads per fragment
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int d = 0; d < FD; ++d) {
+                if constexpr (ROLL_A)
+                    acc[o][d] = mma<FMT>(fr[o], fd[cur][d], acc[o][d], fsr[o], fsd[cur][d]);
+                else
+                    acc[d][o] = mma<FMT>(fd[cur][d], fr[o], acc[d][o], fsd[cur][d], fsr[o]);
+            }
+            frag(nx, r_off, rs_off, o, fr[o], fsr[o]);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = mma<FMT>(fa[set][i], fb[set][j], acc[i][j], fsa[set][i], fsb[set][j]);
+            for (int d = d0; d < d1; ++d)
+                frag(nx, d_off, ds_off, d, fd[cur ^ 1][d], fsd[cur ^ 1][d]);
+            __builtin_amdgcn_sched_group_barrier(0x008, FD, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRD * (1 + d1 - d0), 0);
+        });
     };
-    constexpr int NDS = (FM + FN) * (NR + 1);   // LDS reads per step (data + scale)
 
     // Before the first read of slab k1: wait for this wave's copies of it
     // (later slabs may stay in flight), sync (every wave holds the current
@@ -373,7 +399,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     lds_barrier();
     issue(S - 1, S - 1);
     if (!short_rows) issue_scales(1, 1);
-    load(0, 0, 0, 0, 0, shift_of(0));
+    Src cur = src_of(0, 0, 0, 0, shift_of(0));
+    load_all(cur, 0);
 
     // Main loop: one trip = TS slabs (a multiple of the ring depth and of
     // the scale period) = TS*HS steps, so register set, ring slot, pass and
@@ -393,12 +420,13 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const int per = (k0 + kq) / PS;           // its scale period
             if ((q + 1) % HS == 0)
                 open(k0 + kq, (kq + S - 1) % S, kq % PS == 0, (per + 1) & 1);
-            load((q + 1) & 1, kq % S, (q + 1) % HS, per & 1, kq % PS, shift_of(k0 + kq));
-            mfmas(q & 1);
-            interleave<FM * FN, NDS>();
+            cur = src_of(kq % S, (q + 1) % HS, per & 1, kq % PS, shift_of(k0 + kq));
+            step(q & 1, cur);
         }
     }
-    // Last trip: steps t0 .. nsteps-1 (1 to TRIP of them).
+    // Last trip: steps t0 .. nsteps-1 (1 to TRIP of them).  After the last
+    // step the "next" operands are re-read from the last step's place (in
+    // range, never used), which keeps the step code free of branches.
     {
         const int k0 = t0 / HS;
 #pragma unroll
@@ -406,13 +434,12 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             if (t0 + q < nsteps) {
                 const int kq = (q + 1) / HS;
                 const int per = (k0 + kq) / PS;
-                if (t0 + q + 1 < nsteps) {
-                    if ((q + 1) % HS == 0)
-                        open_guarded(k0 + kq, (kq + S - 1) % S, kq % PS == 0, (per + 1) & 1);
-                    load((q + 1) & 1, kq % S, (q + 1) % HS, per & 1, kq % PS,
-                         shift_of(k0 + kq));
-                }
-                mfmas(q & 1);
+                const bool more = t0 + q + 1 < nsteps;
+                if (more && (q + 1) % HS == 0)
+                    open_guarded(k0 + kq, (kq + S - 1) % S, kq % PS == 0, (per + 1) & 1);
+                cur = sel(more, src_of(kq % S, (q + 1) % HS, per & 1, kq % PS, shift_of(k0 + kq)),
+                          cur);
+                step(q & 1, cur);
             }
         }
     }

@@ -21,7 +21,7 @@ int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
     // K a multiple of 128 (FlyDSL article, "API compatibility is not
     // universal input coverage").
     if (M < 1 || N < 1 || K < 128 || K % 128 != 0) return MX_ERR_SHAPE;
-    if (M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
+    if (M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_K) return MX_ERR_SHAPE;
     return MX_OK;
 }
 
@@ -30,7 +30,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // Tile shapes of the tiled kernel: {BM, BN, waves along M, waves along N}.
 struct TileCfg { int bm, bn, wgm, wgn; };
 constexpr TileCfg kTiles[] = {
-    {256, 256, 2, 2}, {256, 192, 2, 2}, {256, 160, 4, 1}, {256, 128, 2, 2},
+    {256, 256, 4, 2}, {256, 192, 4, 2}, {256, 160, 4, 1}, {256, 128, 4, 2},
     {128, 128, 2, 2},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -131,10 +131,10 @@ bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *
         launch_cfg<FMT, OUT, BM_, BN_, WM_, WN_>(A, As, B, Bs, C, M, N, K, stream);       \
         return true;                                                                      \
     }
-    MX_CFG(256, 256, 2, 2)
-    MX_CFG(256, 192, 2, 2)
+    MX_CFG(256, 256, 4, 2)
+    MX_CFG(256, 192, 4, 2)
     MX_CFG(256, 160, 4, 1)
-    MX_CFG(256, 128, 2, 2)
+    MX_CFG(256, 128, 4, 2)
     MX_CFG(128, 128, 2, 2)
 #undef MX_CFG
     return false;
@@ -177,7 +177,7 @@ extern "C" const char *mx_strerror(int code)
     case MX_OK: return "success";
     case MX_ERR_FORMAT: return "unsupported element format (expected MX_FMT_E2M1 or MX_FMT_E4M3)";
     case MX_ERR_OUT_DTYPE: return "unsupported output type (expected MX_OUT_FP32 or MX_OUT_BF16)";
-    case MX_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 128, K % 128 == 0, all <= 2^30)";
+    case MX_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 128, K % 128 == 0, M and N <= 2^30, K <= 2^24)";
     case MX_ERR_NULL: return "null pointer argument";
     case MX_ERR_ALIGN: return "misaligned pointer (A, B, C need 16 bytes; scales need 4)";
     case MX_ERR_NO_DEVICE: return "no HIP device available";

@@ -36,6 +36,9 @@ def test_header_constants_match_binding():
         elif hasattr(mxg, k):
             assert getattr(mxg, k) == v, k
     assert consts["MX_FMT_E2M1"] == mxg.FMT_E2M1 and consts["MX_OUT_BF16"] == mxg.OUT_BF16
+    limits = dict((k, 1 << int(v)) for k, v in
+                  re.findall(r"#define (MX_MAX_[A-Z]+) \(\(int64_t\)1 << (\d+)\)", src))
+    assert limits == {"MX_MAX_DIM": mxg.MAX_DIM, "MX_MAX_K": mxg.MAX_K}
 
 
 def test_strerror_covers_codes():
@@ -58,6 +61,8 @@ def test_strerror_covers_codes():
     (2, 16, 16, 192, 2, mxg.MX_ERR_SHAPE),
     (2, 16, 16, -128, 2, mxg.MX_ERR_SHAPE),
     (2, (1 << 30) + 1, 16, 128, 2, mxg.MX_ERR_SHAPE),
+    (2, 16, (1 << 30) + 1, 128, 2, mxg.MX_ERR_SHAPE),
+    (2, 16, 16, (1 << 24) + 128, 2, mxg.MX_ERR_SHAPE),
 ])
 def test_argument_errors(fmt, M, N, K, out, code):
     L = mxg.lib()
@@ -65,6 +70,13 @@ def test_argument_errors(fmt, M, N, K, out, code):
     assert L.mx_gemm_plan(fmt, M, N, K, out, ctypes.byref(p)) == code
     # Same code from mx_gemm, before any pointer is looked at or HIP called.
     assert L.mx_gemm(fmt, M, N, K, None, None, None, None, None, out, None) == code
+
+
+def test_largest_shapes_accepted():
+    p = mxg.MxPlan()
+    L = mxg.lib()
+    assert L.mx_gemm_plan(2, 1 << 30, 16, 1 << 24, 2, ctypes.byref(p)) == mxg.MX_OK
+    assert L.mx_gemm_plan(1, 16, 1 << 30, 1 << 24, 1, ctypes.byref(p)) == mxg.MX_OK
 
 
 def test_null_and_alignment_errors():
