@@ -128,18 +128,19 @@ def bench_one(name, steps, warmup, with_cpu):
 
     for _ in range(warmup):
         step()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # One HIP event pair on the launch stream brackets the timed launches:
+    # their span / steps is the average launch duration (kernel time plus any
+    # gap between back-to-back launches).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         step()
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    avg_launch_s = e0.elapsed_time(e1) / steps / 1e3
 
     flops = 2.0 * M * N * K
     nbytes = algorithmic_bytes(fmt, M, N, K, out)

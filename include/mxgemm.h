@@ -97,14 +97,23 @@ int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
 /* Static, NUL-terminated description of a return code. */
 const char *mx_strerror(int code);
 
-/* Kernel variants a plan can choose. */
+/*
+ * Kernel variants a plan can choose.
+ *   MX_VARIANT_TILE    M > 64: each workgroup computes one tile_m x tile_n
+ *                      tile of C over all of K, staging A and B through LDS.
+ *   MX_VARIANT_DECODE  M <= 64: each workgroup computes all rows of C for 32
+ *                      columns; its split_k waves each take a share of K,
+ *                      streaming B from memory into registers, and their
+ *                      partial results are added in LDS in wave order.
+ */
 enum { MX_VARIANT_TILE = 1, MX_VARIANT_DECODE = 2 };
 
 /* How mx_gemm would run a problem (filled by mx_gemm_plan). */
 typedef struct {
     int variant;            /* MX_VARIANT_*                                   */
     int tile_m, tile_n;     /* output tile of one workgroup                   */
-    int split_k;            /* K slices reduced in a second pass (1 = none)   */
+    int split_k;            /* K slices per output tile (1 = none); they are
+                               added in a fixed order, never with atomics       */
     int threads;            /* threads per workgroup                          */
     int lds_bytes;          /* dynamic LDS per workgroup                      */
     int64_t workgroups;     /* workgroups in the main launch                  */

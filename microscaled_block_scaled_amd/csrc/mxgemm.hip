@@ -71,11 +71,32 @@ void fill_plan(int t, int64_t M, int64_t N, mx_plan_t *p)
     p->workspace_bytes = 0;
 }
 
+// Small-M kernel: one workgroup per 32 columns, kDecodeWaves waves splitting
+// K inside the workgroup; used for M <= kDecodeMaxM.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeMaxM = 64;
+
+void fill_decode_plan(int64_t M, int64_t N, mx_plan_t *p)
+{
+    memset(p, 0, sizeof(*p));
+    p->variant = MX_VARIANT_DECODE;
+    p->tile_m = M <= 32 ? 32 : 64;
+    p->tile_n = 32;
+    p->split_k = kDecodeWaves;
+    p->threads = kDecodeWaves * 64;
+    p->lds_bytes = 0;
+    p->workgroups = cdiv(N, 32);
+    p->workspace_bytes = 0;
+}
+
 int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)
 {
     int rc = check_args(fmt, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
-    fill_plan(choose_tile(M, N), M, N, p);
+    if (M <= kDecodeMaxM)
+        fill_decode_plan(M, N, p);
+    else
+        fill_plan(choose_tile(M, N), M, N, p);
     return MX_OK;
 }
 
@@ -140,6 +161,40 @@ bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *
     return false;
 }
 
+template <int FMT, int OUT, int MB>
+void launch_decode_mb(const void *A, const void *As, const void *B, const void *Bs, void *C,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    constexpr int U = (MB == 1) ? 4 : 3;   // 128-K units in flight per wave
+    hipLaunchKernelGGL((mx::decode_kernel<FMT, OUT, MB, kDecodeWaves, U>),
+                       dim3((unsigned)cdiv(N, 32)), dim3(kDecodeWaves * 64), 0, stream,
+                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
+                       (const uint8_t *)Bs, C, (int)M, (int)N, (int)K);
+}
+
+template <int FMT, int OUT>
+bool launch_decode(const mx_plan_t &p, const void *A, const void *As, const void *B,
+                   const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
+                   hipStream_t stream)
+{
+    if (p.tile_m == 32)
+        launch_decode_mb<FMT, OUT, 1>(A, As, B, Bs, C, M, N, K, stream);
+    else if (p.tile_m == 64)
+        launch_decode_mb<FMT, OUT, 2>(A, As, B, Bs, C, M, N, K, stream);
+    else
+        return false;
+    return true;
+}
+
+template <int FMT, int OUT>
+bool launch(const mx_plan_t &p, const void *A, const void *As, const void *B, const void *Bs,
+            void *C, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    if (p.variant == MX_VARIANT_DECODE)
+        return launch_decode<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, stream);
+    return launch_tile<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, stream);
+}
+
 // Checks that need no device, then the device check, then the launch.
 int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
              const void *A, const void *A_scale, const void *B, const void *B_scale,
@@ -158,12 +213,12 @@ int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
     bool launched;
     if (fmt == MX_FMT_E2M1)
         launched = (out_dtype == MX_OUT_FP32)
-            ? launch_tile<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
-            : launch_tile<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+            ? launch<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
+            : launch<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
     else
         launched = (out_dtype == MX_OUT_FP32)
-            ? launch_tile<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
-            : launch_tile<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+            ? launch<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
+            : launch<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
     if (!launched || hipGetLastError() != hipSuccess) return MX_ERR_LAUNCH;
     return MX_OK;
 }

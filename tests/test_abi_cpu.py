@@ -133,6 +133,21 @@ def test_plan_shapes():
         mxg.plan(mxg.FMT_E4M3, 16, 16, 100)
 
 
+@pytest.mark.parametrize("M,N", [(1, 8192), (32, 100), (33, 8192), (64, 28672)])
+def test_plan_small_m_uses_decode_variant(M, N):
+    for fmt in (mxg.FMT_E2M1, mxg.FMT_E4M3):
+        p = mxg.plan(fmt, M, N, 4096)
+        assert p["variant"] == mxg.VARIANT_DECODE
+        assert p["tile_m"] == (32 if M <= 32 else 64) and p["tile_n"] == 32
+        assert p["workgroups"] == -(-N // 32) and p["split_k"] * 64 == p["threads"]
+        assert p["workspace_bytes"] == 0
+
+
+def test_plan_larger_m_uses_tile_variant():
+    for M in (65, 256, 2048):
+        assert mxg.plan(mxg.FMT_E4M3, M, 8192, 4096)["variant"] == mxg.VARIANT_TILE
+
+
 def test_python_shim_rejects_bad_tensors():
     import torch
     a = torch.zeros((16, 64), dtype=torch.uint8)

@@ -49,6 +49,33 @@ def test_tails(fmt, out, M, N, K):
     _assert_ok(res, "tails")
 
 
+DECODE_SHAPES = [(1, 32, 128), (8, 97, 1152), (32, 64, 3968), (33, 40, 640),
+                 (64, 129, 2560), (17, 1000, 384)]
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
+def test_decode_variant(fmt, out, M, N, K):
+    """Small M runs the decode kernel: K split over the waves of a workgroup
+    (fewer 128-K units than waves when K < 1024), ragged N, 1..64 rows."""
+    assert mxg.plan(fmt, M, N, K, out)["variant"] == mxg.VARIANT_DECODE
+    case = mxinputs.make_random(fmt, M, N, K, seed=1000 + M * 3 + N + K)
+    log("decode fmt=%d out=%d M=%d N=%d K=%d" % (fmt, out, M, N, K))
+    res, *_ = check_against_oracle(case, out)
+    _assert_ok(res, "decode")
+
+
+@pytest.mark.parametrize("tile", [(256, 256), (128, 128)], ids=["256x256", "128x128"])
+@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+def test_tile_kernel_small_m(tile, fmt):
+    """The tile kernel, forced, on a problem much shorter than one tile."""
+    case = mxinputs.make_random(fmt, 5, 70, 640, seed=77 + fmt)
+    log("tile kernel small M tile=%s fmt=%d" % (tile, fmt))
+    res, *_ = check_against_oracle(case, BF16, tile=tile)
+    _assert_ok(res, "tile kernel small M")
+
+
 def _tile_ids():
     return ["%dx%d" % t for t in mxg.tile_shapes()]
 
@@ -161,17 +188,19 @@ def test_bf16_is_rounded_fp32(fmt):
     assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c16.view(torch.int16))
 
 
-def test_deterministic_and_stream():
+@pytest.mark.parametrize("M", [300, 40], ids=["tile", "decode"])
+def test_deterministic_and_stream(M):
     import torch
-    case = mxinputs.make_random(E4M3, 300, 260, 1024, seed=12)
+    case = mxinputs.make_random(E4M3, M, 260, 4096, seed=12)
     dev = to_dev(case)
     c1 = run_gpu(case, F32, dev)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        c2 = mxg.mx_gemm(dev["A"], dev["A_scale"], dev["B"], dev["B_scale"], E4M3,
-                         out_dtype=torch.float32)
-    s.synchronize()
-    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+        for _ in range(3):
+            c2 = mxg.mx_gemm(dev["A"], dev["A_scale"], dev["B"], dev["B_scale"], E4M3,
+                             out_dtype=torch.float32)
+            s.synchronize()
+            assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
 
 
 FULL = ["mxfp8_llama8b_qkv", "mxfp4_llama8b_gateup_decode", "mxfp4_qwen32b_down",
