@@ -180,6 +180,20 @@ def bench_one(name, steps, warmup, with_cpu):
     return res
 
 
+def copy_calibration(nbytes=256 << 20, reps=3):
+    """A plain device copy of known size, for scaling the HBM byte counters
+    (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the GEMM kernels."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,12 +203,17 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="one line per workload (no CPU baseline except the default one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
                          "multi-GPU component (each GPU would run its own shard "
                          "independently); use --gpus 1.\n")
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \
         if a.all else [a.workload]
     for name in names:
