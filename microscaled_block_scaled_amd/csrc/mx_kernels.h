@@ -55,13 +55,11 @@ template <int FMT> struct slab {
     static constexpr int sbytes = kvals / 32;        // 8 (E2M1) or 4 (E4M3)
 };
 
-// FP32 -> BF16 bits, round to nearest even; NaN stays a (quiet) NaN.
+// FP32 -> BF16 bits, round to nearest even (NaN stays NaN): one gfx950
+// v_cvt_pk_bf16_f32, branch-free.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // LDS row swizzle for 128-byte rows: chunk c of row r lives at chunk
@@ -444,24 +442,60 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         }
     }
 
-    // No copy may still be writing this workgroup's LDS once its waves exit.
+    // No copy may still be in flight, and every wave must be done reading the
+    // ring and scale buffers, before their LDS is reused for the output.
     wait_vm0();
+    lds_barrier();
 
-    // Epilogue: lane (c, g) of fragment (i, j) holds, in element e, row
-    // 8*(e/4) + 4g + e%4 of column c.
+    // Epilogue, one 32-row band of the wave's sub-tile at a time: the band is
+    // written to a wave-private LDS area (row pitch padded by 16 bytes so the
+    // two lane groups hit different banks), then read back row-major and
+    // stored with 16-byte writes (8 BF16 or 4 FP32 values per lane).  Lane
+    // (c, g) of fragment (i, j) holds, in element e, row 8*(e/4) + 4g + e%4
+    // of column c.  Chunks that cross the end of a row of C, or rows of C
+    // whose byte pitch is not a multiple of 16, are stored element by element.
+    typedef typename std::conditional<OUT == OF32, float, uint16_t>::type otype;
+    constexpr int OS = sizeof(otype);
+    constexpr int VE = 16 / OS;                        // values per 16-byte chunk
+    constexpr int PITCH = WTN * OS + 16;               // staging row pitch, bytes
+    constexpr int CPR = WTN / VE;                      // chunks per band row
+    static_assert(NW * 32 * PITCH <= S * DATA + 2 * SBUF, "epilogue staging fits in LDS");
+    uint8_t *const stage = smem + wave * 32 * PITCH;
+    const bool vec_ok = ((int64_t)N * OS) % 16 == 0;
+    otype *const Cp = (otype *)C;
+    const int col0 = n0 + wn * WTN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + lr;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * WTM + i * 32 + 8 * (e / 4) + 4 * g + (e % 4);
-                if (row < M && col < N) {
-                    if (OUT == OF32)
-                        ((float *)C)[(int64_t)row * N + col] = acc[i][j][e];
+                const int r = 8 * (e / 4) + 4 * g + (e % 4);
+                otype v;
+                if constexpr (OUT == OF32) v = acc[i][j][e];
+                else v = f32_to_bf16(acc[i][j][e]);
+                *(otype *)(stage + r * PITCH + (j * 32 + lr) * OS) = v;
+            }
+        const int row0 = m0 + wm * WTM + i * 32;
+        constexpr int NIT = (32 * CPR + 63) / 64;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int t = it * 64 + lane;
+            const int r = t / CPR, ch = t % CPR;
+            const int row = row0 + r, col = col0 + ch * VE;
+            if (t >= 32 * CPR || row >= M || col >= N) continue;
+            const v4i v = *(const v4i *)(stage + r * PITCH + ch * 16);
+            otype *dst = Cp + (int64_t)row * N + col;
+            if (vec_ok) {
+                *(v4i *)dst = v;
+            } else {
+#pragma unroll
+                for (int q = 0; q < VE; ++q) {
+                    if (col + q >= N) break;
+                    if constexpr (OUT == OF32)
+                        dst[q] = __int_as_float(v[q]);
                     else
-                        ((uint16_t *)C)[(int64_t)row * N + col] = f32_to_bf16(acc[i][j][e]);
+                        dst[q] = (uint16_t)((uint32_t)v[q / 2] >> (16 * (q & 1)));
                 }
             }
         }

@@ -85,8 +85,11 @@ def _tile_ids():
 @pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
 def test_every_tile(tile, fmt, out):
     """Each kernel configuration, forced, on a ragged problem two tiles high
-    and wide whose K walks several full main-loop trips and a partial one."""
-    M, N = tile[0] + 37, tile[1] + 19
+    and wide whose K walks several full main-loop trips and a partial one.
+    E2M1 cases use an odd N (rows of C not 16-byte multiples: element-wise
+    output stores), E4M3 cases an N that is a multiple of 8 (16-byte stores,
+    with a partial last tile)."""
+    M, N = tile[0] + 37, tile[1] + (19 if fmt == E2M1 else 24)
     K = 4736 if fmt == E2M1 else 2432           # 37 / 19 x 128
     case = mxinputs.make_random(fmt, M, N, K, seed=tile[0] + tile[1] + fmt)
     log("every tile %s fmt=%d out=%d M=%d N=%d K=%d" % (tile, fmt, out, M, N, K))
