@@ -67,7 +67,7 @@ enum {
                                array not 4-byte aligned                        */
     MX_ERR_NO_DEVICE = -6,  /* no HIP device is visible                       */
     MX_ERR_ARCH = -7,       /* the current device is not gfx950               */
-    MX_ERR_ALLOC = -8,      /* workspace allocation failed                    */
+    MX_ERR_ALLOC = -8,      /* split-K workspace allocation failed            */
     MX_ERR_LAUNCH = -9      /* a kernel launch failed                         */
 };
 
@@ -100,7 +100,12 @@ const char *mx_strerror(int code);
 /*
  * Kernel variants a plan can choose.
  *   MX_VARIANT_TILE    M > 64: each workgroup computes one tile_m x tile_n
- *                      tile of C over all of K, staging A and B through LDS.
+ *                      tile of C over all of K, staging A and B through LDS;
+ *                      when the tiles cannot fill the GPU, over one of
+ *                      split_k K-slices, each writing FP32 partial results
+ *                      to a workspace that a second kernel adds in slice
+ *                      order (workspace_bytes, taken with hipMallocAsync on
+ *                      the caller's stream and released the same way).
  *   MX_VARIANT_DECODE  M <= 64: each workgroup computes all rows of C for 32
  *                      columns; its split_k waves each take a share of K,
  *                      streaming B from memory into registers, and their
@@ -136,16 +141,21 @@ int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype,
 int mx_tile_shapes(int *pairs, int max_pairs);
 
 /*
- * mx_gemm with the output tile chosen by the caller instead of the plan:
- * (tile_m, tile_n) must be one of the shapes mx_tile_shapes lists, else
- * MX_ERR_SHAPE.  Everything else -- arguments, layouts, errors, results --
- * is as for mx_gemm.  It exists so that every kernel configuration can be
- * exercised (and timed) on any problem size.
+ * mx_gemm on the tile kernel with the output tile (and K split) chosen by the
+ * caller instead of the plan: (tile_m, tile_n) must be one of the shapes
+ * mx_tile_shapes lists, and split_k is 0 (the plan's choice) or 1 ..
+ * MX_MAX_SPLIT_K (K is then cut into that many slices of whole 512-K
+ * periods, or fewer when K is short); otherwise MX_ERR_SHAPE.  Everything
+ * else -- arguments, layouts, errors, results -- is as for mx_gemm.  It
+ * exists so that every kernel configuration can be exercised (and timed) on
+ * any problem size.
  */
+#define MX_MAX_SPLIT_K 8
 int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
                  const void *A, const void *A_scale,
                  const void *B, const void *B_scale,
-                 void *C, int out_dtype, int tile_m, int tile_n, void *stream);
+                 void *C, int out_dtype, int tile_m, int tile_n, int split_k,
+                 void *stream);
 
 #ifdef __cplusplus
 }

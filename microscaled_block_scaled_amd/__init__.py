@@ -21,6 +21,7 @@ OUT_FP32 = 1
 OUT_BF16 = 2
 MAX_DIM = 1 << 30     # largest M or N
 MAX_K = 1 << 24       # largest K
+MAX_SPLIT_K = 8       # largest forced K split (mx_gemm_tile)
 VARIANT_TILE = 1
 VARIANT_DECODE = 2
 
@@ -78,7 +79,7 @@ def lib():
     L.mx_tile_shapes.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int]
     L.mx_gemm_tile.restype = ctypes.c_int
     L.mx_gemm_tile.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp,
-                               ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -112,13 +113,15 @@ def tile_shapes():
     return [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
 
 
-def gemm_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0, tile=None):
+def gemm_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0, tile=None,
+             split_k=0):
     """Raw entry point: integer device addresses, returns the status code.
-    ``tile=(tile_m, tile_n)`` forces a tile shape (mx_gemm_tile)."""
+    ``tile=(tile_m, tile_n)`` forces a tile shape, and ``split_k`` (with a
+    tile) the number of K slices, 0 meaning the plan's choice (mx_gemm_tile)."""
     if tile is not None:
         return lib().mx_gemm_tile(int(fmt), int(M), int(N), int(K), A, A_scale, B,
                                   B_scale, C, int(out_dtype), int(tile[0]), int(tile[1]),
-                                  stream or None)
+                                  int(split_k), stream or None)
     return lib().mx_gemm(int(fmt), int(M), int(N), int(K), A, A_scale, B,
                          B_scale, C, int(out_dtype), stream or None)
 
@@ -150,9 +153,10 @@ def _as_u8(t, name):
 
 
 def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
-            tile=None):
+            tile=None, split_k=0):
     """C = A * B^T for MX-quantized A (M x K) and B (N x K); see module doc.
-    ``tile=(tile_m, tile_n)`` forces one of ``tile_shapes()``."""
+    ``tile=(tile_m, tile_n)`` forces one of ``tile_shapes()``, and with it
+    ``split_k`` the number of K slices (0: the plan's choice)."""
     import torch
     if out_dtype is None:
         out_dtype = torch.bfloat16
@@ -182,7 +186,7 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
         stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         rc = gemm_ptr(fmt, M, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
-                      b_scale.data_ptr(), out.data_ptr(), code, stream, tile)
+                      b_scale.data_ptr(), out.data_ptr(), code, stream, tile, split_k)
     if rc != MX_OK:
         _raise(rc)
     return out

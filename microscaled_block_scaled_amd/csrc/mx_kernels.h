@@ -30,6 +30,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <numeric>
+#include <type_traits>
+#include <utility>
+
 
 namespace mx {
 
@@ -136,7 +140,8 @@ __device__ __forceinline__ void static_for(F &&f)
 // waves, each owning a (BM/WGM) x (BN/WGN) block of 32x32 FP32 accumulators.
 //
 // K is walked in slabs: 128 bytes of every A and B row.  The LDS holds a
-// ring of S = 2 slabs and two scale buffers:
+// ring of S slabs (2 or 3, as the tile's LDS footprint allows) and two scale
+// buffers:
 //   * slab k+S-1 is copied HBM -> LDS directly (global_load_lds, no register
 //     staging) into the ring slot that slab k-1 has just vacated, so S-1
 //     slabs of copies are in flight while slab k is multiplied -- the
@@ -145,7 +150,11 @@ __device__ __forceinline__ void static_for(F &&f)
 //     4 E4M3 or 2 E2M1 slabs), one period ahead, into the scale buffer the
 //     period before last has vacated.  Row scales are K/32 bytes apart in
 //     memory, so a per-slab copy would cost one memory request per row for
-//     4-8 bytes; per period it is one request per row for 16;
+//     4-8 bytes; per period it is one request per row for 16.  A period's
+//     scales are issued at the opening of the previous period's first slab,
+//     before that opening's slab copies; with S-1 <= slabs per period, every
+//     slab of the period is issued after them, so the in-order wait for a
+//     slab's copies also covers its scales;
 //   * the operand fragments of step t+1 are read LDS -> registers (two
 //     register sets) while the MFMAs of step t run, the reads spread between
 //     the MFMAs;
@@ -155,11 +164,12 @@ __device__ __forceinline__ void static_for(F &&f)
 // swizzle is applied on the global side, since each lane's LDS slot is fixed
 // by its lane id.  The main loop is one basic block (no data-dependent
 // branches), so the compiler keeps the MFMAs where they are written.
-template <int FMT, int OUT, int BM, int BN, int WGM, int WGN>
+template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
-            void *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n, int gm)
+            void *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n, int gm,
+            int kchunk, int64_t cplane)
 {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -171,18 +181,15 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int DATA = ROWS * SW;                        // element bytes per slab
     constexpr int NSI = (ROWS + 63) / 64;                  // scale copy instructions
     constexpr int SBUF = NSI * 64 * 16;                    // one scale buffer
-    constexpr int S = 2;                                   // ring depth
     constexpr int RPC = 1024 / SW;                         // rows per copy instruction
     static_assert(S * DATA + 2 * SBUF <= 163840, "LDS budget");
-    static_assert(PS % S == 0 || S % PS == 0, "trip alignment");
+    static_assert(S >= 2 && S - 1 <= PS, "one period of scale lookahead covers the ring");
     static_assert(BM % RPC == 0 && BN % RPC == 0, "rows per copy instruction");
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be 32-aligned");
     constexpr int CPA = (BM / RPC + NW - 1) / NW;          // A copies per wave per slab
     constexpr int CPB = (BN / RPC + NW - 1) / NW;          // B copies per wave per slab
     constexpr int CPS = (NSI + NW - 1) / NW;               // scale copies per wave per period
     constexpr int NCOPY = CPA + CPB;
-    static_assert(NCOPY * (S - 2) < 64, "vmcnt range");
-    static_assert(S == 2 || S == 4, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * DATA + 2 * SBUF];
     uint8_t *const sbase = smem + S * DATA;                // scale buffers
@@ -190,14 +197,23 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
+    // Split-K: workgroup b computes K-slice b / (tiles_m*tiles_n), K-values
+    // [kb, kb + klen) with kb a multiple of kchunk (itself a multiple of 512,
+    // i.e. of whole scale periods), into the FP32 plane C + slice*cplane.
+    // Without split-K, kchunk == K and there is one slice.
+    const int ntiles = tiles_m * tiles_n;
+    const int slice = blockIdx.x / ntiles;
     int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
+    tile_of(blockIdx.x - slice * ntiles, tiles_m, tiles_n, gm, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;
-    const int sp = K / 32;
-    const int nslab = (int)((rowb + SW - 1) / SW);          // E2M1: the last may be half
+    const int kb = slice * kchunk, klen = min(kchunk, K - kb);
+    const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;      // row stride
+    const int64_t rowl = (FMT == FP4) ? (int64_t)klen / 2 : (int64_t)klen; // slice bytes per row
+    const int64_t kboff = (FMT == FP4) ? (int64_t)kb / 2 : (int64_t)kb;
+    const int sps = K / 32, sp = klen / 32;                  // scale row stride, slice extent
+    const int nslab = (int)((rowl + SW - 1) / SW);          // E2M1: the last may be half
     const int nper = (sp + 15) / 16;                       // scale periods
-    const int nsteps = K / 64;
+    const int nsteps = klen / 64;
 
     const int crow = lane / (SW / 16), cpc = lane % (SW / 16);   // row in a copy, LDS chunk
 
@@ -206,8 +222,9 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // Rows past the end of the matrix are clamped to its last row (their
     // results are never stored).
     static_assert(RPC == 8 && BM % 64 == 0, "copy geometry");
-    const uint8_t *const At = A + (int64_t)m0 * rowb, *const Bt = B + (int64_t)n0 * rowb;
-    const uint8_t *const Ast = As + (int64_t)m0 * sp, *const Bst = Bs + (int64_t)n0 * sp;
+    const uint8_t *const At = A + (int64_t)m0 * rowb + kboff, *const Bt = B + (int64_t)n0 * rowb + kboff;
+    const uint8_t *const Ast = As + (int64_t)m0 * sps + kb / 32;
+    const uint8_t *const Bst = Bs + (int64_t)n0 * sps + kb / 32;
     const int last_a = min(BM, M - m0) - 1, last_b = min(BN, N - n0) - 1;   // last row in the tile
     const uint32_t rowb32 = (uint32_t)rowb, lane_row = (uint32_t)crow * rowb32;
     // Global chunk this lane fetches: LDS chunk cpc of row r holds chunk
@@ -228,7 +245,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         const int64_t koff = (int64_t)k * SW;
         // E2M1 with K % 256 == 128: the last slab is half a row segment; its
         // upper half is never read, and its chunks are clamped into the row.
-        const uint32_t cmax = (uint32_t)(rowb - 16 - koff);
+        const uint32_t cmax = (uint32_t)(rowl - 16 - koff);
         const uint8_t *const Ak = At + koff, *const Bk = Bt + koff;
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
@@ -259,7 +276,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const bool in_a = i * 64 < BM;
             const int row = min(i * 64 + lane - (in_a ? 0 : BM), in_a ? last_a : last_b);
             const uint8_t *const src = (in_a ? Ast : Bst) + soff;
-            g2l_16(src + (uint32_t)row * (uint32_t)sp, sbase + buf * SBUF + i * 1024);
+            g2l_16(src + (uint32_t)row * (uint32_t)sps, sbase + buf * SBUF + i * 1024);
         }
     };
 
@@ -359,21 +376,25 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // step's operands in registers, and slab k1-1 is fully read), refill the
     // slot slab k1-1 vacated with slab k1+S-1, and at a period start fetch
     // the next period's scales into the buffer the previous period vacated.
+    // In-order wait for slab k1: after its copies came S-2 openings of
+    // (scales and) NCOPY copies.
+    constexpr int VMW = (S - 2) * NCOPY;
+    static_assert(VMW + NCOPY + CPS < 64, "vmcnt range");
     auto open = [&](int k1, int slot_next, bool period_start, int pbuf_next) {
-        wait_vm<NCOPY * (S - 2)>();
+        wait_vm<VMW>();
         lds_barrier();
-        issue(k1 + S - 1, slot_next);
         if (period_start) issue_scales(k1 / PS + 1, pbuf_next);
+        issue(k1 + S - 1, slot_next);
     };
     // Rows shorter than one period (K < 512: a single period, and too few
     // steps for the main loop to run) get their scale bytes with ordinary
     // loads in the prologue, copied exactly; longer rows use period copies.
     const bool short_rows = sp < 16;
     auto open_guarded = [&](int k1, int slot_next, bool period_start, int pbuf_next) {
-        wait_vm<NCOPY * (S - 2)>();
+        wait_vm<VMW>();
         lds_barrier();
-        issue(k1 + S - 1, slot_next);
         if (period_start && !short_rows) issue_scales(k1 / PS + 1, pbuf_next);
+        issue(k1 + S - 1, slot_next);
     };
     // Scale byte shift for slabs of the last period when it was copied short.
     const int last_shift = short_rows ? 0 : nper * 16 - sp;
@@ -383,8 +404,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // slabs 0..S-2 in flight, then open slab 0 and read step 0.
     if (short_rows) {
         for (int r = tid; r < ROWS; r += NW * 64) {
-            const uint8_t *src = (r < BM) ? As + (int64_t)min(m0 + r, M - 1) * sp
-                                          : Bs + (int64_t)min(n0 + r - BM, N - 1) * sp;
+            const uint8_t *src = ((r < BM) ? As + (int64_t)min(m0 + r, M - 1) * sps
+                                           : Bs + (int64_t)min(n0 + r - BM, N - 1) * sps) + kb / 32;
             for (int d = 0; d < sp; d += 4)
                 *(uint32_t *)(sbase + r * 16 + d) = *(const uint32_t *)(src + d);
         }
@@ -393,10 +414,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     }
 #pragma unroll
     for (int k = 0; k < S - 1; ++k) issue(k, k);
-    wait_vm<NCOPY * (S - 2)>();      // scales of period 0 and slab 0 done
+    wait_vm<VMW>();                  // scales of period 0 and slab 0 done
     lds_barrier();
-    issue(S - 1, S - 1);
     if (!short_rows) issue_scales(1, 1);
+    issue(S - 1, S - 1);
     Src cur = src_of(0, 0, 0, 0, shift_of(0));
     load_all(cur, 0);
 
@@ -406,7 +427,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // trip uses set q&1; step q+1 is in slab (q+1)/HS of the trip.  The loop
     // only runs when K spans more than one trip (K > 512), so its period
     // copies always have rows of at least 16 scale bytes.
-    constexpr int TS = (PS > S) ? PS : S;      // k0 is a multiple of PS: kq % PS is global
+    constexpr int TS = std::lcm(PS, S);       // k0 is a multiple of PS: kq % PS is global
     static_assert(TS % PS == 0 && TS % S == 0, "trip covers whole periods and rings");
     constexpr int TRIP = TS * HS;
     int t0 = 0;
@@ -462,7 +483,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     static_assert(NW * 32 * PITCH <= S * DATA + 2 * SBUF, "epilogue staging fits in LDS");
     uint8_t *const stage = smem + wave * 32 * PITCH;
     const bool vec_ok = ((int64_t)N * OS) % 16 == 0;
-    otype *const Cp = (otype *)C;
+    otype *const Cp = (otype *)C + (int64_t)slice * cplane;
     const int col0 = n0 + wn * WTN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -502,6 +523,37 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     }
 }
 
+
+// --------------------------------------------------------------------------
+// Split-K reduction: C[i] = sum over slices s = 0, 1, ... of W[s*plane + i],
+// added in slice order (so the result does not depend on timing), converted
+// to the output type.  plane is a multiple of 4 and W, C are 16-byte
+// aligned, so every group of 4 elements is one aligned vector access.
+template <int OUT>
+__global__ void __launch_bounds__(256)
+splitk_reduce(const float *__restrict__ W, void *__restrict__ C, int64_t mn, int64_t plane,
+              int slices)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= mn) return;
+    v4f acc = *(const v4f *)(W + i);
+    for (int s = 1; s < slices; ++s) acc += *(const v4f *)(W + s * plane + i);
+    const int n = (int)min((int64_t)4, mn - i);
+    if (OUT == OF32) {
+        float *c = (float *)C + i;
+        if (n == 4) *(v4f *)c = acc;
+        else for (int q = 0; q < n; ++q) c[q] = acc[q];
+    } else {
+        uint16_t *c = (uint16_t *)C + i;
+        if (n == 4) {
+            const uint32_t lo = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+            const uint32_t hi = f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+            *(uint2 *)c = make_uint2(lo, hi);
+        } else {
+            for (int q = 0; q < n; ++q) c[q] = f32_to_bf16(acc[q]);
+        }
+    }
+}
 
 // --------------------------------------------------------------------------
 // Small-M (decode) kernel, for M <= 32*MB.  C has few rows, so the GEMM is a

@@ -27,20 +27,43 @@ int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Tile shapes of the tiled kernel: {BM, BN, waves along M, waves along N}.
-struct TileCfg { int bm, bn, wgm, wgn; };
+// Tile shapes of the tiled kernel: {BM, BN, waves along M, waves along N,
+// LDS ring depth in slabs} (deeper rings where the LDS footprint allows).
+struct TileCfg { int bm, bn, wgm, wgn, stages; };
 constexpr TileCfg kTiles[] = {
-    {256, 256, 4, 2}, {256, 192, 4, 2}, {256, 160, 4, 1}, {256, 128, 4, 2},
-    {128, 128, 2, 2},
+    {256, 256, 4, 2, 2}, {256, 192, 4, 2, 2}, {256, 160, 4, 1, 2}, {256, 128, 4, 2, 3},
+    {128, 128, 2, 2, 3},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kCUs = 256;   // MI355X compute units: one 256-row tile per CU per wave
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Pick the tile whose grid fills whole waves of CUs best, weighting away the
-// padding in partial tiles; ties go to the larger tile (more reuse per byte).
-int choose_tile(int64_t M, int64_t N)
+// Split-K for grids too small to fill the chip: K is cut into slices of
+// whole 512-K scale periods, each slice a workgroup of its own writing an
+// FP32 plane of the workspace, and a second kernel adds the planes in order.
+// Slices double while the grid still fits in one wave of CUs and each slice
+// keeps at least kMinSliceK of K.
+constexpr int kMaxSplit = MX_MAX_SPLIT_K;
+constexpr int64_t kMinSliceK = 2048;
+constexpr int64_t kPeriodK = 512;
+
+int64_t slice_k(int64_t K, int split) { return cdiv(cdiv(K, split), kPeriodK) * kPeriodK; }
+
+int choose_split(int64_t tiles, int64_t K)
+{
+    int s = 1;
+    while (s < kMaxSplit && tiles * 2 * s <= kCUs && K / (2 * s) >= kMinSliceK) s *= 2;
+    return (int)cdiv(K, slice_k(K, s));        // slices actually needed
+}
+
+// FP32 elements per split-K plane (a multiple of 4 keeps planes 16-byte aligned).
+int64_t plane_of(int64_t M, int64_t N) { return cdiv(M * N, 64) * 64; }
+
+// Pick the tile (and split) whose grid fills whole waves of CUs best,
+// weighting away the padding in partial tiles; ties go to the larger tile
+// (more reuse per byte).
+int choose_tile(int64_t M, int64_t N, int64_t K)
 {
     int best = 0;
     double best_eff = -1.0;
@@ -48,27 +71,32 @@ int choose_tile(int64_t M, int64_t N)
         const TileCfg &c = kTiles[t];
         if (c.bm == 128 && M > 128) continue;      // 128-row tiles only for short M
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-        const double fill = (double)tiles / (double)(cdiv(tiles, kCUs) * kCUs);
+        const int64_t wgs = tiles * choose_split(tiles, K);
+        const double fill = (double)wgs / (double)(cdiv(wgs, kCUs) * kCUs);
         const double useful = (double)(M * N) / (double)(tiles * c.bm * c.bn);
-        const double eff = fill * useful;
+        // A split costs a workspace round trip: on a tie, no split wins.
+        const double eff = fill * useful * (wgs > tiles ? 0.98 : 1.0);
         if (eff > best_eff + 1e-9) { best_eff = eff; best = t; }
     }
     return best;
 }
 
-// Plan for tile t: which kernel, which tile, how many workgroups.
-void fill_plan(int t, int64_t M, int64_t N, mx_plan_t *p)
+// Plan for tile t: which kernel, which tile and split, how many workgroups.
+// split_req 0 lets the plan choose; otherwise K is cut into split_req
+// slices of whole periods (fewer if K is short).
+void fill_plan(int t, int64_t M, int64_t N, int64_t K, mx_plan_t *p, int split_req = 0)
 {
     memset(p, 0, sizeof(*p));
     const TileCfg &c = kTiles[t];
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
     p->variant = MX_VARIANT_TILE;
     p->tile_m = c.bm;
     p->tile_n = c.bn;
-    p->split_k = 1;
+    p->split_k = split_req > 0 ? (int)cdiv(K, slice_k(K, split_req)) : choose_split(tiles, K);
     p->threads = c.wgm * c.wgn * 64;
     p->lds_bytes = 0;
-    p->workgroups = cdiv(M, c.bm) * cdiv(N, c.bn);
-    p->workspace_bytes = 0;
+    p->workgroups = tiles * p->split_k;
+    p->workspace_bytes = p->split_k > 1 ? p->split_k * plane_of(M, N) * 4 : 0;
 }
 
 // Small-M kernel: one workgroup per 32 columns, kDecodeWaves waves splitting
@@ -96,7 +124,7 @@ int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t
     if (M <= kDecodeMaxM)
         fill_decode_plan(M, N, p);
     else
-        fill_plan(choose_tile(M, N), M, N, p);
+        fill_plan(choose_tile(M, N, K), M, N, K, p);
     return MX_OK;
 }
 
@@ -130,33 +158,48 @@ int device_ready(int *dev_out)
     return g_dev_status[dev];
 }
 
-template <int FMT, int OUT, int BM, int BN, int WGM, int WGN>
+// One tile-kernel launch; with split > 1 it writes FP32 planes to the
+// workspace W and the reduction kernel then produces C.
+template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S>
 void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
-                int64_t M, int64_t N, int64_t K, hipStream_t stream)
+                int64_t M, int64_t N, int64_t K, int split, float *W, hipStream_t stream)
 {
     const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
     const int gm = 4;
-    hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, BM, BN, WGM, WGN>),
-                       dim3((unsigned)(tiles_m * tiles_n)), dim3(WGM * WGN * 64), 0, stream,
-                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
-                       (const uint8_t *)Bs, C, (int)M, (int)N, (int)K, tiles_m, tiles_n, gm);
+    const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
+    if (split == 1) {
+        hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, BM, BN, WGM, WGN, S>), dim3(grid),
+                           dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
+                           (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, C,
+                           (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)K, (int64_t)0);
+        return;
+    }
+    const int64_t plane = plane_of(M, N);
+    hipLaunchKernelGGL((mx::tile_kernel<FMT, mx::OF32, BM, BN, WGM, WGN, S>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
+                       (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, (void *)W,
+                       (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)slice_k(K, split),
+                       plane);
+    hipLaunchKernelGGL((mx::splitk_reduce<OUT>), dim3((unsigned)cdiv(M * N, 1024)), dim3(256),
+                       0, stream, (const float *)W, C, M * N, plane, split);
 }
 
 template <int FMT, int OUT>
 bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
-                 const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
+                 const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
                  hipStream_t stream)
 {
-#define MX_CFG(BM_, BN_, WM_, WN_)                                                        \
+#define MX_CFG(BM_, BN_, WM_, WN_, S_)                                                    \
     if (p.tile_m == BM_ && p.tile_n == BN_ && p.threads == WM_ * WN_ * 64) {             \
-        launch_cfg<FMT, OUT, BM_, BN_, WM_, WN_>(A, As, B, Bs, C, M, N, K, stream);       \
+        launch_cfg<FMT, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, M, N, K, p.split_k,  \
+                                                     W, stream);                          \
         return true;                                                                      \
     }
-    MX_CFG(256, 256, 4, 2)
-    MX_CFG(256, 192, 4, 2)
-    MX_CFG(256, 160, 4, 1)
-    MX_CFG(256, 128, 4, 2)
-    MX_CFG(128, 128, 2, 2)
+    MX_CFG(256, 256, 4, 2, 2)
+    MX_CFG(256, 192, 4, 2, 2)
+    MX_CFG(256, 160, 4, 1, 2)
+    MX_CFG(256, 128, 4, 2, 3)
+    MX_CFG(128, 128, 2, 2, 3)
 #undef MX_CFG
     return false;
 }
@@ -188,11 +231,11 @@ bool launch_decode(const mx_plan_t &p, const void *A, const void *As, const void
 
 template <int FMT, int OUT>
 bool launch(const mx_plan_t &p, const void *A, const void *As, const void *B, const void *Bs,
-            void *C, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+            void *C, int64_t M, int64_t N, int64_t K, float *W, hipStream_t stream)
 {
     if (p.variant == MX_VARIANT_DECODE)
         return launch_decode<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, stream);
-    return launch_tile<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, stream);
+    return launch_tile<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, W, stream);
 }
 
 // Checks that need no device, then the device check, then the launch.
@@ -209,18 +252,27 @@ int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
     if (rc != MX_OK) return rc;
 
     hipStream_t s = (hipStream_t)stream;
-    (void)hipGetLastError();  // clear any stale error so the check below is ours
+    (void)hipGetLastError();  // clear any stale error so the checks below are ours
+    // Split-K workspace: stream-ordered, so it is released once the
+    // reduction that reads it has run, and reused from the runtime's pool.
+    float *W = nullptr;
+    if (plan.workspace_bytes > 0 &&
+        hipMallocAsync((void **)&W, (size_t)plan.workspace_bytes, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return MX_ERR_ALLOC;
+    }
     bool launched;
     if (fmt == MX_FMT_E2M1)
         launched = (out_dtype == MX_OUT_FP32)
-            ? launch<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
-            : launch<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
+            ? launch<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s)
+            : launch<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else
         launched = (out_dtype == MX_OUT_FP32)
-            ? launch<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, s)
-            : launch<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, s);
-    if (!launched || hipGetLastError() != hipSuccess) return MX_ERR_LAUNCH;
-    return MX_OK;
+            ? launch<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s)
+            : launch<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    const bool launch_ok = launched && hipGetLastError() == hipSuccess;
+    if (W) (void)hipFreeAsync(W, s);
+    return launch_ok ? MX_OK : MX_ERR_LAUNCH;
 }
 
 
@@ -274,14 +326,15 @@ extern "C" int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
 extern "C" int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
                             const void *A, const void *A_scale,
                             const void *B, const void *B_scale,
-                            void *C, int out_dtype, int tile_m, int tile_n, void *stream)
+                            void *C, int out_dtype, int tile_m, int tile_n, int split_k,
+                            void *stream)
 {
     int rc = check_args(fmt, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
     const int t = find_tile(tile_m, tile_n);
-    if (t < 0) return MX_ERR_SHAPE;
+    if (t < 0 || split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
     mx_plan_t plan;
-    fill_plan(t, M, N, &plan);
+    fill_plan(t, M, N, K, &plan, split_k);
     return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
 

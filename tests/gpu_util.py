@@ -22,12 +22,12 @@ def to_dev(case):
     return d
 
 
-def run_gpu(case, out_dtype, dev=None, stream=None, tile=None):
+def run_gpu(case, out_dtype, dev=None, stream=None, tile=None, split_k=0):
     import torch
     dev = dev or to_dev(case)
     tdt = torch.float32 if out_dtype == mxinputs.OUT_FP32 else torch.bfloat16
     C = mxg.mx_gemm(dev["A"], dev["A_scale"], dev["B"], dev["B_scale"], case["fmt"],
-                    out_dtype=tdt, stream=stream, tile=tile)
+                    out_dtype=tdt, stream=stream, tile=tile, split_k=split_k)
     torch.cuda.synchronize()
     return C
 
@@ -36,7 +36,7 @@ def host64(C):
     return C.float().cpu().numpy().astype(np.float64)
 
 
-def check_against_oracle(case, out_dtype, rows=None, C=None, tile=None):
+def check_against_oracle(case, out_dtype, rows=None, C=None, tile=None, split_k=0):
     """Run (or take) the GPU result and compare rows with the oracle.
 
     E4M3 results are judged with the oracle's 8-product group-alignment term
@@ -44,7 +44,7 @@ def check_against_oracle(case, out_dtype, rows=None, C=None, tile=None):
     products to the largest); the result also says how many elements miss
     the plain 1e-5 * T bound."""
     if C is None:
-        C = run_gpu(case, out_dtype, tile=tile)
+        C = run_gpu(case, out_dtype, tile=tile, split_k=split_k)
     g = host64(C)
     e4m3 = case["fmt"] == mxinputs.FMT_E4M3
     out = oracle.gemm(case["fmt"], case["A"], case["A_scale"], case["B"],

@@ -39,6 +39,7 @@ def test_header_constants_match_binding():
     limits = dict((k, 1 << int(v)) for k, v in
                   re.findall(r"#define (MX_MAX_[A-Z]+) \(\(int64_t\)1 << (\d+)\)", src))
     assert limits == {"MX_MAX_DIM": mxg.MAX_DIM, "MX_MAX_K": mxg.MAX_K}
+    assert int(re.search(r"#define MX_MAX_SPLIT_K (\d+)", src).group(1)) == mxg.MAX_SPLIT_K
 
 
 def test_strerror_covers_codes():
@@ -112,14 +113,18 @@ def test_tile_shapes_and_forced_tile_errors():
     assert (p["tile_m"], p["tile_n"]) in shapes
     L = mxg.lib()
     good = 1 << 20
-    # An unknown tile, or a bad shape, is rejected before any HIP call.
-    assert L.mx_gemm_tile(2, 64, 64, 128, good, good, good, good, good, 2, 100, 64,
+    # An unknown tile, a bad split or a bad shape is rejected before any HIP call.
+    assert L.mx_gemm_tile(2, 64, 64, 128, good, good, good, good, good, 2, 100, 64, 0,
                           None) == mxg.MX_ERR_SHAPE
-    assert L.mx_gemm_tile(2, 64, 64, 100, good, good, good, good, good, 2, 256, 192,
+    assert L.mx_gemm_tile(2, 64, 64, 100, good, good, good, good, good, 2, 256, 192, 0,
                           None) == mxg.MX_ERR_SHAPE
-    assert L.mx_gemm_tile(9, 64, 64, 128, good, good, good, good, good, 2, 256, 192,
+    assert L.mx_gemm_tile(2, 64, 64, 128, good, good, good, good, good, 2, 256, 192, -1,
+                          None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_tile(2, 64, 64, 128, good, good, good, good, good, 2, 256, 192,
+                          mxg.MAX_SPLIT_K + 1, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_tile(9, 64, 64, 128, good, good, good, good, good, 2, 256, 192, 0,
                           None) == mxg.MX_ERR_FORMAT
-    assert L.mx_gemm_tile(2, 64, 64, 128, None, good, good, good, good, 2, 256, 192,
+    assert L.mx_gemm_tile(2, 64, 64, 128, None, good, good, good, good, 2, 256, 192, 0,
                           None) == mxg.MX_ERR_NULL
 
 
@@ -141,6 +146,22 @@ def test_plan_small_m_uses_decode_variant(M, N):
         assert p["tile_m"] == (32 if M <= 32 else 64) and p["tile_n"] == 32
         assert p["workgroups"] == -(-N // 32) and p["split_k"] * 64 == p["threads"]
         assert p["workspace_bytes"] == 0
+
+
+def test_plan_split_k():
+    # Too few tiles for the GPU and a long K: K is split into whole 512-K
+    # periods, a workspace of one FP32 plane per slice is reported.
+    p = mxg.plan(mxg.FMT_E4M3, 256, 8192, 28672)
+    assert p["variant"] == mxg.VARIANT_TILE and p["split_k"] > 1
+    slice_k = -(-(-(-28672 // p["split_k"])) // 512) * 512
+    assert -(-28672 // slice_k) == p["split_k"]
+    tiles = -(-256 // p["tile_m"]) * -(-8192 // p["tile_n"])
+    assert p["workgroups"] == tiles * p["split_k"] <= 256
+    assert p["workspace_bytes"] >= p["split_k"] * 256 * 8192 * 4
+    # Enough tiles, or a short K: no split, no workspace.
+    for M, N, K in ((2048, 6144, 4096), (256, 8192, 2048)):
+        p = mxg.plan(mxg.FMT_E4M3, M, N, K)
+        assert p["split_k"] == 1 and p["workspace_bytes"] == 0
 
 
 def test_plan_larger_m_uses_tile_variant():

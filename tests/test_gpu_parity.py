@@ -83,18 +83,36 @@ def _tile_ids():
 @pytest.mark.parametrize("tile", mxg.tile_shapes(), ids=_tile_ids())
 @pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
 @pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
-def test_every_tile(tile, fmt, out):
+@pytest.mark.parametrize("split", [1, 3], ids=["nosplit", "split3"])
+def test_every_tile(tile, fmt, out, split):
     """Each kernel configuration, forced, on a ragged problem two tiles high
     and wide whose K walks several full main-loop trips and a partial one.
     E2M1 cases use an odd N (rows of C not 16-byte multiples: element-wise
     output stores), E4M3 cases an N that is a multiple of 8 (16-byte stores,
-    with a partial last tile)."""
+    with a partial last tile).  With split 3, K is cut into 3 slices of whole
+    512-K periods, the last one short: E2M1 K = 4736 -> 2048 + 2048 + 640
+    (ending in half a slab), E4M3 K = 2432 -> 1024 + 1024 + 384 (fewer than
+    16 scale bytes per row)."""
     M, N = tile[0] + 37, tile[1] + (19 if fmt == E2M1 else 24)
     K = 4736 if fmt == E2M1 else 2432           # 37 / 19 x 128
     case = mxinputs.make_random(fmt, M, N, K, seed=tile[0] + tile[1] + fmt)
-    log("every tile %s fmt=%d out=%d M=%d N=%d K=%d" % (tile, fmt, out, M, N, K))
-    res, *_ = check_against_oracle(case, out, tile=tile)
-    _assert_ok(res, "tile %s" % (tile,))
+    log("every tile %s split=%d fmt=%d out=%d M=%d N=%d K=%d" % (tile, split, fmt, out, M, N, K))
+    res, *_ = check_against_oracle(case, out, tile=tile, split_k=split)
+    _assert_ok(res, "tile %s split %d" % (tile, split))
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
+def test_split_k_planned(fmt, out):
+    """A grid too small for the GPU with a long K: the plan splits K itself
+    (4 slices of 2560 here, the last one 1152; ragged M and N)."""
+    M, N, K = 130, 250, 8192 + 640
+    p = mxg.plan(fmt, M, N, K, out)
+    assert p["variant"] == mxg.VARIANT_TILE and p["split_k"] > 1, p
+    case = mxinputs.make_random(fmt, M, N, K, seed=555 + fmt)
+    log("split-K planned fmt=%d out=%d split=%d" % (fmt, out, p["split_k"]))
+    res, *_ = check_against_oracle(case, out)
+    _assert_ok(res, "split-K planned")
 
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
