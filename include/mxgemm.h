@@ -98,20 +98,15 @@ int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
 const char *mx_strerror(int code);
 
 /*
- * Kernel variants a plan can choose.
- *   MX_VARIANT_TILE    M > 64: each workgroup computes one tile_m x tile_n
- *                      tile of C over all of K, staging A and B through LDS;
- *                      when the tiles cannot fill the GPU, over one of
- *                      split_k K-slices, each writing FP32 partial results
- *                      to a workspace that a second kernel adds in slice
- *                      order (workspace_bytes, taken with hipMallocAsync on
- *                      the caller's stream and released the same way).
- *   MX_VARIANT_DECODE  M <= 64: each workgroup computes all rows of C for 32
- *                      columns; its split_k waves each take a share of K,
- *                      streaming B from memory into registers, and their
- *                      partial results are added in LDS in wave order.
+ * Kernel variants a plan can choose.  There is one: every problem runs the
+ * tiled kernel, in which each workgroup computes one tile_m x tile_n tile of
+ * C, staging A and B through LDS.  Small M uses a 64-row tile.  When the
+ * tiles cannot fill the GPU and K is long, each workgroup takes one of
+ * split_k K-slices and writes FP32 partial results to a workspace that a
+ * second kernel adds in slice order (workspace_bytes, taken with
+ * hipMallocAsync on the caller's stream and released the same way).
  */
-enum { MX_VARIANT_TILE = 1, MX_VARIANT_DECODE = 2 };
+enum { MX_VARIANT_TILE = 1 };
 
 /* How mx_gemm would run a problem (filled by mx_gemm_plan). */
 typedef struct {

@@ -23,7 +23,6 @@ MAX_DIM = 1 << 30     # largest M or N
 MAX_K = 1 << 24       # largest K
 MAX_SPLIT_K = 8       # largest forced K split (mx_gemm_tile)
 VARIANT_TILE = 1
-VARIANT_DECODE = 2
 
 MX_OK = 0
 MX_ERR_FORMAT = -1

@@ -555,151 +555,4 @@ splitk_reduce(const float *__restrict__ W, void *__restrict__ C, int64_t mn, int
     }
 }
 
-// --------------------------------------------------------------------------
-// Small-M (decode) kernel, for M <= 32*MB.  C has few rows, so the GEMM is a
-// stream over B: one workgroup per 32 columns of C, its W waves each taking
-// a contiguous share of K (in 128-K units) and streaming their B rows from
-// HBM straight into registers, U units ahead, with no LDS staging and no
-// barriers.  A (M <= 64 rows) is read the same way; it is small and shared by
-// every workgroup, so it stays in L2.  The W partial 32*MB x 32 results are
-// then added in LDS in wave order, so the result does not depend on timing.
-//
-// Per 128-K unit u and lane (r, g), with row pointers at the lane's row:
-//   * E4M3, step p in {0, 1}: bytes 128u + 64p + 16g .. +15 (block 4u+2p) and
-//     128u + 64p + 32 + 16g .. +15 (block 4u+2p+1);
-//   * E2M1, step p in {0, 1}: bytes 64u + 32p + 16g .. +15;
-//   * scales: the dword of blocks 4u .. 4u+3; step p's MFMA takes block
-//     4u + 2p + g, i.e. byte 2p + g (the MFMA reads the low byte of its scale
-//     operand, so the dword is shifted right by 8*(2p + g)).
-template <int FMT, int OUT, int MB, int W, int U>
-__global__ void __launch_bounds__(W * 64)
-decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
-              const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
-              void *__restrict__ C, int M, int N, int K)
-{
-    constexpr int NL = (FMT == FP8) ? 4 : 2;   // 16-byte loads per row per unit
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = lane & 31, g = lane >> 5;
-    const int n0 = blockIdx.x * 32;
-    const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;
-    const int sp = K / 32;
-    const int nunits = K / 128;
-    const int u0 = wave * nunits / W, u1 = (wave + 1) * nunits / W;
-
-    // Lane rows (rows past the end of the matrix read its last row; their
-    // results are never stored).
-    const uint8_t *const bp = B + (int64_t)min(n0 + r, N - 1) * rowb;
-    const uint8_t *const bsp = Bs + (int64_t)min(n0 + r, N - 1) * sp;
-    const uint8_t *ap[MB], *asp[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int row = min(32 * mb + r, M - 1);
-        ap[mb] = A + (int64_t)row * rowb;
-        asp[mb] = As + (int64_t)row * sp;
-    }
-    // Byte offset of load l of a unit within the unit's row segment.
-    auto loff = [&](int l) {
-        return (FMT == FP8) ? 64 * (l >> 1) + 32 * (l & 1) + 16 * g : 32 * l + 16 * g;
-    };
-    constexpr int UB = (FMT == FP8) ? 128 : 64;   // row bytes per unit
-
-    struct Unit { v4i b[NL]; v4i a[MB][NL]; uint32_t bs, as[MB]; };
-    Unit ring[U];
-    // Every load is in range: u is clamped to the last unit of the matrix.
-    auto load_unit = [&](int u, Unit &x) {
-        u = min(u, nunits - 1);
-        const int64_t o = (int64_t)u * UB;
-#pragma unroll
-        for (int l = 0; l < NL; ++l) x.b[l] = *(const v4i *)(bp + o + loff(l));
-        x.bs = *(const uint32_t *)(bsp + 4 * u);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-            for (int l = 0; l < NL; ++l) x.a[mb][l] = *(const v4i *)(ap[mb] + o + loff(l));
-            x.as[mb] = *(const uint32_t *)(asp[mb] + 4 * u);
-        }
-    };
-
-    v16f acc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
-
-    auto compute = [&](const Unit &x) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int sh = 16 * p + 8 * g;
-            v8i bf;
-            if (FMT == FP8)
-                bf = v8i{x.b[2 * p][0], x.b[2 * p][1], x.b[2 * p][2], x.b[2 * p][3],
-                         x.b[2 * p + 1][0], x.b[2 * p + 1][1], x.b[2 * p + 1][2], x.b[2 * p + 1][3]};
-            else
-                bf = v8i{x.b[p][0], x.b[p][1], x.b[p][2], x.b[p][3], 0, 0, 0, 0};
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                v8i af;
-                if (FMT == FP8)
-                    af = v8i{x.a[mb][2 * p][0], x.a[mb][2 * p][1], x.a[mb][2 * p][2],
-                             x.a[mb][2 * p][3], x.a[mb][2 * p + 1][0], x.a[mb][2 * p + 1][1],
-                             x.a[mb][2 * p + 1][2], x.a[mb][2 * p + 1][3]};
-                else
-                    af = v8i{x.a[mb][p][0], x.a[mb][p][1], x.a[mb][p][2], x.a[mb][p][3],
-                             0, 0, 0, 0};
-                acc[mb] = mma<FMT>(af, bf, acc[mb], (int)(x.as[mb] >> sh), (int)(x.bs >> sh));
-            }
-        }
-    };
-
-    // Prologue: units u0 .. u0+U-1 in flight.  Main loop: whole groups of U
-    // units; each slot is consumed, then refilled with the unit U ahead.
-    // Loads complete in issue order, so the scheduling barriers keep every
-    // unit's loads behind the previous unit's: each compute then waits only
-    // for its own unit, with the U-1 later units still in flight.
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-        load_unit(u0 + i, ring[i]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    int u = u0;
-    for (; u + U <= u1; u += U) {
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-            compute(ring[i]);
-            load_unit(u + U + i, ring[i]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    // Tail: the last 0 .. U-1 units, already loaded.
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-        if (u + i < u1) compute(ring[i]);
-
-    // Deterministic reduction of the W partial results in LDS: element e of
-    // lane l of row block mb of wave w at red[((mb*16 + e)*W + w)*64 + l].
-    __shared__ float red[MB * 16 * W * 64];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) red[((mb * 16 + e) * W + wave) * 64 + lane] = acc[mb][e];
-    __syncthreads();
-    for (int t = threadIdx.x; t < MB * 16 * 64; t += W * 64) {
-        const int l = t & 63, e = (t >> 6) & 15, mb = t >> 10;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) v += red[((mb * 16 + e) * W + w) * 64 + l];
-        // Lane (c, g) of a 32x32 block holds, in element e, row
-        // 8*(e/4) + 4g + e%4 of column c.
-        const int row = 32 * mb + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
-        const int col = n0 + (l & 31);
-        if (row < M && col < N) {
-            if (OUT == OF32)
-                ((float *)C)[(int64_t)row * N + col] = v;
-            else
-                ((uint16_t *)C)[(int64_t)row * N + col] = f32_to_bf16(v);
-        }
-    }
-}
-
 }  // namespace mx

@@ -32,7 +32,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 struct TileCfg { int bm, bn, wgm, wgn, stages; };
 constexpr TileCfg kTiles[] = {
     {256, 256, 4, 2, 2}, {256, 192, 4, 2, 2}, {256, 160, 4, 1, 2}, {256, 128, 4, 2, 3},
-    {128, 128, 2, 2, 3},
+    {128, 128, 2, 2, 3}, {64, 256, 1, 8, 3},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kCUs = 256;   // MI355X compute units: one 256-row tile per CU per wave
@@ -50,10 +50,14 @@ constexpr int64_t kPeriodK = 512;
 
 int64_t slice_k(int64_t K, int split) { return cdiv(cdiv(K, split), kPeriodK) * kPeriodK; }
 
-int choose_split(int64_t tiles, int64_t K)
+// Measured on MI355X: 256-row tiles split until the grid fills the CUs once;
+// the 64-row tile (small M, B streamed from memory) is fastest at about half
+// that many workgroups.
+int choose_split(const TileCfg &c, int64_t tiles, int64_t K)
 {
+    const int64_t target = c.bm >= 128 ? kCUs : kCUs / 2;
     int s = 1;
-    while (s < kMaxSplit && tiles * 2 * s <= kCUs && K / (2 * s) >= kMinSliceK) s *= 2;
+    while (s < kMaxSplit && tiles * 2 * s <= target && K / (2 * s) >= kMinSliceK) s *= 2;
     return (int)cdiv(K, slice_k(K, s));        // slices actually needed
 }
 
@@ -69,13 +73,16 @@ int choose_tile(int64_t M, int64_t N, int64_t K)
     double best_eff = -1.0;
     for (int t = 0; t < kNumTiles; ++t) {
         const TileCfg &c = kTiles[t];
-        if (c.bm == 128 && M > 128) continue;      // 128-row tiles only for short M
+        if (c.bm < 256 && M > c.bm) continue;      // short tiles only for short M
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-        const int64_t wgs = tiles * choose_split(tiles, K);
-        const double fill = (double)wgs / (double)(cdiv(wgs, kCUs) * kCUs);
+        const int64_t wgs = tiles * choose_split(c, tiles, K);
+        const int64_t target = c.bm >= 128 ? kCUs : kCUs / 2;
+        const double fill = (double)wgs / (double)(cdiv(wgs, target) * target);
         const double useful = (double)(M * N) / (double)(tiles * c.bm * c.bn);
-        // A split costs a workspace round trip: on a tie, no split wins.
-        const double eff = fill * useful * (wgs > tiles ? 0.98 : 1.0);
+        // A split costs a workspace round trip of one FP32 plane per slice:
+        // on a tie, fewer slices win.
+        const int64_t split = wgs / tiles;
+        const double eff = fill * useful * (split > 1 ? 1.0 - 0.01 * (double)split : 1.0);
         if (eff > best_eff + 1e-9) { best_eff = eff; best = t; }
     }
     return best;
@@ -92,39 +99,18 @@ void fill_plan(int t, int64_t M, int64_t N, int64_t K, mx_plan_t *p, int split_r
     p->variant = MX_VARIANT_TILE;
     p->tile_m = c.bm;
     p->tile_n = c.bn;
-    p->split_k = split_req > 0 ? (int)cdiv(K, slice_k(K, split_req)) : choose_split(tiles, K);
+    p->split_k = split_req > 0 ? (int)cdiv(K, slice_k(K, split_req)) : choose_split(c, tiles, K);
     p->threads = c.wgm * c.wgn * 64;
     p->lds_bytes = 0;
     p->workgroups = tiles * p->split_k;
     p->workspace_bytes = p->split_k > 1 ? p->split_k * plane_of(M, N) * 4 : 0;
 }
 
-// Small-M kernel: one workgroup per 32 columns, kDecodeWaves waves splitting
-// K inside the workgroup; used for M <= kDecodeMaxM.
-constexpr int kDecodeWaves = 8;
-constexpr int kDecodeMaxM = 64;
-
-void fill_decode_plan(int64_t M, int64_t N, mx_plan_t *p)
-{
-    memset(p, 0, sizeof(*p));
-    p->variant = MX_VARIANT_DECODE;
-    p->tile_m = M <= 32 ? 32 : 64;
-    p->tile_n = 32;
-    p->split_k = kDecodeWaves;
-    p->threads = kDecodeWaves * 64;
-    p->lds_bytes = 0;
-    p->workgroups = cdiv(N, 32);
-    p->workspace_bytes = 0;
-}
-
 int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)
 {
     int rc = check_args(fmt, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
-    if (M <= kDecodeMaxM)
-        fill_decode_plan(M, N, p);
-    else
-        fill_plan(choose_tile(M, N, K), M, N, K, p);
+    fill_plan(choose_tile(M, N, K), M, N, K, p);
     return MX_OK;
 }
 
@@ -200,41 +186,15 @@ bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *
     MX_CFG(256, 160, 4, 1, 2)
     MX_CFG(256, 128, 4, 2, 3)
     MX_CFG(128, 128, 2, 2, 3)
+    MX_CFG(64, 256, 1, 8, 3)
 #undef MX_CFG
     return false;
-}
-
-template <int FMT, int OUT, int MB>
-void launch_decode_mb(const void *A, const void *As, const void *B, const void *Bs, void *C,
-                      int64_t M, int64_t N, int64_t K, hipStream_t stream)
-{
-    constexpr int U = (MB == 1) ? 4 : 3;   // 128-K units in flight per wave
-    hipLaunchKernelGGL((mx::decode_kernel<FMT, OUT, MB, kDecodeWaves, U>),
-                       dim3((unsigned)cdiv(N, 32)), dim3(kDecodeWaves * 64), 0, stream,
-                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
-                       (const uint8_t *)Bs, C, (int)M, (int)N, (int)K);
-}
-
-template <int FMT, int OUT>
-bool launch_decode(const mx_plan_t &p, const void *A, const void *As, const void *B,
-                   const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
-                   hipStream_t stream)
-{
-    if (p.tile_m == 32)
-        launch_decode_mb<FMT, OUT, 1>(A, As, B, Bs, C, M, N, K, stream);
-    else if (p.tile_m == 64)
-        launch_decode_mb<FMT, OUT, 2>(A, As, B, Bs, C, M, N, K, stream);
-    else
-        return false;
-    return true;
 }
 
 template <int FMT, int OUT>
 bool launch(const mx_plan_t &p, const void *A, const void *As, const void *B, const void *Bs,
             void *C, int64_t M, int64_t N, int64_t K, float *W, hipStream_t stream)
 {
-    if (p.variant == MX_VARIANT_DECODE)
-        return launch_decode<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, stream);
     return launch_tile<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, W, stream);
 }
 

@@ -138,14 +138,19 @@ def test_plan_shapes():
         mxg.plan(mxg.FMT_E4M3, 16, 16, 100)
 
 
-@pytest.mark.parametrize("M,N", [(1, 8192), (32, 100), (33, 8192), (64, 28672)])
-def test_plan_small_m_uses_decode_variant(M, N):
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (32, 100, 4096), (64, 8192, 28672),
+                                   (33, 28672, 4096)])
+def test_plan_small_m_uses_short_tile(M, N, K):
     for fmt in (mxg.FMT_E2M1, mxg.FMT_E4M3):
-        p = mxg.plan(fmt, M, N, 4096)
-        assert p["variant"] == mxg.VARIANT_DECODE
-        assert p["tile_m"] == (32 if M <= 32 else 64) and p["tile_n"] == 32
-        assert p["workgroups"] == -(-N // 32) and p["split_k"] * 64 == p["threads"]
-        assert p["workspace_bytes"] == 0
+        p = mxg.plan(fmt, M, N, K)
+        assert p["variant"] == mxg.VARIANT_TILE
+        assert (p["tile_m"], p["tile_n"]) == (64, 256)
+        tiles = -(-N // 256)
+        assert p["workgroups"] == tiles * p["split_k"]
+        # the short tile's grid is split up to about half the CUs
+        assert p["workgroups"] <= 128 or p["split_k"] == 1
+        if tiles <= 16 and K >= 8192:
+            assert p["split_k"] > 1 and p["workspace_bytes"] > 0
 
 
 def test_plan_split_k():
@@ -164,9 +169,10 @@ def test_plan_split_k():
         assert p["split_k"] == 1 and p["workspace_bytes"] == 0
 
 
-def test_plan_larger_m_uses_tile_variant():
+def test_plan_larger_m_uses_taller_tiles():
     for M in (65, 256, 2048):
-        assert mxg.plan(mxg.FMT_E4M3, M, 8192, 4096)["variant"] == mxg.VARIANT_TILE
+        p = mxg.plan(mxg.FMT_E4M3, M, 8192, 4096)
+        assert p["variant"] == mxg.VARIANT_TILE and p["tile_m"] >= 128
 
 
 def test_python_shim_rejects_bad_tensors():

@@ -49,21 +49,22 @@ def test_tails(fmt, out, M, N, K):
     _assert_ok(res, "tails")
 
 
-DECODE_SHAPES = [(1, 32, 128), (8, 97, 1152), (32, 64, 3968), (33, 40, 640),
-                 (64, 129, 2560), (17, 1000, 384)]
+SMALL_M_SHAPES = [(1, 32, 128), (8, 97, 1152), (32, 64, 3968), (33, 40, 640),
+                  (64, 129, 2560), (17, 1000, 384), (8, 300, 9216)]
 
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
 @pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
-def test_decode_variant(fmt, out, M, N, K):
-    """Small M runs the decode kernel: K split over the waves of a workgroup
-    (fewer 128-K units than waves when K < 1024), ragged N, 1..64 rows."""
-    assert mxg.plan(fmt, M, N, K, out)["variant"] == mxg.VARIANT_DECODE
+@pytest.mark.parametrize("M,N,K", SMALL_M_SHAPES)
+def test_small_m(fmt, out, M, N, K):
+    """Small M runs the 64-row tile (rows past M read row M-1, never stored),
+    with split-K when the grid is small and K long (the last shape)."""
+    p = mxg.plan(fmt, M, N, K, out)
+    assert p["tile_m"] == 64, p
     case = mxinputs.make_random(fmt, M, N, K, seed=1000 + M * 3 + N + K)
-    log("decode fmt=%d out=%d M=%d N=%d K=%d" % (fmt, out, M, N, K))
+    log("small M fmt=%d out=%d M=%d N=%d K=%d split=%d" % (fmt, out, M, N, K, p["split_k"]))
     res, *_ = check_against_oracle(case, out)
-    _assert_ok(res, "decode")
+    _assert_ok(res, "small M")
 
 
 @pytest.mark.parametrize("tile", [(256, 256), (128, 128)], ids=["256x256", "128x128"])
@@ -209,7 +210,7 @@ def test_bf16_is_rounded_fp32(fmt):
     assert torch.equal(c32.to(torch.bfloat16).view(torch.int16), c16.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [300, 40], ids=["tile", "decode"])
+@pytest.mark.parametrize("M", [300, 40], ids=["tall", "short"])
 def test_deterministic_and_stream(M):
     import torch
     case = mxinputs.make_random(E4M3, M, 260, 4096, seed=12)
