@@ -37,8 +37,10 @@
  * bit-for-bit deterministic for a given (M, N, K, formats, device).
  *
  * Thread safety.  Calls may be made concurrently from several host threads
- * and streams; the library keeps only read-only per-device state, set up
- * once per device on first use.
+ * and streams.  The library keeps read-only per-device state, set up once per
+ * device on first use, and, for split-K calls (see mx_plan_t), one workspace
+ * per (device, stream), grown on demand and held until the process exits;
+ * split-K calls on one stream are serialised while they are enqueued.
  */
 #ifndef MXGEMM_H
 #define MXGEMM_H
@@ -103,8 +105,9 @@ const char *mx_strerror(int code);
  * C, staging A and B through LDS.  Small M uses a 64-row tile.  When the
  * tiles cannot fill the GPU and K is long, each workgroup takes one of
  * split_k K-slices and writes FP32 partial results to a workspace that a
- * second kernel adds in slice order (workspace_bytes, taken with
- * hipMallocAsync on the caller's stream and released the same way).
+ * second kernel adds in slice order (workspace_bytes, taken from the
+ * library's per-stream workspace, allocated with hipMallocAsync on the
+ * caller's stream the first time a call needs more).
  */
 enum { MX_VARIANT_TILE = 1 };
 
@@ -117,7 +120,7 @@ typedef struct {
     int threads;            /* threads per workgroup                          */
     int lds_bytes;          /* dynamic LDS per workgroup                      */
     int64_t workgroups;     /* workgroups in the main launch                  */
-    int64_t workspace_bytes;/* device scratch the call allocates (0 = none)   */
+    int64_t workspace_bytes;/* split-K workspace the call uses (0 = none)     */
 } mx_plan_t;
 
 /*

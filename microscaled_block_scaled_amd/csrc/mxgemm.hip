@@ -3,6 +3,7 @@
 // the launch plan, and the kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
 #include <stdint.h>
 #include <string.h>
@@ -198,6 +199,32 @@ bool launch(const mx_plan_t &p, const void *A, const void *As, const void *B, co
     return launch_tile<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, W, stream);
 }
 
+// Split-K workspace, one per (device, stream), grown on demand with the
+// stream-ordered allocator and kept until the process exits, so repeated
+// calls do not allocate.  g_ws_mu is held from the lookup until both
+// kernels of a call are enqueued, so two host threads sharing a stream
+// cannot interleave their use of its workspace.
+struct Workspace { void *ptr = nullptr; size_t bytes = 0; };
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+float *stream_workspace(int dev, hipStream_t s, size_t bytes)
+{
+    Workspace &w = g_ws[{dev, s}];
+    if (w.bytes < bytes) {
+        if (w.ptr) (void)hipFreeAsync(w.ptr, s);
+        w = Workspace{};
+        void *p = nullptr;
+        if (hipMallocAsync(&p, bytes, s) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        w.ptr = p;
+        w.bytes = bytes;
+    }
+    return (float *)w.ptr;
+}
+
 // Checks that need no device, then the device check, then the launch.
 int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
              const void *A, const void *A_scale, const void *B, const void *B_scale,
@@ -213,13 +240,12 @@ int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();  // clear any stale error so the checks below are ours
-    // Split-K workspace: stream-ordered, so it is released once the
-    // reduction that reads it has run, and reused from the runtime's pool.
+    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     float *W = nullptr;
-    if (plan.workspace_bytes > 0 &&
-        hipMallocAsync((void **)&W, (size_t)plan.workspace_bytes, s) != hipSuccess) {
-        (void)hipGetLastError();
-        return MX_ERR_ALLOC;
+    if (plan.workspace_bytes > 0) {
+        ws_lock.lock();
+        W = stream_workspace(dev, s, (size_t)plan.workspace_bytes);
+        if (!W) return MX_ERR_ALLOC;
     }
     bool launched;
     if (fmt == MX_FMT_E2M1)
@@ -231,7 +257,6 @@ int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
             ? launch<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s)
             : launch<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s);
     const bool launch_ok = launched && hipGetLastError() == hipSuccess;
-    if (W) (void)hipFreeAsync(W, s);
     return launch_ok ? MX_OK : MX_ERR_LAUNCH;
 }
 
