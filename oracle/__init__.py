@@ -4,9 +4,10 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package.  It wraps ``liboracle.so`` (plain C, ``mx_oracle.c``), which
 shares no code with the GPU library.
 
-What the oracle computes, and where it comes from, is stated at the top of
+What the oracle computes, and where it comes from, is stated in
 ``mx_oracle.c``: exact per-32 block dot products of table-decoded E2M1/E4M3
-elements, each scaled by 2^(sA+sB-254), summed over blocks in double.
+elements, each scaled by 2^(sA+sB-254), summed over blocks in double; and the
+OCP MX quantization of a matrix (``quantize``).
 
 The acceptance rule lives here too:
   FP32 output: |gpu - C| <= 1e-5 * T
@@ -51,6 +52,8 @@ def _bind(lib):
     lib.mxo_block_contrib.restype = ctypes.c_double
     lib.mxo_block_contrib.argtypes = [ctypes.c_int, i64, u8p, u8p, u8p, u8p,
                                       i64, i64, i64, dp]
+    lib.mxo_quantize.restype = ctypes.c_int
+    lib.mxo_quantize.argtypes = [ctypes.c_int, i64, i64, dp, u8p, u8p]
     lib.mxo_gemm.restype = ctypes.c_int
     lib.mxo_gemm.argtypes = [ctypes.c_int, i64, i64, i64, u8p, u8p, u8p, u8p,
                              ctypes.POINTER(ctypes.c_int64), i64, dp, dp, dp,
@@ -131,6 +134,23 @@ class Oracle:
             raise ValueError("oracle rejected the arguments")
         return (C, T, E) if group_bound else (C, T)
 
+    def quantize(self, fmt, X):
+        """MX-quantize X (rows x K, values exactly representable in float64,
+        K a multiple of 32) -> (codes, scales) uint8 arrays: codes rows x K
+        (E4M3) or rows x K/2 (E2M1), scales rows x K/32."""
+        X = np.ascontiguousarray(X, dtype=np.float64)
+        if X.ndim != 2 or X.shape[1] % 32:
+            raise ValueError("X must be 2-D with a multiple of 32 columns")
+        rows, K = X.shape
+        Q = np.zeros((rows, K // 2 if fmt == FMT_E2M1 else K), np.uint8)
+        S = np.zeros((rows, K // 32), np.uint8)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        rc = self.lib.mxo_quantize(int(fmt), rows, K, X.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                   Q.ctypes.data_as(u8p), S.ctypes.data_as(u8p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return Q, S
+
     def block_contrib(self, fmt, A, A_scale, B, B_scale, K, m, n, b):
         """(contribution, magnitude) of block b to C[m][n]."""
         A, pa = _u8(A)
@@ -161,6 +181,10 @@ def gemm(*args, **kw):
 
 def block_contrib(*args, **kw):
     return default().block_contrib(*args, **kw)
+
+
+def quantize(*args, **kw):
+    return default().quantize(*args, **kw)
 
 
 def tables():

@@ -235,3 +235,99 @@ int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
     free(adec);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * MX quantization (the step before the GEMM): conversion of a matrix of
+ * wider values to MX elements and E8M0 scales by the OCP Microscaling v1.0
+ * rule, for checking a GPU quantizer.  The FlyDSL article times its scaled
+ * GEMMs from operands already in this form (section "Performance numbers
+ * need their baselines"); the rule itself is the OCP one:
+ *
+ * per block of 32 consecutive values x_j along K,
+ *   amax = max_j |x_j|
+ *   X    = floor(log2 amax) - emax   (emax: exponent of the element format's
+ *                                     largest normal, 2 for E2M1, 8 for E4M3)
+ *   s    = X + 127 clamped to [0, 254]   (the E8M0 byte; s = 0 if amax = 0)
+ *   P_j  = x_j * 2^(127 - s) rounded to the nearest element value, ties to
+ *          the even code (even last mantissa bit), magnitudes above the
+ *          format's largest (6, 448) saturating to it; the sign bit is x_j's
+ *          sign, also when the magnitude rounds to zero.
+ * A block holding a NaN or an infinity gets s = 255 (E8M0 NaN) and every
+ * element code 0.
+ */
+
+/* Magnitude a >= 0 (finite) -> element code without its sign bit, for a
+ * format with `man` mantissa bits, exponent bias `bias`, smallest normal
+ * exponent 1 - bias and largest magnitude `maxv`. */
+static unsigned encode_magnitude(double a, int man, int bias, double maxv)
+{
+    const int emin = 1 - bias;
+    if (a > maxv) a = maxv;
+    int e2;
+    frexp(a, &e2);                                   /* a = f * 2^e2, f in [0.5, 1) */
+    const int e = (a > 0.0) ? e2 - 1 : emin;         /* floor(log2 a) */
+    const double quantum = ldexp(1.0, (e < emin ? emin : e) - man);
+    const double v = nearbyint(a / quantum) * quantum;   /* ties to even */
+    if (v < ldexp(1.0, emin))                        /* subnormal or zero */
+        return (unsigned)(v / ldexp(1.0, emin - man));
+    frexp(v, &e2);
+    const int ev = e2 - 1;
+    const unsigned mant = (unsigned)((v / ldexp(1.0, ev) - 1.0) * (double)(1 << man));
+    return ((unsigned)(ev + bias) << man) | mant;
+}
+
+/* Quantize X (rows x K doubles, each an exact FP32 or BF16 value; K a
+ * multiple of 32) to Q (rows x K bytes for E4M3, rows x K/2 for E2M1, element
+ * 2i in the low nibble) and S (rows x K/32 E8M0 bytes).  Returns 0, or -1 on
+ * an argument the rule does not cover. */
+int mxo_quantize(int fmt, int64_t rows, int64_t K, const double *X, uint8_t *Q, uint8_t *S)
+{
+    if (fmt != MXO_FMT_E2M1 && fmt != MXO_FMT_E4M3) return -1;
+    if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
+    const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 8;
+    const int man = (fmt == MXO_FMT_E2M1) ? 1 : 3;
+    const int bias = (fmt == MXO_FMT_E2M1) ? 1 : 7;
+    const double maxv = (fmt == MXO_FMT_E2M1) ? 6.0 : 448.0;
+    const unsigned sign_bit = (fmt == MXO_FMT_E2M1) ? 8u : 128u;
+    const int64_t nb = K / 32, rb = row_bytes(fmt, K);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const double *x = X + r * K + 32 * b;
+            double amax = 0.0;
+            int finite = 1;
+            for (int j = 0; j < 32; ++j) {
+                if (!isfinite(x[j])) finite = 0;
+                else if (fabs(x[j]) > amax) amax = fabs(x[j]);
+            }
+            int s;
+            if (!finite) {
+                s = 255;
+            } else if (amax == 0.0) {
+                s = 0;
+            } else {
+                int e2;
+                frexp(amax, &e2);
+                s = (e2 - 1) - emax + 127;
+                s = s < 0 ? 0 : (s > 254 ? 254 : s);
+            }
+            S[r * nb + b] = (uint8_t)s;
+            for (int j = 0; j < 32; ++j) {
+                unsigned code = 0;
+                if (finite) {
+                    code = encode_magnitude(fabs(x[j]) * ldexp(1.0, 127 - s), man, bias, maxv);
+                    if (signbit(x[j])) code |= sign_bit;
+                }
+                const int64_t k = 32 * b + j;
+                if (fmt == MXO_FMT_E4M3) {
+                    Q[r * rb + k] = (uint8_t)code;
+                } else {
+                    uint8_t *byte = &Q[r * rb + (k >> 1)];
+                    if (k & 1) *byte = (uint8_t)((*byte & 0x0fu) | (code << 4));
+                    else *byte = (uint8_t)((*byte & 0xf0u) | code);
+                }
+            }
+        }
+    }
+    return 0;
+}

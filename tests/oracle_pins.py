@@ -352,7 +352,130 @@ def pin_group_bound(orc):
         assert E.any()
 
 
+# --------------------------------------------------------------------------
+# The quantizer (mxo_quantize): OCP MX conversion of wider values.
+
+def _sweep_values(vmax, positive_grid):
+    """Values in [-vmax, vmax]: every grid point, every midpoint between
+    neighbours (the ties), points just beside each midpoint, and a random
+    sample; as float32 (all exact in float64)."""
+    g = np.asarray(sorted(set(positive_grid)), np.float64)
+    mids = (g[1:] + g[:-1]) / 2
+    eps = np.float32(1e-6)
+    extra = np.concatenate([mids * (1 - eps), mids * (1 + eps)])
+    rng = np.random.default_rng(7)
+    rnd = rng.uniform(0, vmax, 4000)
+    v = np.concatenate([g, mids, extra, rnd]).astype(np.float32).astype(np.float64)
+    v = v[v <= vmax]
+    return np.concatenate([v, -v])
+
+
+def _blocks_with_amax(vals, amax):
+    """Pack values into blocks of 31 plus one element equal to amax, so that
+    every block's shared exponent is floor(log2 amax) - emax."""
+    n = -(-len(vals) // 31)
+    vals = np.concatenate([vals, np.zeros(n * 31 - len(vals))])
+    blocks = np.concatenate([np.full((n, 1), amax), vals.reshape(n, 31)], axis=1)
+    return blocks.reshape(1, -1)
+
+
+def pin_quantize_e4m3_vs_torch(orc):
+    """Elements: with amax = 448 the shared exponent is 0 (byte 127), so each
+    code must equal torch's float8_e4m3fn conversion (round to nearest even)
+    of the value itself."""
+    import torch
+    t8 = torch_e4m3()
+    grid = [abs(x) for x in t8[np.isfinite(t8)]]
+    vals = _sweep_values(448.0, grid)
+    X = _blocks_with_amax(vals, 448.0)
+    Q, S = orc.quantize(E4M3, X)
+    assert (S == 127).all(), "E4M3 scale byte for amax 448 must be 127"
+    ref = torch.from_numpy(X.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (Q == ref).all(), "E4M3 codes differ from torch's conversion at %s" % (
+        X[Q != ref][:5],)
+    # Saturation: above 448 (torch would give NaN past 464) the code is +-448.
+    X = _blocks_with_amax(np.array([449.0, 460.0, 479.0, -470.0]), 479.0)
+    Q, S = orc.quantize(E4M3, X)
+    assert S[0, 0] == 127 and (Q[0, :5] == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]).all(), Q[0, :5]
+
+
+def pin_quantize_e2m1_bruteforce(orc):
+    """Elements: with amax = 6 the shared exponent is 0, so each code must be
+    the nearest E2M1 value (independent golden table), ties to the code with
+    an even last bit, sign from the value."""
+    g = golden_e2m1()
+    vals = _sweep_values(6.0, [abs(x) for x in g])
+    X = _blocks_with_amax(vals, 6.0)
+    Q, S = orc.quantize(E2M1, X)
+    assert (S == 127).all(), "E2M1 scale byte for amax 6 must be 127"
+    codes = mxinputs.unpack_e2m1(Q)[0]
+    mags = np.abs(g[:8])
+    for x, c in zip(X[0], codes):
+        d = np.abs(mags - abs(x))
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        want |= 8 if np.signbit(x) else 0
+        assert c == want, "E2M1 code for %r: got %d want %d" % (x, c, want)
+
+
+def pin_quantize_scale_rule(orc):
+    """Scale bytes: floor(log2 amax) from Python's frexp, minus emax, plus
+    127, clamped to [0, 254]; 0 for an all-zero block.  amax ranges over
+    FP32 subnormals, exact powers of two and the values just below them."""
+    amaxes = [0.0, 2.0 ** -149, 2.0 ** -140, 2.0 ** -126, 3.0 * 2 ** -130, 1.0, 6.0, 7.99,
+              8.0, 448.0, 512.0, 1e30, 2.0 ** 127, 3.4e38]
+    for e in range(-120, 120, 7):
+        amaxes += [2.0 ** e, float(np.nextafter(np.float32(2.0 ** e), np.float32(0)))]
+    for fmt, emax in ((E2M1, 2), (E4M3, 8)):
+        X = np.zeros((len(amaxes), 32))
+        X[:, 5] = amaxes
+        X[:, 9] = -np.asarray(amaxes) / 3.0          # smaller magnitude, other sign
+        _, S = orc.quantize(fmt, X)
+        for a, s in zip(amaxes, S[:, 0]):
+            want = 0 if a == 0 else min(254, max(0, math.frexp(a)[1] - 1 - emax + 127))
+            assert s == want, "fmt %d amax %r: scale %d want %d" % (fmt, a, s, want)
+
+
+def pin_quantize_nonfinite(orc):
+    """A block holding a NaN or an infinity gets scale byte 255 and zero codes;
+    its neighbours are unaffected."""
+    for fmt in (E2M1, E4M3):
+        X = np.ones((3, 64))
+        X[0, 3] = np.nan
+        X[1, 40] = np.inf
+        X[2, 0] = -np.inf
+        Q, S = orc.quantize(fmt, X)
+        assert S[0, 0] == 255 and S[1, 1] == 255 and S[2, 0] == 255
+        assert S[0, 1] != 255 and S[1, 0] != 255 and S[2, 1] != 255
+        codes = Q if fmt == E4M3 else mxinputs.unpack_e2m1(Q)
+        assert (codes[0, :32] == 0).all() and (codes[1, 32:] == 0).all()
+        assert (codes[0, 32:] != 0).all()
+
+
+def pin_quantize_roundtrip(orc):
+    """Decoding (independent tables) the quantized values of random data gives
+    back each value to within half the element spacing times 2^X, except
+    where it saturated; and each nonzero block's largest value lands in the
+    format's top binade (the definition of the shared exponent)."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((40, 256)) * np.exp2(rng.integers(-30, 30, (40, 1)))
+    X = X.astype(np.float32).astype(np.float64)
+    for fmt, man, top in ((E2M1, 1, 4.0), (E4M3, 3, 256.0)):
+        Q, S = orc.quantize(fmt, X)
+        deq = dequant(fmt, Q, S)
+        scale = np.repeat(np.exp2(S.astype(np.int64) - 127.0), 32, axis=1)
+        mag = np.abs(X) / scale
+        _, e = np.frexp(np.maximum(mag, 2.0 ** -60))
+        spacing = np.exp2(np.maximum(e - 1, 1 - (1 if fmt == E2M1 else 7)) - man) * scale
+        sat = mag > (6.0 if fmt == E2M1 else 448.0)
+        err = np.abs(deq - X)
+        assert (err[~sat] <= spacing[~sat] / 2 * (1 + 1e-12)).all(), fmt
+        bmax = np.abs(deq).reshape(40, -1, 32).max(axis=2) / scale[:, ::32]
+        assert (bmax >= top).all(), fmt
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
-            pin_group_bound]
+            pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
+            pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip]

@@ -114,3 +114,16 @@ def test_case_shapes():
     assert c["B"].shape == (256, 128) and c["B_scale"].shape == (256, 8)
     c2 = mxinputs.make_random(E4M3, 3, 5, 128, seed=1)
     assert c2["A"].shape == (3, 128) and c2["B_scale"].shape == (5, 4)
+
+
+@pytest.mark.parametrize("fmt", [mxinputs.FMT_E2M1, mxinputs.FMT_E4M3], ids=["e2m1", "e4m3"])
+def test_generator_quantizer_matches_oracle(orc, fmt):
+    """The input generator's numpy quantizer and the oracle's C quantizer are
+    two implementations of the same OCP rule: they agree on every byte."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((64, 512)) * np.exp2(rng.integers(-20, 20, (64, 1)))).astype(np.float32)
+    x[3, :32] = 0.0
+    codes, scales = mxinputs.quantize(x, fmt)
+    q, s = orc.quantize(fmt, x.astype(np.float64))
+    assert (scales == s).all()
+    assert (codes == q).all()

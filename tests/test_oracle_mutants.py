@@ -44,6 +44,20 @@ MUTANTS = [
      "int64_t m = rows ? rows[i0] : i0 + i;\n                    const"),
     ("b_row_stride", "bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);",
      "bdec[k] = decode_elem(fmt, B + n * (rb - 1), k, t4, t8);"),
+    # The quantizer.
+    ("q_e4m3_emax", "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 8;",
+     "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 7;"),
+    ("q_ties_away", "nearbyint(a / quantum)", "round(a / quantum)"),
+    ("q_no_saturation", "if (a > maxv) a = maxv;", ""),
+    ("q_negative_zero", "if (signbit(x[j])) code |= sign_bit;",
+     "if (x[j] < 0.0) code |= sign_bit;"),
+    ("q_scale_unclamped_low", "s = s < 0 ? 0 : (s > 254 ? 254 : s);",
+     "s = s > 254 ? 254 : s;"),
+    ("q_log2_off_by_one", "s = (e2 - 1) - emax + 127;", "s = e2 - emax + 127;"),
+    ("q_subnormal_grid", "ldexp(1.0, (e < emin ? emin : e) - man)", "ldexp(1.0, e - man)"),
+    ("q_nibble_order", "if (k & 1) *byte", "if (!(k & 1)) *byte"),
+    ("q_nonfinite_ignored", "if (!isfinite(x[j])) finite = 0;\n                else if",
+     "if (0) finite = 0;\n                else if"),
 ]
 
 
