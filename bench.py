@@ -180,6 +180,51 @@ def bench_one(name, steps, warmup, with_cpu):
     return res
 
 
+def bench_quantize(steps, warmup, fmt, in_dtype):
+    """MX quantization of the fused-QKV operands (A and B stacked: 8192 x
+    4096 values) from FP32 or BF16: HBM-bound, reported against 8 TB/s."""
+    import torch
+    import microscaled_block_scaled_amd as mxg
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    rows, K = 8192, 4096
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    x = torch.randn((rows, K), generator=g, dtype=torch.float32)
+    tdt = torch.float32 if in_dtype == mxg.IN_FP32 else torch.bfloat16
+    x = x.to(tdt).to(dev)
+    q = torch.empty((rows, K // 2 if fmt == mxinputs.FMT_E2M1 else K), dtype=torch.uint8, device=dev)
+    qs = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = (fmt, in_dtype, rows, K, x.data_ptr(), q.data_ptr(), qs.data_ptr(), stream.cuda_stream)
+    for _ in range(warmup):
+        if mxg.quantize_ptr(*args) != 0:
+            raise RuntimeError("mx_quantize failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        mxg.quantize_ptr(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = e0.elapsed_time(e1) / steps / 1e3
+    nbytes = rows * K * x.element_size() + q.numel() + qs.numel()
+    achieved = nbytes / launch_s / 1e9
+    return {"metric": "MX quantize GB/s (HBM bytes read + written)",
+            "value": round(nbytes * steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32" if in_dtype == mxg.IN_FP32 else "bf16", "data": "synthetic",
+            "config": {"workload": "quantize_%s_from_%s_8192x4096" % (
+                mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
+                "rows": rows, "K": K, "kernel_source_sha256": kernel_source_hash()},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "traffic": None, "algorithmic_bytes": nbytes,
+                         "launch_us": round(launch_s * 1e6, 2)}}
+
+
 def copy_calibration(nbytes=256 << 20, reps=3):
     """A plain device copy of known size, for scaling the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the GEMM kernels."""
@@ -205,6 +250,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
+    ap.add_argument("--quantize", action="store_true",
+                    help="time mx_quantize (both formats, FP32 and BF16 input) instead")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
@@ -213,6 +260,11 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.quantize:
+        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):
+            for ind in (1, 2):
+                print(json.dumps(bench_quantize(a.steps, a.warmup, fmt, ind)), flush=True)
         return
     names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \
         if a.all else [a.workload]

@@ -70,8 +70,12 @@ enum {
     MX_ERR_NO_DEVICE = -6,  /* no HIP device is visible                       */
     MX_ERR_ARCH = -7,       /* the current device is not gfx950               */
     MX_ERR_ALLOC = -8,      /* split-K workspace allocation failed            */
-    MX_ERR_LAUNCH = -9      /* a kernel launch failed                         */
+    MX_ERR_LAUNCH = -9,     /* a kernel launch failed                         */
+    MX_ERR_IN_DTYPE = -10   /* in_dtype is not MX_IN_FP32 / MX_IN_BF16       */
 };
+
+/* Input element types of mx_quantize. */
+enum { MX_IN_FP32 = 1, MX_IN_BF16 = 2 };
 
 /* Largest M or N accepted (keeps every tile index in 32 bits). */
 #define MX_MAX_DIM ((int64_t)1 << 30)
@@ -154,6 +158,33 @@ int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
                  const void *B, const void *B_scale,
                  void *C, int out_dtype, int tile_m, int tile_n, int split_k,
                  void *stream);
+
+/*
+ * MX quantization, the step that produces mx_gemm's operands: X (rows x K,
+ * FP32 or BF16, K-contiguous) -> Q and Q_scale in the layouts described
+ * above for A and A_scale.  The rule is the OCP Microscaling v1.0
+ * conversion (the FlyDSL article times its scaled GEMMs from operands
+ * already in this form, section "Performance numbers need their
+ * baselines"); per block of 32 consecutive values x along K:
+ *   X = floor(log2 max|x|) - emax      (emax = 2 for E2M1, 8 for E4M3)
+ *   scale byte = X + 127, clamped to [0, 254]; 0 for an all-zero block
+ *   element    = x * 2^(127 - scale byte) rounded to the nearest element
+ *                value (ties to the code with an even last bit), magnitudes
+ *                above 6 (E2M1) / 448 (E4M3) saturating, sign kept
+ *   a block holding a NaN or an infinity: scale byte 255, element codes 0.
+ *   fmt        MX_FMT_E2M1 or MX_FMT_E4M3
+ *   in_dtype   MX_IN_FP32 or MX_IN_BF16
+ *   rows, K    rows >= 1, K >= 32, K % 32 == 0, both <= MX_MAX_DIM
+ *   X          device pointer, 16-byte aligned
+ *   Q          device pointer, 8-byte aligned: rows x K bytes (E4M3) or
+ *              rows x K/2 bytes (E2M1, element 2i in the low nibble)
+ *   Q_scale    device pointer: rows x K/32 bytes
+ *   stream     hipStream_t, or NULL
+ * Returns MX_OK or a negative MX_ERR_* code; errors and asynchrony as for
+ * mx_gemm.  Outputs must not overlap X.
+ */
+int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
+                const void *X, void *Q, void *Q_scale, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,10 @@ a: (M, K/2) uint8 for MXFP4 (E2M1, two elements per byte, element 2i in the
    low nibble), or (M, K) uint8 / float8_e4m3fn for MXFP8 (E4M3);
 b: (N, ...) likewise; a_scale: (M, K/32) uint8 E8M0; b_scale: (N, K/32).
 Returns C = A * B^T, (M, N), float32 or bfloat16.
+
+    q, q_scale = mx_quantize(x, fmt)
+
+quantizes a float32 / bfloat16 matrix into that operand layout (OCP MX rule).
 """
 import ctypes
 import os
@@ -34,8 +38,13 @@ MX_ERR_NO_DEVICE = -6
 MX_ERR_ARCH = -7
 MX_ERR_ALLOC = -8
 MX_ERR_LAUNCH = -9
+MX_ERR_IN_DTYPE = -10
 
-_VALUE_ERRORS = (MX_ERR_FORMAT, MX_ERR_OUT_DTYPE, MX_ERR_SHAPE, MX_ERR_NULL, MX_ERR_ALIGN)
+IN_FP32 = 1
+IN_BF16 = 2
+
+_VALUE_ERRORS = (MX_ERR_FORMAT, MX_ERR_OUT_DTYPE, MX_ERR_SHAPE, MX_ERR_NULL, MX_ERR_ALIGN,
+                 MX_ERR_IN_DTYPE)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxgemm.so")
 _lib = None
@@ -79,6 +88,8 @@ def lib():
     L.mx_gemm_tile.restype = ctypes.c_int
     L.mx_gemm_tile.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp,
                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    L.mx_quantize.restype = ctypes.c_int
+    L.mx_quantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, vp, vp, vp, vp]
     _lib = L
     return L
 
@@ -189,3 +200,38 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
     if rc != MX_OK:
         _raise(rc)
     return out
+
+
+def quantize_ptr(fmt, in_dtype, rows, K, X, Q, Q_scale, stream=0):
+    """Raw entry point of mx_quantize: integer device addresses, status code."""
+    return lib().mx_quantize(int(fmt), int(in_dtype), int(rows), int(K), X, Q, Q_scale,
+                             stream or None)
+
+
+def mx_quantize(x, fmt, stream=None):
+    """MX-quantize x (rows x K float32 or bfloat16 on the GPU, K a multiple of
+    32) -> (q, q_scale) uint8 tensors in mx_gemm's operand layout: q is
+    rows x K (E4M3) or rows x K/2 (E2M1), q_scale rows x K/32."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D torch.Tensor")
+    if x.dtype == torch.float32:
+        code = IN_FP32
+    elif x.dtype == torch.bfloat16:
+        code = IN_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    if not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous GPU tensor")
+    if fmt not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    rows, K = x.shape
+    q = torch.empty((rows, K // 2 if fmt == FMT_E2M1 else K), dtype=torch.uint8, device=x.device)
+    qs = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = quantize_ptr(fmt, code, rows, K, x.data_ptr(), q.data_ptr(), qs.data_ptr(), stream)
+    if rc != MX_OK:
+        _raise(rc)
+    return q, qs

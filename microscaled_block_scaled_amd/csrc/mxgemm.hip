@@ -3,6 +3,7 @@
 // the launch plan, and the kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <stdint.h>
@@ -10,6 +11,7 @@
 
 #include "mxgemm.h"
 #include "mx_kernels.h"
+#include "mx_quant.h"
 
 namespace {
 
@@ -276,6 +278,7 @@ extern "C" const char *mx_strerror(int code)
     case MX_ERR_ARCH: return "current device is not gfx950";
     case MX_ERR_ALLOC: return "workspace allocation failed";
     case MX_ERR_LAUNCH: return "kernel launch failed";
+    case MX_ERR_IN_DTYPE: return "unsupported input type (expected MX_IN_FP32 or MX_IN_BF16)";
     default: return "unknown error code";
     }
 }
@@ -323,3 +326,36 @@ extern "C" int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
     return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
 
+
+extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
+                           const void *X, void *Q, void *Q_scale, void *stream)
+{
+    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3) return MX_ERR_FORMAT;
+    if (in_dtype != MX_IN_FP32 && in_dtype != MX_IN_BF16) return MX_ERR_IN_DTYPE;
+    if (rows < 1 || K < 32 || K % 32 != 0 || rows > MX_MAX_DIM || K > MX_MAX_DIM)
+        return MX_ERR_SHAPE;
+    if (!X || !Q || !Q_scale) return MX_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(Q, 8)) return MX_ERR_ALIGN;
+    int dev = -1;
+    const int rc = device_ready(&dev);
+    if (rc != MX_OK) return rc;
+    const int64_t nblocks = rows * (K / 32);
+    const int lpb = in_dtype == MX_IN_FP32 ? 8 : 4;            // lanes per block
+    const int64_t per_wg = 256 / lpb;                          // blocks per pass
+    const unsigned grid = (unsigned)std::min<int64_t>(cdiv(nblocks, per_wg), 8 * kCUs);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    uint8_t *q = (uint8_t *)Q, *qs = (uint8_t *)Q_scale;
+    if (fmt == MX_FMT_E2M1) {
+        if (in_dtype == MX_IN_FP32)
+            hipLaunchKernelGGL((mx::quantize_kernel<mx::FP4, mx::IN_F32>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+        else
+            hipLaunchKernelGGL((mx::quantize_kernel<mx::FP4, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+    } else {
+        if (in_dtype == MX_IN_FP32)
+            hipLaunchKernelGGL((mx::quantize_kernel<mx::FP8, mx::IN_F32>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+        else
+            hipLaunchKernelGGL((mx::quantize_kernel<mx::FP8, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+    }
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}

@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_strerror_covers_codes():
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = mxg.strerror(code)
         assert s and s != "unknown error code", code
     assert mxg.strerror(5) == "unknown error code"
@@ -188,3 +188,27 @@ def test_python_shim_rejects_bad_tensors():
     with pytest.raises(ValueError):          # non-contiguous
         mxg.mx_gemm(torch.zeros((16, 128), dtype=torch.uint8)[:, ::2], s, a, s,
                     fmt=mxg.FMT_E2M1)
+
+
+@pytest.mark.parametrize("fmt,ind,rows,K,code", [
+    (3, 1, 4, 64, mxg.MX_ERR_FORMAT),
+    (1, 3, 4, 64, mxg.MX_ERR_IN_DTYPE),
+    (2, 0, 4, 64, mxg.MX_ERR_IN_DTYPE),
+    (1, 1, 0, 64, mxg.MX_ERR_SHAPE),
+    (1, 1, 4, 0, mxg.MX_ERR_SHAPE),
+    (2, 2, 4, 48, mxg.MX_ERR_SHAPE),
+    (2, 2, 4, 16, mxg.MX_ERR_SHAPE),
+    (2, 1, (1 << 30) + 1, 32, mxg.MX_ERR_SHAPE),
+])
+def test_quantize_argument_errors(fmt, ind, rows, K, code):
+    good = 1 << 20            # never dereferenced: the checks fail first
+    assert mxg.lib().mx_quantize(fmt, ind, rows, K, good, good, good, None) == code
+
+
+def test_quantize_null_and_alignment_errors():
+    L = mxg.lib()
+    good = 1 << 20
+    assert L.mx_quantize(1, 1, 4, 64, None, good, good, None) == mxg.MX_ERR_NULL
+    assert L.mx_quantize(1, 1, 4, 64, good, good, None, None) == mxg.MX_ERR_NULL
+    assert L.mx_quantize(1, 1, 4, 64, good + 8, good, good, None) == mxg.MX_ERR_ALIGN
+    assert L.mx_quantize(2, 2, 4, 64, good, good + 4, good, None) == mxg.MX_ERR_ALIGN
