@@ -30,16 +30,12 @@ __device__ __forceinline__ int floor_log2(float a)
     return (31 - __clz((int)(u & 0x7fffffu))) - 149;
 }
 
-// E2M1 code of y (|y| already at most a little above 6): the number of
-// midpoints between neighbouring values that |y| lies above, where a tie
-// goes to the even code (0.75, 1.75 and 3.5 round up; 0.25, 1.25, 2.5 and 5
-// round down), plus the sign bit.
-__device__ __forceinline__ uint32_t e2m1_code(float y)
+// Two E2M1 codes in one byte (low nibble: a, high nibble: b): gfx950's
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest, ties to the even
+// code, saturates at +-6 and keeps the sign (also of zero).
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b)
 {
-    const float a = fabsf(y);
-    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-                 (a >= 3.5f) + (a > 5.0f);
-    return c | ((__float_as_uint(y) >> 28) & 8u);
+    return (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xffu;
 }
 
 // Two E4M3 codes (low byte: a, high byte: b), round to nearest even, values
@@ -52,9 +48,24 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// Maximum over each group of LPB (4 or 8) consecutive lanes, by DPP moves
+// within registers: swap neighbours, swap pairs, then (groups of 8) mirror
+// each half-row of 8 lanes, which pairs every lane with one of the other
+// quad of its group.
+template <int LPB>
+__device__ __forceinline__ float group_max(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    if (LPB == 8)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    return v;
+}
+
 // One lane holds V = 4 (FP32 input) or 8 (BF16 input) consecutive values of
 // a block, so LPB = 32 / V lanes share a block; a workgroup of 256 threads
-// covers 256 / LPB blocks per pass and walks the blocks grid-stride.
+// covers 256 / LPB blocks per pass, UNR passes per loop trip (their loads
+// issued together), walking the blocks grid-stride.
 template <int FMT, int IN>
 __global__ void __launch_bounds__(256)
 quantize_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *__restrict__ S,
@@ -63,36 +74,42 @@ quantize_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *__
     constexpr int V = (IN == IN_F32) ? 4 : 8;
     constexpr int LPB = 32 / V;
     constexpr int EMAX = (FMT == FP4) ? 2 : 8;
+    constexpr int UNR = 2;
     const int sub = threadIdx.x % LPB;
     const int64_t first = (int64_t)blockIdx.x * (256 / LPB) + threadIdx.x / LPB;
     const int64_t stride = (int64_t)gridDim.x * (256 / LPB);
-    for (int64_t b = first; b < nblocks; b += stride) {
+    for (int64_t b0 = first; b0 < nblocks; b0 += UNR * stride) {
+        v4i raw[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int64_t b = min(b0 + u * stride, nblocks - 1);   // a repeat past the end is not stored
+            raw[u] = (IN == IN_F32) ? *(const v4i *)((const float *)X + b * 32 + sub * V)
+                                    : *(const v4i *)((const uint16_t *)X + b * 32 + sub * V);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+        const int64_t b = b0 + u * stride;
+        if (b >= nblocks) break;
         float v[V];
         const int64_t e0 = b * 32 + sub * V;          // first value of the lane
         if (IN == IN_F32) {
-            const v4f x = *(const v4f *)((const float *)X + e0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = x[i];
+            for (int i = 0; i < 4; ++i) v[i] = __int_as_float(raw[u][i]);
         } else {
-            const v4i x = *(const v4i *)((const uint16_t *)X + e0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                v[2 * i] = __uint_as_float((uint32_t)x[i] << 16);
-                v[2 * i + 1] = __uint_as_float((uint32_t)x[i] & 0xffff0000u);
+                v[2 * i] = __uint_as_float((uint32_t)raw[u][i] << 16);
+                v[2 * i + 1] = __uint_as_float((uint32_t)raw[u][i] & 0xffff0000u);
             }
         }
+        // A non-finite value makes the lane's maximum +inf, which no finite
+        // block reaches: after the group maximum, amax == inf marks the block.
         float amax = 0.f;
-        int bad = 0;
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            bad |= !isfinite(v[i]);
-            amax = fmaxf(amax, fabsf(v[i]));
-        }
-#pragma unroll
-        for (int m = 1; m < LPB; m <<= 1) {
-            amax = fmaxf(amax, __shfl_xor(amax, m));
-            bad |= __shfl_xor(bad, m);
-        }
+        for (int i = 0; i < V; ++i)
+            amax = fmaxf(amax, isfinite(v[i]) ? fabsf(v[i]) : __builtin_inff());
+        amax = group_max<LPB>(amax);
+        const bool bad = amax == __builtin_inff();
         int s = 0;
         if (bad) s = 255;
         else if (amax > 0.f) s = min(254, max(0, floor_log2(amax) - EMAX + 127));
@@ -115,10 +132,11 @@ quantize_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *__
         } else {
             uint32_t w = 0;
 #pragma unroll
-            for (int i = 0; i < V; ++i) w |= e2m1_code(y[i]) << (4 * i);
+            for (int i = 0; i < V / 2; ++i) w |= e2m1_pair(y[2 * i], y[2 * i + 1]) << (8 * i);
             if (bad) w = 0;
             if (V == 4) *(uint16_t *)(Q + e0 / 2) = (uint16_t)w;
             else *(uint32_t *)(Q + e0 / 2) = w;
+        }
         }
     }
 }
