@@ -34,7 +34,11 @@ PEAK_TFLOPS = {mxinputs.FMT_E2M1: 10100.0, mxinputs.FMT_E4M3: 5000.0}
 PEAK_HBM_GBS = 8000.0
 # Ridge points (FLOP per byte) above which the MFMA, not HBM, bounds a shape.
 RIDGE = {f: PEAK_TFLOPS[f] * 1e12 / (PEAK_HBM_GBS * 1e9) for f in PEAK_TFLOPS}
-KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "microscaled_block_scaled_amd", "csrc", "*")))
+CSRC = os.path.join(ROOT, "microscaled_block_scaled_amd", "csrc")
+# The device code of each kernel family: a counter summary taken on other
+# device code is stale.
+GEMM_SOURCES = [os.path.join(CSRC, "mx_kernels.h")]
+QUANT_SOURCES = [os.path.join(CSRC, "mx_quant.h")]
 
 
 def algorithmic_bytes(fmt, M, N, K, out):
@@ -43,18 +47,19 @@ def algorithmic_bytes(fmt, M, N, K, out):
     return (M + N) * eb + (M + N) * (K // 32) + M * N * (4 if out == mxinputs.OUT_FP32 else 2)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (GEMM_SOURCES if sources is None else sources):
         h.update(os.path.basename(p).encode())
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, sources=None, plan=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current device code (and, for the GEMM, the same launch
+    plan); else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -64,7 +69,9 @@ def measured_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
+        return None
+    if plan is not None and kv.get("plan") != plan:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -146,7 +153,10 @@ def bench_one(name, steps, warmup, with_cpu):
     nbytes = algorithmic_bytes(fmt, M, N, K, out)
     tflops = flops * steps / wall / 1e12
     bound = "mfma" if flops / nbytes >= RIDGE[fmt] else "hbm"
-    traffic = measured_traffic(name)
+    plan = mxg.plan(fmt, M, N, K, out)
+    plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
+        plan["variant"], plan["tile_m"], plan["tile_n"], plan["split_k"], plan["workgroups"])
+    traffic = measured_traffic(name, GEMM_SOURCES, plan_str)
     if bound == "mfma":
         achieved = flops / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[fmt],
@@ -158,7 +168,6 @@ def bench_one(name, steps, warmup, with_cpu):
     roof["traffic"] = traffic
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(avg_launch_s * 1e6, 2)
-    plan = mxg.plan(fmt, M, N, K, out)
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
@@ -169,10 +178,8 @@ def bench_one(name, steps, warmup, with_cpu):
                    "format": mxinputs.fmt_name(fmt),
                    "out": "fp32" if out == mxinputs.OUT_FP32 else "bf16",
                    "accumulate": "fp32", "peak_frac": round(tflops / PEAK_TFLOPS[fmt], 4),
-                   "plan": "variant %d tile %dx%d split %d, %d workgroups" % (
-                       plan["variant"], plan["tile_m"], plan["tile_n"], plan["split_k"],
-                       plan["workgroups"]),
-                   "kernel_source_sha256": kernel_source_hash()},
+                   "plan": plan_str,
+                   "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
         "roofline": roof,
     }
     if with_cpu:
@@ -218,10 +225,13 @@ def bench_quantize(steps, warmup, fmt, in_dtype):
             "dtype": "f32" if in_dtype == mxg.IN_FP32 else "bf16", "data": "synthetic",
             "config": {"workload": "quantize_%s_from_%s_8192x4096" % (
                 mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
-                "rows": rows, "K": K, "kernel_source_sha256": kernel_source_hash()},
+                "rows": rows, "K": K, "kernel_source_sha256": kernel_source_hash(QUANT_SOURCES)},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                         "traffic": None, "algorithmic_bytes": nbytes,
+                         "traffic": measured_traffic("quantize_%s_from_%s_8192x4096" % (
+                             mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
+                             QUANT_SOURCES),
+                         "algorithmic_bytes": nbytes,
                          "launch_us": round(launch_s * 1e6, 2)}}
 
 
