@@ -13,6 +13,7 @@ MFMA peak, from HIP events around every launch on the launch stream), and
 the CPU oracle's rate on a bounded row sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+    python bench.py --quantize | --grouped    (the quantizer / grouped GEMM)
 """
 import argparse
 import glob
@@ -235,6 +236,73 @@ def bench_quantize(steps, warmup, fmt, in_dtype):
                          "launch_us": round(launch_s * 1e6, 2)}}
 
 
+# Eight experts of a mixture-of-experts layer: token counts of one 4096-token
+# batch (uneven load), each expert's weight N x K.
+GROUPED_ROWS = [704, 320, 512, 896, 128, 640, 448, 448]
+GROUPED_N, GROUPED_K = 4096, 2048
+
+
+def bench_grouped(steps, warmup, fmt):
+    """mx_gemm_grouped over eight uneven experts (4096 tokens in all, N=4096,
+    K=2048, BF16 out): TFLOP/s of the useful products, roofline by the same
+    ridge rule as the plain GEMM."""
+    import torch
+    import microscaled_block_scaled_amd as mxg
+    rows, N, K = GROUPED_ROWS, GROUPED_N, GROUPED_K
+    G, M, out = len(rows), sum(rows), mxinputs.OUT_BF16
+    case = mxinputs.make_random(fmt, M, G * N, K, seed=2024 + fmt)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = (fmt, rows, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
+            C.data_ptr(), out, stream.cuda_stream)
+    for _ in range(warmup):
+        if mxg.grouped_ptr(*args) != 0:
+            raise RuntimeError("mx_gemm_grouped failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        mxg.grouped_ptr(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = e0.elapsed_time(e1) / steps / 1e3
+    flops = 2.0 * M * N * K
+    eb = K // 2 if fmt == mxinputs.FMT_E2M1 else K
+    nbytes = (M + G * N) * (eb + K // 32) + M * N * 2
+    p = mxg.grouped_plan(fmt, rows, N, K, out)
+    plan_str = "grouped tile %dx%d, %d workgroups" % (p["tile_m"], p["tile_n"], p["workgroups"])
+    workload = "grouped_%s_experts8_4096x4096x2048" % mxinputs.fmt_name(fmt)
+    bound = "mfma" if flops / nbytes >= RIDGE[fmt] else "hbm"
+    if bound == "mfma":
+        achieved = flops / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[fmt],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[fmt], 4)}
+    else:
+        achieved = nbytes / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(workload, GEMM_SOURCES, plan_str)
+    roof["algorithmic_bytes"] = nbytes
+    roof["launch_us"] = round(launch_s * 1e6, 2)
+    tflops = flops * steps / wall / 1e12
+    return {"metric": "MX grouped GEMM TFLOPS and % of MI355X dense MX MFMA peak",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "mxfp8_e4m3" if fmt == mxinputs.FMT_E4M3 else "mxfp4_e2m1",
+            "data": "synthetic",
+            "config": {"workload": workload, "group_rows": rows, "N": N, "K": K,
+                       "format": mxinputs.fmt_name(fmt), "out": "bf16",
+                       "peak_frac": round(tflops / PEAK_TFLOPS[fmt], 4), "plan": plan_str,
+                       "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
+            "roofline": roof}
+
+
 def copy_calibration(nbytes=256 << 20, reps=3):
     """A plain device copy of known size, for scaling the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the GEMM kernels."""
@@ -262,6 +330,8 @@ def main():
                     help="only run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--quantize", action="store_true",
                     help="time mx_quantize (both formats, FP32 and BF16 input) instead")
+    ap.add_argument("--grouped", action="store_true",
+                    help="time mx_gemm_grouped (eight uneven experts, both formats) instead")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
@@ -275,6 +345,10 @@ def main():
         for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):
             for ind in (1, 2):
                 print(json.dumps(bench_quantize(a.steps, a.warmup, fmt, ind)), flush=True)
+        return
+    if a.grouped:
+        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):
+            print(json.dumps(bench_grouped(a.steps, a.warmup, fmt)), flush=True)
         return
     names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \
         if a.all else [a.workload]

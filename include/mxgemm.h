@@ -63,7 +63,8 @@ enum {
     MX_ERR_FORMAT = -1,     /* fmt is not MX_FMT_E2M1 / MX_FMT_E4M3          */
     MX_ERR_OUT_DTYPE = -2,  /* out_dtype is not MX_OUT_FP32 / MX_OUT_BF16     */
     MX_ERR_SHAPE = -3,      /* M < 1, N < 1, K < 128, K % 128 != 0, M or N
-                               above MX_MAX_DIM, or K above MX_MAX_K           */
+                               above MX_MAX_DIM, K above MX_MAX_K, or more
+                               than 2^31 - 1 workgroups of tiles needed        */
     MX_ERR_NULL = -4,       /* a required pointer is NULL                     */
     MX_ERR_ALIGN = -5,      /* A, B or C not 16-byte aligned, or a scale
                                array not 4-byte aligned                        */
@@ -185,6 +186,43 @@ int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
  */
 int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
                 const void *X, void *Q, void *Q_scale, void *stream);
+
+/* Largest number of groups of mx_gemm_grouped. */
+#define MX_MAX_GROUPS 256
+
+/*
+ * Grouped MX GEMM, as in a mixture-of-experts layer (the FlyDSL article's
+ * grouped-GEMM cases, section "Performance numbers need their baselines":
+ * uniform groups, changing projection sizes, uneven expert loads): group g
+ * multiplies its group_rows[g] rows of A by its own N x K weight B_g,
+ *   C_g = A_g * B_g^T  for g = 0 .. groups-1,
+ * each exactly as mx_gemm would.
+ *   groups       1 .. MX_MAX_GROUPS
+ *   group_rows   HOST array of `groups` row counts, each >= 0 (0 allowed)
+ *   A, A_scale   the groups' rows stacked in group order: (sum of
+ *                group_rows) rows, laid out as mx_gemm's A / A_scale
+ *   B, B_scale   the groups' weights stacked: groups * N rows, laid out as
+ *                mx_gemm's B / B_scale (weight g is rows g*N .. g*N+N-1)
+ *   C            (sum of group_rows) x N, rows in the order of A's rows
+ * N, K, formats, alignment, errors and asynchrony as for mx_gemm (checked
+ * with M = the total row count); groups * N must not exceed MX_MAX_DIM.
+ * With no rows at all it returns MX_OK at once: nothing is launched and no
+ * pointer is looked at.  No workspace is used.
+ */
+int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
+                    int64_t N, int64_t K, const void *A, const void *A_scale,
+                    const void *B, const void *B_scale, void *C, int out_dtype,
+                    void *stream);
+
+/*
+ * How mx_gemm_grouped would run a problem: one tile shape for all groups
+ * (split_k is always 1, workspace_bytes 0; workgroups is the total number of
+ * tiles over the groups, 0 when there are no rows).  Host logic only: no
+ * HIP call, no device needed.  Returns MX_OK or mx_gemm_grouped's argument
+ * error (MX_ERR_NULL also for a NULL plan).
+ */
+int mx_gemm_grouped_plan(int fmt, int64_t groups, const int64_t *group_rows,
+                         int64_t N, int64_t K, int out_dtype, mx_plan_t *plan);
 
 #ifdef __cplusplus
 }

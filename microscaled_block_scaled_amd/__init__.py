@@ -15,6 +15,11 @@ Returns C = A * B^T, (M, N), float32 or bfloat16.
     q, q_scale = mx_quantize(x, fmt)
 
 quantizes a float32 / bfloat16 matrix into that operand layout (OCP MX rule).
+
+    C = mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt)
+
+multiplies consecutive row groups of a by their own weights: b is
+(G*N, ...), rows g*N .. g*N+N-1 being group g's weight.
 """
 import ctypes
 import os
@@ -26,6 +31,7 @@ OUT_BF16 = 2
 MAX_DIM = 1 << 30     # largest M or N
 MAX_K = 1 << 24       # largest K
 MAX_SPLIT_K = 8       # largest forced K split (mx_gemm_tile)
+MAX_GROUPS = 256      # most groups of mx_gemm_grouped
 VARIANT_TILE = 1
 
 MX_OK = 0
@@ -90,6 +96,12 @@ def lib():
                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     L.mx_quantize.restype = ctypes.c_int
     L.mx_quantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, vp, vp, vp, vp]
+    L.mx_gemm_grouped_plan.restype = ctypes.c_int
+    L.mx_gemm_grouped_plan.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64,
+                                       ctypes.c_int, ctypes.POINTER(MxPlan)]
+    L.mx_gemm_grouped.restype = ctypes.c_int
+    L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
+                                  vp, vp, vp, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -235,3 +247,73 @@ def mx_quantize(x, fmt, stream=None):
     if rc != MX_OK:
         _raise(rc)
     return q, qs
+
+
+def grouped_plan(fmt, group_rows, N, K, out_dtype=OUT_BF16):
+    """How mx_gemm_grouped would run these groups (a dict); host logic only."""
+    rows = [int(r) for r in group_rows]
+    arr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    p = MxPlan()
+    rc = lib().mx_gemm_grouped_plan(int(fmt), len(rows), arr, int(N), int(K), int(out_dtype),
+                                    ctypes.byref(p))
+    if rc != MX_OK:
+        _raise(rc)
+    return p.as_dict()
+
+
+def grouped_ptr(fmt, group_rows, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0):
+    """Raw entry point of mx_gemm_grouped: a list of row counts, integer
+    device addresses; returns the status code."""
+    rows = list(group_rows)
+    arr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    return lib().mx_gemm_grouped(int(fmt), len(rows), arr, int(N), int(K), A, A_scale, B,
+                                 B_scale, C, int(out_dtype), stream or None)
+
+
+def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out=None,
+                    stream=None):
+    """C_g = A_g * B_g^T for consecutive row groups of a (group_rows[g] rows
+    each, summing to a's row count; zeros allowed) and the G = len(group_rows)
+    weights stacked in b, (G*N, K) in mx_gemm's operand layout.  Returns
+    (sum(group_rows), N)."""
+    import torch
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if fmt not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    code, tdt = _out_code(out_dtype)
+    rows = [int(r) for r in group_rows]
+    G = len(rows)
+    if not 1 <= G <= MAX_GROUPS or min(rows) < 0:
+        raise ValueError("group_rows: 1 .. %d non-negative row counts" % MAX_GROUPS)
+    a, b = _as_u8(a, "a"), _as_u8(b, "b")
+    a_scale, b_scale = _as_u8(a_scale, "a_scale"), _as_u8(b_scale, "b_scale")
+    M = a.shape[0]
+    if sum(rows) != M:
+        raise ValueError("group_rows sum to %d, a has %d rows" % (sum(rows), M))
+    if b.shape[0] % G != 0:
+        raise ValueError("b's rows are not a multiple of the group count")
+    N = b.shape[0] // G
+    per = 2 if fmt == FMT_E2M1 else 1
+    K = a.shape[1] * per
+    if b.shape[1] * per != K:
+        raise ValueError("a and b disagree on K")
+    if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (G * N, K // 32):
+        raise ValueError("scales must be (rows, K/32)")
+    dev = a.device
+    for t in (b, a_scale, b_scale):
+        if t.device != dev:
+            raise ValueError("all operands must be on the same device")
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=dev)
+    elif out.dtype != tdt or tuple(out.shape) != (M, N) or not out.is_contiguous() \
+            or out.device != dev:
+        raise ValueError("out must be a contiguous (M, N) %s tensor on %s" % (tdt, dev))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = grouped_ptr(fmt, rows, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
+                         b_scale.data_ptr(), out.data_ptr(), code, stream)
+    if rc != MX_OK:
+        _raise(rc)
+    return out

@@ -123,6 +123,22 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
     tn = w / gsz;
 }
 
+// Grouped GEMM (one weight matrix per group, as in a mixture-of-experts
+// layer): group g owns rows row_start[g] .. row_start[g+1]-1 of A and C,
+// weight g of B (N rows each) and tiles tile_start[g] .. tile_start[g+1]-1 of
+// the grid.  Passed by value in the kernel arguments.  NoGroups marks a
+// plain GEMM.
+constexpr int kMaxGroups = 256;
+struct GroupTable {
+    static constexpr bool grouped = true;
+    int n;
+    int tile_start[kMaxGroups + 1];
+    int row_start[kMaxGroups + 1];
+};
+struct NoGroups {
+    static constexpr bool grouped = false;
+};
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
@@ -164,12 +180,12 @@ __device__ __forceinline__ void static_for(F &&f)
 // swizzle is applied on the global side, since each lane's LDS slot is fixed
 // by its lane id.  The main loop is one basic block (no data-dependent
 // branches), so the compiler keeps the MFMAs where they are written.
-template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S>
+template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S, typename GT = NoGroups>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
             void *__restrict__ C, int M, int N, int K, int tiles_m, int tiles_n, int gm,
-            int kchunk, int64_t cplane)
+            int kchunk, int64_t cplane, GT groups = GT{})
 {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -201,10 +217,32 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // [kb, kb + klen) with kb a multiple of kchunk (itself a multiple of 512,
     // i.e. of whole scale periods), into the FP32 plane C + slice*cplane.
     // Without split-K, kchunk == K and there is one slice.
+    int bid = blockIdx.x;
+    if constexpr (GT::grouped) {
+        // This workgroup's group: the last g with tile_start[g] <= bid (an
+        // empty group shares its start with the next one, so g is never
+        // empty).  Then rebase every operand on the group and make the rest
+        // of the kernel see one plain GEMM of M_g rows.
+        int lo = 0, hi = groups.n - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (groups.tile_start[mid] <= bid) lo = mid; else hi = mid - 1;
+        }
+        const int r0 = groups.row_start[lo];
+        const int64_t rb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;
+        M = groups.row_start[lo + 1] - r0;
+        tiles_m = (M + BM - 1) / BM;
+        bid -= groups.tile_start[lo];
+        A += (int64_t)r0 * rb;
+        As += (int64_t)r0 * (K / 32);
+        B += (int64_t)lo * N * rb;
+        Bs += (int64_t)lo * N * (K / 32);
+        C = (uint8_t *)C + (int64_t)r0 * N * (OUT == OF32 ? 4 : 2);
+    }
     const int ntiles = tiles_m * tiles_n;
-    const int slice = blockIdx.x / ntiles;
+    const int slice = bid / ntiles;
     int tm, tn;
-    tile_of(blockIdx.x - slice * ntiles, tiles_m, tiles_n, gm, tm, tn);
+    tile_of(bid - slice * ntiles, tiles_m, tiles_n, gm, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kb = slice * kchunk, klen = min(kchunk, K - kb);
     const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;      // row stride

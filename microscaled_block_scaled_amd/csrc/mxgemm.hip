@@ -13,6 +13,8 @@
 #include "mx_kernels.h"
 #include "mx_quant.h"
 
+static_assert(MX_MAX_GROUPS == mx::kMaxGroups, "group table size");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -41,6 +43,9 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kCUs = 256;   // MI355X compute units: one 256-row tile per CU per wave
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The kernels number workgroups (tile, slice) with a 32-bit int.
+constexpr int64_t kMaxGrid = 0x7fffffff;
 
 // Split-K for grids too small to fill the chip: K is cut into slices of
 // whole 512-K scale periods, each slice a workgroup of its own writing an
@@ -114,7 +119,7 @@ int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t
     int rc = check_args(fmt, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
     fill_plan(choose_tile(M, N, K), M, N, K, p);
-    return MX_OK;
+    return p->workgroups > kMaxGrid ? MX_ERR_SHAPE : MX_OK;
 }
 
 int find_tile(int tile_m, int tile_n)
@@ -323,6 +328,7 @@ extern "C" int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
     if (t < 0 || split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
     mx_plan_t plan;
     fill_plan(t, M, N, K, &plan, split_k);
+    if (plan.workgroups > kMaxGrid) return MX_ERR_SHAPE;
     return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
 
@@ -358,4 +364,145 @@ extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
             hipLaunchKernelGGL((mx::quantize_kernel<mx::FP8, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
     }
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+namespace {
+
+// Grouped GEMM: one tile shape for every group, chosen like choose_tile over
+// the whole grid of the groups' tiles (no K split: the groups supply the
+// parallelism).
+int choose_tile_grouped(const int64_t *rows, int64_t groups, int64_t N, int64_t total,
+                        int64_t maxm)
+{
+    int best = 0;
+    double best_eff = -1.0;
+    for (int t = 0; t < kNumTiles; ++t) {
+        const TileCfg &c = kTiles[t];
+        if (c.bm < 256 && maxm > c.bm) continue;
+        int64_t tiles = 0;
+        for (int64_t g = 0; g < groups; ++g) tiles += cdiv(rows[g], c.bm) * cdiv(N, c.bn);
+        if (tiles == 0) return best;                          // no rows
+        const int64_t target = c.bm >= 128 ? kCUs : kCUs / 2;
+        const double fill = (double)tiles / (double)(cdiv(tiles, target) * target);
+        const double useful = (double)(total * N) / (double)(tiles * c.bm * c.bn);
+        const double eff = fill * useful;
+        if (eff > best_eff + 1e-9) { best_eff = eff; best = t; }
+    }
+    return best;
+}
+
+template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S>
+void launch_grouped_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
+                        int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t stream)
+{
+    const int tiles_n = (int)cdiv(N, BN);
+    hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
+                       dim3((unsigned)gt.tile_start[gt.n]), dim3(WGM * WGN * 64), 0, stream,
+                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
+                       (const uint8_t *)Bs, C, 0, (int)N, (int)K, 0, tiles_n, 4, (int)K,
+                       (int64_t)0, gt);
+}
+
+template <int FMT, int OUT>
+bool launch_grouped(int t, const void *A, const void *As, const void *B, const void *Bs,
+                    void *C, int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t s)
+{
+    const TileCfg &c = kTiles[t];
+#define MX_GCFG(BM_, BN_, WM_, WN_, S_)                                                   \
+    if (c.bm == BM_ && c.bn == BN_ && c.wgm == WM_ && c.wgn == WN_) {                    \
+        launch_grouped_cfg<FMT, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, N, K, gt, s); \
+        return true;                                                                      \
+    }
+    MX_GCFG(256, 256, 4, 2, 2)
+    MX_GCFG(256, 192, 4, 2, 2)
+    MX_GCFG(256, 160, 4, 1, 2)
+    MX_GCFG(256, 128, 4, 2, 3)
+    MX_GCFG(128, 128, 2, 2, 3)
+    MX_GCFG(64, 256, 1, 8, 3)
+#undef MX_GCFG
+    return false;
+}
+
+}  // namespace
+
+// Checks a grouped problem and plans it: the tile (plan->tile_m/tile_n),
+// the grid and, when gt is given, the group table.  Host logic only.
+int grouped_plan(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, int64_t K,
+                 int out_dtype, mx_plan_t *plan, int *tile, mx::GroupTable *gt)
+{
+    int rc = check_args(fmt, 1, N, K, out_dtype);            // format, output, N, K
+    if (rc != MX_OK) return rc;
+    if (groups < 1 || groups > MX_MAX_GROUPS || groups * N > MX_MAX_DIM) return MX_ERR_SHAPE;
+    if (!group_rows || !plan) return MX_ERR_NULL;
+    int64_t total = 0, maxm = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+        if (group_rows[g] < 0 || group_rows[g] > MX_MAX_DIM) return MX_ERR_SHAPE;
+        total += group_rows[g];
+        maxm = std::max(maxm, group_rows[g]);
+    }
+    if (total > MX_MAX_DIM) return MX_ERR_SHAPE;
+    const int t = choose_tile_grouped(group_rows, groups, N, total, maxm);
+    const TileCfg &c = kTiles[t];
+    int64_t tiles = 0;
+    if (gt) {
+        gt->n = (int)groups;
+        gt->tile_start[0] = 0;
+        gt->row_start[0] = 0;
+    }
+    for (int64_t g = 0; g < groups; ++g) {
+        tiles += cdiv(group_rows[g], c.bm) * cdiv(N, c.bn);
+        if (tiles > kMaxGrid) return MX_ERR_SHAPE;
+        if (gt) {
+            gt->tile_start[g + 1] = (int)tiles;
+            gt->row_start[g + 1] = gt->row_start[g] + (int)group_rows[g];
+        }
+    }
+    memset(plan, 0, sizeof(*plan));
+    plan->variant = MX_VARIANT_TILE;
+    plan->tile_m = c.bm;
+    plan->tile_n = c.bn;
+    plan->split_k = 1;
+    plan->threads = c.wgm * c.wgn * 64;
+    plan->workgroups = tiles;
+    *tile = t;
+    return MX_OK;
+}
+
+extern "C" int mx_gemm_grouped_plan(int fmt, int64_t groups, const int64_t *group_rows,
+                                    int64_t N, int64_t K, int out_dtype, mx_plan_t *plan)
+{
+    int t = 0;
+    return grouped_plan(fmt, groups, group_rows, N, K, out_dtype, plan, &t, nullptr);
+}
+
+extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
+                               int64_t N, int64_t K, const void *A, const void *A_scale,
+                               const void *B, const void *B_scale, void *C, int out_dtype,
+                               void *stream)
+{
+    mx_plan_t plan;
+    mx::GroupTable gt;
+    int t = 0;
+    int rc = grouped_plan(fmt, groups, group_rows, N, K, out_dtype, &plan, &t, &gt);
+    if (rc != MX_OK) return rc;
+    if (plan.workgroups == 0) return MX_OK;                 // no rows: nothing to compute
+    if (!A || !A_scale || !B || !B_scale || !C) return MX_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
+        !aligned(A_scale, 4) || !aligned(B_scale, 4))
+        return MX_ERR_ALIGN;
+    int dev = -1;
+    rc = device_ready(&dev);
+    if (rc != MX_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    bool launched;
+    if (fmt == MX_FMT_E2M1)
+        launched = (out_dtype == MX_OUT_FP32)
+            ? launch_grouped<mx::FP4, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)
+            : launch_grouped<mx::FP4, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s);
+    else
+        launched = (out_dtype == MX_OUT_FP32)
+            ? launch_grouped<mx::FP8, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)
+            : launch_grouped<mx::FP8, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s);
+    return (launched && hipGetLastError() == hipSuccess) ? MX_OK : MX_ERR_LAUNCH;
 }

@@ -134,6 +134,36 @@ class Oracle:
             raise ValueError("oracle rejected the arguments")
         return (C, T, E) if group_bound else (C, T)
 
+    def gemm_grouped(self, fmt, A, A_scale, B, B_scale, K, group_rows, rows=None,
+                     threads=0, group_bound=False):
+        """Grouped GEMM of a mixture-of-experts layer, by its definition: A's
+        rows come in consecutive groups of ``group_rows[g]`` rows, B holds G
+        weights of N rows each (weight g = rows g*N .. g*N+N-1), and group g's
+        rows of C are A_g * B_g^T, each an ordinary ``gemm``.  ``rows``
+        selects A rows by their index in A.  Returns (C, T) or (C, T, E), with
+        the rows in A's (or ``rows``') order."""
+        group_rows = [int(r) for r in group_rows]
+        G = len(group_rows)
+        if G < 1 or min(group_rows) < 0 or sum(group_rows) != A.shape[0]:
+            raise ValueError("group_rows must be >= 0 and sum to A's row count")
+        if B.shape[0] % G or B_scale.shape[0] != B.shape[0]:
+            raise ValueError("B must hold G weights of equal row count")
+        N = B.shape[0] // G
+        want = np.arange(A.shape[0]) if rows is None else np.asarray(rows, np.int64)
+        nout = 3 if group_bound else 2
+        out = [np.zeros((want.shape[0], N), np.float64) for _ in range(nout)]
+        r0 = 0
+        for g, m in enumerate(group_rows):
+            pos = np.nonzero((want >= r0) & (want < r0 + m))[0]
+            if pos.size:
+                res = self.gemm(fmt, A[r0:r0 + m], A_scale[r0:r0 + m], B[g * N:(g + 1) * N],
+                                B_scale[g * N:(g + 1) * N], K, rows=want[pos] - r0,
+                                threads=threads, group_bound=group_bound)
+                for o, r in zip(out, res):
+                    o[pos] = r
+            r0 += m
+        return tuple(out)
+
     def quantize(self, fmt, X):
         """MX-quantize X (rows x K, values exactly representable in float64,
         K a multiple of 32) -> (codes, scales) uint8 arrays: codes rows x K
@@ -177,6 +207,10 @@ def default():
 
 def gemm(*args, **kw):
     return default().gemm(*args, **kw)
+
+
+def gemm_grouped(*args, **kw):
+    return default().gemm_grouped(*args, **kw)
 
 
 def block_contrib(*args, **kw):

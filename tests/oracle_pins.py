@@ -474,8 +474,38 @@ def pin_quantize_roundtrip(orc):
         assert (bmax >= top).all(), fmt
 
 
+def pin_grouped(orc):
+    """Grouped GEMM: each group's rows equal a numpy matmul of the dequantized
+    group rows against that group's weight (independent tables), and the
+    whole result is the block diagonal of one plain GEMM of A against every
+    weight; empty groups take no rows."""
+    for fmt in (E2M1, E4M3):
+        rows, N, K = [5, 0, 9, 1, 0, 6], 7, 256
+        G = len(rows)
+        case = mxinputs.make_random(fmt, sum(rows), G * N, K, seed=11)
+        A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+        C, T = orc.gemm_grouped(fmt, A, As, B, Bs, K, rows)
+        Cf, Tf = orc.gemm(fmt, A, As, B, Bs, K)
+        dA, dB = dequant(fmt, A, As), dequant(fmt, B, Bs)
+        r0 = 0
+        for g, m in enumerate(rows):
+            sl = slice(r0, r0 + m)
+            wl = slice(g * N, (g + 1) * N)
+            assert np.array_equal(C[sl], Cf[sl, wl]) and np.array_equal(T[sl], Tf[sl, wl])
+            ref = dA[sl] @ dB[wl].T
+            assert np.all(np.abs(C[sl] - ref) <= 1e-12 * T[sl]), (fmt, g)
+            r0 += m
+        # a row subset, in any order, picks the same values
+        pick = [20, 0, 14, 5, 5]
+        Cs, Ts, Es = orc.gemm_grouped(fmt, A, As, B, Bs, K, rows, rows=pick, group_bound=True)
+        assert np.array_equal(Cs, C[pick]) and np.array_equal(Ts, T[pick])
+        _, _, Ef = orc.gemm(fmt, A, As, B, Bs, K, group_bound=True)
+        assert np.array_equal(Es[1], Ef[0, :N]) and np.array_equal(Es[0], Ef[20, 5 * N:])
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
-            pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip]
+            pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
+            pin_grouped]

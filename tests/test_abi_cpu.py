@@ -40,6 +40,7 @@ def test_header_constants_match_binding():
                   re.findall(r"#define (MX_MAX_[A-Z]+) \(\(int64_t\)1 << (\d+)\)", src))
     assert limits == {"MX_MAX_DIM": mxg.MAX_DIM, "MX_MAX_K": mxg.MAX_K}
     assert int(re.search(r"#define MX_MAX_SPLIT_K (\d+)", src).group(1)) == mxg.MAX_SPLIT_K
+    assert int(re.search(r"#define MX_MAX_GROUPS (\d+)", src).group(1)) == mxg.MAX_GROUPS
 
 
 def test_strerror_covers_codes():
@@ -212,3 +213,82 @@ def test_quantize_null_and_alignment_errors():
     assert L.mx_quantize(1, 1, 4, 64, good, good, None, None) == mxg.MX_ERR_NULL
     assert L.mx_quantize(1, 1, 4, 64, good + 8, good, good, None) == mxg.MX_ERR_ALIGN
     assert L.mx_quantize(2, 2, 4, 64, good, good + 4, good, None) == mxg.MX_ERR_ALIGN
+
+
+def _grouped(fmt, rows, N, K, ptrs=(1 << 20,) * 5, out=2):
+    arr = None if rows is None else (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    G = 1 if rows is None else len(rows)
+    return mxg.lib().mx_gemm_grouped(fmt, G, arr, N, K, *ptrs, out, None)
+
+
+@pytest.mark.parametrize("fmt,rows,N,K,out,code", [
+    (0, [4], 16, 128, 2, mxg.MX_ERR_FORMAT),
+    (2, [4], 16, 128, 5, mxg.MX_ERR_OUT_DTYPE),
+    (2, [4], 0, 128, 2, mxg.MX_ERR_SHAPE),
+    (2, [4], 16, 96, 2, mxg.MX_ERR_SHAPE),
+    (2, [4, -1], 16, 128, 2, mxg.MX_ERR_SHAPE),
+    (1, [4] * 257, 16, 128, 2, mxg.MX_ERR_SHAPE),
+    (1, [1 << 29, 1 << 29, 1], 16, 128, 2, mxg.MX_ERR_SHAPE),   # rows above MX_MAX_DIM
+    (1, [4, 4], 1 << 29 | 1, 128, 2, mxg.MX_ERR_SHAPE),         # G * N above MX_MAX_DIM
+])
+def test_grouped_argument_errors(fmt, rows, N, K, out, code):
+    assert _grouped(fmt, rows, N, K, out=out) == code
+
+
+def test_grouped_null_alignment_and_empty():
+    L = mxg.lib()
+    good = 1 << 20
+    assert L.mx_gemm_grouped(2, 0, None, 16, 128, good, good, good, good, good, 2, None) \
+        == mxg.MX_ERR_SHAPE
+    assert _grouped(2, None, 16, 128) == mxg.MX_ERR_NULL
+    for i in range(5):
+        ptrs = [good] * 5
+        ptrs[i] = None
+        assert _grouped(2, [3, 0, 5], 16, 128, ptrs) == mxg.MX_ERR_NULL, i
+    for i, mis in ((0, 8), (2, 4), (4, 2), (1, 2), (3, 1)):
+        ptrs = [good] * 5
+        ptrs[i] = good + mis
+        assert _grouped(1, [3, 0, 5], 16, 128, ptrs) == mxg.MX_ERR_ALIGN, i
+    # no rows at all: success without looking at a pointer or the device
+    assert _grouped(1, [0, 0, 0], 16, 128, (None,) * 5) == mxg.MX_OK
+    assert _grouped(2, [0] * mxg.MAX_GROUPS, 16, 128, (None,) * 5) == mxg.MX_OK
+
+
+def test_grouped_no_device_reported():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible here")
+    assert _grouped(2, [3, 0, 5], 16, 128) == mxg.MX_ERR_NO_DEVICE
+
+
+def test_grouped_python_shim_checks():
+    import torch
+    a = torch.zeros((10, 64), dtype=torch.uint8)
+    s = torch.zeros((10, 2), dtype=torch.uint8)
+    b = torch.zeros((8, 64), dtype=torch.uint8)
+    bs = torch.zeros((8, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError):          # group rows do not sum to a's rows
+        mxg.mx_gemm_grouped(a, s, b, bs, [3, 3], fmt=mxg.FMT_E4M3)
+    with pytest.raises(ValueError):          # b's rows not a multiple of the groups
+        mxg.mx_gemm_grouped(a, s, b, bs, [3, 3, 4], fmt=mxg.FMT_E4M3)
+    with pytest.raises(ValueError):          # negative count
+        mxg.mx_gemm_grouped(a, s, b, bs, [12, -2], fmt=mxg.FMT_E4M3)
+    with pytest.raises(ValueError):          # not on the GPU
+        mxg.mx_gemm_grouped(a, s, b, bs, [6, 4], fmt=mxg.FMT_E4M3)
+
+
+def test_grouped_plan():
+    rows = [704, 320, 512, 896, 128, 640, 448, 448]
+    p = mxg.grouped_plan(mxg.FMT_E4M3, rows, 4096, 2048)
+    assert p["split_k"] == 1 and p["workspace_bytes"] == 0
+    assert (p["tile_m"], p["tile_n"]) in mxg.tile_shapes() and p["tile_m"] == 256
+    tiles = sum(-(-r // p["tile_m"]) for r in rows) * -(-4096 // p["tile_n"])
+    assert p["workgroups"] == tiles
+    # every group short: the 64-row tile; no rows: an empty grid
+    p = mxg.grouped_plan(mxg.FMT_E2M1, [8, 1, 0, 33], 4096, 2048)
+    assert (p["tile_m"], p["tile_n"]) == (64, 256) and p["workgroups"] == 3 * 16
+    assert mxg.grouped_plan(mxg.FMT_E2M1, [0, 0], 64, 128)["workgroups"] == 0
+    with pytest.raises(ValueError):
+        mxg.grouped_plan(mxg.FMT_E2M1, [1] * (mxg.MAX_GROUPS + 1), 64, 128)
+    arr = (ctypes.c_int64 * 1)(4)
+    assert mxg.lib().mx_gemm_grouped_plan(1, 1, arr, 64, 128, 2, None) == mxg.MX_ERR_NULL

@@ -85,3 +85,30 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, "no pin caught mutant %s" % name
+
+
+# Mistakes planted in the oracle's grouped GEMM (Python): a neighbour's
+# weight, an empty group taking a row, row indices not rebased to the group,
+# the first group's scales for every group.
+GROUPED_MUTANTS = [
+    ("weight_of_next_group", "B[g * N:(g + 1) * N]", "B[(g + 1) % G * N:((g + 1) % G + 1) * N]"),
+    ("empty_group_takes_a_row", "r0 += m", "r0 += max(m, 1)"),
+    ("a_scale_not_rebased", "A_scale[r0:r0 + m]", "A_scale[0:m]"),
+    ("b_scale_not_rebased", "B_scale[g * N:(g + 1) * N]", "B_scale[0:N]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GROUPED_MUTANTS, ids=[m[0] for m in GROUPED_MUTANTS])
+def test_pins_catch_grouped_mutant(name, old, new):
+    import inspect
+    import textwrap
+
+    import numpy as np
+    src = textwrap.dedent(inspect.getsource(oracle.Oracle.gemm_grouped))
+    assert old in src
+    ns = {"np": np}
+    exec(src.replace(old, new, 1), ns)
+    mut = oracle.Oracle()
+    mut.gemm_grouped = ns["gemm_grouped"].__get__(mut)
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_grouped(mut)
