@@ -86,7 +86,11 @@ int choose_tile(int64_t M, int64_t N, int64_t K)
         const int64_t wgs = tiles * choose_split(c, tiles, K);
         const int64_t target = c.bm >= 128 ? kCUs : kCUs / 2;
         const double fill = (double)wgs / (double)(cdiv(wgs, target) * target);
-        const double useful = (double)(M * N) / (double)(tiles * c.bm * c.bn);
+        // With M <= 128 the GEMM is HBM-bound (under 2M FLOP per byte of B,
+        // below either format's ridge), so the MFMA work wasted on padding rows
+        // of a short tile costs nothing: only the fill counts.
+        const double useful = (M <= 128 && c.bm < 256)
+            ? 1.0 : (double)(M * N) / (double)(tiles * c.bm * c.bn);
         // A split costs a workspace round trip of one FP32 plane per slice:
         // on a tie, fewer slices win.
         const int64_t split = wgs / tiles;

@@ -53,17 +53,21 @@ SMALL_M_SHAPES = [(1, 32, 128), (8, 97, 1152), (32, 64, 3968), (33, 40, 640),
                   (64, 129, 2560), (17, 1000, 384), (8, 300, 9216)]
 
 
+@pytest.mark.parametrize("tile", [None, (64, 256), (128, 128)], ids=["plan", "64x256", "128x128"])
 @pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
 @pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", SMALL_M_SHAPES)
-def test_small_m(fmt, out, M, N, K):
-    """Small M runs the 64-row tile (rows past M read row M-1, never stored),
-    with split-K when the grid is small and K long (the last shape)."""
+def test_small_m(tile, fmt, out, M, N, K):
+    """Small M runs a short tile, 128x128 or 64x256 (rows past M read row
+    M-1, never stored), with split-K when the grid is small and K long (the
+    last shapes): the plan's pick and each short tile forced, at its planned
+    split."""
     p = mxg.plan(fmt, M, N, K, out)
-    assert p["tile_m"] == 64, p
+    assert p["tile_m"] in (64, 128), p
     case = mxinputs.make_random(fmt, M, N, K, seed=1000 + M * 3 + N + K)
-    log("small M fmt=%d out=%d M=%d N=%d K=%d split=%d" % (fmt, out, M, N, K, p["split_k"]))
-    res, *_ = check_against_oracle(case, out)
+    log("small M fmt=%d out=%d M=%d N=%d K=%d tile=%s plan split=%d"
+        % (fmt, out, M, N, K, tile, p["split_k"]))
+    res, *_ = check_against_oracle(case, out, tile=tile)
     _assert_ok(res, "small M")
 
 
