@@ -58,6 +58,10 @@ def _bind(lib):
     lib.mxo_gemm.argtypes = [ctypes.c_int, i64, i64, i64, u8p, u8p, u8p, u8p,
                              ctypes.POINTER(ctypes.c_int64), i64, dp, dp, dp,
                              ctypes.c_int]
+    lib.mxo_gemm_ab.restype = ctypes.c_int
+    lib.mxo_gemm_ab.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u8p, u8p, u8p, u8p,
+                                ctypes.POINTER(ctypes.c_int64), i64, dp, dp, dp,
+                                ctypes.c_int]
     return lib
 
 
@@ -66,12 +70,14 @@ def _u8(a):
     return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
 
 
-def _check_shapes(fmt, A, As, B, Bs, K):
-    if fmt not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
-    rb = K // 2 if fmt == FMT_E2M1 else K
-    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != rb or B.shape[1] != rb:
-        raise ValueError("A and B must be 2-D with %d bytes per row" % rb)
+def _check_shapes(fmt, A, As, B, Bs, K, fmt_b=None):
+    fmt_b = fmt if fmt_b is None else fmt_b
+    if fmt not in (FMT_E2M1, FMT_E4M3) or fmt_b not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("formats must be FMT_E2M1 or FMT_E4M3")
+    rba = K // 2 if fmt == FMT_E2M1 else K
+    rbb = K // 2 if fmt_b == FMT_E2M1 else K
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != rba or B.shape[1] != rbb:
+        raise ValueError("A and B must be 2-D with %d and %d bytes per row" % (rba, rbb))
     if As.shape != (A.shape[0], K // 32) or Bs.shape != (B.shape[0], K // 32):
         raise ValueError("scale arrays must be rows x K/32")
 
@@ -103,18 +109,20 @@ class Oracle:
         return t4, t8
 
     def gemm(self, fmt, A, A_scale, B, B_scale, K, rows=None, threads=0,
-             group_bound=False):
+             group_bound=False, fmt_b=None):
         """Return (C, T), or (C, T, E) with ``group_bound``, as float64 arrays
         of shape (len(rows) or M, N).
 
         A: uint8 M x (K/2 or K); B: uint8 N x (K/2 or K); scales uint8
-        rows x K/32.  ``rows`` selects a subset of A's rows; ``threads`` <= 0
-        lets OpenMP choose."""
+        rows x K/32.  ``fmt`` is A's element format, and B's too unless
+        ``fmt_b`` names another (mixed formats).  ``rows`` selects a subset of
+        A's rows; ``threads`` <= 0 lets OpenMP choose."""
+        fmt_b = fmt if fmt_b is None else fmt_b
         A, pa = _u8(A)
         As, pas = _u8(A_scale)
         B, pb = _u8(B)
         Bs, pbs = _u8(B_scale)
-        _check_shapes(fmt, A, As, B, Bs, K)
+        _check_shapes(fmt, A, As, B, Bs, K, fmt_b)
         M, N = A.shape[0], B.shape[0]
         if rows is None:
             nrows, prow = M, None
@@ -126,10 +134,16 @@ class Oracle:
         T = np.zeros((nrows, N), np.float64)
         E = np.zeros((nrows, N), np.float64) if group_bound else None
         dp = ctypes.POINTER(ctypes.c_double)
-        rc = self.lib.mxo_gemm(fmt, M, N, K, pa, pas, pb, pbs, prow, nrows,
-                               C.ctypes.data_as(dp), T.ctypes.data_as(dp),
-                               E.ctypes.data_as(dp) if group_bound else None,
-                               int(threads))
+        if fmt_b == fmt:
+            rc = self.lib.mxo_gemm(fmt, M, N, K, pa, pas, pb, pbs, prow, nrows,
+                                   C.ctypes.data_as(dp), T.ctypes.data_as(dp),
+                                   E.ctypes.data_as(dp) if group_bound else None,
+                                   int(threads))
+        else:
+            rc = self.lib.mxo_gemm_ab(fmt, fmt_b, M, N, K, pa, pas, pb, pbs, prow, nrows,
+                                      C.ctypes.data_as(dp), T.ctypes.data_as(dp),
+                                      E.ctypes.data_as(dp) if group_bound else None,
+                                      int(threads))
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return (C, T, E) if group_bound else (C, T)

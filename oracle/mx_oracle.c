@@ -34,10 +34,16 @@
  * For E2M1 every product is a multiple of 1/4 no smaller than the grid, so
  * E is zero.
  *
+ * Mixed formats.  A and B may hold different element formats (A E4M3 with
+ * B E2M1, "W4A8", or the reverse): the scaled MFMA takes a format selector
+ * per operand, and the OCP MX definition of a block dot product does not
+ * require equal formats.  dec() is then each operand's own decode.
+ *
  * Precision.  P is exact in double: E2M1 values are multiples of 1/2 with
  * |v| <= 6, so a block sum is a multiple of 1/4 below 2^11; E4M3 values are
  * multiples of 2^-9 with |v| <= 448, so a product is a multiple of 2^-18
- * below 2^18 and a 32-term sum needs at most 41 significant bits.  Scaling by
+ * below 2^18 and a 32-term sum needs at most 41 significant bits; a mixed
+ * E4M3 x E2M1 product is a multiple of 2^-10 below 2^12 (27 bits per sum).  Scaling by
  * a power of two in [2^-254, 2^254] is exact.  The only rounding is the final
  * double-precision sum over the K/32 blocks, taken in increasing b.
  *
@@ -152,18 +158,19 @@ double mxo_block_contrib(int fmt, int64_t K,
 
 /*
  * C[i][n], T[i][n] and E[i][n] for the rows m = rows[i] (i < nrows), all
- * n < N.  rows may be NULL, meaning rows 0..nrows-1.  C, T and E are
+ * n < N, with A's elements in fmt_a and B's in fmt_b.  rows may be NULL, meaning rows 0..nrows-1.  C, T and E are
  * nrows x N doubles, row-major; T and E may be NULL.  nthreads <= 0 uses
  * OpenMP's default.  Returns 0, or -1 on an argument the definition does
  * not cover.
  */
-int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
-             const uint8_t *A, const uint8_t *A_scale,
-             const uint8_t *B, const uint8_t *B_scale,
-             const int64_t *rows, int64_t nrows,
-             double *C, double *T, double *E, int nthreads)
+int mxo_gemm_ab(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                const uint8_t *A, const uint8_t *A_scale,
+                const uint8_t *B, const uint8_t *B_scale,
+                const int64_t *rows, int64_t nrows,
+                double *C, double *T, double *E, int nthreads)
 {
-    if (fmt != MXO_FMT_E2M1 && fmt != MXO_FMT_E4M3) return -1;
+    if (fmt_a != MXO_FMT_E2M1 && fmt_a != MXO_FMT_E4M3) return -1;
+    if (fmt_b != MXO_FMT_E2M1 && fmt_b != MXO_FMT_E4M3) return -1;
     if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || nrows < 0) return -1;
     for (int64_t i = 0; rows && i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= M) return -1;
@@ -171,7 +178,7 @@ int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
 
     double t4[16], t8[256], pow2[509];
     make_tables(t4, t8, pow2);
-    const int64_t nb = K / 32, rb = row_bytes(fmt, K);
+    const int64_t nb = K / 32, rba = row_bytes(fmt_a, K), rbb = row_bytes(fmt_b, K);
     const int64_t chunk = 128;      /* decoded A rows held at once */
     double *adec = (double *)malloc(sizeof(double) * (size_t)(chunk * K));
     if (!adec) return -1;
@@ -183,7 +190,7 @@ int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
         for (int64_t i = 0; i < ni; ++i) {
             int64_t m = rows ? rows[i0 + i] : i0 + i;
             for (int64_t k = 0; k < K; ++k)
-                adec[i * K + k] = decode_elem(fmt, A + m * rb, k, t4, t8);
+                adec[i * K + k] = decode_elem(fmt_a, A + m * rba, k, t4, t8);
         }
         int failed = 0;
 #pragma omp parallel num_threads(nthreads)
@@ -198,7 +205,7 @@ int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
                 if (!bdec) continue;
                 /* Step 1 (B side): decode row n of B by table. */
                 for (int64_t k = 0; k < K; ++k)
-                    bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);
+                    bdec[k] = decode_elem(fmt_b, B + n * rbb, k, t4, t8);
                 const uint8_t *sbrow = B_scale + n * nb;
                 for (int64_t i = 0; i < ni; ++i) {
                     int64_t m = rows ? rows[i0 + i] : i0 + i;
@@ -234,6 +241,17 @@ int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
     }
     free(adec);
     return 0;
+}
+
+/* Both operands in one format. */
+int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
+             const uint8_t *A, const uint8_t *A_scale,
+             const uint8_t *B, const uint8_t *B_scale,
+             const int64_t *rows, int64_t nrows,
+             double *C, double *T, double *E, int nthreads)
+{
+    return mxo_gemm_ab(fmt, fmt, M, N, K, A, A_scale, B, B_scale, rows, nrows, C, T, E,
+                       nthreads);
 }
 
 /* ------------------------------------------------------------------------

@@ -503,9 +503,38 @@ def pin_grouped(orc):
         assert np.array_equal(Es[1], Ef[0, :N]) and np.array_equal(Es[0], Ef[20, 5 * N:])
 
 
+def pin_mixed_formats(orc):
+    """A and B in different formats (E4M3 x E2M1 and the reverse): a numpy
+    matmul of the dequantized operands (independent tables), exact rationals
+    on a tiny case, and the transpose symmetry across the two directions."""
+    for fa, fb in ((E4M3, E2M1), (E2M1, E4M3)):
+        ca = mxinputs.make_random(fa, 24, 3, 512, seed=31)
+        cb = mxinputs.make_random(fb, 3, 20, 512, seed=32)
+        A, As, B, Bs = ca["A"], ca["A_scale"], cb["B"], cb["B_scale"]
+        C, T = orc.gemm(fa, A, As, B, Bs, 512, fmt_b=fb)
+        ref = dequant(fa, A, As) @ dequant(fb, B, Bs).T
+        tref = np.abs(dequant(fa, A, As)) @ np.abs(dequant(fb, B, Bs)).T
+        assert np.all(np.abs(C - ref) <= 1e-12 * T), (fa, fb)
+        assert np.all(np.abs(T - tref) <= 1e-12 * T), (fa, fb)
+        Ct, Tt = orc.gemm(fb, B, Bs, A, As, 512, fmt_b=fa)
+        assert np.array_equal(C, Ct.T) and np.array_equal(T, Tt.T), (fa, fb)
+        # exact rationals on 2 x 2 outputs, one 128-K block row each
+        ca = mxinputs.make_random(fa, 2, 2, 128, seed=33, scale_lo=110, scale_hi=140)
+        cb = mxinputs.make_random(fb, 2, 2, 128, seed=34, scale_lo=110, scale_hi=140)
+        va, vb = decode_rows(fa, ca["A"]), decode_rows(fb, cb["B"])
+        C, _ = orc.gemm(fa, ca["A"], ca["A_scale"], cb["B"], cb["B_scale"], 128, fmt_b=fb)
+        for m in range(2):
+            for n in range(2):
+                tot = Fraction(0)
+                for k in range(128):
+                    w = Fraction(2) ** (int(ca["A_scale"][m, k // 32]) + int(cb["B_scale"][n, k // 32]) - 254)
+                    tot += Fraction(va[m, k]) * Fraction(vb[n, k]) * w
+                assert C[m, n] == float(tot), (fa, fb, m, n)
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
-            pin_grouped]
+            pin_grouped, pin_mixed_formats]

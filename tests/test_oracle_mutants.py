@@ -14,8 +14,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "mx_oracle.c")
 # decode_elem is not listed: it permutes K within a 32-block identically for
 # A and B, which leaves every block dot product, and so C and T, unchanged.
 MUTANTS = [
-    ("b_pair_swap", "bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);",
-     "bdec[k] = decode_elem(fmt, B + n * rb, k ^ 1, t4, t8);"),
+    ("b_pair_swap", "bdec[k] = decode_elem(fmt_b, B + n * rbb, k, t4, t8);",
+     "bdec[k] = decode_elem(fmt_b, B + n * rbb, k ^ 1, t4, t8);"),
     ("scale_bias", "pow2[i] = ldexp(1.0, i - 254)", "pow2[i] = ldexp(1.0, i - 253)"),
     ("b_scale_from_a", "unsigned sa = sarow[b], sb = sbrow[b];",
      "unsigned sa = sarow[b], sb = sarow[b];"),
@@ -42,8 +42,15 @@ MUTANTS = [
     ("e8m0_bias", "return ldexp(1.0, (int)byte - 127);", "return ldexp(1.0, (int)byte - 128);"),
     ("row_index", "int64_t m = rows ? rows[i0 + i] : i0 + i;\n                    const",
      "int64_t m = rows ? rows[i0] : i0 + i;\n                    const"),
-    ("b_row_stride", "bdec[k] = decode_elem(fmt, B + n * rb, k, t4, t8);",
-     "bdec[k] = decode_elem(fmt, B + n * (rb - 1), k, t4, t8);"),
+    ("b_row_stride", "bdec[k] = decode_elem(fmt_b, B + n * rbb, k, t4, t8);",
+     "bdec[k] = decode_elem(fmt_b, B + n * (rbb - 1), k, t4, t8);"),
+    # Mixed formats: an operand decoded with the other operand's format or
+    # row pitch.
+    ("mixed_a_decoded_as_b", "adec[i * K + k] = decode_elem(fmt_a, A + m * rba, k, t4, t8);",
+     "adec[i * K + k] = decode_elem(fmt_b, A + m * rba, k, t4, t8);"),
+    ("mixed_b_pitch_of_a", "bdec[k] = decode_elem(fmt_b, B + n * rbb, k, t4, t8);",
+     "bdec[k] = decode_elem(fmt_b, B + n * rba, k, t4, t8);"),
+    ("mixed_same_format_entry", "return mxo_gemm_ab(fmt, fmt, M,", "return mxo_gemm_ab(fmt, MXO_FMT_E4M3, M,"),
     # The quantizer.
     ("q_e4m3_emax", "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 8;",
      "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 7;"),
