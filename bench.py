@@ -13,7 +13,8 @@ MFMA peak, from HIP events around every launch on the launch stream), and
 the CPU oracle's rate on a bounded row sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
-    python bench.py --quantize | --grouped    (the quantizer / grouped GEMM)
+    python bench.py --quantize | --grouped | --mixed
+        (the quantizer / grouped GEMM / mixed-format GEMM)
 """
 import argparse
 import glob
@@ -303,6 +304,74 @@ def bench_grouped(steps, warmup, fmt):
             "roofline": roof}
 
 
+# Mixed formats ("W4A8": A E4M3 activations, B E2M1 weights), BF16 out, on
+# the fused-QKV shape and the 70B down projection at batch 8.
+MIXED_WORKLOADS = {
+    "w4a8_llama8b_qkv": (2048, 6144, 4096),
+    "w4a8_llama70b_down_m8": (8, 8192, 28672),
+}
+
+
+def bench_mixed(steps, warmup, name):
+    """mx_gemm_mixed with A in E4M3 and B in E2M1.  The MFMA peak taken is
+    the MXFP8 one (an E4M3 operand runs at the E4M3 rate)."""
+    import torch
+    import microscaled_block_scaled_amd as mxg
+    M, N, K = MIXED_WORKLOADS[name]
+    fa, fb, out = mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, mxinputs.OUT_BF16
+    ca = mxinputs.make_random(fa, M, 1, K, seed=3000)
+    cb = mxinputs.make_random(fb, 1, N, K, seed=3001)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A, As = torch.from_numpy(ca["A"]).to(dev), torch.from_numpy(ca["A_scale"]).to(dev)
+    B, Bs = torch.from_numpy(cb["B"]).to(dev), torch.from_numpy(cb["B_scale"]).to(dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = (fa, M, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
+            C.data_ptr(), out, stream.cuda_stream, None, 0, fb)
+    for _ in range(warmup):
+        if mxg.gemm_ptr(*args) != 0:
+            raise RuntimeError("mx_gemm_mixed failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        mxg.gemm_ptr(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = e0.elapsed_time(e1) / steps / 1e3
+    flops = 2.0 * M * N * K
+    nbytes = M * K + N * (K // 2) + (M + N) * (K // 32) + M * N * 2
+    peak = PEAK_TFLOPS[mxinputs.FMT_E4M3]
+    p = mxg.plan(fa, M, N, K, out)
+    plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
+        p["variant"], p["tile_m"], p["tile_n"], p["split_k"], p["workgroups"])
+    if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flops / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        achieved = nbytes / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(name, GEMM_SOURCES, plan_str)
+    roof["algorithmic_bytes"] = nbytes
+    roof["launch_us"] = round(launch_s * 1e6, 2)
+    tflops = flops * steps / wall / 1e12
+    return {"metric": "MX mixed-format GEMM TFLOPS and % of MI355X dense MXFP8 MFMA peak",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "mxfp8_e4m3 x mxfp4_e2m1", "data": "synthetic",
+            "config": {"workload": name, "M": M, "N": N, "K": K, "format_a": "mxfp8",
+                       "format_b": "mxfp4", "out": "bf16",
+                       "peak_frac": round(tflops / peak, 4), "plan": plan_str,
+                       "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
+            "roofline": roof}
+
+
 def copy_calibration(nbytes=256 << 20, reps=3):
     """A plain device copy of known size, for scaling the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the GEMM kernels."""
@@ -332,6 +401,8 @@ def main():
                     help="time mx_quantize (both formats, FP32 and BF16 input) instead")
     ap.add_argument("--grouped", action="store_true",
                     help="time mx_gemm_grouped (eight uneven experts, both formats) instead")
+    ap.add_argument("--mixed", action="store_true",
+                    help="time mx_gemm_mixed (A E4M3 x B E2M1) on two serving shapes instead")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
@@ -345,6 +416,10 @@ def main():
         for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):
             for ind in (1, 2):
                 print(json.dumps(bench_quantize(a.steps, a.warmup, fmt, ind)), flush=True)
+        return
+    if a.mixed:
+        for name in MIXED_WORKLOADS:
+            print(json.dumps(bench_mixed(a.steps, a.warmup, name)), flush=True)
         return
     if a.grouped:
         for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):

@@ -187,6 +187,26 @@ int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
 int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
                 const void *X, void *Q, void *Q_scale, void *stream);
 
+/*
+ * MX GEMM with A and B in different element formats: fmt_a for A, fmt_b for
+ * B, each MX_FMT_E2M1 or MX_FMT_E4M3 (A E4M3 with B E2M1 is the usual
+ * "W4A8" serving layout).  The block dot product is the one of mx_gemm with
+ * each operand decoded in its own format (the OCP MX v1.0 dot product does
+ * not require equal formats; the pages' "broader low precision" outlook, and
+ * gfx950's scaled MFMA takes a format per operand).  A is M x K in fmt_a's
+ * layout (K or K/2 bytes per row), B is N x K in fmt_b's; scales, C, the
+ * output types, alignment, errors and asynchrony as for mx_gemm.
+ * tile_m = tile_n = 0 takes the plan's tile (the plan depends on M, N and K
+ * only, so mx_gemm_plan describes it); otherwise (tile_m, tile_n) must be one
+ * of mx_tile_shapes.  split_k as for mx_gemm_tile (0: the plan's).  With
+ * fmt_a == fmt_b the result equals mx_gemm's / mx_gemm_tile's bit for bit.
+ */
+int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                  const void *A, const void *A_scale,
+                  const void *B, const void *B_scale,
+                  void *C, int out_dtype, int tile_m, int tile_n, int split_k,
+                  void *stream);
+
 /* Largest number of groups of mx_gemm_grouped. */
 #define MX_MAX_GROUPS 256
 

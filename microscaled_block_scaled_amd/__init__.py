@@ -96,6 +96,9 @@ def lib():
                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     L.mx_quantize.restype = ctypes.c_int
     L.mx_quantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, vp, vp, vp, vp]
+    L.mx_gemm_mixed.restype = ctypes.c_int
+    L.mx_gemm_mixed.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     L.mx_gemm_grouped_plan.restype = ctypes.c_int
     L.mx_gemm_grouped_plan.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64,
                                        ctypes.c_int, ctypes.POINTER(MxPlan)]
@@ -136,10 +139,16 @@ def tile_shapes():
 
 
 def gemm_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0, tile=None,
-             split_k=0):
+             split_k=0, fmt_b=None):
     """Raw entry point: integer device addresses, returns the status code.
     ``tile=(tile_m, tile_n)`` forces a tile shape, and ``split_k`` (with a
-    tile) the number of K slices, 0 meaning the plan's choice (mx_gemm_tile)."""
+    tile) the number of K slices, 0 meaning the plan's choice (mx_gemm_tile).
+    ``fmt_b`` other than ``fmt`` gives B its own format (mx_gemm_mixed)."""
+    if fmt_b is not None and fmt_b != fmt:
+        tm, tn = tile if tile is not None else (0, 0)
+        return lib().mx_gemm_mixed(int(fmt), int(fmt_b), int(M), int(N), int(K), A, A_scale,
+                                   B, B_scale, C, int(out_dtype), int(tm), int(tn),
+                                   int(split_k), stream or None)
     if tile is not None:
         return lib().mx_gemm_tile(int(fmt), int(M), int(N), int(K), A, A_scale, B,
                                   B_scale, C, int(out_dtype), int(tile[0]), int(tile[1]),
@@ -175,22 +184,24 @@ def _as_u8(t, name):
 
 
 def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
-            tile=None, split_k=0):
+            tile=None, split_k=0, fmt_b=None):
     """C = A * B^T for MX-quantized A (M x K) and B (N x K); see module doc.
-    ``tile=(tile_m, tile_n)`` forces one of ``tile_shapes()``, and with it
-    ``split_k`` the number of K slices (0: the plan's choice)."""
+    ``fmt`` is the element format of A, and of B unless ``fmt_b`` gives B
+    another one (E4M3 x E2M1 and the reverse).  ``tile=(tile_m, tile_n)``
+    forces one of ``tile_shapes()``, and with it ``split_k`` the number of K
+    slices (0: the plan's choice)."""
     import torch
     if out_dtype is None:
         out_dtype = torch.bfloat16
-    if fmt not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    fmt_b = fmt if fmt_b is None else fmt_b
+    if fmt not in (FMT_E2M1, FMT_E4M3) or fmt_b not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("fmt and fmt_b must be FMT_E2M1 or FMT_E4M3")
     code, tdt = _out_code(out_dtype)
     a, b = _as_u8(a, "a"), _as_u8(b, "b")
     a_scale, b_scale = _as_u8(a_scale, "a_scale"), _as_u8(b_scale, "b_scale")
     M, N = a.shape[0], b.shape[0]
-    per = 2 if fmt == FMT_E2M1 else 1
-    K = a.shape[1] * per
-    if b.shape[1] * per != K:
+    K = a.shape[1] * (2 if fmt == FMT_E2M1 else 1)
+    if b.shape[1] * (2 if fmt_b == FMT_E2M1 else 1) != K:
         raise ValueError("a and b disagree on K")
     if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (N, K // 32):
         raise ValueError("scales must be (rows, K/32) = (%d, %d) and (%d, %d)"
@@ -208,7 +219,7 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
         stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         rc = gemm_ptr(fmt, M, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
-                      b_scale.data_ptr(), out.data_ptr(), code, stream, tile, split_k)
+                      b_scale.data_ptr(), out.data_ptr(), code, stream, tile, split_k, fmt_b)
     if rc != MX_OK:
         _raise(rc)
     return out

@@ -48,15 +48,18 @@ enum { OF32 = 1, OBF16 = 2 };   // equal to MX_OUT_FP32 / MX_OUT_BF16
 // Format selector of the scaled MFMA (cbsz for A, blgp for B).
 template <int FMT> struct mfma_fmt { static constexpr int sel = (FMT == FP4) ? 4 : 0; };
 
-// A slab is SW = 128 bytes of every row of the A and B tiles: 256 E2M1 or
-// 128 E4M3 K-values, i.e. four or two 64-K instruction steps, and their
-// scale bytes (8 or 4 per row).  128-byte rows make every copy request a
-// whole 128-byte line.
+// A slab is a run of K-values of every row of the A and B tiles: 256 when
+// both operands are E2M1, else 128 -- four or two 64-K instruction steps, and
+// their scale bytes (8 or 4 per row).  An operand's slab row is 128 bytes
+// (E4M3, or E2M1 with E2M1), which makes every copy request a whole 128-byte
+// line, or 64 bytes (E2M1 beside E4M3, half a line).
 constexpr int SW = 128;
-template <int FMT> struct slab {
-    static constexpr int kvals = (FMT == FP4) ? 2 * SW : SW;
-    static constexpr int steps = kvals / 64;         // 4 (E2M1) or 2 (E4M3)
-    static constexpr int sbytes = kvals / 32;        // 8 (E2M1) or 4 (E4M3)
+template <int FA, int FB> struct slab {
+    static constexpr int kvals = (FA == FP4 && FB == FP4) ? 2 * SW : SW;
+    static constexpr int steps = kvals / 64;         // 4 or 2
+    static constexpr int sbytes = kvals / 32;        // 8 or 4
+    // bytes of one row of an operand of format F in a slab
+    template <int F> static constexpr int row_bytes = (F == FP4) ? kvals / 2 : kvals;
 };
 
 // FP32 -> BF16 bits, round to nearest even (NaN stays NaN): one gfx950
@@ -72,12 +75,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 // consecutive rows is free of bank conflicts whether the LDS serves 8 or 16
 // lanes per cycle.  swz depends on r mod 16 only.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// The same for 64-byte rows (4 chunks): two rows share a 128-byte bank
+// window, and the rows of one parity among 8 aligned rows, or of one residue
+// mod 4 among 16, get 4 distinct values, so 8 or 16 consecutive rows reading
+// one chunk again touch distinct banks.  Depends on r mod 16 only.
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+template <int RB> __device__ __forceinline__ int swz_row(int r) { return RB == 128 ? swz(r) : swz64(r); }
 
-template <int FMT>
+template <int FA, int FB>
 __device__ __forceinline__ v16f mma(const v8i &a, const v8i &b, v16f acc, int sa, int sb)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        a, b, acc, mfma_fmt<FMT>::sel, mfma_fmt<FMT>::sel, 0, sa, 0, sb);
+        a, b, acc, mfma_fmt<FA>::sel, mfma_fmt<FB>::sel, 0, sa, 0, sb);
 }
 
 // Direct HBM -> LDS copies (gfx950 global_load_lds): lane l of the wave
@@ -155,8 +164,9 @@ __device__ __forceinline__ void static_for(F &&f)
 // Tiled kernel: one workgroup computes a BM x BN tile of C with WGM x WGN
 // waves, each owning a (BM/WGM) x (BN/WGN) block of 32x32 FP32 accumulators.
 //
-// K is walked in slabs: 128 bytes of every A and B row.  The LDS holds a
-// ring of S slabs (2 or 3, as the tile's LDS footprint allows) and two scale
+// A's elements are in format FA and B's in FB (equal, or one E4M3 and one
+// E2M1).  K is walked in slabs of 128 or 256 K-values of every A and B row
+// (see slab<>).  The LDS holds a ring of S slabs (2 or 3, as the tile's LDS footprint allows) and two scale
 // buffers:
 //   * slab k+S-1 is copied HBM -> LDS directly (global_load_lds, no register
 //     staging) into the ring slot that slab k-1 has just vacated, so S-1
@@ -180,7 +190,7 @@ __device__ __forceinline__ void static_for(F &&f)
 // swizzle is applied on the global side, since each lane's LDS slot is fixed
 // by its lane id.  The main loop is one basic block (no data-dependent
 // branches), so the compiler keeps the MFMAs where they are written.
-template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S, typename GT = NoGroups>
+template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S, typename GT = NoGroups>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
@@ -190,24 +200,34 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int HS = slab<FMT>::steps;                   // MFMA steps per slab
-    constexpr int SBS = slab<FMT>::sbytes;                 // scale bytes per row per slab
+    using SL = slab<FA, FB>;
+    constexpr int KS = SL::kvals;                          // K-values per slab
+    constexpr int HS = SL::steps;                          // MFMA steps per slab
+    constexpr int SBS = SL::sbytes;                        // scale bytes per row per slab
     constexpr int PS = 16 / SBS;                           // slabs per scale period
+    constexpr int RA = SL::template row_bytes<FA>;         // slab row bytes, A and B
+    constexpr int RB = SL::template row_bytes<FB>;
     constexpr int ROWS = BM + BN;
-    constexpr int DATA = ROWS * SW;                        // element bytes per slab
+    constexpr int DATA = BM * RA + BN * RB;                // element bytes per slab
     constexpr int NSI = (ROWS + 63) / 64;                  // scale copy instructions
     constexpr int SBUF = NSI * 64 * 16;                    // one scale buffer
-    constexpr int RPC = 1024 / SW;                         // rows per copy instruction
-    static_assert(S * DATA + 2 * SBUF <= 163840, "LDS budget");
+    constexpr int RPCA = 1024 / RA, RPCB = 1024 / RB;      // rows per copy instruction
     static_assert(S >= 2 && S - 1 <= PS, "one period of scale lookahead covers the ring");
-    static_assert(BM % RPC == 0 && BN % RPC == 0, "rows per copy instruction");
+    static_assert(BM % RPCA == 0 && BN % RPCB == 0, "rows per copy instruction");
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be 32-aligned");
-    constexpr int CPA = (BM / RPC + NW - 1) / NW;          // A copies per wave per slab
-    constexpr int CPB = (BN / RPC + NW - 1) / NW;          // B copies per wave per slab
+    constexpr int CPA = (BM / RPCA + NW - 1) / NW;         // A copies per wave per slab
+    constexpr int CPB = (BN / RPCB + NW - 1) / NW;         // B copies per wave per slab
     constexpr int CPS = (NSI + NW - 1) / NW;               // scale copies per wave per period
     constexpr int NCOPY = CPA + CPB;
+    // The epilogue reuses the LDS to stage output bands (see below).
+    typedef typename std::conditional<OUT == OF32, float, uint16_t>::type otype;
+    constexpr int OS = sizeof(otype);
+    constexpr int PITCH = WTN * OS + 16;                   // staging row pitch, bytes
+    constexpr int RING = S * DATA + 2 * SBUF;
+    constexpr int SMEM = RING > NW * 32 * PITCH ? RING : NW * 32 * PITCH;
+    static_assert(SMEM <= 163840, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * DATA + 2 * SBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
     uint8_t *const sbase = smem + S * DATA;                // scale buffers
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -229,13 +249,14 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             if (groups.tile_start[mid] <= bid) lo = mid; else hi = mid - 1;
         }
         const int r0 = groups.row_start[lo];
-        const int64_t rb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;
+        const int64_t rba = (FA == FP4) ? (int64_t)K / 2 : (int64_t)K;
+        const int64_t rbb = (FB == FP4) ? (int64_t)K / 2 : (int64_t)K;
         M = groups.row_start[lo + 1] - r0;
         tiles_m = (M + BM - 1) / BM;
         bid -= groups.tile_start[lo];
-        A += (int64_t)r0 * rb;
+        A += (int64_t)r0 * rba;
         As += (int64_t)r0 * (K / 32);
-        B += (int64_t)lo * N * rb;
+        B += (int64_t)lo * N * rbb;
         Bs += (int64_t)lo * N * (K / 32);
         C = (uint8_t *)C + (int64_t)r0 * N * (OUT == OF32 ? 4 : 2);
     }
@@ -245,32 +266,47 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     tile_of(bid - slice * ntiles, tiles_m, tiles_n, gm, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kb = slice * kchunk, klen = min(kchunk, K - kb);
-    const int64_t rowb = (FMT == FP4) ? (int64_t)K / 2 : (int64_t)K;      // row stride
-    const int64_t rowl = (FMT == FP4) ? (int64_t)klen / 2 : (int64_t)klen; // slice bytes per row
-    const int64_t kboff = (FMT == FP4) ? (int64_t)kb / 2 : (int64_t)kb;
+    // Row stride, slice bytes per row and slice offset of each operand.
+    const int64_t rowba = (FA == FP4) ? (int64_t)K / 2 : (int64_t)K;
+    const int64_t rowbb = (FB == FP4) ? (int64_t)K / 2 : (int64_t)K;
+    const int64_t rowla = (FA == FP4) ? (int64_t)klen / 2 : (int64_t)klen;
+    const int64_t rowlb = (FB == FP4) ? (int64_t)klen / 2 : (int64_t)klen;
+    const int64_t kboffa = (FA == FP4) ? (int64_t)kb / 2 : (int64_t)kb;
+    const int64_t kboffb = (FB == FP4) ? (int64_t)kb / 2 : (int64_t)kb;
     const int sps = K / 32, sp = klen / 32;                  // scale row stride, slice extent
-    const int nslab = (int)((rowl + SW - 1) / SW);          // E2M1: the last may be half
+    const int nslab = (klen + KS - 1) / KS;                  // E2M1 x E2M1: the last may be half
     const int nper = (sp + 15) / 16;                       // scale periods
     const int nsteps = klen / 64;
-
-    const int crow = lane / (SW / 16), cpc = lane % (SW / 16);   // row in a copy, LDS chunk
 
     // Copy addresses are a wave-uniform base (scalar registers) plus a 32-bit
     // per-lane offset, which stays below 256 rows * rowb < 2^32 for K <= 2^24.
     // Rows past the end of the matrix are clamped to its last row (their
     // results are never stored).
-    static_assert(RPC == 8 && BM % 64 == 0, "copy geometry");
-    const uint8_t *const At = A + (int64_t)m0 * rowb + kboff, *const Bt = B + (int64_t)n0 * rowb + kboff;
+    static_assert(BM % 64 == 0, "copy geometry");
+    const uint8_t *const At = A + (int64_t)m0 * rowba + kboffa;
+    const uint8_t *const Bt = B + (int64_t)n0 * rowbb + kboffb;
     const uint8_t *const Ast = As + (int64_t)m0 * sps + kb / 32;
     const uint8_t *const Bst = Bs + (int64_t)n0 * sps + kb / 32;
     const int last_a = min(BM, M - m0) - 1, last_b = min(BN, N - n0) - 1;   // last row in the tile
-    const uint32_t rowb32 = (uint32_t)rowb, lane_row = (uint32_t)crow * rowb32;
-    // Global chunk this lane fetches: LDS chunk cpc of row r holds chunk
-    // cpc ^ swz(r), and swz(i*8 + crow) depends only on crow and i's parity.
-    const uint32_t ch0 = (uint32_t)(cpc ^ swz(crow)) << 4;
-    const uint32_t ch1 = (uint32_t)(cpc ^ swz(crow + RPC)) << 4;
-    auto row_off = [&](int r0, int last) -> uint32_t {       // r0: first row of the block
-        return (r0 + crow <= last) ? (uint32_t)r0 * rowb32 + lane_row : (uint32_t)last * rowb32;
+    // Per operand (slab row bytes R, rows per copy instruction 1024/R): lane
+    // l copies chunk l % (R/16) of row l / (R/16) of a block of rows, into
+    // LDS chunk cpc of that row, which holds global chunk cpc ^ swz(row).
+    // For 128-byte rows swz(i*8 + crow) depends only on crow and i's parity
+    // (ch0 / ch1); for 64-byte rows swz64(i*16 + crow) only on crow.
+    struct CopyGeo { int crow; uint32_t lane_row, ch0, ch1, rowb32; };
+    auto copy_geo = [&](auto rc, int64_t rowb) {
+        constexpr int R = decltype(rc)::value;
+        const int crow = lane / (R / 16), cpc = lane % (R / 16);
+        const uint32_t rb32 = (uint32_t)rowb;
+        return CopyGeo{crow, (uint32_t)crow * rb32,
+                       (uint32_t)(cpc ^ swz_row<R>(crow)) << 4,
+                       (uint32_t)(cpc ^ swz_row<R>(crow + 1024 / R)) << 4, rb32};
+    };
+    const CopyGeo ga = copy_geo(std::integral_constant<int, RA>{}, rowba);
+    const CopyGeo gb = copy_geo(std::integral_constant<int, RB>{}, rowbb);
+    auto row_off = [&](const CopyGeo &c, int r0, int last) -> uint32_t {   // r0: first row of the block
+        return (r0 + c.crow <= last) ? (uint32_t)r0 * c.rowb32 + c.lane_row
+                                     : (uint32_t)last * c.rowb32;
     };
 
     // Copy slab k into ring slot `slot`.  Branch-free: every wave issues the
@@ -280,22 +316,24 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     auto issue = [&](int k, int slot) {
         k = min(k, nslab - 1);
         uint8_t *base = smem + slot * DATA;
-        const int64_t koff = (int64_t)k * SW;
-        // E2M1 with K % 256 == 128: the last slab is half a row segment; its
-        // upper half is never read, and its chunks are clamped into the row.
-        const uint32_t cmax = (uint32_t)(rowl - 16 - koff);
-        const uint8_t *const Ak = At + koff, *const Bk = Bt + koff;
+        const int64_t koffa = (int64_t)k * RA, koffb = (int64_t)k * RB;
+        // E2M1 x E2M1 with K % 256 == 128: the last slab is half a row
+        // segment; its upper half is never read, and its chunks are clamped
+        // into the row.  (With 64-byte slab rows every slab is whole.)
+        const uint32_t cmaxa = (uint32_t)(rowla - 16 - koffa);
+        const uint32_t cmaxb = (uint32_t)(rowlb - 16 - koffb);
+        const uint8_t *const Ak = At + koffa, *const Bk = Bt + koffb;
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
-            const int i = min(wave + u * NW, BM / RPC - 1);
-            const uint32_t ch = min((i & 1) ? ch1 : ch0, cmax);
-            g2l_16(Ak + (row_off(i * RPC, last_a) + ch), base + i * 1024);
+            const int i = min(wave + u * NW, BM / RPCA - 1);
+            const uint32_t ch = min((RA == 128 && (i & 1)) ? ga.ch1 : ga.ch0, cmaxa);
+            g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * 1024);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
-            const int i = min(wave + u * NW, BN / RPC - 1);
-            const uint32_t ch = min((i & 1) ? ch1 : ch0, cmax);
-            g2l_16(Bk + (row_off(i * RPC, last_b) + ch), base + BM * SW + i * 1024);
+            const int i = min(wave + u * NW, BN / RPCB - 1);
+            const uint32_t ch = min((RB == 128 && (i & 1)) ? gb.ch1 : gb.ch0, cmaxb);
+            g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * RA + i * 1024);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
@@ -321,10 +359,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int lr = lane & 31, g = lane >> 5;
     // Per-lane LDS offsets.  A fragment row r = wm*WTM + 32i + lr has
     // swz(r) = swz(lr) (WTM and 32i are multiples of 16), so fragment i is the
-    // lane's offset plus the constant 32*SW*i.
-    const int swl = swz(lr);
-    const int a_off = (wm * WTM + lr) * SW;
-    const int b_off = BM * SW + (wn * WTN + lr) * SW;
+    // lane's offset plus the constant 32*R*i.
+    const int swla = swz_row<RA>(lr), swlb = swz_row<RB>(lr);
+    const int a_off = (wm * WTM + lr) * RA;
+    const int b_off = BM * RA + (wn * WTN + lr) * RB;
     const int sa_off = (wm * WTM + lr) * 16;
     const int sb_off = (BM + wn * WTN + lr) * 16;
 
@@ -343,37 +381,52 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 
     // Where one step's operands are: ring slot `slot`, pass p of the slab,
     // scale buffer `sbuf`, slab `kp` within its scale period, and the scale
-    // byte shift of a short last period.  Data chunk offsets and the scale
-    // byte are per lane (they depend on the lane group g and the swizzle).
-    struct Src { int data, scale, o0, o1; };
+    // byte shift of a short last period.  Data chunk offsets (per operand)
+    // and the scale byte are per lane (they depend on the lane group g and
+    // the swizzle).
+    struct Src { int data, scale, a0, a1, b0, b1; };
+    auto chunk_offs = [&](auto fc, int p, int swl, int &o0, int &o1) {
+        // Step p of a slab: E4M3 chunks 4p+g and 4p+2+g of a 128-byte row,
+        // E2M1 chunk 2p+g (of a 128- or a 64-byte row).
+        const int c0 = (decltype(fc)::value == FP8) ? 4 * p + g : 2 * p + g;
+        o0 = (c0 ^ swl) << 4;
+        o1 = ((c0 + 2) ^ swl) << 4;
+    };
     auto src_of = [&](int slot, int p, int sbuf, int kp, int shift) {
-        // Step p of a slab: E4M3 chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g;
-        // in both, scale block 2p+g of the slab.
-        const int c0 = (FMT == FP8) ? 4 * p + g : 2 * p + g;
-        return Src{slot * DATA, S * DATA + sbuf * SBUF + kp * SBS + 2 * p + g + shift,
-                   (c0 ^ swl) << 4, ((c0 + 2) ^ swl) << 4};
+        Src r;
+        r.data = slot * DATA;
+        r.scale = S * DATA + sbuf * SBUF + kp * SBS + 2 * p + g + shift;   // scale block 2p+g of the slab
+        chunk_offs(std::integral_constant<int, FA>{}, p, swla, r.a0, r.a1);
+        chunk_offs(std::integral_constant<int, FB>{}, p, swlb, r.b0, r.b1);
+        return r;
     };
     auto sel = [](bool c, const Src &x, const Src &y) {
-        return Src{c ? x.data : y.data, c ? x.scale : y.scale, c ? x.o0 : y.o0, c ? x.o1 : y.o1};
+        return Src{c ? x.data : y.data, c ? x.scale : y.scale, c ? x.a0 : y.a0,
+                   c ? x.a1 : y.a1, c ? x.b0 : y.b0, c ? x.b1 : y.b1};
     };
-    // Fragment f of an operand whose lane rows start at LDS offset `off`
-    // (scale rows at `soff`): 16 (E2M1) or 32 (E4M3) bytes and a scale byte.
-    auto frag = [&](const Src &s, int off, int soff, int f, v8i &v, int &sv) {
-        const uint8_t *rp = smem + s.data + off + f * 32 * SW;
-        const v4i lo = *(const v4i *)(rp + s.o0);
-        if (FMT == FP8) {
-            const v4i hi = *(const v4i *)(rp + s.o1);
+    // Fragment f of operand A (ia true) or B, whose lane rows start at LDS
+    // offset `off` (scale rows at `soff`): 16 (E2M1) or 32 (E4M3) bytes and
+    // a scale byte.
+    auto frag = [&](auto ia, const Src &s, int off, int soff, int f, v8i &v, int &sv) {
+        constexpr bool IA = decltype(ia)::value;
+        constexpr int F = IA ? FA : FB, R = IA ? RA : RB;
+        const uint8_t *rp = smem + s.data + off + f * 32 * R;
+        const v4i lo = *(const v4i *)(rp + (IA ? s.a0 : s.b0));
+        if (F == FP8) {
+            const v4i hi = *(const v4i *)(rp + (IA ? s.a1 : s.b1));
             v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         } else {
             v = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
         }
         sv = smem[s.scale + soff + f * 32 * 16];
     };
+    const std::integral_constant<bool, ROLL_A> is_r{};       // the rolled operand is A?
+    const std::integral_constant<bool, !ROLL_A> is_d{};
     auto load_all = [&](const Src &s, int set) {
 #pragma unroll
-        for (int f = 0; f < FR; ++f) frag(s, r_off, rs_off, f, fr[f], fsr[f]);
+        for (int f = 0; f < FR; ++f) frag(is_r, s, r_off, rs_off, f, fr[f], fsr[f]);
 #pragma unroll
-        for (int f = 0; f < FD; ++f) frag(s, d_off, ds_off, f, fd[set][f], fsd[set][f]);
+        for (int f = 0; f < FD; ++f) frag(is_d, s, d_off, ds_off, f, fd[set][f], fsd[set][f]);
     };
 
     v16f acc[FM][FN];
@@ -392,20 +445,22 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         static_for<FR>([&](auto oc) {
             constexpr int o = decltype(oc)::value;
             constexpr int d0 = o * FD / FR, d1 = (o + 1) * FD / FR;
-            constexpr int NRD = (FMT == FP8) ? 3 : 2;           // LDS reads per fragment
+            // LDS reads per fragment: data (2 for E4M3, 1 for E2M1) + scale
+            constexpr int NRR = ((ROLL_A ? FA : FB) == FP8) ? 3 : 2;
+            constexpr int NRD = ((ROLL_A ? FB : FA) == FP8) ? 3 : 2;
 #pragma unroll
             for (int d = 0; d < FD; ++d) {
                 if constexpr (ROLL_A)
-                    acc[o][d] = mma<FMT>(fr[o], fd[cur][d], acc[o][d], fsr[o], fsd[cur][d]);
+                    acc[o][d] = mma<FA, FB>(fr[o], fd[cur][d], acc[o][d], fsr[o], fsd[cur][d]);
                 else
-                    acc[d][o] = mma<FMT>(fd[cur][d], fr[o], acc[d][o], fsd[cur][d], fsr[o]);
+                    acc[d][o] = mma<FA, FB>(fd[cur][d], fr[o], acc[d][o], fsd[cur][d], fsr[o]);
             }
-            frag(nx, r_off, rs_off, o, fr[o], fsr[o]);
+            frag(is_r, nx, r_off, rs_off, o, fr[o], fsr[o]);
 #pragma unroll
             for (int d = d0; d < d1; ++d)
-                frag(nx, d_off, ds_off, d, fd[cur ^ 1][d], fsd[cur ^ 1][d]);
+                frag(is_d, nx, d_off, ds_off, d, fd[cur ^ 1][d], fsd[cur ^ 1][d]);
             __builtin_amdgcn_sched_group_barrier(0x008, FD, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NRD * (1 + d1 - d0), 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRR + NRD * (d1 - d0), 0);
         });
     };
 
@@ -513,12 +568,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // (c, g) of fragment (i, j) holds, in element e, row 8*(e/4) + 4g + e%4
     // of column c.  Chunks that cross the end of a row of C, or rows of C
     // whose byte pitch is not a multiple of 16, are stored element by element.
-    typedef typename std::conditional<OUT == OF32, float, uint16_t>::type otype;
-    constexpr int OS = sizeof(otype);
     constexpr int VE = 16 / OS;                        // values per 16-byte chunk
-    constexpr int PITCH = WTN * OS + 16;               // staging row pitch, bytes
     constexpr int CPR = WTN / VE;                      // chunks per band row
-    static_assert(NW * 32 * PITCH <= S * DATA + 2 * SBUF, "epilogue staging fits in LDS");
     uint8_t *const stage = smem + wave * 32 * PITCH;
     const bool vec_ok = ((int64_t)N * OS) % 16 == 0;
     otype *const Cp = (otype *)C + (int64_t)slice * cplane;

@@ -158,7 +158,7 @@ int device_ready(int *dev_out)
 
 // One tile-kernel launch; with split > 1 it writes FP32 planes to the
 // workspace W and the reduction kernel then produces C.
-template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S>
+template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>
 void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
                 int64_t M, int64_t N, int64_t K, int split, float *W, hipStream_t stream)
 {
@@ -166,14 +166,14 @@ void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, vo
     const int gm = 4;
     const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
     if (split == 1) {
-        hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, BM, BN, WGM, WGN, S>), dim3(grid),
+        hipLaunchKernelGGL((mx::tile_kernel<FA, FB, OUT, BM, BN, WGM, WGN, S>), dim3(grid),
                            dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
                            (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, C,
                            (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)K, (int64_t)0);
         return;
     }
     const int64_t plane = plane_of(M, N);
-    hipLaunchKernelGGL((mx::tile_kernel<FMT, mx::OF32, BM, BN, WGM, WGN, S>), dim3(grid),
+    hipLaunchKernelGGL((mx::tile_kernel<FA, FB, mx::OF32, BM, BN, WGM, WGN, S>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
                        (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, (void *)W,
                        (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)slice_k(K, split),
@@ -182,15 +182,15 @@ void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, vo
                        0, stream, (const float *)W, C, M * N, plane, split);
 }
 
-template <int FMT, int OUT>
+template <int FA, int FB, int OUT>
 bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
                  const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
                  hipStream_t stream)
 {
 #define MX_CFG(BM_, BN_, WM_, WN_, S_)                                                    \
     if (p.tile_m == BM_ && p.tile_n == BN_ && p.threads == WM_ * WN_ * 64) {             \
-        launch_cfg<FMT, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, M, N, K, p.split_k,  \
-                                                     W, stream);                          \
+        launch_cfg<FA, FB, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, M, N, K,          \
+                                                        p.split_k, W, stream);             \
         return true;                                                                      \
     }
     MX_CFG(256, 256, 4, 2, 2)
@@ -203,11 +203,15 @@ bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *
     return false;
 }
 
-template <int FMT, int OUT>
-bool launch(const mx_plan_t &p, const void *A, const void *As, const void *B, const void *Bs,
-            void *C, int64_t M, int64_t N, int64_t K, float *W, hipStream_t stream)
+// Dispatch on the output type for formats (FA, FB).
+template <int FA, int FB>
+bool launch(const mx_plan_t &p, int out_dtype, const void *A, const void *As, const void *B,
+            const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
+            hipStream_t stream)
 {
-    return launch_tile<FMT, OUT>(p, A, As, B, Bs, C, M, N, K, W, stream);
+    return out_dtype == MX_OUT_FP32
+        ? launch_tile<FA, FB, mx::OF32>(p, A, As, B, Bs, C, M, N, K, W, stream)
+        : launch_tile<FA, FB, mx::OBF16>(p, A, As, B, Bs, C, M, N, K, W, stream);
 }
 
 // Split-K workspace, one per (device, stream), grown on demand with the
@@ -237,7 +241,7 @@ float *stream_workspace(int dev, hipStream_t s, size_t bytes)
 }
 
 // Checks that need no device, then the device check, then the launch.
-int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
+int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
              const void *A, const void *A_scale, const void *B, const void *B_scale,
              void *C, int out_dtype, void *stream)
 {
@@ -259,14 +263,15 @@ int run_plan(const mx_plan_t &plan, int fmt, int64_t M, int64_t N, int64_t K,
         if (!W) return MX_ERR_ALLOC;
     }
     bool launched;
-    if (fmt == MX_FMT_E2M1)
-        launched = (out_dtype == MX_OUT_FP32)
-            ? launch<mx::FP4, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s)
-            : launch<mx::FP4, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    const int o = out_dtype;
+    if (fmt_a == MX_FMT_E2M1 && fmt_b == MX_FMT_E2M1)
+        launched = launch<mx::FP4, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
+        launched = launch<mx::FP8, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E4M3)
+        launched = launch<mx::FP8, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else
-        launched = (out_dtype == MX_OUT_FP32)
-            ? launch<mx::FP8, mx::OF32>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s)
-            : launch<mx::FP8, mx::OBF16>(plan, A, A_scale, B, B_scale, C, M, N, K, W, s);
+        launched = launch<mx::FP4, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     const bool launch_ok = launched && hipGetLastError() == hipSuccess;
     return launch_ok ? MX_OK : MX_ERR_LAUNCH;
 }
@@ -317,7 +322,7 @@ extern "C" int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
     mx_plan_t plan;
     int rc = make_plan(fmt, M, N, K, out_dtype, &plan);
     if (rc != MX_OK) return rc;
-    return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
+    return run_plan(plan, fmt, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
 
 extern "C" int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
@@ -333,7 +338,29 @@ extern "C" int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
     mx_plan_t plan;
     fill_plan(t, M, N, K, &plan, split_k);
     if (plan.workgroups > kMaxGrid) return MX_ERR_SHAPE;
-    return run_plan(plan, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
+    return run_plan(plan, fmt, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
+}
+
+extern "C" int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                             const void *A, const void *A_scale,
+                             const void *B, const void *B_scale,
+                             void *C, int out_dtype, int tile_m, int tile_n, int split_k,
+                             void *stream)
+{
+    int rc = check_args(fmt_a, M, N, K, out_dtype);
+    if (rc != MX_OK) return rc;
+    if (fmt_b != MX_FMT_E2M1 && fmt_b != MX_FMT_E4M3) return MX_ERR_FORMAT;
+    if (split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
+    mx_plan_t plan;
+    if (tile_m == 0 && tile_n == 0) {
+        fill_plan(choose_tile(M, N, K), M, N, K, &plan, split_k);
+    } else {
+        const int t = find_tile(tile_m, tile_n);
+        if (t < 0) return MX_ERR_SHAPE;
+        fill_plan(t, M, N, K, &plan, split_k);
+    }
+    if (plan.workgroups > kMaxGrid) return MX_ERR_SHAPE;
+    return run_plan(plan, fmt_a, fmt_b, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
 
 
@@ -400,7 +427,7 @@ void launch_grouped_cfg(const void *A, const void *As, const void *B, const void
                         int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t stream)
 {
     const int tiles_n = (int)cdiv(N, BN);
-    hipLaunchKernelGGL((mx::tile_kernel<FMT, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
+    hipLaunchKernelGGL((mx::tile_kernel<FMT, FMT, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
                        dim3((unsigned)gt.tile_start[gt.n]), dim3(WGM * WGN * 64), 0, stream,
                        (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
                        (const uint8_t *)Bs, C, 0, (int)N, (int)K, 0, tiles_n, 4, (int)K,

@@ -294,3 +294,37 @@ def test_grouped_plan():
         mxg.grouped_plan(mxg.FMT_E2M1, [1] * (mxg.MAX_GROUPS + 1), 64, 128)
     arr = (ctypes.c_int64 * 1)(4)
     assert mxg.lib().mx_gemm_grouped_plan(1, 1, arr, 64, 128, 2, None) == mxg.MX_ERR_NULL
+
+
+def test_mixed_argument_errors():
+    L = mxg.lib()
+    good = 1 << 20
+    args = (good,) * 5
+    # format of A, then of B; output type; shapes; tile and split
+    assert L.mx_gemm_mixed(0, 1, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    assert L.mx_gemm_mixed(2, 3, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    assert L.mx_gemm_mixed(2, 1, 16, 16, 128, *args, 9, 0, 0, 0, None) == mxg.MX_ERR_OUT_DTYPE
+    assert L.mx_gemm_mixed(2, 1, 16, 16, 96, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_mixed(2, 1, 16, 16, 128, *args, 2, 100, 64, 0, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_mixed(2, 1, 16, 16, 128, *args, 2, 0, 0, -1, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_mixed(2, 1, 16, 16, 128, *args, 2, 0, 0, mxg.MAX_SPLIT_K + 1,
+                           None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_mixed(2, 1, 16, 16, 128, None, good, good, good, good, 2, 0, 0, 0,
+                           None) == mxg.MX_ERR_NULL
+    assert L.mx_gemm_mixed(1, 2, 16, 16, 128, good, good, good + 8, good, good, 2, 256, 192, 0,
+                           None) == mxg.MX_ERR_ALIGN
+
+
+def test_mixed_shim_checks_k_per_operand():
+    import torch
+    a8 = torch.zeros((16, 128), dtype=torch.uint8)     # E4M3: K = 128
+    b4 = torch.zeros((8, 64), dtype=torch.uint8)       # E2M1: K = 128
+    b4_bad = torch.zeros((8, 128), dtype=torch.uint8)  # E2M1: K = 256
+    sa = torch.zeros((16, 4), dtype=torch.uint8)
+    sb = torch.zeros((8, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError):                    # K mismatch
+        mxg.mx_gemm(a8, sa, b4_bad, sb, fmt=mxg.FMT_E4M3, fmt_b=mxg.FMT_E2M1)
+    with pytest.raises(ValueError):                    # shapes fine, but not on the GPU
+        mxg.mx_gemm(a8, sa, b4, sb, fmt=mxg.FMT_E4M3, fmt_b=mxg.FMT_E2M1)
+    with pytest.raises(ValueError):
+        mxg.mx_gemm(a8, sa, b4, sb, fmt=mxg.FMT_E4M3, fmt_b=5)
