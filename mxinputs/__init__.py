@@ -6,11 +6,12 @@ scale application).  It draws Gaussian values with numpy and turns them into
 MX operands by the OCP Microscaling v1.0 conversion rule:
 
   * per block of 32 consecutive values along K, shared exponent
-    X = floor(log2(max |v|)) - emax_elem  (emax_elem = 2 for E2M1, 8 for E4M3),
+    X = floor(log2(max |v|)) - emax_elem  (emax_elem = 2 for E2M1, 8 for E4M3,
+    15 for E5M2),
     stored as the E8M0 byte X + 127, clamped to [0, 254] (an all-zero block
     gets byte 0; its elements are zero whatever the byte);
   * each element v / 2^X rounded to nearest, ties to even, saturated at the
-    format's largest magnitude (6 for E2M1, 448 for E4M3).
+    format's largest magnitude (6 for E2M1, 448 for E4M3, 57344 for E5M2).
 
 The pages fix the block size (32 along K), the scale type (E8M0) and that the
 measured kernels start from already-quantized inputs (FlyDSL summary page,
@@ -19,7 +20,7 @@ not universal input coverage").  They give no quantizer; the OCP rule above
 is the plain reading.
 
 Layouts produced (all row-major, dense):
-  E4M3 operand  rows x K     uint8, element k in byte k
+  E4M3 / E5M2   rows x K     uint8, element k in byte k
   E2M1 operand  rows x K/2   uint8, element 2i in the low nibble of byte i
   scales        rows x K/32  uint8, byte b covers K-values 32b .. 32b+31
 """
@@ -27,10 +28,11 @@ import numpy as np
 
 FMT_E2M1 = 1
 FMT_E4M3 = 2
+FMT_E5M2 = 3
 OUT_FP32 = 1
 OUT_BF16 = 2
 
-_EMAX = {FMT_E2M1: 2, FMT_E4M3: 8}
+_EMAX = {FMT_E2M1: 2, FMT_E4M3: 8, FMT_E5M2: 15}
 _CHUNK_ROWS = 256
 
 # The workloads.  Shapes come from the serving models the pages measure
@@ -53,7 +55,7 @@ for _fmt, _fname in ((FMT_E4M3, "mxfp8"), (FMT_E2M1, "mxfp4")):
 
 
 def fmt_name(fmt):
-    return {FMT_E2M1: "mxfp4", FMT_E4M3: "mxfp8"}[fmt]
+    return {FMT_E2M1: "mxfp4", FMT_E4M3: "mxfp8", FMT_E5M2: "mxfp8_e5m2"}[fmt]
 
 
 def row_bytes(fmt, K):
@@ -92,6 +94,16 @@ def encode_e4m3(v):
     return t.view(torch.uint8).numpy().copy()
 
 
+def encode_e5m2(v):
+    """float array -> uint8 E5M2 codes, RNE, saturating at 57344 (torch's
+    float8_e5m2 conversion rounds to nearest even; clamping first keeps
+    out-of-range values off its infinity path)."""
+    import torch
+    v = np.clip(np.asarray(v, np.float32), -57344.0, 57344.0)
+    t = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e5m2)
+    return t.view(torch.uint8).numpy().copy()
+
+
 def quantize(x, fmt):
     """float32 rows x K -> (codes, scales) per the OCP MX conversion rule."""
     x = np.asarray(x, np.float32)
@@ -109,6 +121,8 @@ def quantize(x, fmt):
     scaled = scaled.reshape(rows, K)
     if fmt == FMT_E4M3:
         codes = encode_e4m3(scaled)
+    elif fmt == FMT_E5M2:
+        codes = encode_e5m2(scaled)
     else:
         c = encode_e2m1(scaled)
         codes = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)

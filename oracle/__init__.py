@@ -30,6 +30,8 @@ import numpy as np
 
 FMT_E2M1 = 1
 FMT_E4M3 = 2
+FMT_E5M2 = 3
+_FORMATS = (FMT_E2M1, FMT_E4M3, FMT_E5M2)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -45,6 +47,8 @@ def _bind(lib):
     lib.mxo_e2m1_value.argtypes = [ctypes.c_uint]
     lib.mxo_e4m3_value.restype = ctypes.c_double
     lib.mxo_e4m3_value.argtypes = [ctypes.c_uint]
+    lib.mxo_e5m2_value.restype = ctypes.c_double
+    lib.mxo_e5m2_value.argtypes = [ctypes.c_uint]
     lib.mxo_e8m0_value.restype = ctypes.c_double
     lib.mxo_e8m0_value.argtypes = [ctypes.c_uint]
     lib.mxo_tables.restype = None
@@ -72,8 +76,9 @@ def _u8(a):
 
 def _check_shapes(fmt, A, As, B, Bs, K, fmt_b=None):
     fmt_b = fmt if fmt_b is None else fmt_b
-    if fmt not in (FMT_E2M1, FMT_E4M3) or fmt_b not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("formats must be FMT_E2M1 or FMT_E4M3")
+    if fmt not in _FORMATS or fmt_b not in _FORMATS or \
+            (fmt == FMT_E5M2) != (fmt_b == FMT_E5M2):
+        raise ValueError("formats must be E2M1 / E4M3 (any pair) or E5M2 with E5M2")
     rba = K // 2 if fmt == FMT_E2M1 else K
     rbb = K // 2 if fmt_b == FMT_E2M1 else K
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != rba or B.shape[1] != rbb:
@@ -96,6 +101,9 @@ class Oracle:
 
     def e4m3_value(self, code):
         return self.lib.mxo_e4m3_value(int(code))
+
+    def e5m2_value(self, code):
+        return self.lib.mxo_e5m2_value(int(code))
 
     def e8m0_value(self, byte):
         return self.lib.mxo_e8m0_value(int(byte))

@@ -39,6 +39,13 @@
  * per operand, and the OCP MX definition of a block dot product does not
  * require equal formats.  dec() is then each operand's own decode.
  *
+ * E5M2 (MXFP8's other encoding, both operands) has a wider range: values are
+ * multiples of 2^-16 up to 57344, so a product is a multiple of 2^-32 below
+ * 2^32 and a 32-term sum can need about 69 significant bits.  Its block sums
+ * are therefore taken exactly in 128-bit integers (units of 2^-32) and
+ * rounded to double once (block_exact); a block holding an infinity or a
+ * NaN keeps IEEE double arithmetic instead.
+ *
  * Precision.  P is exact in double: E2M1 values are multiples of 1/2 with
  * |v| <= 6, so a block sum is a multiple of 1/4 below 2^11; E4M3 values are
  * multiples of 2^-9 with |v| <= 448, so a product is a multiple of 2^-18
@@ -59,6 +66,7 @@
 
 #define MXO_FMT_E2M1 1
 #define MXO_FMT_E4M3 2
+#define MXO_FMT_E5M2 3
 
 /* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.  Exponent
  * field 0 is subnormal: m * 2^-1.  No Inf, no NaN (OCP MX v1.0, FP4). */
@@ -80,6 +88,18 @@ double mxo_e4m3_value(unsigned code)
     return s ? -mag : mag;
 }
 
+/* E5M2: sign bit 7, exponent bits 6..2 (bias 15), mantissa bits 1..0.
+ * Exponent field 0 is subnormal: m/4 * 2^-14.  Exponent field 31 is
+ * infinity (m = 0) or NaN (OCP MX v1.0, FP8 E5M2, IEEE-like). */
+double mxo_e5m2_value(unsigned code)
+{
+    unsigned s = (code >> 7) & 1u, e = (code >> 2) & 31u, m = code & 3u;
+    double mag;
+    if (e == 31) mag = (m == 0) ? INFINITY : NAN;
+    else mag = (e == 0) ? ldexp((double)m / 4.0, -14) : ldexp(1.0 + (double)m / 4.0, (int)e - 15);
+    return s ? -mag : mag;
+}
+
 /* E8M0 scale: 2^(byte - 127); byte 255 is NaN (OCP MX v1.0, E8M0). */
 double mxo_e8m0_value(unsigned byte)
 {
@@ -92,6 +112,7 @@ static double decode_elem(int fmt, const uint8_t *row, int64_t k,
                           const double *t4, const double *t8)
 {
     if (fmt == MXO_FMT_E4M3) return t8[row[k]];
+    if (fmt == MXO_FMT_E5M2) return mxo_e5m2_value(row[k]);
     uint8_t byte = row[k >> 1];
     return t4[(k & 1) ? (byte >> 4) : (byte & 15u)];
 }
@@ -106,6 +127,26 @@ static void make_tables(double t4[16], double t8[256], double pow2[509])
 }
 
 static int64_t row_bytes(int fmt, int64_t K) { return fmt == MXO_FMT_E2M1 ? K / 2 : K; }
+
+/* Exact block sums for E5M2 operands: every finite E5M2 value is an integer
+ * multiple of 2^-16 below 2^32 in those units, so each product is an exact
+ * 64-bit-magnitude integer in units of 2^-32 and 32 of them sum exactly in
+ * 128 bits.  Writes sum p and magnitude sum q rounded once to double;
+ * returns 0 if a value is not finite (the caller keeps its IEEE sums). */
+static int block_exact(const double *x, const double *y, double *p, double *q)
+{
+    __int128 sp = 0, sq = 0;
+    for (int j = 0; j < 32; ++j) {
+        if (!isfinite(x[j]) || !isfinite(y[j])) return 0;
+        __int128 a = (__int128)(int64_t)ldexp(x[j], 16), b = (__int128)(int64_t)ldexp(y[j], 16);
+        __int128 t = a * b;
+        sp += t;
+        sq += t < 0 ? -t : t;
+    }
+    *p = ldexp((double)sp, -32);
+    *q = ldexp((double)sq, -32);
+    return 1;
+}
 
 /* Sub-grid loss of one group of 8 products: sum of |p| mod grid, with grid =
  * 2^(floor(log2 max|p|) - 12).  Products are exact doubles. */
@@ -169,8 +210,11 @@ int mxo_gemm_ab(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                 const int64_t *rows, int64_t nrows,
                 double *C, double *T, double *E, int nthreads)
 {
-    if (fmt_a != MXO_FMT_E2M1 && fmt_a != MXO_FMT_E4M3) return -1;
-    if (fmt_b != MXO_FMT_E2M1 && fmt_b != MXO_FMT_E4M3) return -1;
+    if (fmt_a != MXO_FMT_E2M1 && fmt_a != MXO_FMT_E4M3 && fmt_a != MXO_FMT_E5M2) return -1;
+    if (fmt_b != MXO_FMT_E2M1 && fmt_b != MXO_FMT_E4M3 && fmt_b != MXO_FMT_E5M2) return -1;
+    /* E5M2 pairs only with itself (its block sums are not exact in double). */
+    if ((fmt_a == MXO_FMT_E5M2) != (fmt_b == MXO_FMT_E5M2)) return -1;
+    const int exact128 = fmt_a == MXO_FMT_E5M2;
     if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || nrows < 0) return -1;
     for (int64_t i = 0; rows && i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= M) return -1;
@@ -220,6 +264,7 @@ int mxo_gemm_ab(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                             p += prod[j - 32 * b];
                             q += fabs(prod[j - 32 * b]);
                         }
+                        if (exact128) block_exact(a + 32 * b, bdec + 32 * b, &p, &q);
                         if (E)
                             for (int gi = 0; gi < 4; ++gi) loss += group_loss(prod + 8 * gi);
                         /* Step 3: the block's power-of-two scale. */

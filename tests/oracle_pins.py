@@ -23,7 +23,7 @@ import numpy as np
 import mxinputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-E2M1, E4M3 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3
+E2M1, E4M3, E5M2 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2
 
 
 # --------------------------------------------------------------------------
@@ -45,6 +45,11 @@ def torch_e4m3():
     return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
 
 
+def torch_e5m2():
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).double().numpy()
+
+
 def torch_e8m0():
     import torch
     return torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
@@ -54,6 +59,8 @@ def decode_rows(fmt, packed):
     """uint8 operand rows -> float64 values with the independent tables."""
     if fmt == E2M1:
         return golden_e2m1()[mxinputs.unpack_e2m1(packed)]
+    if fmt == E5M2:
+        return torch_e5m2()[np.asarray(packed, np.uint8)]
     return torch_e4m3()[np.asarray(packed, np.uint8)]
 
 
@@ -532,9 +539,51 @@ def pin_mixed_formats(orc):
                 assert C[m, n] == float(tot), (fa, fb, m, n)
 
 
+def pin_e5m2(orc):
+    """E5M2 (both operands): the decode table against torch's float8_e5m2
+    (infinities and NaNs included); a numpy matmul of dequantized operands;
+    exact rationals over a wide exponent spread; and a block whose exact sum
+    is a tiny remainder between two products 63 binades larger, which a
+    double-precision running sum would lose."""
+    ref = torch_e5m2()
+    got = np.array([orc.e5m2_value(c) for c in range(256)])
+    assert _same(got, ref)
+    case = mxinputs.make_random(E5M2, 40, 24, 512, seed=41)
+    A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+    C, T = orc.gemm(E5M2, A, As, B, Bs, 512)
+    refc = dequant(E5M2, A, As) @ dequant(E5M2, B, Bs).T
+    assert np.all(np.abs(C - refc) <= 1e-12 * T)
+    # exact rationals: random finite codes over the whole exponent range
+    rng = np.random.default_rng(5)
+    finite = np.array([c for c in range(256) if np.isfinite(ref[c])], np.uint8)
+    A = rng.choice(finite, size=(3, 64)).astype(np.uint8)
+    B = rng.choice(finite, size=(2, 64)).astype(np.uint8)
+    As = rng.integers(100, 150, size=(3, 2)).astype(np.uint8)
+    Bs = rng.integers(100, 150, size=(2, 2)).astype(np.uint8)
+    C, _ = orc.gemm(E5M2, A, As, B, Bs, 64)
+    for m in range(3):
+        for n in range(2):
+            blocks = []
+            for b in range(2):
+                w = Fraction(2) ** (int(As[m, b]) + int(Bs[n, b]) - 254)
+                blocks.append(float(sum(Fraction(ref[A[m, k]]) * Fraction(ref[B[n, k]])
+                                        for k in range(32 * b, 32 * b + 32)) * w))
+            assert C[m, n] == blocks[0] + blocks[1], (m, n)
+    # cancellation: 57344 * 57344 - 57344 * 57344 + 2^-16 * 2^-16 = 2^-32
+    code_max, code_min = 0x7B, 0x01            # 57344 and 2^-16
+    A = np.zeros((1, 32), np.uint8)
+    B = np.zeros((1, 32), np.uint8)
+    A[0, :3] = [code_max, code_min, code_max | 0x80]
+    B[0, :3] = [code_max, code_min, code_max]
+    s = np.full((1, 1), 127, np.uint8)
+    C, T = orc.gemm(E5M2, A, s, B, s, 32)
+    assert C[0, 0] == 2.0 ** -32, C[0, 0]
+    assert T[0, 0] == 2 * 57344.0 ** 2 + 2.0 ** -32 or T[0, 0] == 2 * 57344.0 ** 2
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
-            pin_grouped, pin_mixed_formats]
+            pin_grouped, pin_mixed_formats, pin_e5m2]
