@@ -305,21 +305,24 @@ def bench_grouped(steps, warmup, fmt):
             "roofline": roof}
 
 
-# Mixed formats ("W4A8": A E4M3 activations, B E2M1 weights), BF16 out, on
-# the fused-QKV shape and the 70B down projection at batch 8.
+# Other element formats, BF16 out: mixed "W4A8" (A E4M3 activations, B E2M1
+# weights) on the fused-QKV shape and the 70B down projection at batch 8, and
+# E5M2 for both operands on the fused-QKV shape.
 MIXED_WORKLOADS = {
-    "w4a8_llama8b_qkv": (2048, 6144, 4096),
-    "w4a8_llama70b_down_m8": (8, 8192, 28672),
+    "w4a8_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
+    "w4a8_llama70b_down_m8": (8, 8192, 28672, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
+    "mxfp8_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E5M2, mxinputs.FMT_E5M2),
 }
 
 
 def bench_mixed(steps, warmup, name):
-    """mx_gemm_mixed with A in E4M3 and B in E2M1.  The MFMA peak taken is
-    the MXFP8 one (an E4M3 operand runs at the E4M3 rate)."""
+    """A GEMM in another format pair (mx_gemm_mixed or E5M2 mx_gemm).  The
+    MFMA peak taken is the MXFP8 one (an 8-bit operand runs at the 8-bit
+    rate)."""
     import torch
     import microscaled_block_scaled_amd as mxg
-    M, N, K = MIXED_WORKLOADS[name]
-    fa, fb, out = mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, mxinputs.OUT_BF16
+    M, N, K, fa, fb = MIXED_WORKLOADS[name]
+    out = mxinputs.OUT_BF16
     ca = mxinputs.make_random(fa, M, 1, K, seed=3000)
     cb = mxinputs.make_random(fb, 1, N, K, seed=3001)
     dev = torch.device("cuda", 0)
@@ -344,7 +347,8 @@ def bench_mixed(steps, warmup, name):
     wall = time.perf_counter() - t0
     launch_s = e0.elapsed_time(e1) / steps / 1e3
     flops = 2.0 * M * N * K
-    nbytes = M * K + N * (K // 2) + (M + N) * (K // 32) + M * N * 2
+    nbytes = (M * mxinputs.row_bytes(fa, K) + N * mxinputs.row_bytes(fb, K)
+              + (M + N) * (K // 32) + M * N * 2)
     peak = PEAK_TFLOPS[mxinputs.FMT_E4M3]
     p = mxg.plan(fa, M, N, K, out)
     plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
@@ -361,13 +365,15 @@ def bench_mixed(steps, warmup, name):
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)
     tflops = flops * steps / wall / 1e12
-    return {"metric": "MX mixed-format GEMM TFLOPS and % of MI355X dense MXFP8 MFMA peak",
+    return {"metric": "MX GEMM TFLOPS (other formats) and % of MI355X dense MXFP8 MFMA peak",
             "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "mxfp8_e4m3 x mxfp4_e2m1", "data": "synthetic",
-            "config": {"workload": name, "M": M, "N": N, "K": K, "format_a": "mxfp8",
-                       "format_b": "mxfp4", "out": "bf16",
+            "dtype": "%s x %s" % (mxinputs.fmt_name(fa), mxinputs.fmt_name(fb)),
+            "data": "synthetic",
+            "config": {"workload": name, "M": M, "N": N, "K": K,
+                       "format_a": mxinputs.fmt_name(fa), "format_b": mxinputs.fmt_name(fb),
+                       "out": "bf16",
                        "peak_frac": round(tflops / peak, 4), "plan": plan_str,
                        "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
             "roofline": roof}
@@ -458,7 +464,7 @@ def main():
                     help="per-launch cold-cache and warm timings (median, p10, p90) of "
                          "--workload, or of every workload with --all")
     ap.add_argument("--mixed", action="store_true",
-                    help="time mx_gemm_mixed (A E4M3 x B E2M1) on two serving shapes instead")
+                    help="time the other formats (A E4M3 x B E2M1; E5M2) instead")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "

@@ -51,8 +51,11 @@
 extern "C" {
 #endif
 
-/* Element formats (MXFP4 = E2M1, MXFP8 = E4M3). */
-enum { MX_FMT_E2M1 = 1, MX_FMT_E4M3 = 2 };
+/* Element formats: MXFP4 = E2M1; MXFP8 = E4M3, or its other OCP encoding
+ * E5M2 (wider range: 2^-16 .. 57344, with infinities and NaNs).  E5M2 is
+ * accepted by mx_gemm, mx_gemm_tile and mx_gemm_mixed (E5M2 with E5M2 only);
+ * mx_gemm_grouped and mx_quantize take E2M1 and E4M3. */
+enum { MX_FMT_E2M1 = 1, MX_FMT_E4M3 = 2, MX_FMT_E5M2 = 3 };
 
 /* Output element types. */
 enum { MX_OUT_FP32 = 1, MX_OUT_BF16 = 2 };
@@ -60,7 +63,7 @@ enum { MX_OUT_FP32 = 1, MX_OUT_BF16 = 2 };
 /* Return codes. */
 enum {
     MX_OK = 0,
-    MX_ERR_FORMAT = -1,     /* fmt is not MX_FMT_E2M1 / MX_FMT_E4M3          */
+    MX_ERR_FORMAT = -1,     /* unknown format, or one this call does not take */
     MX_ERR_OUT_DTYPE = -2,  /* out_dtype is not MX_OUT_FP32 / MX_OUT_BF16     */
     MX_ERR_SHAPE = -3,      /* M < 1, N < 1, K < 128, K % 128 != 0, M or N
                                above MX_MAX_DIM, K above MX_MAX_K, or more
@@ -189,7 +192,8 @@ int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
 
 /*
  * MX GEMM with A and B in different element formats: fmt_a for A, fmt_b for
- * B, each MX_FMT_E2M1 or MX_FMT_E4M3 (A E4M3 with B E2M1 is the usual
+ * B, each MX_FMT_E2M1 or MX_FMT_E4M3, or both MX_FMT_E5M2 (another pair
+ * with E5M2 gives MX_ERR_FORMAT) (A E4M3 with B E2M1 is the usual
  * "W4A8" serving layout).  The block dot product is the one of mx_gemm with
  * each operand decoded in its own format (the OCP MX v1.0 dot product does
  * not require equal formats; the pages' "broader low precision" outlook, and

@@ -8,7 +8,8 @@ raise.
     C = mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=torch.bfloat16)
 
 a: (M, K/2) uint8 for MXFP4 (E2M1, two elements per byte, element 2i in the
-   low nibble), or (M, K) uint8 / float8_e4m3fn for MXFP8 (E4M3);
+   low nibble), or (M, K) uint8 / float8_e4m3fn for MXFP8 (E4M3; or E5M2,
+   FMT_E5M2, as uint8 / float8_e5m2);
 b: (N, ...) likewise; a_scale: (M, K/32) uint8 E8M0; b_scale: (N, K/32).
 Returns C = A * B^T, (M, N), float32 or bfloat16.
 
@@ -26,6 +27,7 @@ import os
 
 FMT_E2M1 = 1
 FMT_E4M3 = 2
+FMT_E5M2 = 3
 OUT_FP32 = 1
 OUT_BF16 = 2
 MAX_DIM = 1 << 30     # largest M or N
@@ -170,7 +172,7 @@ def _as_u8(t, name):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu,
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2, torch.float8_e8m0fnu,
                        getattr(torch, "float4_e2m1fn_x2", torch.uint8)):
         raise ValueError("%s must hold bytes (uint8 or an 8-bit float view), got %s"
                          % (name, t.dtype))
@@ -194,8 +196,8 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
     if out_dtype is None:
         out_dtype = torch.bfloat16
     fmt_b = fmt if fmt_b is None else fmt_b
-    if fmt not in (FMT_E2M1, FMT_E4M3) or fmt_b not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("fmt and fmt_b must be FMT_E2M1 or FMT_E4M3")
+    if fmt not in (FMT_E2M1, FMT_E4M3, FMT_E5M2) or fmt_b not in (FMT_E2M1, FMT_E4M3, FMT_E5M2):
+        raise ValueError("fmt and fmt_b must be FMT_E2M1, FMT_E4M3 or FMT_E5M2")
     code, tdt = _out_code(out_dtype)
     a, b = _as_u8(a, "a"), _as_u8(b, "b")
     a_scale, b_scale = _as_u8(a_scale, "a_scale"), _as_u8(b_scale, "b_scale")

@@ -42,11 +42,14 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-enum { FP4 = 1, FP8 = 2 };      // equal to MX_FMT_E2M1 / MX_FMT_E4M3
+enum { FP4 = 1, FP8 = 2, BF8 = 3 };   // equal to MX_FMT_E2M1 / MX_FMT_E4M3 / MX_FMT_E5M2
 enum { OF32 = 1, OBF16 = 2 };   // equal to MX_OUT_FP32 / MX_OUT_BF16
 
-// Format selector of the scaled MFMA (cbsz for A, blgp for B).
-template <int FMT> struct mfma_fmt { static constexpr int sel = (FMT == FP4) ? 4 : 0; };
+// Format selector of the scaled MFMA (cbsz for A, blgp for B): 0 E4M3,
+// 1 E5M2, 4 E2M1.  E4M3 and E5M2 share one byte-per-element layout.
+template <int FMT> struct mfma_fmt {
+    static constexpr int sel = (FMT == FP4) ? 4 : (FMT == BF8) ? 1 : 0;
+};
 
 // A slab is a run of K-values of every row of the A and B tiles: 256 when
 // both operands are E2M1, else 128 -- four or two 64-K instruction steps, and
@@ -388,7 +391,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     auto chunk_offs = [&](auto fc, int p, int swl, int &o0, int &o1) {
         // Step p of a slab: E4M3 chunks 4p+g and 4p+2+g of a 128-byte row,
         // E2M1 chunk 2p+g (of a 128- or a 64-byte row).
-        const int c0 = (decltype(fc)::value == FP8) ? 4 * p + g : 2 * p + g;
+        const int c0 = (decltype(fc)::value != FP4) ? 4 * p + g : 2 * p + g;
         o0 = (c0 ^ swl) << 4;
         o1 = ((c0 + 2) ^ swl) << 4;
     };
@@ -412,7 +415,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         constexpr int F = IA ? FA : FB, R = IA ? RA : RB;
         const uint8_t *rp = smem + s.data + off + f * 32 * R;
         const v4i lo = *(const v4i *)(rp + (IA ? s.a0 : s.b0));
-        if (F == FP8) {
+        if (F != FP4) {
             const v4i hi = *(const v4i *)(rp + (IA ? s.a1 : s.b1));
             v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         } else {
@@ -446,8 +449,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             constexpr int o = decltype(oc)::value;
             constexpr int d0 = o * FD / FR, d1 = (o + 1) * FD / FR;
             // LDS reads per fragment: data (2 for E4M3, 1 for E2M1) + scale
-            constexpr int NRR = ((ROLL_A ? FA : FB) == FP8) ? 3 : 2;
-            constexpr int NRD = ((ROLL_A ? FB : FA) == FP8) ? 3 : 2;
+            constexpr int NRR = ((ROLL_A ? FA : FB) != FP4) ? 3 : 2;
+            constexpr int NRD = ((ROLL_A ? FB : FA) != FP4) ? 3 : 2;
 #pragma unroll
             for (int d = 0; d < FD; ++d) {
                 if constexpr (ROLL_A)

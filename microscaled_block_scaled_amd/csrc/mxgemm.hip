@@ -21,7 +21,7 @@ constexpr int kMaxDevices = 64;
 
 int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
 {
-    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3) return MX_ERR_FORMAT;
+    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3 && fmt != MX_FMT_E5M2) return MX_ERR_FORMAT;
     if (out_dtype != MX_OUT_FP32 && out_dtype != MX_OUT_BF16) return MX_ERR_OUT_DTYPE;
     // K a multiple of 128 (FlyDSL article, "API compatibility is not
     // universal input coverage").
@@ -268,6 +268,8 @@ int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, 
         launched = launch<mx::FP4, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
         launched = launch<mx::FP8, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E5M2)                       // checked: then fmt_b is E5M2 too
+        launched = launch<mx::BF8, mx::BF8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E4M3)
         launched = launch<mx::FP8, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else
@@ -283,7 +285,7 @@ extern "C" const char *mx_strerror(int code)
 {
     switch (code) {
     case MX_OK: return "success";
-    case MX_ERR_FORMAT: return "unsupported element format (expected MX_FMT_E2M1 or MX_FMT_E4M3)";
+    case MX_ERR_FORMAT: return "unsupported element format or format pair";
     case MX_ERR_OUT_DTYPE: return "unsupported output type (expected MX_OUT_FP32 or MX_OUT_BF16)";
     case MX_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 128, K % 128 == 0, M and N <= 2^30, K <= 2^24)";
     case MX_ERR_NULL: return "null pointer argument";
@@ -349,7 +351,8 @@ extern "C" int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t
 {
     int rc = check_args(fmt_a, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
-    if (fmt_b != MX_FMT_E2M1 && fmt_b != MX_FMT_E4M3) return MX_ERR_FORMAT;
+    if (fmt_b != MX_FMT_E2M1 && fmt_b != MX_FMT_E4M3 && fmt_b != MX_FMT_E5M2) return MX_ERR_FORMAT;
+    if ((fmt_a == MX_FMT_E5M2) != (fmt_b == MX_FMT_E5M2)) return MX_ERR_FORMAT;   // E5M2 only with E5M2
     if (split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
     mx_plan_t plan;
     if (tile_m == 0 && tile_n == 0) {
@@ -463,6 +466,7 @@ int grouped_plan(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, 
 {
     int rc = check_args(fmt, 1, N, K, out_dtype);            // format, output, N, K
     if (rc != MX_OK) return rc;
+    if (fmt == MX_FMT_E5M2) return MX_ERR_FORMAT;            // grouped: E2M1 and E4M3 only
     if (groups < 1 || groups > MX_MAX_GROUPS || groups * N > MX_MAX_DIM) return MX_ERR_SHAPE;
     if (!group_rows || !plan) return MX_ERR_NULL;
     int64_t total = 0, maxm = 0;

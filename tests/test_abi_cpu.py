@@ -52,7 +52,7 @@ def test_strerror_covers_codes():
 
 @pytest.mark.parametrize("fmt,M,N,K,out,code", [
     (0, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
-    (3, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
+    (4, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
     (1, 16, 16, 128, 0, mxg.MX_ERR_OUT_DTYPE),
     (2, 16, 16, 128, 7, mxg.MX_ERR_OUT_DTYPE),
     (1, 0, 16, 128, 1, mxg.MX_ERR_SHAPE),
@@ -328,3 +328,17 @@ def test_mixed_shim_checks_k_per_operand():
         mxg.mx_gemm(a8, sa, b4, sb, fmt=mxg.FMT_E4M3, fmt_b=mxg.FMT_E2M1)
     with pytest.raises(ValueError):
         mxg.mx_gemm(a8, sa, b4, sb, fmt=mxg.FMT_E4M3, fmt_b=5)
+
+
+def test_e5m2_accepted_where_documented():
+    L = mxg.lib()
+    good = 1 << 20
+    args = (good,) * 5
+    p = mxg.MxPlan()
+    assert L.mx_gemm_plan(mxg.FMT_E5M2, 64, 64, 256, 2, ctypes.byref(p)) == mxg.MX_OK
+    # E5M2 pairs only with itself
+    assert L.mx_gemm_mixed(3, 2, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    assert L.mx_gemm_mixed(1, 3, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    # grouped GEMM and the quantizer take E2M1 / E4M3 only
+    assert _grouped(3, [4], 16, 128) == mxg.MX_ERR_FORMAT
+    assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
