@@ -191,6 +191,15 @@ def make_case(name, M=None):
                 A=A, A_scale=As, B=B, B_scale=Bs)
 
 
+def make_bf16(rows, K, seed, tensor=0):
+    """Seeded Gaussian rows x K matrix rounded to BF16 (torch's
+    round-to-nearest-even conversion), returned as uint16 bit patterns."""
+    import torch
+    x = _rng(200 + seed, tensor, 0).standard_normal((rows, K), dtype=np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def make_random(fmt, M, N, K, seed, kind="gauss", scale_lo=None, scale_hi=None):
     """Small seeded Gaussian case of any shape (K a multiple of 32).  With
     scale_lo/scale_hi set, scale bytes are replaced by uniform draws in that

@@ -56,6 +56,12 @@ def _bind(lib):
     lib.mxo_block_contrib.restype = ctypes.c_double
     lib.mxo_block_contrib.argtypes = [ctypes.c_int, i64, u8p, u8p, u8p, u8p,
                                       i64, i64, i64, dp]
+    lib.mxo_bf16_value.restype = ctypes.c_double
+    lib.mxo_bf16_value.argtypes = [ctypes.c_uint]
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.mxo_gemm_bf16.restype = ctypes.c_int
+    lib.mxo_gemm_bf16.argtypes = [i64, i64, i64, u16p, u16p, ctypes.POINTER(ctypes.c_int64), i64,
+                                  dp, dp, ctypes.c_int]
     lib.mxo_quantize.restype = ctypes.c_int
     lib.mxo_quantize.argtypes = [ctypes.c_int, i64, i64, dp, u8p, u8p]
     lib.mxo_gemm.restype = ctypes.c_int
@@ -186,6 +192,35 @@ class Oracle:
             r0 += m
         return tuple(out)
 
+    def bf16_value(self, bits):
+        return self.lib.mxo_bf16_value(int(bits))
+
+    def gemm_bf16(self, A, B, rows=None, threads=0):
+        """BF16 dense NT GEMM: A (M x K) and B (N x K) uint16 arrays of BF16
+        bit patterns -> (C, T) float64, rows of A as in ``gemm``."""
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        B = np.ascontiguousarray(B, dtype=np.uint16)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[1]:
+            raise ValueError("A and B must be 2-D with the same K")
+        M, K = A.shape
+        N = B.shape[0]
+        if rows is None:
+            nrows, prow = M, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            nrows = rows_arr.shape[0]
+            prow = rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        C = np.zeros((nrows, N), np.float64)
+        T = np.zeros((nrows, N), np.float64)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        dp = ctypes.POINTER(ctypes.c_double)
+        rc = self.lib.mxo_gemm_bf16(M, N, K, A.ctypes.data_as(u16p), B.ctypes.data_as(u16p),
+                                    prow, nrows, C.ctypes.data_as(dp), T.ctypes.data_as(dp),
+                                    int(threads))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return C, T
+
     def quantize(self, fmt, X):
         """MX-quantize X (rows x K, values exactly representable in float64,
         K a multiple of 32) -> (codes, scales) uint8 arrays: codes rows x K
@@ -241,6 +276,10 @@ def block_contrib(*args, **kw):
 
 def quantize(*args, **kw):
     return default().quantize(*args, **kw)
+
+
+def gemm_bf16(*args, **kw):
+    return default().gemm_bf16(*args, **kw)
 
 
 def tables():

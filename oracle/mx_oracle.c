@@ -394,3 +394,54 @@ int mxo_quantize(int fmt, int64_t rows, int64_t K, const double *X, uint8_t *Q, 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * BF16 dense NT GEMM (the pages' second GEMM workload: BF16 dense GEMMs,
+ * FlyDSL article, "Performance numbers need their baselines"; no scales):
+ *   C[m][n] = sum_k a[m][k] * b[n][k],  T[m][n] = sum_k |a[m][k] * b[n][k]|
+ * with a, b BF16 values given as their 16-bit patterns (the upper half of
+ * the IEEE binary32 pattern).  A product of two BF16 values (8-bit
+ * significands) is exact in double; the K-term sum, taken in increasing k,
+ * is the only rounding (at most K * 2^-53 * T).
+ */
+double mxo_bf16_value(unsigned bits)
+{
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)(bits & 0xffffu) << 16;
+    return (double)v.f;
+}
+
+int mxo_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                  const int64_t *rows, int64_t nrows, double *C, double *T, int nthreads)
+{
+    if (M < 0 || N < 0 || K <= 0 || nrows < 0) return -1;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return -1;
+    if (!rows && nrows > M) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    double *bdec = (double *)malloc(sizeof(double) * (size_t)(N * K));
+    double *adec = (double *)malloc(sizeof(double) * (size_t)(nrows * K));
+    if (!bdec || !adec) { free(bdec); free(adec); return -1; }
+    for (int64_t i = 0; i < N * K; ++i) bdec[i] = mxo_bf16_value(B[i]);
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t m = rows ? rows[i] : i;
+        for (int64_t k = 0; k < K; ++k) adec[i * K + k] = mxo_bf16_value(A[m * K + k]);
+    }
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 4)
+    for (int64_t i = 0; i < nrows; ++i) {
+        const double *a = adec + i * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const double *b = bdec + n * K;
+            double c = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                c += a[k] * b[k];
+                t += fabs(a[k] * b[k]);
+            }
+            C[i * N + n] = c;
+            if (T) T[i * N + n] = t;
+        }
+    }
+    free(bdec);
+    free(adec);
+    return 0;
+}

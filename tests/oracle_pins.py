@@ -581,9 +581,41 @@ def pin_e5m2(orc):
     assert T[0, 0] == 2 * 57344.0 ** 2 + 2.0 ** -32 or T[0, 0] == 2 * 57344.0 ** 2
 
 
+def pin_bf16(orc):
+    """BF16 dense GEMM: the decode against torch's bfloat16 (every pattern);
+    a numpy matmul of torch-decoded values; exact rationals on a tiny case;
+    exact integers (small integer values make every sum exact); and the
+    transpose symmetry."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([orc.bf16_value(int(b)) for b in bits[::97]])
+    assert _same(got, ref[::97])
+    A = mxinputs.make_bf16(20, 256, seed=1)
+    B = mxinputs.make_bf16(12, 256, seed=1, tensor=1)
+    dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).double().numpy()
+    dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).double().numpy()
+    C, T = orc.gemm_bf16(A, B)
+    assert np.all(np.abs(C - dA @ dB.T) <= 1e-12 * T)
+    assert np.all(np.abs(T - np.abs(dA) @ np.abs(dB).T) <= 1e-12 * T)
+    Ct, Tt = orc.gemm_bf16(B, A)
+    assert np.array_equal(C, Ct.T) and np.array_equal(T, Tt.T)
+    Cs, _ = orc.gemm_bf16(A[:2, :8], B[:2, :8])
+    for m in range(2):
+        for n in range(2):
+            exact = sum(Fraction(dA[m, k]) * Fraction(dB[n, k]) for k in range(8))
+            assert Cs[m, n] == float(exact)
+    rng = np.random.default_rng(2)
+    ia = rng.integers(-8, 9, size=(5, 64)).astype(np.float32)
+    ib = rng.integers(-8, 9, size=(4, 64)).astype(np.float32)
+    to_bits = lambda x: torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    Ci, _ = orc.gemm_bf16(to_bits(ia), to_bits(ib))
+    assert np.array_equal(Ci, ia.astype(np.int64) @ ib.astype(np.int64).T)
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
-            pin_grouped, pin_mixed_formats, pin_e5m2]
+            pin_grouped, pin_mixed_formats, pin_e5m2, pin_bf16]

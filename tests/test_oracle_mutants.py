@@ -55,6 +55,11 @@ MUTANTS = [
     ("e5m2_subnormal", "ldexp((double)m / 4.0, -14)", "ldexp((double)m / 4.0, -15)"),
     ("e5m2_inf_as_nan", "mag = (m == 0) ? INFINITY : NAN;", "mag = NAN;"),
     ("e5m2_double_sums", "if (exact128) block_exact(", "if (0) block_exact("),
+    # BF16 GEMM.
+    ("bf16_decode_shift", "v.u = (uint32_t)(bits & 0xffffu) << 16;", "v.u = (uint32_t)(bits & 0xffffu) << 15;"),
+    ("bf16_b_row", "const double *b = bdec + n * K;", "const double *b = bdec + (n / 2) * K;"),
+    ("bf16_last_k", "for (int64_t k = 0; k < K; ++k) {\n                c += a[k] * b[k];",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n                c += a[k] * b[k];"),
     ("mixed_same_format_entry", "return mxo_gemm_ab(fmt, fmt, M,", "return mxo_gemm_ab(fmt, MXO_FMT_E4M3, M,"),
     # The quantizer.
     ("q_e4m3_emax", "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 8;",
