@@ -14,8 +14,8 @@ the CPU oracle's rate on a bounded row sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
     python bench.py --cold [--all]    (per-launch cold-cache timing)
-    python bench.py --quantize | --grouped | --mixed
-        (the quantizer / grouped GEMM / mixed-format GEMM)
+    python bench.py --quantize | --grouped | --mixed | --bf16
+        (the quantizer / grouped GEMM / mixed-format GEMM / dense BF16 GEMM)
 """
 import argparse
 import glob
@@ -445,6 +445,93 @@ def copy_calibration(nbytes=256 << 20, reps=3):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+# Dense BF16 GEMM workloads (mx_gemm_bf16): name -> (M, N, K), BF16 out.
+BF16_WORKLOADS = {
+    "bf16_llama8b_qkv": (2048, 6144, 4096),
+    "bf16_llama70b_down_m2048": (2048, 8192, 28672),
+    "bf16_llama70b_down_m8": (8, 8192, 28672),
+}
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
+
+
+def bench_bf16(steps, warmup, name, with_cpu):
+    """The dense BF16 NT GEMM on the same tile kernels, from seeded Gaussian
+    BF16 operands resident in HBM."""
+    import numpy as np
+    import torch
+    import microscaled_block_scaled_amd as mxg
+    M, N, K = BF16_WORKLOADS[name]
+    out = mxinputs.OUT_BF16
+    ha = mxinputs.make_bf16(M, K, seed=4000, tensor=0)
+    hb = mxinputs.make_bf16(N, K, seed=4000, tensor=1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A = torch.from_numpy(ha.view(np.int16)).to(dev)
+    B = torch.from_numpy(hb.view(np.int16)).to(dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    args = (M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), out, stream.cuda_stream)
+    for _ in range(warmup):
+        if mxg.gemm_bf16_ptr(*args) != 0:
+            raise RuntimeError("mx_gemm_bf16 failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        mxg.gemm_bf16_ptr(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = e0.elapsed_time(e1) / steps / 1e3
+    flops = 2.0 * M * N * K
+    nbytes = (M + N) * K * 2 + M * N * 2
+    peak = PEAK_BF16_TFLOPS
+    p = mxg.plan_bf16(M, N, K, out)
+    plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
+        p["variant"], p["tile_m"], p["tile_n"], p["split_k"], p["workgroups"])
+    if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flops / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        achieved = nbytes / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(name, GEMM_SOURCES, plan_str)
+    roof["algorithmic_bytes"] = nbytes
+    roof["launch_us"] = round(launch_s * 1e6, 2)
+    tflops = flops * steps / wall / 1e12
+    res = {"metric": "Dense BF16 GEMM TFLOPS and % of MI355X dense BF16 MFMA peak",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": name, "M": M, "N": N, "K": K, "format": "bf16",
+                      "out": "bf16", "accumulate": "fp32",
+                      "peak_frac": round(tflops / peak, 4), "plan": plan_str,
+                      "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
+           "roofline": roof}
+    if with_cpu:
+        import oracle
+        threads = cpu_threads()
+        r0 = min(M, 2)
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(ha, hb, rows=np.arange(r0), threads=threads)
+        t_probe = time.perf_counter() - t0
+        nrows = int(max(r0, min(M, r0 * 12.0 / max(t_probe, 1e-6))))
+        rows = np.linspace(0, M - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(ha, hb, rows=rows, threads=threads)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {
+            "value": round(2.0 * nrows * N * K / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d of %d rows of A (all %d columns, K=%d), %.1f s on %d threads"
+                      % (nrows, M, N, K, t, threads)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +552,8 @@ def main():
                          "--workload, or of every workload with --all")
     ap.add_argument("--mixed", action="store_true",
                     help="time the other formats (A E4M3 x B E2M1; E5M2) instead")
+    ap.add_argument("--bf16", action="store_true",
+                    help="time the dense BF16 GEMM (mx_gemm_bf16) instead")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
@@ -488,6 +577,11 @@ def main():
     if a.mixed:
         for name in MIXED_WORKLOADS:
             print(json.dumps(bench_mixed(a.steps, a.warmup, name)), flush=True)
+        return
+    if a.bf16:
+        for i, name in enumerate(BF16_WORKLOADS):
+            with_cpu = (not a.no_cpu_baseline) and i == 0
+            print(json.dumps(bench_bf16(a.steps, a.warmup, name, with_cpu)), flush=True)
         return
     if a.grouped:
         for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):

@@ -211,6 +211,41 @@ int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                   void *C, int out_dtype, int tile_m, int tile_n, int split_k,
                   void *stream);
 
+/*
+ * Dense BF16 NT GEMM, C = A * B^T with no scales:
+ *   C[m][n] = sum_{k<K} A[m][k] * B[n][k]
+ * accumulated in FP32 -- the FlyDSL article's second GEMM workload (dense
+ * BF16 GEMMs, section "Performance numbers need their baselines").  It runs
+ * on the same tile kernels as mx_gemm, on gfx950's BF16 matrix instruction.
+ *   M, N, K    M, N >= 1 and <= MX_MAX_DIM; K >= 16, K % 16 == 0,
+ *              K <= MX_MAX_K_BF16
+ *   A          M x K bfloat16 values (16-bit patterns), K-contiguous, row
+ *              pitch K; 16-byte aligned device pointer
+ *   B          N x K bfloat16 values, likewise ("NT": C is A times B
+ *              transposed)
+ *   C          output, 16-byte aligned; float if out_dtype == MX_OUT_FP32,
+ *              bfloat16 bits (round to nearest even) if MX_OUT_BF16
+ *   tile_m, tile_n, split_k  as for mx_gemm_mixed: 0, 0, 0 takes the plan's
+ *              choice (mx_gemm_bf16_plan describes it), otherwise one of
+ *              mx_tile_shapes and 0 .. MX_MAX_SPLIT_K slices of whole 512-K
+ *              periods
+ *   stream     hipStream_t, or NULL
+ * Returns MX_OK or a negative MX_ERR_* code.  Errors, asynchrony, the
+ * split-K workspace and determinism are as for mx_gemm; C must not overlap
+ * A or B.
+ */
+#define MX_MAX_K_BF16 ((int64_t)1 << 23)
+int mx_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                 void *C, int out_dtype, int tile_m, int tile_n, int split_k,
+                 void *stream);
+
+/*
+ * The launch mx_gemm_bf16 would make with tile and split 0.  Host logic only:
+ * no HIP call, no device needed.  Returns MX_OK or mx_gemm_bf16's argument
+ * error (MX_ERR_NULL for a NULL plan).
+ */
+int mx_gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *plan);
+
 /* Largest number of groups of mx_gemm_grouped. */
 #define MX_MAX_GROUPS 256
 

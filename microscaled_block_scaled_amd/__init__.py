@@ -21,6 +21,11 @@ quantizes a float32 / bfloat16 matrix into that operand layout (OCP MX rule).
 
 multiplies consecutive row groups of a by their own weights: b is
 (G*N, ...), rows g*N .. g*N+N-1 being group g's weight.
+
+    C = mx_gemm_bf16(a, b, out_dtype=torch.bfloat16)
+
+is the dense BF16 GEMM on the same tile kernels: a (M, K) and b (N, K)
+bfloat16, no scales, K a multiple of 16.
 """
 import ctypes
 import os
@@ -32,6 +37,7 @@ OUT_FP32 = 1
 OUT_BF16 = 2
 MAX_DIM = 1 << 30     # largest M or N
 MAX_K = 1 << 24       # largest K
+MAX_K_BF16 = 1 << 23  # largest K of the dense BF16 GEMM
 MAX_SPLIT_K = 8       # largest forced K split (mx_gemm_tile)
 MAX_GROUPS = 256      # most groups of mx_gemm_grouped
 VARIANT_TILE = 1
@@ -104,6 +110,11 @@ def lib():
     L.mx_gemm_grouped_plan.restype = ctypes.c_int
     L.mx_gemm_grouped_plan.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64,
                                        ctypes.c_int, ctypes.POINTER(MxPlan)]
+    L.mx_gemm_bf16.restype = ctypes.c_int
+    L.mx_gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, vp]
+    L.mx_gemm_bf16_plan.restype = ctypes.c_int
+    L.mx_gemm_bf16_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(MxPlan)]
     L.mx_gemm_grouped.restype = ctypes.c_int
     L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
                                   vp, vp, vp, ctypes.c_int, vp]
@@ -222,6 +233,72 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
     with torch.cuda.device(dev):
         rc = gemm_ptr(fmt, M, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
                       b_scale.data_ptr(), out.data_ptr(), code, stream, tile, split_k, fmt_b)
+    if rc != MX_OK:
+        _raise(rc)
+    return out
+
+
+def plan_bf16(M, N, K, out_dtype=OUT_BF16):
+    """How mx_gemm_bf16 would run this problem (a dict); host logic only."""
+    p = MxPlan()
+    rc = lib().mx_gemm_bf16_plan(int(M), int(N), int(K), int(out_dtype), ctypes.byref(p))
+    if rc != MX_OK:
+        _raise(rc)
+    return p.as_dict()
+
+
+def gemm_bf16_ptr(M, N, K, A, B, C, out_dtype, stream=0, tile=None, split_k=0):
+    """Raw dense BF16 entry point (mx_gemm_bf16): integer device addresses,
+    returns the status code.  ``tile=None`` and ``split_k=0`` take the plan's
+    choice."""
+    tm, tn = tile if tile is not None else (0, 0)
+    return lib().mx_gemm_bf16(int(M), int(N), int(K), A, B, C, int(out_dtype), int(tm),
+                              int(tn), int(split_k), stream or None)
+
+
+def _as_bf16(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("%s must hold bfloat16 values (bfloat16, or int16 / uint16 bit "
+                         "patterns), got %s" % (name, t.dtype))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (no stride arguments; copy first)" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    return t
+
+
+def mx_gemm_bf16(a, b, out_dtype=None, out=None, stream=None, tile=None, split_k=0):
+    """Dense C = A * B^T for BF16 A (M x K) and B (N x K), FP32 accumulation,
+    C in ``out_dtype`` (torch.bfloat16 by default, or torch.float32).
+    ``tile=(tile_m, tile_n)`` forces one of ``tile_shapes()``, ``split_k``
+    the number of K slices (0: the plan's choice)."""
+    import torch
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    code, tdt = _out_code(out_dtype)
+    a, b = _as_bf16(a, "a"), _as_bf16(b, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    if b.device != a.device:
+        raise ValueError("all operands must be on the same device")
+    dev = a.device
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=dev)
+    elif out.dtype != tdt or tuple(out.shape) != (M, N) or not out.is_contiguous() \
+            or out.device != dev:
+        raise ValueError("out must be a contiguous (M, N) %s tensor on %s" % (tdt, dev))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = gemm_bf16_ptr(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), code, stream,
+                           tile, split_k)
     if rc != MX_OK:
         _raise(rc)
     return out

@@ -21,10 +21,16 @@
 //     8*(e/4) + 4g + e%4 of column c.
 // (The 16x16x128 form, measured the same way, places E4M3 K-values 16g..+15
 // and 64+16g..+15 in lane group g of four; it is not used here.)
+// Dense BF16 operands (no scales) use v_mfma_f32_32x32x16_bf16: lane (r, g)
+// holds 8 K-values of row r, 16 bytes.  Which 8 of the 16 does not matter
+// here: A and B fragments are read with the same lane-to-K map, and a dot
+// product does not depend on the order of its terms.  The kernel hands
+// lane group g the K-values 8g .. 8g+7.
 // With a row's K-values staged as 16-byte chunks (chunk c = bytes 16c..16c+15
 // of a 128-byte row segment), one instruction's K-step p of a segment reads:
 //   * E4M3 (2 steps per segment): chunks 4p+g and 4p+2+g, scale block 2p+g;
-//   * E2M1 (4 steps per segment): chunk 2p+g, scale block 2p+g.
+//   * E2M1 (4 steps per segment): chunk 2p+g, scale block 2p+g;
+//   * BF16 (4 steps of 16 K-values per segment): chunk 2p+g.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,11 +44,13 @@
 namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 enum { FP4 = 1, FP8 = 2, BF8 = 3 };   // equal to MX_FMT_E2M1 / MX_FMT_E4M3 / MX_FMT_E5M2
+enum { B16 = 4 };                     // dense BF16 elements, no scales (B16 pairs with B16 only)
 enum { OF32 = 1, OBF16 = 2 };   // equal to MX_OUT_FP32 / MX_OUT_BF16
 
 // Format selector of the scaled MFMA (cbsz for A, blgp for B): 0 E4M3,
@@ -52,18 +60,27 @@ template <int FMT> struct mfma_fmt {
 };
 
 // A slab is a run of K-values of every row of the A and B tiles: 256 when
-// both operands are E2M1, else 128 -- four or two 64-K instruction steps, and
-// their scale bytes (8 or 4 per row).  An operand's slab row is 128 bytes
-// (E4M3, or E2M1 with E2M1), which makes every copy request a whole 128-byte
-// line, or 64 bytes (E2M1 beside E4M3, half a line).
+// both operands are E2M1, 64 for BF16, else 128 -- four or two 64-K scaled
+// instruction steps and their scale bytes (8 or 4 per row), or four 16-K
+// BF16 steps.  An operand's slab row is 128 bytes (E4M3, E2M1 with E2M1, or
+// BF16), which makes every copy request a whole 128-byte line, or 64 bytes
+// (E2M1 beside E4M3, half a line).
 constexpr int SW = 128;
 template <int FA, int FB> struct slab {
-    static constexpr int kvals = (FA == FP4 && FB == FP4) ? 2 * SW : SW;
-    static constexpr int steps = kvals / 64;         // 4 or 2
-    static constexpr int sbytes = kvals / 32;        // 8 or 4
+    static_assert((FA == B16) == (FB == B16), "BF16 pairs with BF16 only");
+    static constexpr bool scaled = FA != B16;
+    static constexpr int kvals = (FA == B16) ? SW / 2 : (FA == FP4 && FB == FP4) ? 2 * SW : SW;
+    static constexpr int kstep = scaled ? 64 : 16;   // K-values per MFMA
+    static constexpr int steps = kvals / kstep;      // 4, 2 or 4
+    static constexpr int sbytes = scaled ? kvals / 32 : 0;   // 8, 4 or none
     // bytes of one row of an operand of format F in a slab
-    template <int F> static constexpr int row_bytes = (F == FP4) ? kvals / 2 : kvals;
+    template <int F> static constexpr int row_bytes = (F == FP4) ? kvals / 2 : (F == B16) ? 2 * kvals : kvals;
 };
+// Bytes of k consecutive elements of format F.
+template <int F> __device__ __forceinline__ int64_t kbytes(int64_t k)
+{
+    return (F == FP4) ? k / 2 : (F == B16) ? 2 * k : k;
+}
 
 // FP32 -> BF16 bits, round to nearest even (NaN stays NaN): one gfx950
 // v_cvt_pk_bf16_f32, branch-free.
@@ -90,6 +107,13 @@ __device__ __forceinline__ v16f mma(const v8i &a, const v8i &b, v16f acc, int sa
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
         a, b, acc, mfma_fmt<FA>::sel, mfma_fmt<FB>::sel, 0, sa, 0, sb);
+}
+// Dense BF16: 16 bytes (8 values) per lane and operand, no scales.
+template <int FA, int FB>
+__device__ __forceinline__ v16f mma(const v4i &a, const v4i &b, v16f acc, int, int)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                  __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
 }
 
 // Direct HBM -> LDS copies (gfx950 global_load_lds): lane l of the wave
@@ -206,13 +230,14 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     using SL = slab<FA, FB>;
     constexpr int KS = SL::kvals;                          // K-values per slab
     constexpr int HS = SL::steps;                          // MFMA steps per slab
+    constexpr bool SCALED = SL::scaled;                    // MX formats (BF16 has no scales)
     constexpr int SBS = SL::sbytes;                        // scale bytes per row per slab
-    constexpr int PS = 16 / SBS;                           // slabs per scale period
+    constexpr int PS = SCALED ? 16 / SBS : S;              // slabs per scale period
     constexpr int RA = SL::template row_bytes<FA>;         // slab row bytes, A and B
     constexpr int RB = SL::template row_bytes<FB>;
     constexpr int ROWS = BM + BN;
     constexpr int DATA = BM * RA + BN * RB;                // element bytes per slab
-    constexpr int NSI = (ROWS + 63) / 64;                  // scale copy instructions
+    constexpr int NSI = SCALED ? (ROWS + 63) / 64 : 0;     // scale copy instructions
     constexpr int SBUF = NSI * 64 * 16;                    // one scale buffer
     constexpr int RPCA = 1024 / RA, RPCB = 1024 / RB;      // rows per copy instruction
     static_assert(S >= 2 && S - 1 <= PS, "one period of scale lookahead covers the ring");
@@ -220,7 +245,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be 32-aligned");
     constexpr int CPA = (BM / RPCA + NW - 1) / NW;         // A copies per wave per slab
     constexpr int CPB = (BN / RPCB + NW - 1) / NW;         // B copies per wave per slab
-    constexpr int CPS = (NSI + NW - 1) / NW;               // scale copies per wave per period
+    constexpr int CPS = SCALED ? (NSI + NW - 1) / NW : 0;  // scale copies per wave per period
     constexpr int NCOPY = CPA + CPB;
     // The epilogue reuses the LDS to stage output bands (see below).
     typedef typename std::conditional<OUT == OF32, float, uint16_t>::type otype;
@@ -252,8 +277,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             if (groups.tile_start[mid] <= bid) lo = mid; else hi = mid - 1;
         }
         const int r0 = groups.row_start[lo];
-        const int64_t rba = (FA == FP4) ? (int64_t)K / 2 : (int64_t)K;
-        const int64_t rbb = (FB == FP4) ? (int64_t)K / 2 : (int64_t)K;
+        const int64_t rba = kbytes<FA>(K), rbb = kbytes<FB>(K);
         M = groups.row_start[lo + 1] - r0;
         tiles_m = (M + BM - 1) / BM;
         bid -= groups.tile_start[lo];
@@ -270,16 +294,13 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int m0 = tm * BM, n0 = tn * BN;
     const int kb = slice * kchunk, klen = min(kchunk, K - kb);
     // Row stride, slice bytes per row and slice offset of each operand.
-    const int64_t rowba = (FA == FP4) ? (int64_t)K / 2 : (int64_t)K;
-    const int64_t rowbb = (FB == FP4) ? (int64_t)K / 2 : (int64_t)K;
-    const int64_t rowla = (FA == FP4) ? (int64_t)klen / 2 : (int64_t)klen;
-    const int64_t rowlb = (FB == FP4) ? (int64_t)klen / 2 : (int64_t)klen;
-    const int64_t kboffa = (FA == FP4) ? (int64_t)kb / 2 : (int64_t)kb;
-    const int64_t kboffb = (FB == FP4) ? (int64_t)kb / 2 : (int64_t)kb;
+    const int64_t rowba = kbytes<FA>(K), rowbb = kbytes<FB>(K);
+    const int64_t rowla = kbytes<FA>(klen), rowlb = kbytes<FB>(klen);
+    const int64_t kboffa = kbytes<FA>(kb), kboffb = kbytes<FB>(kb);
     const int sps = K / 32, sp = klen / 32;                  // scale row stride, slice extent
     const int nslab = (klen + KS - 1) / KS;                  // E2M1 x E2M1: the last may be half
     const int nper = (sp + 15) / 16;                       // scale periods
-    const int nsteps = klen / 64;
+    const int nsteps = klen / SL::kstep;
 
     // Copy addresses are a wave-uniform base (scalar registers) plus a 32-bit
     // per-lane offset, which stays below 256 rows * rowb < 2^32 for K <= 2^24.
@@ -347,6 +368,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // readers shift their byte index to match.  Every byte read lies inside
     // its row.
     auto issue_scales = [&](int p, int buf) {
+        if constexpr (!SCALED) return;
         p = min(p, nper - 1);
         const int soff = min(p * 16, sp - 16);
 #pragma unroll
@@ -379,8 +401,11 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int FR = ROLL_A ? FM : FN, FD = ROLL_A ? FN : FM;
     const int r_off = ROLL_A ? a_off : b_off, d_off = ROLL_A ? b_off : a_off;
     const int rs_off = ROLL_A ? sa_off : sb_off, ds_off = ROLL_A ? sb_off : sa_off;
-    v8i fr[FR], fd[2][FD];
-    int fsr[FR], fsd[2][FD];
+    // Fragment registers: 8 dwords for the scaled MFMA (E2M1 uses the low
+    // 4), 4 for BF16.
+    typedef typename std::conditional<SCALED, v8i, v4i>::type fv;
+    fv fr[FR], fd[2][FD];
+    int fsr[FR] = {}, fsd[2][FD] = {};                     // scale bytes (unused for BF16)
 
     // Where one step's operands are: ring slot `slot`, pass p of the slab,
     // scale buffer `sbuf`, slab `kp` within its scale period, and the scale
@@ -389,9 +414,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // the swizzle).
     struct Src { int data, scale, a0, a1, b0, b1; };
     auto chunk_offs = [&](auto fc, int p, int swl, int &o0, int &o1) {
-        // Step p of a slab: E4M3 chunks 4p+g and 4p+2+g of a 128-byte row,
-        // E2M1 chunk 2p+g (of a 128- or a 64-byte row).
-        const int c0 = (decltype(fc)::value != FP4) ? 4 * p + g : 2 * p + g;
+        // Step p of a slab: E4M3 / E5M2 chunks 4p+g and 4p+2+g of a 128-byte
+        // row, E2M1 chunk 2p+g (of a 128- or a 64-byte row), BF16 chunk 2p+g.
+        constexpr int F = decltype(fc)::value;
+        const int c0 = (F == FP4 || F == B16) ? 2 * p + g : 4 * p + g;
         o0 = (c0 ^ swl) << 4;
         o1 = ((c0 + 2) ^ swl) << 4;
     };
@@ -410,18 +436,22 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // Fragment f of operand A (ia true) or B, whose lane rows start at LDS
     // offset `off` (scale rows at `soff`): 16 (E2M1) or 32 (E4M3) bytes and
     // a scale byte.
-    auto frag = [&](auto ia, const Src &s, int off, int soff, int f, v8i &v, int &sv) {
+    auto frag = [&](auto ia, const Src &s, int off, int soff, int f, fv &v, int &sv) {
         constexpr bool IA = decltype(ia)::value;
         constexpr int F = IA ? FA : FB, R = IA ? RA : RB;
         const uint8_t *rp = smem + s.data + off + f * 32 * R;
         const v4i lo = *(const v4i *)(rp + (IA ? s.a0 : s.b0));
-        if (F != FP4) {
-            const v4i hi = *(const v4i *)(rp + (IA ? s.a1 : s.b1));
-            v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (!SCALED) {
+            v = lo;
         } else {
-            v = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+            if constexpr (F != FP4) {
+                const v4i hi = *(const v4i *)(rp + (IA ? s.a1 : s.b1));
+                v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                v = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+            }
+            sv = smem[s.scale + soff + f * 32 * 16];
         }
-        sv = smem[s.scale + soff + f * 32 * 16];
     };
     const std::integral_constant<bool, ROLL_A> is_r{};       // the rolled operand is A?
     const std::integral_constant<bool, !ROLL_A> is_d{};
@@ -448,9 +478,11 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         static_for<FR>([&](auto oc) {
             constexpr int o = decltype(oc)::value;
             constexpr int d0 = o * FD / FR, d1 = (o + 1) * FD / FR;
-            // LDS reads per fragment: data (2 for E4M3, 1 for E2M1) + scale
-            constexpr int NRR = ((ROLL_A ? FA : FB) != FP4) ? 3 : 2;
-            constexpr int NRD = ((ROLL_A ? FB : FA) != FP4) ? 3 : 2;
+            // LDS reads per fragment: data (2 for E4M3 / E5M2, 1 for E2M1
+            // and BF16) + scale (none for BF16)
+            constexpr int FRF = ROLL_A ? FA : FB, FDF = ROLL_A ? FB : FA;
+            constexpr int NRR = !SCALED ? 1 : (FRF != FP4) ? 3 : 2;
+            constexpr int NRD = !SCALED ? 1 : (FDF != FP4) ? 3 : 2;
 #pragma unroll
             for (int d = 0; d < FD; ++d) {
                 if constexpr (ROLL_A)
@@ -498,7 +530,9 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 
     // Prologue: scale period 0 (period 1 follows at slab 0's opening),
     // slabs 0..S-2 in flight, then open slab 0 and read step 0.
-    if (short_rows) {
+    if (!SCALED) {
+        // no scales
+    } else if (short_rows) {
         for (int r = tid; r < ROWS; r += NW * 64) {
             const uint8_t *src = ((r < BM) ? As + (int64_t)min(m0 + r, M - 1) * sps
                                            : Bs + (int64_t)min(n0 + r - BM, N - 1) * sps) + kb / 32;

@@ -30,6 +30,16 @@ int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
     return MX_OK;
 }
 
+// Dense BF16 GEMM: K a multiple of 16 (one BF16 MFMA step), rows of at most
+// MX_MAX_K bytes (the same 32-bit copy offsets as the MX formats).
+int check_args_bf16(int64_t M, int64_t N, int64_t K, int out_dtype)
+{
+    if (out_dtype != MX_OUT_FP32 && out_dtype != MX_OUT_BF16) return MX_ERR_OUT_DTYPE;
+    if (M < 1 || N < 1 || K < 16 || K % 16 != 0) return MX_ERR_SHAPE;
+    if (M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_K_BF16) return MX_ERR_SHAPE;
+    return MX_OK;
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Tile shapes of the tiled kernel: {BM, BN, waves along M, waves along N,
@@ -240,14 +250,19 @@ float *stream_workspace(int dev, hipStream_t s, size_t bytes)
     return (float *)w.ptr;
 }
 
+// Formats as run_plan sees them: the MX_FMT_* codes, and dense BF16 (no
+// scales), which has no format code of its own in the ABI.
+constexpr int kFmtBF16 = 0x100;
+
 // Checks that need no device, then the device check, then the launch.
 int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
              const void *A, const void *A_scale, const void *B, const void *B_scale,
              void *C, int out_dtype, void *stream)
 {
-    if (!A || !A_scale || !B || !B_scale || !C) return MX_ERR_NULL;
+    const bool scaled = fmt_a != kFmtBF16;
+    if (!A || !B || !C || (scaled && (!A_scale || !B_scale))) return MX_ERR_NULL;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
-        !aligned(A_scale, 4) || !aligned(B_scale, 4))
+        (scaled && (!aligned(A_scale, 4) || !aligned(B_scale, 4))))
         return MX_ERR_ALIGN;
     int dev = -1;
     const int rc = device_ready(&dev);
@@ -264,7 +279,9 @@ int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, 
     }
     bool launched;
     const int o = out_dtype;
-    if (fmt_a == MX_FMT_E2M1 && fmt_b == MX_FMT_E2M1)
+    if (!scaled)
+        launched = launch<mx::B16, mx::B16>(plan, o, A, nullptr, B, nullptr, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E2M1 && fmt_b == MX_FMT_E2M1)
         launched = launch<mx::FP4, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
         launched = launch<mx::FP8, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
@@ -366,6 +383,35 @@ extern "C" int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t
     return run_plan(plan, fmt_a, fmt_b, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
 }
 
+extern "C" int mx_gemm_bf16_plan(int64_t M, int64_t N, int64_t K, int out_dtype,
+                                 mx_plan_t *plan)
+{
+    if (!plan) return MX_ERR_NULL;
+    const int rc = check_args_bf16(M, N, K, out_dtype);
+    if (rc != MX_OK) return rc;
+    fill_plan(choose_tile(M, N, K), M, N, K, plan);
+    return plan->workgroups > kMaxGrid ? MX_ERR_SHAPE : MX_OK;
+}
+
+extern "C" int mx_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                            void *C, int out_dtype, int tile_m, int tile_n, int split_k,
+                            void *stream)
+{
+    const int rc = check_args_bf16(M, N, K, out_dtype);
+    if (rc != MX_OK) return rc;
+    if (split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
+    mx_plan_t plan;
+    if (tile_m == 0 && tile_n == 0) {
+        fill_plan(choose_tile(M, N, K), M, N, K, &plan, split_k);
+    } else {
+        const int t = find_tile(tile_m, tile_n);
+        if (t < 0) return MX_ERR_SHAPE;
+        fill_plan(t, M, N, K, &plan, split_k);
+    }
+    if (plan.workgroups > kMaxGrid) return MX_ERR_SHAPE;
+    return run_plan(plan, kFmtBF16, kFmtBF16, M, N, K, A, nullptr, B, nullptr, C, out_dtype,
+                    stream);
+}
 
 extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
                            const void *X, void *Q, void *Q_scale, void *stream)

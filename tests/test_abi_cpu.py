@@ -39,6 +39,8 @@ def test_header_constants_match_binding():
     limits = dict((k, 1 << int(v)) for k, v in
                   re.findall(r"#define (MX_MAX_[A-Z]+) \(\(int64_t\)1 << (\d+)\)", src))
     assert limits == {"MX_MAX_DIM": mxg.MAX_DIM, "MX_MAX_K": mxg.MAX_K}
+    assert int(re.search(r"#define MX_MAX_K_BF16 \(\(int64_t\)1 << (\d+)\)", src).group(1)) \
+        == mxg.MAX_K_BF16.bit_length() - 1
     assert int(re.search(r"#define MX_MAX_SPLIT_K (\d+)", src).group(1)) == mxg.MAX_SPLIT_K
     assert int(re.search(r"#define MX_MAX_GROUPS (\d+)", src).group(1)) == mxg.MAX_GROUPS
 
@@ -342,3 +344,61 @@ def test_e5m2_accepted_where_documented():
     # grouped GEMM and the quantizer take E2M1 / E4M3 only
     assert _grouped(3, [4], 16, 128) == mxg.MX_ERR_FORMAT
     assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
+
+
+def test_bf16_argument_errors():
+    L = mxg.lib()
+    good = 1 << 20
+    p = mxg.MxPlan()
+    # output type; K from one 16-K step up, a multiple of 16, at most MAX_K_BF16
+    assert L.mx_gemm_bf16(16, 16, 64, good, good, good, 0, 0, 0, 0, None) == mxg.MX_ERR_OUT_DTYPE
+    for M, N, K in ((0, 16, 64), (16, 0, 64), (16, 16, 0), (16, 16, 8), (16, 16, 40),
+                    (mxg.MAX_DIM + 1, 16, 64), (16, 16, mxg.MAX_K_BF16 + 16)):
+        assert L.mx_gemm_bf16(M, N, K, good, good, good, 2, 0, 0, 0, None) == mxg.MX_ERR_SHAPE
+        assert L.mx_gemm_bf16_plan(M, N, K, 2, ctypes.byref(p)) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_bf16_plan(16, 16, mxg.MAX_K_BF16, 2, ctypes.byref(p)) == mxg.MX_OK
+    # forced tile and split
+    assert L.mx_gemm_bf16(16, 16, 64, good, good, good, 2, 100, 64, 0, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_bf16(16, 16, 64, good, good, good, 2, 0, 0, -1, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_bf16(16, 16, 64, good, good, good, 2, 0, 0, mxg.MAX_SPLIT_K + 1,
+                          None) == mxg.MX_ERR_SHAPE
+    # pointers: no scales to pass; A, B and C must be non-null and 16-byte aligned
+    assert L.mx_gemm_bf16(16, 16, 64, None, good, good, 2, 0, 0, 0, None) == mxg.MX_ERR_NULL
+    assert L.mx_gemm_bf16(16, 16, 64, good, good, None, 2, 0, 0, 0, None) == mxg.MX_ERR_NULL
+    assert L.mx_gemm_bf16(16, 16, 64, good, good + 8, good, 2, 0, 0, 0, None) == mxg.MX_ERR_ALIGN
+    assert L.mx_gemm_bf16(16, 16, 64, good, good, good + 4, 2, 256, 128, 2,
+                          None) == mxg.MX_ERR_ALIGN
+    assert L.mx_gemm_bf16_plan(16, 16, 64, 2, None) == mxg.MX_ERR_NULL
+
+
+def test_bf16_plan_matches_mx_plan():
+    """The BF16 GEMM runs on the tile kernels with the MX GEMM's tile and
+    split choice (both depend on M, N and K only)."""
+    for M, N, K in ((2048, 6144, 4096), (8, 8192, 28672), (256, 28672, 4096),
+                    (2048, 5120, 25600), (1, 1, 128)):
+        assert mxg.plan_bf16(M, N, K) == mxg.plan(mxg.FMT_E4M3, M, N, K)
+    p = mxg.plan_bf16(5, 7, 48)
+    assert p["split_k"] == 1 and p["workgroups"] >= 1
+
+
+def test_bf16_shim_checks():
+    import torch
+    a = torch.zeros((16, 64), dtype=torch.bfloat16)
+    b = torch.zeros((8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):                    # K mismatch
+        mxg.mx_gemm_bf16(a, torch.zeros((8, 32), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):                    # wrong element type
+        mxg.mx_gemm_bf16(a.float(), b)
+    with pytest.raises(ValueError):                    # not contiguous
+        mxg.mx_gemm_bf16(torch.zeros((64, 16), dtype=torch.bfloat16).t(), b)
+    with pytest.raises(ValueError):                    # shapes fine, but not on the GPU
+        mxg.mx_gemm_bf16(a, b)
+
+
+def test_bf16_no_device_reported():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible here")
+    good = 1 << 20
+    rc = mxg.lib().mx_gemm_bf16(16, 16, 64, good, good, good, 2, 0, 0, 0, None)
+    assert rc == mxg.MX_ERR_NO_DEVICE
