@@ -192,6 +192,34 @@ class Oracle:
             r0 += m
         return tuple(out)
 
+    def gemm_grouped_bf16(self, A, B, group_rows, rows=None, threads=0):
+        """Grouped dense BF16 GEMM, by its definition: A's rows come in
+        consecutive groups of ``group_rows[g]`` rows, B holds G weights of N
+        rows each (weight g = rows g*N .. g*N+N-1), and group g's rows of C
+        are A_g * B_g^T, each an ordinary ``gemm_bf16``.  ``rows`` selects A
+        rows by their index in A.  Returns (C, T) with the rows in A's (or
+        ``rows``') order."""
+        group_rows = [int(r) for r in group_rows]
+        G = len(group_rows)
+        if G < 1 or min(group_rows) < 0 or sum(group_rows) != A.shape[0]:
+            raise ValueError("group_rows must be >= 0 and sum to A's row count")
+        if B.shape[0] % G:
+            raise ValueError("B must hold G weights of equal row count")
+        N = B.shape[0] // G
+        want = np.arange(A.shape[0]) if rows is None else np.asarray(rows, np.int64)
+        C = np.zeros((want.shape[0], N), np.float64)
+        T = np.zeros((want.shape[0], N), np.float64)
+        r0 = 0
+        for g, m in enumerate(group_rows):
+            pos = np.nonzero((want >= r0) & (want < r0 + m))[0]
+            if pos.size:
+                Cg, Tg = self.gemm_bf16(A[r0:r0 + m], B[g * N:(g + 1) * N], rows=want[pos] - r0,
+                                        threads=threads)
+                C[pos] = Cg
+                T[pos] = Tg
+            r0 += m
+        return C, T
+
     def bf16_value(self, bits):
         return self.lib.mxo_bf16_value(int(bits))
 
@@ -280,6 +308,10 @@ def quantize(*args, **kw):
 
 def gemm_bf16(*args, **kw):
     return default().gemm_bf16(*args, **kw)
+
+
+def gemm_grouped_bf16(*args, **kw):
+    return default().gemm_grouped_bf16(*args, **kw)
 
 
 def tables():

@@ -613,9 +613,35 @@ def pin_bf16(orc):
     assert np.array_equal(Ci, ia.astype(np.int64) @ ib.astype(np.int64).T)
 
 
+def pin_grouped_bf16(orc):
+    """Grouped dense BF16 GEMM: each group's rows equal a numpy matmul of
+    the torch-decoded group rows against that group's weight, and the whole
+    result is the block diagonal of one plain BF16 GEMM of A against every
+    weight; empty groups take no rows; a row subset picks the same values."""
+    import torch
+    rows, N, K = [4, 0, 7, 1, 0, 3], 5, 96
+    G = len(rows)
+    A = mxinputs.make_bf16(sum(rows), K, seed=21)
+    B = mxinputs.make_bf16(G * N, K, seed=21, tensor=1)
+    dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).double().numpy()
+    dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).double().numpy()
+    C, T = orc.gemm_grouped_bf16(A, B, rows)
+    Cf, Tf = orc.gemm_bf16(A, B)
+    r0 = 0
+    for g, m in enumerate(rows):
+        sl = slice(r0, r0 + m)
+        wl = slice(g * N, (g + 1) * N)
+        assert np.array_equal(C[sl], Cf[sl, wl]) and np.array_equal(T[sl], Tf[sl, wl])
+        assert np.all(np.abs(C[sl] - dA[sl] @ dB[wl].T) <= 1e-12 * T[sl]), g
+        r0 += m
+    pick = [14, 0, 11, 4, 4]
+    Cs, Ts = orc.gemm_grouped_bf16(A, B, rows, rows=pick)
+    assert np.array_equal(Cs, C[pick]) and np.array_equal(Ts, T[pick])
+
+
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
-            pin_grouped, pin_mixed_formats, pin_e5m2, pin_bf16]
+            pin_grouped, pin_mixed_formats, pin_e5m2, pin_bf16, pin_grouped_bf16]

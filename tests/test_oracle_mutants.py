@@ -129,3 +129,28 @@ def test_pins_catch_grouped_mutant(name, old, new):
     mut.gemm_grouped = ns["gemm_grouped"].__get__(mut)
     with pytest.raises(AssertionError):
         oracle_pins.pin_grouped(mut)
+
+
+# The same kind of mistakes in the grouped BF16 GEMM.
+GROUPED_BF16_MUTANTS = [
+    ("weight_of_next_group", "B[g * N:(g + 1) * N]", "B[(g + 1) % G * N:((g + 1) % G + 1) * N]"),
+    ("empty_group_takes_a_row", "r0 += m", "r0 += max(m, 1)"),
+    ("rows_not_rebased", "rows=want[pos] - r0", "rows=want[pos]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GROUPED_BF16_MUTANTS,
+                         ids=[m[0] for m in GROUPED_BF16_MUTANTS])
+def test_pins_catch_grouped_bf16_mutant(name, old, new):
+    import inspect
+    import textwrap
+
+    import numpy as np
+    src = textwrap.dedent(inspect.getsource(oracle.Oracle.gemm_grouped_bf16))
+    assert old in src
+    ns = {"np": np}
+    exec(src.replace(old, new, 1), ns)
+    mut = oracle.Oracle()
+    mut.gemm_grouped_bf16 = ns["gemm_grouped_bf16"].__get__(mut)
+    with pytest.raises((AssertionError, ValueError)):
+        oracle_pins.pin_grouped_bf16(mut)
