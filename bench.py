@@ -245,45 +245,62 @@ GROUPED_N, GROUPED_K = 4096, 2048
 
 
 def bench_grouped(steps, warmup, fmt):
-    """mx_gemm_grouped over eight uneven experts (4096 tokens in all, N=4096,
-    K=2048, BF16 out): TFLOP/s of the useful products, roofline by the same
-    ridge rule as the plain GEMM."""
+    """mx_gemm_grouped (fmt an MX format) or mx_gemm_grouped_bf16 (fmt
+    "bf16") over eight uneven experts (4096 tokens in all, N=4096, K=2048,
+    BF16 out): TFLOP/s of the useful products, roofline by the same ridge
+    rule as the plain GEMM."""
+    import numpy as np
     import torch
     import microscaled_block_scaled_amd as mxg
     rows, N, K = GROUPED_ROWS, GROUPED_N, GROUPED_K
     G, M, out = len(rows), sum(rows), mxinputs.OUT_BF16
-    case = mxinputs.make_random(fmt, M, G * N, K, seed=2024 + fmt)
+    dense = fmt == "bf16"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-    args = (fmt, rows, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
-            C.data_ptr(), out, stream.cuda_stream)
+    if dense:
+        A = torch.from_numpy(mxinputs.make_bf16(M, K, seed=2030).view(np.int16)).to(dev)
+        B = torch.from_numpy(mxinputs.make_bf16(G * N, K, seed=2030, tensor=1).view(np.int16)).to(dev)
+        args = (rows, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), out, stream.cuda_stream)
+        run = mxg.grouped_bf16_ptr
+        peak = PEAK_BF16_TFLOPS
+    else:
+        case = mxinputs.make_random(fmt, M, G * N, K, seed=2024 + fmt)
+        A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
+        args = (fmt, rows, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
+                C.data_ptr(), out, stream.cuda_stream)
+        run = mxg.grouped_ptr
+        peak = PEAK_TFLOPS[fmt]
     for _ in range(warmup):
-        if mxg.grouped_ptr(*args) != 0:
-            raise RuntimeError("mx_gemm_grouped failed")
+        if run(*args) != 0:
+            raise RuntimeError("grouped GEMM failed")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        mxg.grouped_ptr(*args)
+        run(*args)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_s = e0.elapsed_time(e1) / steps / 1e3
     flops = 2.0 * M * N * K
-    eb = K // 2 if fmt == mxinputs.FMT_E2M1 else K
-    nbytes = (M + G * N) * (eb + K // 32) + M * N * 2
-    p = mxg.grouped_plan(fmt, rows, N, K, out)
+    if dense:
+        nbytes = (M + G * N) * K * 2 + M * N * 2
+        p = mxg.grouped_bf16_plan(rows, N, K, out)
+    else:
+        eb = K // 2 if fmt == mxinputs.FMT_E2M1 else K
+        nbytes = (M + G * N) * (eb + K // 32) + M * N * 2
+        p = mxg.grouped_plan(fmt, rows, N, K, out)
     plan_str = "grouped tile %dx%d, %d workgroups" % (p["tile_m"], p["tile_n"], p["workgroups"])
-    workload = "grouped_%s_experts8_4096x4096x2048" % mxinputs.fmt_name(fmt)
-    bound = "mfma" if flops / nbytes >= RIDGE[fmt] else "hbm"
+    fname = "bf16" if dense else mxinputs.fmt_name(fmt)
+    workload = "grouped_%s_experts8_4096x4096x2048" % fname
+    bound = "mfma" if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     if bound == "mfma":
         achieved = flops / launch_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[fmt],
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[fmt], 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
     else:
         achieved = nbytes / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -292,15 +309,16 @@ def bench_grouped(steps, warmup, fmt):
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)
     tflops = flops * steps / wall / 1e12
-    return {"metric": "MX grouped GEMM TFLOPS and % of MI355X dense MX MFMA peak",
+    return {"metric": "Grouped GEMM TFLOPS and % of MI355X dense MFMA peak of the format",
             "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "mxfp8_e4m3" if fmt == mxinputs.FMT_E4M3 else "mxfp4_e2m1",
+            "dtype": "bf16" if dense else
+                     ("mxfp8_e4m3" if fmt == mxinputs.FMT_E4M3 else "mxfp4_e2m1"),
             "data": "synthetic",
             "config": {"workload": workload, "group_rows": rows, "N": N, "K": K,
-                       "format": mxinputs.fmt_name(fmt), "out": "bf16",
-                       "peak_frac": round(tflops / PEAK_TFLOPS[fmt], 4), "plan": plan_str,
+                       "format": fname, "out": "bf16",
+                       "peak_frac": round(tflops / peak, 4), "plan": plan_str,
                        "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
             "roofline": roof}
 
@@ -546,7 +564,7 @@ def main():
     ap.add_argument("--quantize", action="store_true",
                     help="time mx_quantize (both formats, FP32 and BF16 input) instead")
     ap.add_argument("--grouped", action="store_true",
-                    help="time mx_gemm_grouped (eight uneven experts, both formats) instead")
+                    help="time the grouped GEMM (eight uneven experts; MXFP8, MXFP4, BF16) instead")
     ap.add_argument("--cold", action="store_true",
                     help="per-launch cold-cache and warm timings (median, p10, p90) of "
                          "--workload, or of every workload with --all")
@@ -584,7 +602,7 @@ def main():
             print(json.dumps(bench_bf16(a.steps, a.warmup, name, with_cpu)), flush=True)
         return
     if a.grouped:
-        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):
+        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, "bf16"):
             print(json.dumps(bench_grouped(a.steps, a.warmup, fmt)), flush=True)
         return
     names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \

@@ -283,6 +283,33 @@ int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
 int mx_gemm_grouped_plan(int fmt, int64_t groups, const int64_t *group_rows,
                          int64_t N, int64_t K, int out_dtype, mx_plan_t *plan);
 
+/*
+ * Grouped dense BF16 GEMM (the FlyDSL article's grouped-GEMM cases, section
+ * "Performance numbers need their baselines", with the dense BF16 GEMM's
+ * element type): group g multiplies its group_rows[g] rows of A by its own
+ * N x K weight B_g with no scales,
+ *   C_g = A_g * B_g^T  for g = 0 .. groups-1,
+ * each exactly as mx_gemm_bf16 would (with its plan's tile and no K split).
+ *   groups       1 .. MX_MAX_GROUPS
+ *   group_rows   HOST array of `groups` row counts, each >= 0
+ *   A            (sum of group_rows) x K bfloat16 values, K-contiguous
+ *   B            groups * N rows of K bfloat16 values (weight g is rows
+ *                g*N .. g*N+N-1)
+ *   C            (sum of group_rows) x N, rows in the order of A's rows
+ * K, the output types, alignment (16 bytes for A, B and C), errors and
+ * asynchrony as for mx_gemm_bf16; groups * N must not exceed MX_MAX_DIM.
+ * With no rows at all it returns MX_OK at once.  No workspace is used.
+ */
+int mx_gemm_grouped_bf16(int64_t groups, const int64_t *group_rows, int64_t N, int64_t K,
+                         const void *A, const void *B, void *C, int out_dtype, void *stream);
+
+/*
+ * How mx_gemm_grouped_bf16 would run a problem (as mx_gemm_grouped_plan
+ * does for MX formats).  Host logic only.
+ */
+int mx_gemm_grouped_bf16_plan(int64_t groups, const int64_t *group_rows, int64_t N,
+                              int64_t K, int out_dtype, mx_plan_t *plan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -115,6 +115,12 @@ def lib():
                                ctypes.c_int, ctypes.c_int, vp]
     L.mx_gemm_bf16_plan.restype = ctypes.c_int
     L.mx_gemm_bf16_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(MxPlan)]
+    L.mx_gemm_grouped_bf16.restype = ctypes.c_int
+    L.mx_gemm_grouped_bf16.argtypes = [i64, ctypes.POINTER(i64), i64, i64, vp, vp, vp,
+                                       ctypes.c_int, vp]
+    L.mx_gemm_grouped_bf16_plan.restype = ctypes.c_int
+    L.mx_gemm_grouped_bf16_plan.argtypes = [i64, ctypes.POINTER(i64), i64, i64, ctypes.c_int,
+                                            ctypes.POINTER(MxPlan)]
     L.mx_gemm_grouped.restype = ctypes.c_int
     L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
                                   vp, vp, vp, ctypes.c_int, vp]
@@ -404,6 +410,66 @@ def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out
     with torch.cuda.device(dev):
         rc = grouped_ptr(fmt, rows, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
                          b_scale.data_ptr(), out.data_ptr(), code, stream)
+    if rc != MX_OK:
+        _raise(rc)
+    return out
+
+
+def grouped_bf16_plan(group_rows, N, K, out_dtype=OUT_BF16):
+    """How mx_gemm_grouped_bf16 would run these groups (a dict); host logic
+    only."""
+    rows = [int(r) for r in group_rows]
+    arr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    p = MxPlan()
+    rc = lib().mx_gemm_grouped_bf16_plan(len(rows), arr, int(N), int(K), int(out_dtype),
+                                         ctypes.byref(p))
+    if rc != MX_OK:
+        _raise(rc)
+    return p.as_dict()
+
+
+def grouped_bf16_ptr(group_rows, N, K, A, B, C, out_dtype, stream=0):
+    """Raw entry point of mx_gemm_grouped_bf16; returns the status code."""
+    rows = list(group_rows)
+    arr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    return lib().mx_gemm_grouped_bf16(len(rows), arr, int(N), int(K), A, B, C, int(out_dtype),
+                                      stream or None)
+
+
+def mx_gemm_grouped_bf16(a, b, group_rows, out_dtype=None, out=None, stream=None):
+    """C_g = A_g * B_g^T for consecutive row groups of BF16 a (group_rows[g]
+    rows each) and the G = len(group_rows) BF16 weights stacked in b,
+    (G*N, K).  Returns (sum(group_rows), N)."""
+    import torch
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    code, tdt = _out_code(out_dtype)
+    rows = [int(r) for r in group_rows]
+    G = len(rows)
+    if not 1 <= G <= MAX_GROUPS or min(rows) < 0:
+        raise ValueError("group_rows: 1 .. %d non-negative row counts" % MAX_GROUPS)
+    a, b = _as_bf16(a, "a"), _as_bf16(b, "b")
+    M, K = a.shape
+    if sum(rows) != M:
+        raise ValueError("group_rows sum to %d, a has %d rows" % (sum(rows), M))
+    if b.shape[0] % G != 0:
+        raise ValueError("b's rows are not a multiple of the group count")
+    N = b.shape[0] // G
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    if b.device != a.device:
+        raise ValueError("all operands must be on the same device")
+    dev = a.device
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=dev)
+    elif out.dtype != tdt or tuple(out.shape) != (M, N) or not out.is_contiguous() \
+            or out.device != dev:
+        raise ValueError("out must be a contiguous (M, N) %s tensor on %s" % (tdt, dev))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = grouped_bf16_ptr(rows, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), code,
+                              stream)
     if rc != MX_OK:
         _raise(rc)
     return out

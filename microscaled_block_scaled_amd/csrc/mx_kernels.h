@@ -282,9 +282,11 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         tiles_m = (M + BM - 1) / BM;
         bid -= groups.tile_start[lo];
         A += (int64_t)r0 * rba;
-        As += (int64_t)r0 * (K / 32);
         B += (int64_t)lo * N * rbb;
-        Bs += (int64_t)lo * N * (K / 32);
+        if constexpr (SL::scaled) {
+            As += (int64_t)r0 * (K / 32);
+            Bs += (int64_t)lo * N * (K / 32);
+        }
         C = (uint8_t *)C + (int64_t)r0 * N * (OUT == OF32 ? 4 : 2);
     }
     const int ntiles = tiles_m * tiles_n;

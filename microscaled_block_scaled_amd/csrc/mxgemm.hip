@@ -507,12 +507,14 @@ bool launch_grouped(int t, const void *A, const void *As, const void *B, const v
 
 // Checks a grouped problem and plans it: the tile (plan->tile_m/tile_n),
 // the grid and, when gt is given, the group table.  Host logic only.
+// fmt is MX_FMT_E2M1, MX_FMT_E4M3 or kFmtBF16 (dense BF16, no scales).
 int grouped_plan(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, int64_t K,
                  int out_dtype, mx_plan_t *plan, int *tile, mx::GroupTable *gt)
 {
-    int rc = check_args(fmt, 1, N, K, out_dtype);            // format, output, N, K
+    int rc = fmt == kFmtBF16 ? check_args_bf16(1, N, K, out_dtype)
+                             : check_args(fmt, 1, N, K, out_dtype);   // format, output, N, K
     if (rc != MX_OK) return rc;
-    if (fmt == MX_FMT_E5M2) return MX_ERR_FORMAT;            // grouped: E2M1 and E4M3 only
+    if (fmt == MX_FMT_E5M2) return MX_ERR_FORMAT;            // grouped: E2M1, E4M3 and BF16
     if (groups < 1 || groups > MX_MAX_GROUPS || groups * N > MX_MAX_DIM) return MX_ERR_SHAPE;
     if (!group_rows || !plan) return MX_ERR_NULL;
     int64_t total = 0, maxm = 0;
@@ -552,14 +554,18 @@ int grouped_plan(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, 
 extern "C" int mx_gemm_grouped_plan(int fmt, int64_t groups, const int64_t *group_rows,
                                     int64_t N, int64_t K, int out_dtype, mx_plan_t *plan)
 {
+    if (fmt == kFmtBF16) return MX_ERR_FORMAT;
     int t = 0;
     return grouped_plan(fmt, groups, group_rows, N, K, out_dtype, plan, &t, nullptr);
 }
 
-extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
-                               int64_t N, int64_t K, const void *A, const void *A_scale,
-                               const void *B, const void *B_scale, void *C, int out_dtype,
-                               void *stream)
+namespace {
+
+// Grouped GEMM in format fmt (MX_FMT_E2M1, MX_FMT_E4M3, or kFmtBF16 with no
+// scale arrays).
+int run_grouped(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, int64_t K,
+                const void *A, const void *A_scale, const void *B, const void *B_scale, void *C,
+                int out_dtype, void *stream)
 {
     mx_plan_t plan;
     mx::GroupTable gt;
@@ -567,9 +573,10 @@ extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_row
     int rc = grouped_plan(fmt, groups, group_rows, N, K, out_dtype, &plan, &t, &gt);
     if (rc != MX_OK) return rc;
     if (plan.workgroups == 0) return MX_OK;                 // no rows: nothing to compute
-    if (!A || !A_scale || !B || !B_scale || !C) return MX_ERR_NULL;
+    const bool scaled = fmt != kFmtBF16;
+    if (!A || !B || !C || (scaled && (!A_scale || !B_scale))) return MX_ERR_NULL;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
-        !aligned(A_scale, 4) || !aligned(B_scale, 4))
+        (scaled && (!aligned(A_scale, 4) || !aligned(B_scale, 4))))
         return MX_ERR_ALIGN;
     int dev = -1;
     rc = device_ready(&dev);
@@ -577,7 +584,11 @@ extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_row
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     bool launched;
-    if (fmt == MX_FMT_E2M1)
+    if (fmt == kFmtBF16)
+        launched = (out_dtype == MX_OUT_FP32)
+            ? launch_grouped<mx::B16, mx::OF32>(t, A, nullptr, B, nullptr, C, N, K, gt, s)
+            : launch_grouped<mx::B16, mx::OBF16>(t, A, nullptr, B, nullptr, C, N, K, gt, s);
+    else if (fmt == MX_FMT_E2M1)
         launched = (out_dtype == MX_OUT_FP32)
             ? launch_grouped<mx::FP4, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)
             : launch_grouped<mx::FP4, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s);
@@ -586,4 +597,31 @@ extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_row
             ? launch_grouped<mx::FP8, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)
             : launch_grouped<mx::FP8, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s);
     return (launched && hipGetLastError() == hipSuccess) ? MX_OK : MX_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
+                               int64_t N, int64_t K, const void *A, const void *A_scale,
+                               const void *B, const void *B_scale, void *C, int out_dtype,
+                               void *stream)
+{
+    if (fmt == kFmtBF16) return MX_ERR_FORMAT;
+    return run_grouped(fmt, groups, group_rows, N, K, A, A_scale, B, B_scale, C, out_dtype,
+                       stream);
+}
+
+extern "C" int mx_gemm_grouped_bf16(int64_t groups, const int64_t *group_rows, int64_t N,
+                                    int64_t K, const void *A, const void *B, void *C,
+                                    int out_dtype, void *stream)
+{
+    return run_grouped(kFmtBF16, groups, group_rows, N, K, A, nullptr, B, nullptr, C,
+                       out_dtype, stream);
+}
+
+extern "C" int mx_gemm_grouped_bf16_plan(int64_t groups, const int64_t *group_rows, int64_t N,
+                                         int64_t K, int out_dtype, mx_plan_t *plan)
+{
+    int t = 0;
+    return grouped_plan(kFmtBF16, groups, group_rows, N, K, out_dtype, plan, &t, nullptr);
 }

@@ -402,3 +402,33 @@ def test_bf16_no_device_reported():
     good = 1 << 20
     rc = mxg.lib().mx_gemm_bf16(16, 16, 64, good, good, good, 2, 0, 0, 0, None)
     assert rc == mxg.MX_ERR_NO_DEVICE
+
+
+def _grouped_bf16(rows, N, K, ptrs=(1 << 20,) * 3, out=2):
+    arr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    return mxg.lib().mx_gemm_grouped_bf16(len(rows), arr, N, K, *ptrs, out, None)
+
+
+def test_grouped_bf16_argument_errors():
+    good = 1 << 20
+    assert _grouped_bf16([4], 16, 64, out=7) == mxg.MX_ERR_OUT_DTYPE
+    for rows, N, K in (([4], 16, 40), ([4], 16, 0), ([4], 0, 64), ([-1], 16, 64),
+                       ([1] * (mxg.MAX_GROUPS + 1), 16, 64), ([4], 16, mxg.MAX_K_BF16 + 16)):
+        assert _grouped_bf16(rows, N, K) == mxg.MX_ERR_SHAPE, (rows, N, K)
+    assert _grouped_bf16([4], 16, 64, ptrs=(None, good, good)) == mxg.MX_ERR_NULL
+    assert _grouped_bf16([4], 16, 64, ptrs=(good, good + 8, good)) == mxg.MX_ERR_ALIGN
+    assert _grouped_bf16([0, 0], 16, 64, ptrs=(None, None, None)) == mxg.MX_OK   # no rows
+    # the MX entry points do not take the BF16 marker as a format
+    arr = (ctypes.c_int64 * 1)(4)
+    p = mxg.MxPlan()
+    assert mxg.lib().mx_gemm_grouped_plan(0x100, 1, arr, 16, 128, 2, ctypes.byref(p)) \
+        == mxg.MX_ERR_FORMAT
+    assert _grouped(0x100, [4], 16, 128) == mxg.MX_ERR_FORMAT
+
+
+def test_grouped_bf16_plan_matches_mx_plan():
+    """The grouped BF16 GEMM picks its tile like the MX grouped GEMM."""
+    for rows, N, K in (([704, 320, 512, 896, 128, 640, 448, 448], 4096, 2048),
+                       ([8, 1, 0, 33], 4096, 2048), ([0, 0], 64, 128)):
+        assert mxg.grouped_bf16_plan(rows, N, K) == mxg.grouped_plan(mxg.FMT_E4M3, rows, N, K)
+    assert mxg.grouped_bf16_plan([5, 3], 64, 48)["workgroups"] >= 2
