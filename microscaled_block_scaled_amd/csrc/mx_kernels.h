@@ -142,15 +142,26 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Tile order: workgroups are dispatched round-robin over the 8 XCDs (bid % 8).
-// Give each XCD a contiguous run of tiles, walked in groups of `gm` M-tiles,
-// so the workgroups sharing an XCD's L2 also share A and B panels.
+// Workgroups are dispatched round-robin over the 8 XCDs: workgroup b runs on
+// XCD b % 8.  xcd_run(b, T) numbers T workgroups so that each XCD gets a
+// contiguous run of indices: XCD x holds T/8 of them, one more if x < T % 8,
+// starting after the runs of XCDs 0 .. x-1.
+__device__ __forceinline__ int xcd_run(int b, int T)
+{
+    const int q = T >> 3, r = T & 7, x = b & 7;
+    return x * q + min(x, r) + (b >> 3);
+}
+
+// Tile order: give each XCD a contiguous run of tiles (when the tile count is
+// a multiple of 8; `remap` false when the caller has already ordered the
+// grid), walked in groups of `gm` M-tiles, so the workgroups sharing an
+// XCD's L2 also share A and B panels.
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int gm,
-                                        int &tm, int &tn)
+                                        int &tm, int &tn, bool remap = true)
 {
     const int ntiles = tiles_m * tiles_n;
     int t = bid;
-    if ((ntiles & 7) == 0) t = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    if (remap && (ntiles & 7) == 0) t = xcd_run(bid, ntiles);
     const int per_group = gm * tiles_n;
     const int grp = t / per_group, first_m = grp * gm;
     const int gsz = min(tiles_m - first_m, gm);
@@ -267,6 +278,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // Without split-K, kchunk == K and there is one slice.
     int bid = blockIdx.x;
     if constexpr (GT::grouped) {
+        // The whole grid (every group's tiles) is ordered per XCD first, so
+        // consecutive tiles of a group, which share its weight panels, run
+        // on one XCD whatever the group sizes.
+        bid = xcd_run(bid, groups.tile_start[groups.n]);
         // This workgroup's group: the last g with tile_start[g] <= bid (an
         // empty group shares its start with the next one, so g is never
         // empty).  Then rebase every operand on the group and make the rest
@@ -292,7 +307,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int ntiles = tiles_m * tiles_n;
     const int slice = bid / ntiles;
     int tm, tn;
-    tile_of(bid - slice * ntiles, tiles_m, tiles_n, gm, tm, tn);
+    tile_of(bid - slice * ntiles, tiles_m, tiles_n, gm, tm, tn, !GT::grouped);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kb = slice * kchunk, klen = min(kchunk, K - kb);
     // Row stride, slice bytes per row and slice offset of each operand.
