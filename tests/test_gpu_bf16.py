@@ -149,3 +149,15 @@ def test_bf16_full_size():
     C = _run(A, B, BF16, dA=dA, dB=dB)
     assert torch.equal(C, _run(A, B, BF16, dA=dA, dB=dB))
     _check(A, B, BF16, C, rows=sample_rows(M, n=24), what="full size")
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 8192, 28672), (8, 8192, 28672)],
+                         ids=["llama70b_down_m2048", "llama70b_down_m8"])
+def test_bf16_bench_workloads(M, N, K):
+    """The 70B down-projection shapes bench.py times, in the plan's
+    configuration (256x256 tiles; 128x128 with a 4-way K split at M = 8),
+    checked on sampled rows."""
+    log("bf16 bench workload M=%d N=%d K=%d plan=%s" % (M, N, K, mxg.plan_bf16(M, N, K)))
+    A, B = _case(M, N, K, seed=40 + M)
+    C = _run(A, B, BF16)
+    _check(A, B, BF16, C, rows=sample_rows(M, n=12), what="bench workload")
