@@ -82,9 +82,8 @@ def _u8(a):
 
 def _check_shapes(fmt, A, As, B, Bs, K, fmt_b=None):
     fmt_b = fmt if fmt_b is None else fmt_b
-    if fmt not in _FORMATS or fmt_b not in _FORMATS or \
-            (fmt == FMT_E5M2) != (fmt_b == FMT_E5M2):
-        raise ValueError("formats must be E2M1 / E4M3 (any pair) or E5M2 with E5M2")
+    if fmt not in _FORMATS or fmt_b not in _FORMATS:
+        raise ValueError("formats must be E2M1, E4M3 or E5M2 (any pair)")
     rba = K // 2 if fmt == FMT_E2M1 else K
     rbb = K // 2 if fmt_b == FMT_E2M1 else K
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != rba or B.shape[1] != rbb:

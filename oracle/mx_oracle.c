@@ -128,8 +128,9 @@ static void make_tables(double t4[16], double t8[256], double pow2[509])
 
 static int64_t row_bytes(int fmt, int64_t K) { return fmt == MXO_FMT_E2M1 ? K / 2 : K; }
 
-/* Exact block sums for E5M2 operands: every finite E5M2 value is an integer
- * multiple of 2^-16 below 2^32 in those units, so each product is an exact
+/* Exact block sums with an E5M2 operand: every finite E5M2, E4M3 or E2M1
+ * value is an integer multiple of 2^-16 below 2^32 in those units, so each
+ * product is an exact
  * 64-bit-magnitude integer in units of 2^-32 and 32 of them sum exactly in
  * 128 bits.  Writes sum p and magnitude sum q rounded once to double;
  * returns 0 if a value is not finite (the caller keeps its IEEE sums). */
@@ -212,9 +213,11 @@ int mxo_gemm_ab(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
 {
     if (fmt_a != MXO_FMT_E2M1 && fmt_a != MXO_FMT_E4M3 && fmt_a != MXO_FMT_E5M2) return -1;
     if (fmt_b != MXO_FMT_E2M1 && fmt_b != MXO_FMT_E4M3 && fmt_b != MXO_FMT_E5M2) return -1;
-    /* E5M2 pairs only with itself (its block sums are not exact in double). */
-    if ((fmt_a == MXO_FMT_E5M2) != (fmt_b == MXO_FMT_E5M2)) return -1;
-    const int exact128 = fmt_a == MXO_FMT_E5M2;
+    /* With an E5M2 operand a block sum can need more than 53 bits (E5M2 x
+     * E4M3 products span 50 binades, E5M2 x E5M2 64), so it is taken in
+     * 128-bit integers; every value of the three formats is a whole multiple
+     * of 2^-16. */
+    const int exact128 = fmt_a == MXO_FMT_E5M2 || fmt_b == MXO_FMT_E5M2;
     if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || nrows < 0) return -1;
     for (int64_t i = 0; rows && i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= M) return -1;

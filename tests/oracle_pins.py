@@ -581,6 +581,33 @@ def pin_e5m2(orc):
     assert T[0, 0] == 2 * 57344.0 ** 2 + 2.0 ** -32 or T[0, 0] == 2 * 57344.0 ** 2
 
 
+def pin_e5m2_pairs(orc):
+    """E5M2 paired with E4M3 or E2M1, in both directions: a numpy matmul of
+    the dequantized operands (torch's tables); the transpose symmetry
+    between the two directions; and a block whose exact sum is 2^-25, the
+    smallest E4M3 x E5M2 product, left over after fifteen products of
+    448 * 57344 cancel, which a double-precision running sum rounds away."""
+    for fa, fb in ((E4M3, E5M2), (E5M2, E2M1)):
+        ca = mxinputs.make_random(fa, 20, 3, 256, seed=51)
+        cb = mxinputs.make_random(fb, 3, 14, 256, seed=52)
+        A, As, B, Bs = ca["A"], ca["A_scale"], cb["B"], cb["B_scale"]
+        C, T = orc.gemm(fa, A, As, B, Bs, 256, fmt_b=fb)
+        ref = dequant(fa, A, As) @ dequant(fb, B, Bs).T
+        assert np.all(np.abs(C - ref) <= 1e-12 * T), (fa, fb)
+        Ct, Tt = orc.gemm(fb, B, Bs, A, As, 256, fmt_b=fa)
+        assert np.array_equal(C, Ct.T) and np.array_equal(T, Tt.T), (fa, fb)
+    A = np.zeros((1, 32), np.uint8)            # E4M3
+    B = np.zeros((1, 32), np.uint8)            # E5M2
+    A[0, :15] = 0x7E                           # 448
+    A[0, 15] = 0x01                            # 2^-9
+    A[0, 16:31] = 0xFE                         # -448
+    B[0, :31] = 0x7B                           # 57344
+    B[0, 15] = 0x01                            # 2^-16
+    s = np.full((1, 1), 127, np.uint8)
+    C, T = orc.gemm(E4M3, A, s, B, s, 32, fmt_b=E5M2)
+    assert C[0, 0] == 2.0 ** -25, C[0, 0]
+
+
 def pin_bf16(orc):
     """BF16 dense GEMM: the decode against torch's bfloat16 (every pattern);
     a numpy matmul of torch-decoded values; exact rationals on a tiny case;
@@ -644,4 +671,5 @@ ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
-            pin_grouped, pin_mixed_formats, pin_e5m2, pin_bf16, pin_grouped_bf16]
+            pin_grouped, pin_mixed_formats, pin_e5m2, pin_e5m2_pairs, pin_bf16,
+            pin_grouped_bf16]

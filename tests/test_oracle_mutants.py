@@ -55,6 +55,8 @@ MUTANTS = [
     ("e5m2_subnormal", "ldexp((double)m / 4.0, -14)", "ldexp((double)m / 4.0, -15)"),
     ("e5m2_inf_as_nan", "mag = (m == 0) ? INFINITY : NAN;", "mag = NAN;"),
     ("e5m2_double_sums", "if (exact128) block_exact(", "if (0) block_exact("),
+    ("e5m2_pair_double_sums", "const int exact128 = fmt_a == MXO_FMT_E5M2 || fmt_b == MXO_FMT_E5M2;",
+     "const int exact128 = fmt_a == MXO_FMT_E5M2 && fmt_b == MXO_FMT_E5M2;"),
     # BF16 GEMM.
     ("bf16_decode_shift", "v.u = (uint32_t)(bits & 0xffffu) << 16;", "v.u = (uint32_t)(bits & 0xffffu) << 15;"),
     ("bf16_b_row", "const double *b = bdec + n * K;", "const double *b = bdec + (n / 2) * K;"),
