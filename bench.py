@@ -324,12 +324,13 @@ def bench_grouped(steps, warmup, fmt):
 
 
 # Other element formats, BF16 out: mixed "W4A8" (A E4M3 activations, B E2M1
-# weights) on the fused-QKV shape and the 70B down projection at batch 8, and
-# E5M2 for both operands on the fused-QKV shape.
+# weights) on the fused-QKV shape and the 70B down projection at batch 8,
+# E5M2 for both operands, and E4M3 x E5M2, on the fused-QKV shape.
 MIXED_WORKLOADS = {
     "w4a8_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
     "w4a8_llama70b_down_m8": (8, 8192, 28672, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
     "mxfp8_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E5M2, mxinputs.FMT_E5M2),
+    "mxfp8_e4m3_x_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2),
 }
 
 

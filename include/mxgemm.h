@@ -53,8 +53,8 @@ extern "C" {
 
 /* Element formats: MXFP4 = E2M1; MXFP8 = E4M3, or its other OCP encoding
  * E5M2 (wider range: 2^-16 .. 57344, with infinities and NaNs).  E5M2 is
- * accepted by mx_gemm, mx_gemm_tile and mx_gemm_mixed (E5M2 with E5M2 only);
- * mx_gemm_grouped and mx_quantize take E2M1 and E4M3. */
+ * accepted by mx_gemm, mx_gemm_tile and mx_gemm_mixed (paired with any of
+ * the three); mx_gemm_grouped and mx_quantize take E2M1 and E4M3. */
 enum { MX_FMT_E2M1 = 1, MX_FMT_E4M3 = 2, MX_FMT_E5M2 = 3 };
 
 /* Output element types. */
@@ -192,9 +192,9 @@ int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
 
 /*
  * MX GEMM with A and B in different element formats: fmt_a for A, fmt_b for
- * B, each MX_FMT_E2M1 or MX_FMT_E4M3, or both MX_FMT_E5M2 (another pair
- * with E5M2 gives MX_ERR_FORMAT) (A E4M3 with B E2M1 is the usual
- * "W4A8" serving layout).  The block dot product is the one of mx_gemm with
+ * B, each MX_FMT_E2M1, MX_FMT_E4M3 or MX_FMT_E5M2, in any pair (A E4M3 with
+ * B E2M1 is the usual "W4A8" serving layout; E4M3 with E5M2 pairs the two
+ * MXFP8 encodings).  The block dot product is the one of mx_gemm with
  * each operand decoded in its own format (the OCP MX v1.0 dot product does
  * not require equal formats; the pages' "broader low precision" outlook, and
  * gfx950's scaled MFMA takes a format per operand).  A is M x K in fmt_a's

@@ -285,12 +285,20 @@ int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, 
         launched = launch<mx::FP4, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
         launched = launch<mx::FP8, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
-    else if (fmt_a == MX_FMT_E5M2)                       // checked: then fmt_b is E5M2 too
+    else if (fmt_a == MX_FMT_E5M2 && fmt_b == MX_FMT_E5M2)
         launched = launch<mx::BF8, mx::BF8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
-    else if (fmt_a == MX_FMT_E4M3)
+    else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E2M1)
         launched = launch<mx::FP8, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
-    else
+    else if (fmt_a == MX_FMT_E2M1 && fmt_b == MX_FMT_E4M3)
         launched = launch<mx::FP4, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E5M2)
+        launched = launch<mx::FP8, mx::BF8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E5M2 && fmt_b == MX_FMT_E4M3)
+        launched = launch<mx::BF8, mx::FP8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E5M2)                       // checked: fmt_b is E2M1
+        launched = launch<mx::BF8, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else                                                 // E2M1 x E5M2
+        launched = launch<mx::FP4, mx::BF8>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     const bool launch_ok = launched && hipGetLastError() == hipSuccess;
     return launch_ok ? MX_OK : MX_ERR_LAUNCH;
 }
@@ -369,7 +377,6 @@ extern "C" int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t
     int rc = check_args(fmt_a, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
     if (fmt_b != MX_FMT_E2M1 && fmt_b != MX_FMT_E4M3 && fmt_b != MX_FMT_E5M2) return MX_ERR_FORMAT;
-    if ((fmt_a == MX_FMT_E5M2) != (fmt_b == MX_FMT_E5M2)) return MX_ERR_FORMAT;   // E5M2 only with E5M2
     if (split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
     mx_plan_t plan;
     if (tile_m == 0 && tile_n == 0) {

@@ -65,5 +65,5 @@ def sample_rows(M, tile=256, n=64):
     rows = set(range(8)) | set(range(M - 8, M))
     last_tile = (M - 1) // tile * tile
     rows |= set(range(last_tile, min(M, last_tile + 8)))
-    rows |= set(int(x) for x in np.linspace(0, M - 1, n - len(rows)))
+    rows |= set(int(x) for x in np.linspace(0, M - 1, max(0, n - len(rows))))
     return sorted(rows)

@@ -304,7 +304,7 @@ def test_mixed_argument_errors():
     args = (good,) * 5
     # format of A, then of B; output type; shapes; tile and split
     assert L.mx_gemm_mixed(0, 1, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-    assert L.mx_gemm_mixed(2, 3, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    assert L.mx_gemm_mixed(2, 0, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
     assert L.mx_gemm_mixed(2, 1, 16, 16, 128, *args, 9, 0, 0, 0, None) == mxg.MX_ERR_OUT_DTYPE
     assert L.mx_gemm_mixed(2, 1, 16, 16, 96, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_SHAPE
     assert L.mx_gemm_mixed(2, 1, 16, 16, 128, *args, 2, 100, 64, 0, None) == mxg.MX_ERR_SHAPE
@@ -338,9 +338,11 @@ def test_e5m2_accepted_where_documented():
     args = (good,) * 5
     p = mxg.MxPlan()
     assert L.mx_gemm_plan(mxg.FMT_E5M2, 64, 64, 256, 2, ctypes.byref(p)) == mxg.MX_OK
-    # E5M2 pairs only with itself
-    assert L.mx_gemm_mixed(3, 2, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-    assert L.mx_gemm_mixed(1, 3, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    # E5M2 pairs with any format (only argument checks run here: no device)
+    for fa, fb in ((3, 2), (2, 3), (3, 1), (1, 3)):
+        assert L.mx_gemm_mixed(fa, fb, 16, 16, 128, *args, 2, 0, 0, 0, None) \
+            == mxg.MX_ERR_NO_DEVICE, (fa, fb)
+    assert L.mx_gemm_mixed(3, 4, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
     # grouped GEMM and the quantizer take E2M1 / E4M3 only
     assert _grouped(3, [4], 16, 128) == mxg.MX_ERR_FORMAT
     assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT

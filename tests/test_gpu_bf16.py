@@ -160,4 +160,4 @@ def test_bf16_bench_workloads(M, N, K):
     log("bf16 bench workload M=%d N=%d K=%d plan=%s" % (M, N, K, mxg.plan_bf16(M, N, K)))
     A, B = _case(M, N, K, seed=40 + M)
     C = _run(A, B, BF16)
-    _check(A, B, BF16, C, rows=sample_rows(M, n=12), what="bench workload")
+    _check(A, B, BF16, C, rows=sample_rows(M, n=32), what="bench workload")
