@@ -162,13 +162,14 @@ class Oracle:
         return (C, T, E) if group_bound else (C, T)
 
     def gemm_grouped(self, fmt, A, A_scale, B, B_scale, K, group_rows, rows=None,
-                     threads=0, group_bound=False):
+                     threads=0, group_bound=False, fmt_b=None):
         """Grouped GEMM of a mixture-of-experts layer, by its definition: A's
         rows come in consecutive groups of ``group_rows[g]`` rows, B holds G
         weights of N rows each (weight g = rows g*N .. g*N+N-1), and group g's
-        rows of C are A_g * B_g^T, each an ordinary ``gemm``.  ``rows``
-        selects A rows by their index in A.  Returns (C, T) or (C, T, E), with
-        the rows in A's (or ``rows``') order."""
+        rows of C are A_g * B_g^T, each an ordinary ``gemm`` (with B in
+        ``fmt_b`` when given).  ``rows`` selects A rows by their index in A.
+        Returns (C, T) or (C, T, E), with the rows in A's (or ``rows``')
+        order."""
         group_rows = [int(r) for r in group_rows]
         G = len(group_rows)
         if G < 1 or min(group_rows) < 0 or sum(group_rows) != A.shape[0]:
@@ -185,7 +186,7 @@ class Oracle:
             if pos.size:
                 res = self.gemm(fmt, A[r0:r0 + m], A_scale[r0:r0 + m], B[g * N:(g + 1) * N],
                                 B_scale[g * N:(g + 1) * N], K, rows=want[pos] - r0,
-                                threads=threads, group_bound=group_bound)
+                                threads=threads, group_bound=group_bound, fmt_b=fmt_b)
                 for o, r in zip(out, res):
                     o[pos] = r
             r0 += m

@@ -508,6 +508,22 @@ def pin_grouped(orc):
         assert np.array_equal(Cs, C[pick]) and np.array_equal(Ts, T[pick])
         _, _, Ef = orc.gemm(fmt, A, As, B, Bs, K, group_bound=True)
         assert np.array_equal(Es[1], Ef[0, :N]) and np.array_equal(Es[0], Ef[20, 5 * N:])
+    # E4M3 activations with E2M1 weights, and the reverse
+    for fa, fb in ((E4M3, E2M1), (E2M1, E4M3)):
+        rows, N, K = [3, 0, 6, 1], 5, 256
+        G = len(rows)
+        ca = mxinputs.make_random(fa, sum(rows), 1, K, seed=13)
+        cb = mxinputs.make_random(fb, 1, G * N, K, seed=14)
+        A, As, B, Bs = ca["A"], ca["A_scale"], cb["B"], cb["B_scale"]
+        C, T = orc.gemm_grouped(fa, A, As, B, Bs, K, rows, fmt_b=fb)
+        Cf, Tf = orc.gemm(fa, A, As, B, Bs, K, fmt_b=fb)
+        dA, dB = dequant(fa, A, As), dequant(fb, B, Bs)
+        r0 = 0
+        for g, m in enumerate(rows):
+            sl, wl = slice(r0, r0 + m), slice(g * N, (g + 1) * N)
+            assert np.array_equal(C[sl], Cf[sl, wl]) and np.array_equal(T[sl], Tf[sl, wl])
+            assert np.all(np.abs(C[sl] - dA[sl] @ dB[wl].T) <= 1e-12 * T[sl]), (fa, fb, g)
+            r0 += m
 
 
 def pin_mixed_formats(orc):

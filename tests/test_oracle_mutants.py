@@ -114,6 +114,7 @@ GROUPED_MUTANTS = [
     ("empty_group_takes_a_row", "r0 += m", "r0 += max(m, 1)"),
     ("a_scale_not_rebased", "A_scale[r0:r0 + m]", "A_scale[0:m]"),
     ("b_scale_not_rebased", "B_scale[g * N:(g + 1) * N]", "B_scale[0:N]"),
+    ("b_format_dropped", "group_bound=group_bound, fmt_b=fmt_b)", "group_bound=group_bound)"),
 ]
 
 
@@ -129,7 +130,7 @@ def test_pins_catch_grouped_mutant(name, old, new):
     exec(src.replace(old, new, 1), ns)
     mut = oracle.Oracle()
     mut.gemm_grouped = ns["gemm_grouped"].__get__(mut)
-    with pytest.raises(AssertionError):
+    with pytest.raises((AssertionError, ValueError)):    # a wrong value, or a rejected call
         oracle_pins.pin_grouped(mut)
 
 
