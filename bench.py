@@ -255,6 +255,8 @@ def bench_grouped(steps, warmup, fmt):
     rows, N, K = GROUPED_ROWS, GROUPED_N, GROUPED_K
     G, M, out = len(rows), sum(rows), mxinputs.OUT_BF16
     dense = fmt == "bf16"
+    # (fa, fb): E4M3 activations with E2M1 expert weights
+    fa, fb = fmt if isinstance(fmt, tuple) else (fmt, fmt)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -266,12 +268,15 @@ def bench_grouped(steps, warmup, fmt):
         run = mxg.grouped_bf16_ptr
         peak = PEAK_BF16_TFLOPS
     else:
-        case = mxinputs.make_random(fmt, M, G * N, K, seed=2024 + fmt)
-        A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
-        args = (fmt, rows, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
-                C.data_ptr(), out, stream.cuda_stream)
+        ca = mxinputs.make_random(fa, M, 1, K, seed=2024 + fa)
+        cb = mxinputs.make_random(fb, 1, G * N, K, seed=2024 + fb)
+        A, As = torch.from_numpy(ca["A"]).to(dev), torch.from_numpy(ca["A_scale"]).to(dev)
+        B, Bs = torch.from_numpy(cb["B"]).to(dev), torch.from_numpy(cb["B_scale"]).to(dev)
+        args = (fa, rows, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
+                C.data_ptr(), out, stream.cuda_stream, fb)
         run = mxg.grouped_ptr
-        peak = PEAK_TFLOPS[fmt]
+        # an 8-bit operand runs the MFMA at the 8-bit rate
+        peak = PEAK_TFLOPS[mxinputs.FMT_E4M3 if mxinputs.FMT_E4M3 in (fa, fb) else fa]
     for _ in range(warmup):
         if run(*args) != 0:
             raise RuntimeError("grouped GEMM failed")
@@ -290,11 +295,11 @@ def bench_grouped(steps, warmup, fmt):
         nbytes = (M + G * N) * K * 2 + M * N * 2
         p = mxg.grouped_bf16_plan(rows, N, K, out)
     else:
-        eb = K // 2 if fmt == mxinputs.FMT_E2M1 else K
-        nbytes = (M + G * N) * (eb + K // 32) + M * N * 2
-        p = mxg.grouped_plan(fmt, rows, N, K, out)
+        nbytes = (M * mxinputs.row_bytes(fa, K) + G * N * mxinputs.row_bytes(fb, K)
+                  + (M + G * N) * (K // 32) + M * N * 2)
+        p = mxg.grouped_plan(fa, rows, N, K, out)
     plan_str = "grouped tile %dx%d, %d workgroups" % (p["tile_m"], p["tile_n"], p["workgroups"])
-    fname = "bf16" if dense else mxinputs.fmt_name(fmt)
+    fname = "bf16" if dense else (mxinputs.fmt_name(fa) if fa == fb else "w4a8")
     workload = "grouped_%s_experts8_4096x4096x2048" % fname
     bound = "mfma" if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     if bound == "mfma":
@@ -314,7 +319,8 @@ def bench_grouped(steps, warmup, fmt):
             "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16" if dense else
-                     ("mxfp8_e4m3" if fmt == mxinputs.FMT_E4M3 else "mxfp4_e2m1"),
+                     ("mxfp8_e4m3 x mxfp4_e2m1" if fa != fb else
+                      "mxfp8_e4m3" if fa == mxinputs.FMT_E4M3 else "mxfp4_e2m1"),
             "data": "synthetic",
             "config": {"workload": workload, "group_rows": rows, "N": N, "K": K,
                        "format": fname, "out": "bf16",
@@ -603,7 +609,8 @@ def main():
             print(json.dumps(bench_bf16(a.steps, a.warmup, name, with_cpu)), flush=True)
         return
     if a.grouped:
-        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, "bf16"):
+        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
+                    "bf16"):
             print(json.dumps(bench_grouped(a.steps, a.warmup, fmt)), flush=True)
         return
     names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \

@@ -274,6 +274,20 @@ int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
                     void *stream);
 
 /*
+ * mx_gemm_grouped with the weights in their own format: A (and A_scale) in
+ * fmt_a, every B_g (and B_scale) in fmt_b, each MX_FMT_E2M1 or MX_FMT_E4M3
+ * (E4M3 activations with E2M1 expert weights is the usual serving layout of
+ * a mixture-of-experts layer; the block dot product is mx_gemm_mixed's).
+ * A's rows are K or K/2 bytes as fmt_a says, B's as fmt_b says; everything
+ * else as for mx_gemm_grouped, whose plan (mx_gemm_grouped_plan with fmt_a)
+ * describes the launch.  With fmt_a == fmt_b it is mx_gemm_grouped.
+ */
+int mx_gemm_grouped_mixed(int fmt_a, int fmt_b, int64_t groups, const int64_t *group_rows,
+                          int64_t N, int64_t K, const void *A, const void *A_scale,
+                          const void *B, const void *B_scale, void *C, int out_dtype,
+                          void *stream);
+
+/*
  * How mx_gemm_grouped would run a problem: one tile shape for all groups
  * (split_k is always 1, workspace_bytes 0; workgroups is the total number of
  * tiles over the groups, 0 when there are no rows).  Host logic only: no

@@ -121,6 +121,9 @@ def lib():
     L.mx_gemm_grouped_bf16_plan.restype = ctypes.c_int
     L.mx_gemm_grouped_bf16_plan.argtypes = [i64, ctypes.POINTER(i64), i64, i64, ctypes.c_int,
                                             ctypes.POINTER(MxPlan)]
+    L.mx_gemm_grouped_mixed.restype = ctypes.c_int
+    L.mx_gemm_grouped_mixed.argtypes = [ctypes.c_int, ctypes.c_int, i64, ctypes.POINTER(i64), i64,
+                                        i64, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     L.mx_gemm_grouped.restype = ctypes.c_int
     L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
                                   vp, vp, vp, ctypes.c_int, vp]
@@ -357,26 +360,34 @@ def grouped_plan(fmt, group_rows, N, K, out_dtype=OUT_BF16):
     return p.as_dict()
 
 
-def grouped_ptr(fmt, group_rows, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0):
-    """Raw entry point of mx_gemm_grouped: a list of row counts, integer
-    device addresses; returns the status code."""
+def grouped_ptr(fmt, group_rows, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0,
+                fmt_b=None):
+    """Raw entry point of mx_gemm_grouped (mx_gemm_grouped_mixed when
+    ``fmt_b`` differs from ``fmt``): a list of row counts, integer device
+    addresses; returns the status code."""
     rows = list(group_rows)
     arr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    if fmt_b is not None and fmt_b != fmt:
+        return lib().mx_gemm_grouped_mixed(int(fmt), int(fmt_b), len(rows), arr, int(N), int(K),
+                                           A, A_scale, B, B_scale, C, int(out_dtype),
+                                           stream or None)
     return lib().mx_gemm_grouped(int(fmt), len(rows), arr, int(N), int(K), A, A_scale, B,
                                  B_scale, C, int(out_dtype), stream or None)
 
 
 def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out=None,
-                    stream=None):
+                    stream=None, fmt_b=None):
     """C_g = A_g * B_g^T for consecutive row groups of a (group_rows[g] rows
     each, summing to a's row count; zeros allowed) and the G = len(group_rows)
-    weights stacked in b, (G*N, K) in mx_gemm's operand layout.  Returns
-    (sum(group_rows), N)."""
+    weights stacked in b, (G*N, K) in mx_gemm's operand layout.  ``fmt_b``
+    gives the weights their own format (E4M3 x E2M1 or the reverse).
+    Returns (sum(group_rows), N)."""
     import torch
     if out_dtype is None:
         out_dtype = torch.bfloat16
-    if fmt not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    fmt_b = fmt if fmt_b is None else fmt_b
+    if fmt not in (FMT_E2M1, FMT_E4M3) or fmt_b not in (FMT_E2M1, FMT_E4M3):
+        raise ValueError("fmt and fmt_b must be FMT_E2M1 or FMT_E4M3")
     code, tdt = _out_code(out_dtype)
     rows = [int(r) for r in group_rows]
     G = len(rows)
@@ -390,9 +401,8 @@ def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out
     if b.shape[0] % G != 0:
         raise ValueError("b's rows are not a multiple of the group count")
     N = b.shape[0] // G
-    per = 2 if fmt == FMT_E2M1 else 1
-    K = a.shape[1] * per
-    if b.shape[1] * per != K:
+    K = a.shape[1] * (2 if fmt == FMT_E2M1 else 1)
+    if b.shape[1] * (2 if fmt_b == FMT_E2M1 else 1) != K:
         raise ValueError("a and b disagree on K")
     if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (G * N, K // 32):
         raise ValueError("scales must be (rows, K/32)")
@@ -409,7 +419,7 @@ def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out
         stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         rc = grouped_ptr(fmt, rows, N, K, a.data_ptr(), a_scale.data_ptr(), b.data_ptr(),
-                         b_scale.data_ptr(), out.data_ptr(), code, stream)
+                         b_scale.data_ptr(), out.data_ptr(), code, stream, fmt_b)
     if rc != MX_OK:
         _raise(rc)
     return out

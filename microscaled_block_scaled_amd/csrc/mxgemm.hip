@@ -478,26 +478,26 @@ int choose_tile_grouped(const int64_t *rows, int64_t groups, int64_t N, int64_t 
     return best;
 }
 
-template <int FMT, int OUT, int BM, int BN, int WGM, int WGN, int S>
+template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>
 void launch_grouped_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
                         int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t stream)
 {
     const int tiles_n = (int)cdiv(N, BN);
-    hipLaunchKernelGGL((mx::tile_kernel<FMT, FMT, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
+    hipLaunchKernelGGL((mx::tile_kernel<FA, FB, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
                        dim3((unsigned)gt.tile_start[gt.n]), dim3(WGM * WGN * 64), 0, stream,
                        (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
                        (const uint8_t *)Bs, C, 0, (int)N, (int)K, 0, tiles_n, 4, (int)K,
                        (int64_t)0, gt);
 }
 
-template <int FMT, int OUT>
+template <int FA, int FB, int OUT>
 bool launch_grouped(int t, const void *A, const void *As, const void *B, const void *Bs,
                     void *C, int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t s)
 {
     const TileCfg &c = kTiles[t];
 #define MX_GCFG(BM_, BN_, WM_, WN_, S_)                                                   \
     if (c.bm == BM_ && c.bn == BN_ && c.wgm == WM_ && c.wgn == WN_) {                    \
-        launch_grouped_cfg<FMT, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, N, K, gt, s); \
+        launch_grouped_cfg<FA, FB, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, N, K, gt, s); \
         return true;                                                                      \
     }
     MX_GCFG(256, 256, 4, 2, 2)
@@ -568,17 +568,20 @@ extern "C" int mx_gemm_grouped_plan(int fmt, int64_t groups, const int64_t *grou
 
 namespace {
 
-// Grouped GEMM in format fmt (MX_FMT_E2M1, MX_FMT_E4M3, or kFmtBF16 with no
-// scale arrays).
-int run_grouped(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, int64_t K,
-                const void *A, const void *A_scale, const void *B, const void *B_scale, void *C,
-                int out_dtype, void *stream)
+// Grouped GEMM with A in fmt and B in fmt_b (MX_FMT_E2M1 / MX_FMT_E4M3 in
+// any pair), or fmt = fmt_b = kFmtBF16 with no scale arrays.
+int run_grouped(int fmt, int fmt_b, int64_t groups, const int64_t *group_rows, int64_t N,
+                int64_t K, const void *A, const void *A_scale, const void *B,
+                const void *B_scale, void *C, int out_dtype, void *stream)
 {
     mx_plan_t plan;
     mx::GroupTable gt;
     int t = 0;
     int rc = grouped_plan(fmt, groups, group_rows, N, K, out_dtype, &plan, &t, &gt);
     if (rc != MX_OK) return rc;
+    if ((fmt == kFmtBF16) != (fmt_b == kFmtBF16) ||
+        (fmt_b != kFmtBF16 && fmt_b != MX_FMT_E2M1 && fmt_b != MX_FMT_E4M3))
+        return MX_ERR_FORMAT;
     if (plan.workgroups == 0) return MX_OK;                 // no rows: nothing to compute
     const bool scaled = fmt != kFmtBF16;
     if (!A || !B || !C || (scaled && (!A_scale || !B_scale))) return MX_ERR_NULL;
@@ -591,18 +594,21 @@ int run_grouped(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, i
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     bool launched;
+    const bool f32 = out_dtype == MX_OUT_FP32;
+#define MX_GRUN(FA_, FB_)                                                                         \
+    (f32 ? launch_grouped<FA_, FB_, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)         \
+         : launch_grouped<FA_, FB_, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s))
     if (fmt == kFmtBF16)
-        launched = (out_dtype == MX_OUT_FP32)
-            ? launch_grouped<mx::B16, mx::OF32>(t, A, nullptr, B, nullptr, C, N, K, gt, s)
-            : launch_grouped<mx::B16, mx::OBF16>(t, A, nullptr, B, nullptr, C, N, K, gt, s);
-    else if (fmt == MX_FMT_E2M1)
-        launched = (out_dtype == MX_OUT_FP32)
-            ? launch_grouped<mx::FP4, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)
-            : launch_grouped<mx::FP4, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s);
-    else
-        launched = (out_dtype == MX_OUT_FP32)
-            ? launch_grouped<mx::FP8, mx::OF32>(t, A, A_scale, B, B_scale, C, N, K, gt, s)
-            : launch_grouped<mx::FP8, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s);
+        launched = MX_GRUN(mx::B16, mx::B16);
+    else if (fmt == MX_FMT_E2M1 && fmt_b == MX_FMT_E2M1)
+        launched = MX_GRUN(mx::FP4, mx::FP4);
+    else if (fmt == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
+        launched = MX_GRUN(mx::FP8, mx::FP8);
+    else if (fmt == MX_FMT_E4M3)                                   // E4M3 x E2M1
+        launched = MX_GRUN(mx::FP8, mx::FP4);
+    else                                                           // E2M1 x E4M3
+        launched = MX_GRUN(mx::FP4, mx::FP8);
+#undef MX_GRUN
     return (launched && hipGetLastError() == hipSuccess) ? MX_OK : MX_ERR_LAUNCH;
 }
 
@@ -614,15 +620,25 @@ extern "C" int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_row
                                void *stream)
 {
     if (fmt == kFmtBF16) return MX_ERR_FORMAT;
-    return run_grouped(fmt, groups, group_rows, N, K, A, A_scale, B, B_scale, C, out_dtype,
+    return run_grouped(fmt, fmt, groups, group_rows, N, K, A, A_scale, B, B_scale, C, out_dtype,
                        stream);
+}
+
+extern "C" int mx_gemm_grouped_mixed(int fmt_a, int fmt_b, int64_t groups,
+                                     const int64_t *group_rows, int64_t N, int64_t K,
+                                     const void *A, const void *A_scale, const void *B,
+                                     const void *B_scale, void *C, int out_dtype, void *stream)
+{
+    if (fmt_a == kFmtBF16 || fmt_b == kFmtBF16) return MX_ERR_FORMAT;
+    return run_grouped(fmt_a, fmt_b, groups, group_rows, N, K, A, A_scale, B, B_scale, C,
+                       out_dtype, stream);
 }
 
 extern "C" int mx_gemm_grouped_bf16(int64_t groups, const int64_t *group_rows, int64_t N,
                                     int64_t K, const void *A, const void *B, void *C,
                                     int out_dtype, void *stream)
 {
-    return run_grouped(kFmtBF16, groups, group_rows, N, K, A, nullptr, B, nullptr, C,
+    return run_grouped(kFmtBF16, kFmtBF16, groups, group_rows, N, K, A, nullptr, B, nullptr, C,
                        out_dtype, stream);
 }
 

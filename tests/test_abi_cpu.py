@@ -434,3 +434,17 @@ def test_grouped_bf16_plan_matches_mx_plan():
                        ([8, 1, 0, 33], 4096, 2048), ([0, 0], 64, 128)):
         assert mxg.grouped_bf16_plan(rows, N, K) == mxg.grouped_plan(mxg.FMT_E4M3, rows, N, K)
     assert mxg.grouped_bf16_plan([5, 3], 64, 48)["workgroups"] >= 2
+
+
+def test_grouped_mixed_argument_errors():
+    good = 1 << 20
+    arr = (ctypes.c_int64 * 2)(4, 3)
+    L = mxg.lib()
+    call = lambda fa, fb, K=128, ptrs=(good,) * 5: L.mx_gemm_grouped_mixed(
+        fa, fb, 2, arr, 16, K, *ptrs, 2, None)
+    for fa, fb in ((2, 3), (3, 1), (0, 1), (2, 9), (0x100, 0x100)):
+        assert call(fa, fb) == mxg.MX_ERR_FORMAT, (fa, fb)
+    assert call(2, 1, K=96) == mxg.MX_ERR_SHAPE
+    assert call(2, 1, ptrs=(good, None, good, good, good)) == mxg.MX_ERR_NULL
+    assert call(1, 2, ptrs=(good, good, good + 8, good, good)) == mxg.MX_ERR_ALIGN
+    assert call(2, 1) == mxg.MX_ERR_NO_DEVICE or __import__("torch").cuda.device_count() > 0
