@@ -252,7 +252,7 @@ class Oracle:
     def quantize(self, fmt, X):
         """MX-quantize X (rows x K, values exactly representable in float64,
         K a multiple of 32) -> (codes, scales) uint8 arrays: codes rows x K
-        (E4M3) or rows x K/2 (E2M1), scales rows x K/32."""
+        (E4M3, E5M2) or rows x K/2 (E2M1), scales rows x K/32."""
         X = np.ascontiguousarray(X, dtype=np.float64)
         if X.ndim != 2 or X.shape[1] % 32:
             raise ValueError("X must be 2-D with a multiple of 32 columns")

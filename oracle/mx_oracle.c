@@ -343,18 +343,21 @@ static unsigned encode_magnitude(double a, int man, int bias, double maxv)
 }
 
 /* Quantize X (rows x K doubles, each an exact FP32 or BF16 value; K a
- * multiple of 32) to Q (rows x K bytes for E4M3, rows x K/2 for E2M1, element
+ * multiple of 32) to Q (rows x K bytes for E4M3 / E5M2, rows x K/2 for E2M1, element
  * 2i in the low nibble) and S (rows x K/32 E8M0 bytes).  Returns 0, or -1 on
  * an argument the rule does not cover. */
 int mxo_quantize(int fmt, int64_t rows, int64_t K, const double *X, uint8_t *Q, uint8_t *S)
 {
-    if (fmt != MXO_FMT_E2M1 && fmt != MXO_FMT_E4M3) return -1;
+    if (fmt != MXO_FMT_E2M1 && fmt != MXO_FMT_E4M3 && fmt != MXO_FMT_E5M2) return -1;
     if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
-    const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 8;
-    const int man = (fmt == MXO_FMT_E2M1) ? 1 : 3;
-    const int bias = (fmt == MXO_FMT_E2M1) ? 1 : 7;
-    const double maxv = (fmt == MXO_FMT_E2M1) ? 6.0 : 448.0;
-    const unsigned sign_bit = (fmt == MXO_FMT_E2M1) ? 8u : 128u;
+    /* emax = exponent of the largest normal value: 6 = 1.5 * 2^2,
+     * 448 = 1.75 * 2^8, 57344 = 1.75 * 2^15. */
+    const int e2m1 = fmt == MXO_FMT_E2M1, e5m2 = fmt == MXO_FMT_E5M2;
+    const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;
+    const int man = e2m1 ? 1 : e5m2 ? 2 : 3;
+    const int bias = e2m1 ? 1 : e5m2 ? 15 : 7;
+    const double maxv = e2m1 ? 6.0 : e5m2 ? 57344.0 : 448.0;
+    const unsigned sign_bit = e2m1 ? 8u : 128u;
     const int64_t nb = K / 32, rb = row_bytes(fmt, K);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
@@ -385,7 +388,7 @@ int mxo_quantize(int fmt, int64_t rows, int64_t K, const double *X, uint8_t *Q, 
                     if (signbit(x[j])) code |= sign_bit;
                 }
                 const int64_t k = 32 * b + j;
-                if (fmt == MXO_FMT_E4M3) {
+                if (!e2m1) {
                     Q[r * rb + k] = (uint8_t)code;
                 } else {
                     uint8_t *byte = &Q[r * rb + (k >> 1)];

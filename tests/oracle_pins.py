@@ -406,6 +406,31 @@ def pin_quantize_e4m3_vs_torch(orc):
     assert S[0, 0] == 127 and (Q[0, :5] == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]).all(), Q[0, :5]
 
 
+def pin_quantize_e5m2_vs_torch(orc):
+    """E5M2 elements: with amax = 57344 the shared exponent is 0 (byte 127),
+    so each code must equal torch's float8_e5m2 conversion (round to nearest
+    even, subnormals down to 2^-16) of the value itself; above 57344 the code
+    saturates, where torch's conversion would overflow to infinity."""
+    import torch
+    t = torch_e5m2()
+    grid = [abs(x) for x in t[np.isfinite(t)]]
+    vals = _sweep_values(57344.0, grid)
+    X = _blocks_with_amax(vals, 57344.0)
+    Q, S = orc.quantize(E5M2, X)
+    assert (S == 127).all(), "E5M2 scale byte for amax 57344 must be 127"
+    ref = torch.from_numpy(X.astype(np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert (Q == ref).all(), "E5M2 codes differ from torch's conversion at %s" % (
+        X[Q != ref][:5],)
+    X = _blocks_with_amax(np.array([57345.0, 61440.0, 65000.0, -62000.0]), 65000.0)
+    Q, S = orc.quantize(E5M2, X)
+    assert S[0, 0] == 127 and (Q[0, :5] == [0x7B, 0x7B, 0x7B, 0x7B, 0xFB]).all(), Q[0, :5]
+    # the scale rule with emax 15: amax 1.0 -> byte 112, amax 2^-20 -> 92
+    X = _blocks_with_amax(np.array([0.5]), 1.0)
+    assert orc.quantize(E5M2, X)[1][0, 0] == 127 - 15
+    X = _blocks_with_amax(np.array([2.0 ** -21]), 2.0 ** -20)
+    assert orc.quantize(E5M2, X)[1][0, 0] == 127 - 20 - 15
+
+
 def pin_quantize_e2m1_bruteforce(orc):
     """Elements: with amax = 6 the shared exponent is 0, so each code must be
     the nearest E2M1 value (independent golden table), ties to the code with
@@ -685,7 +710,8 @@ def pin_grouped_bf16(orc):
 ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
-            pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e2m1_bruteforce,
+            pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e5m2_vs_torch,
+            pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
             pin_grouped, pin_mixed_formats, pin_e5m2, pin_e5m2_pairs, pin_bf16,
             pin_grouped_bf16]

@@ -116,7 +116,8 @@ def test_case_shapes():
     assert c2["A"].shape == (3, 128) and c2["B_scale"].shape == (5, 4)
 
 
-@pytest.mark.parametrize("fmt", [mxinputs.FMT_E2M1, mxinputs.FMT_E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("fmt", [mxinputs.FMT_E2M1, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2],
+                         ids=["e2m1", "e4m3", "e5m2"])
 def test_generator_quantizer_matches_oracle(orc, fmt):
     """The input generator's numpy quantizer and the oracle's C quantizer are
     two implementations of the same OCP rule: they agree on every byte."""

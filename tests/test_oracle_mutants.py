@@ -55,6 +55,10 @@ MUTANTS = [
     ("e5m2_subnormal", "ldexp((double)m / 4.0, -14)", "ldexp((double)m / 4.0, -15)"),
     ("e5m2_inf_as_nan", "mag = (m == 0) ? INFINITY : NAN;", "mag = NAN;"),
     ("e5m2_double_sums", "if (exact128) block_exact(", "if (0) block_exact("),
+    ("e5m2_quant_emax", "const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;",
+     "const int emax = e2m1 ? 2 : e5m2 ? 14 : 8;"),
+    ("e5m2_quant_bias", "const int bias = e2m1 ? 1 : e5m2 ? 15 : 7;",
+     "const int bias = e2m1 ? 1 : e5m2 ? 16 : 7;"),
     ("e5m2_pair_double_sums", "const int exact128 = fmt_a == MXO_FMT_E5M2 || fmt_b == MXO_FMT_E5M2;",
      "const int exact128 = fmt_a == MXO_FMT_E5M2 && fmt_b == MXO_FMT_E5M2;"),
     # BF16 GEMM.
@@ -64,8 +68,8 @@ MUTANTS = [
      "for (int64_t k = 0; k < K - 1; ++k) {\n                c += a[k] * b[k];"),
     ("mixed_same_format_entry", "return mxo_gemm_ab(fmt, fmt, M,", "return mxo_gemm_ab(fmt, MXO_FMT_E4M3, M,"),
     # The quantizer.
-    ("q_e4m3_emax", "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 8;",
-     "const int emax = (fmt == MXO_FMT_E2M1) ? 2 : 7;"),
+    ("q_e4m3_emax", "const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;",
+     "const int emax = e2m1 ? 2 : e5m2 ? 15 : 7;"),
     ("q_ties_away", "nearbyint(a / quantum)", "round(a / quantum)"),
     ("q_no_saturation", "if (a > maxv) a = maxv;", ""),
     ("q_negative_zero", "if (signbit(x[j])) code |= sign_bit;",
