@@ -589,7 +589,7 @@ def main():
         copy_calibration()
         return
     if a.quantize:
-        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1):
+        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, mxinputs.FMT_E5M2):
             for ind in (1, 2):
                 print(json.dumps(bench_quantize(a.steps, a.warmup, fmt, ind)), flush=True)
         return

@@ -334,8 +334,8 @@ def mx_quantize(x, fmt, stream=None):
         raise ValueError("x must be float32 or bfloat16")
     if not x.is_contiguous() or not x.is_cuda:
         raise ValueError("x must be a contiguous GPU tensor")
-    if fmt not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("fmt must be FMT_E2M1 or FMT_E4M3")
+    if fmt not in (FMT_E2M1, FMT_E4M3, FMT_E5M2):
+        raise ValueError("fmt must be FMT_E2M1, FMT_E4M3 or FMT_E5M2")
     rows, K = x.shape
     q = torch.empty((rows, K // 2 if fmt == FMT_E2M1 else K), dtype=torch.uint8, device=x.device)
     qs = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)

@@ -1,17 +1,17 @@
 // mx_quant.h -- gfx950 device code for MX quantization: FP32 or BF16 values
-// -> MXFP4 (E2M1) or MXFP8 (E4M3) elements plus one E8M0 scale per 32 values
-// along K, by the OCP Microscaling v1.0 conversion rule (the operands the MX
-// scaled GEMM of the FlyDSL article starts from; section "Performance numbers
-// need their baselines"):
+// -> MXFP4 (E2M1) or MXFP8 (E4M3 or E5M2) elements plus one E8M0 scale per
+// 32 values along K, by the OCP Microscaling v1.0 conversion rule (the
+// operands the MX scaled GEMM of the FlyDSL article starts from; section
+// "Performance numbers need their baselines"):
 //   per block of 32 values: X = floor(log2 max|x|) - emax (emax 2 for E2M1,
-//   8 for E4M3), scale byte s = X + 127 clamped to [0, 254] (0 for an
-//   all-zero block), element = x * 2^(127 - s) rounded to the nearest element
-//   value, ties to the even code, saturating at 6 / 448, sign kept; a block
-//   with a NaN or an infinity gets s = 255 and zero codes.
+//   8 for E4M3, 15 for E5M2), scale byte s = X + 127 clamped to [0, 254] (0
+//   for an all-zero block), element = x * 2^(127 - s) rounded to the nearest
+//   element value, ties to the even code, saturating at 6 / 448 / 57344, sign
+//   kept; a block with a NaN or an infinity gets s = 255 and zero codes.
 //
 // Rows are dense and K is a multiple of 32, so the matrix is a flat sequence
 // of 32-value blocks: block b is input values 32b .. 32b+31, scale byte b,
-// and output bytes 32b .. (E4M3) or 16b .. (E2M1).
+// and output bytes 32b .. (E4M3, E5M2) or 16b .. (E2M1).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,6 +48,16 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// Two E5M2 codes (low byte: a, high byte: b), round to nearest even, values
+// clamped to +-57344 first so nothing rounds to an infinity (gfx950 converts
+// to the OCP E5M2 format).
+__device__ __forceinline__ uint32_t e5m2_pair(float a, float b)
+{
+    a = fminf(fmaxf(a, -57344.f), 57344.f);
+    b = fminf(fmaxf(b, -57344.f), 57344.f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xffffu;
+}
+
 // Maximum over each group of LPB (4 or 8) consecutive lanes, by DPP moves
 // within registers: swap neighbours, swap pairs, then (groups of 8) mirror
 // each half-row of 8 lanes, which pairs every lane with one of the other
@@ -73,7 +83,7 @@ quantize_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *__
 {
     constexpr int V = (IN == IN_F32) ? 4 : 8;
     constexpr int LPB = 32 / V;
-    constexpr int EMAX = (FMT == FP4) ? 2 : 8;
+    constexpr int EMAX = (FMT == FP4) ? 2 : (FMT == BF8) ? 15 : 8;
     constexpr int UNR = 2;
     const int sub = threadIdx.x % LPB;
     const int64_t first = (int64_t)blockIdx.x * (256 / LPB) + threadIdx.x / LPB;
@@ -117,12 +127,14 @@ quantize_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *__
         float y[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) y[i] = bad ? 0.f : ldexpf(v[i], 127 - s);
-        if (FMT == FP8) {
+        if (FMT != FP4) {
             uint32_t w[V / 4];
 #pragma unroll
             for (int i = 0; i < V / 4; ++i)
-                w[i] = e4m3_pair(y[4 * i], y[4 * i + 1]) |
-                       (e4m3_pair(y[4 * i + 2], y[4 * i + 3]) << 16);
+                w[i] = (FMT == BF8) ? e5m2_pair(y[4 * i], y[4 * i + 1]) |
+                                          (e5m2_pair(y[4 * i + 2], y[4 * i + 3]) << 16)
+                                    : e4m3_pair(y[4 * i], y[4 * i + 1]) |
+                                          (e4m3_pair(y[4 * i + 2], y[4 * i + 3]) << 16);
             if (bad) {
 #pragma unroll
                 for (int i = 0; i < V / 4; ++i) w[i] = 0;

@@ -196,7 +196,7 @@ def test_python_shim_rejects_bad_tensors():
 
 
 @pytest.mark.parametrize("fmt,ind,rows,K,code", [
-    (3, 1, 4, 64, mxg.MX_ERR_FORMAT),
+    (4, 1, 4, 64, mxg.MX_ERR_FORMAT),
     (1, 3, 4, 64, mxg.MX_ERR_IN_DTYPE),
     (2, 0, 4, 64, mxg.MX_ERR_IN_DTYPE),
     (1, 1, 0, 64, mxg.MX_ERR_SHAPE),
@@ -343,9 +343,11 @@ def test_e5m2_accepted_where_documented():
         assert L.mx_gemm_mixed(fa, fb, 16, 16, 128, *args, 2, 0, 0, 0, None) \
             == mxg.MX_ERR_NO_DEVICE, (fa, fb)
     assert L.mx_gemm_mixed(3, 4, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-    # grouped GEMM and the quantizer take E2M1 / E4M3 only
+    # the grouped GEMM takes E2M1 / E4M3 only; the quantizer takes E5M2 too
     assert _grouped(3, [4], 16, 128) == mxg.MX_ERR_FORMAT
-    assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
+    assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_NO_DEVICE \
+        or __import__("torch").cuda.device_count() > 0
+    assert L.mx_quantize(4, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
 
 
 def test_bf16_argument_errors():

@@ -10,7 +10,8 @@ from gpu_util import log
 
 pytestmark = pytest.mark.gpu
 
-E2M1, E4M3 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3
+E2M1, E4M3, E5M2 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2
+FMTS, FMT_IDS = [E2M1, E4M3, E5M2], ["e2m1", "e4m3", "e5m2"]
 
 
 def _gpu(x, fmt):
@@ -43,7 +44,7 @@ def _random(rows, K, seed, dtype):
 SHAPES = [(1, 32), (3, 96), (17, 4128), (256, 4096), (1000, 128)]
 
 
-@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
 @pytest.mark.parametrize("rows,K", SHAPES)
 def test_quantize_random(fmt, dtype, rows, K):
@@ -53,16 +54,20 @@ def test_quantize_random(fmt, dtype, rows, K):
     _check(x, fmt, "random")
 
 
-@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
 def test_quantize_edge_values(fmt, dtype):
     """Ties after scaling, saturation, negative zero, values rounding to zero
     with either sign, FP32 and BF16 subnormal and huge block maxima, and
     blocks holding a NaN or an infinity."""
     import torch
-    top = 6.0 if fmt == E2M1 else 448.0
-    grid = (oracle.tables()[0][:8] if fmt == E2M1 else
-            np.abs(oracle.tables()[1][:127]))
+    top = {E2M1: 6.0, E4M3: 448.0, E5M2: 57344.0}[fmt]
+    if fmt == E2M1:
+        grid = oracle.tables()[0][:8]
+    elif fmt == E4M3:
+        grid = np.abs(oracle.tables()[1][:127])
+    else:                                   # E5M2 codes 0 .. 123 are the finite magnitudes
+        grid = np.array([oracle.default().e5m2_value(c) for c in range(124)])
     g = np.unique(np.abs(grid[np.isfinite(grid)]))
     mids = (g[1:] + g[:-1]) / 2
     vals = np.concatenate([g, mids, -mids, [-0.0, -1e-3, 1e-3, top * 1.06, -top * 1.12]])
@@ -85,7 +90,7 @@ def test_quantize_edge_values(fmt, dtype):
     _check(x, fmt, "edge values")
 
 
-@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_quantize_full_size(fmt):
     """The 8B-Llama fused-QKV operands (2048 + 6144 rows, K = 4096) from FP32."""
     import torch
@@ -94,7 +99,7 @@ def test_quantize_full_size(fmt):
     _check(x, fmt, "full size")
 
 
-@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_quantize_then_gemm(fmt):
     """Operands quantized on the GPU feed mx_gemm directly."""
     import torch
