@@ -29,10 +29,12 @@ import numpy as np
 FMT_E2M1 = 1
 FMT_E4M3 = 2
 FMT_E5M2 = 3
+FMT_E2M3 = 4
+FMT_E3M2 = 5
 OUT_FP32 = 1
 OUT_BF16 = 2
 
-_EMAX = {FMT_E2M1: 2, FMT_E4M3: 8, FMT_E5M2: 15}
+_EMAX = {FMT_E2M1: 2, FMT_E4M3: 8, FMT_E5M2: 15, FMT_E2M3: 2, FMT_E3M2: 4}
 _CHUNK_ROWS = 256
 
 # The workloads.  Shapes come from the serving models the pages measure
@@ -55,11 +57,16 @@ for _fmt, _fname in ((FMT_E4M3, "mxfp8"), (FMT_E2M1, "mxfp4")):
 
 
 def fmt_name(fmt):
-    return {FMT_E2M1: "mxfp4", FMT_E4M3: "mxfp8", FMT_E5M2: "mxfp8_e5m2"}[fmt]
+    return {FMT_E2M1: "mxfp4", FMT_E4M3: "mxfp8", FMT_E5M2: "mxfp8_e5m2",
+            FMT_E2M3: "mxfp6_e2m3", FMT_E3M2: "mxfp6_e3m2"}[fmt]
 
 
 def row_bytes(fmt, K):
-    return K // 2 if fmt == FMT_E2M1 else K
+    if fmt == FMT_E2M1:
+        return K // 2
+    if fmt in (FMT_E2M3, FMT_E3M2):
+        return K // 4 * 3
+    return K
 
 
 # --------------------------------------------------------------------------
@@ -104,6 +111,54 @@ def encode_e5m2(v):
     return t.view(torch.uint8).numpy().copy()
 
 
+def _fp6_magnitudes(fmt):
+    """The 32 non-negative FP6 magnitudes by code (E2M3: 2 exponent bits,
+    bias 1, 3 mantissa bits; E3M2: 3 exponent bits, bias 3, 2 mantissa bits;
+    exponent field 0 subnormal)."""
+    mb = 3 if fmt == FMT_E2M3 else 2
+    bias = 1 if fmt == FMT_E2M3 else 3
+    out = []
+    for c in range(32):
+        e, m = c >> mb, c & ((1 << mb) - 1)
+        frac = m / float(1 << mb)
+        out.append(np.ldexp(frac, 1 - bias) if e == 0 else np.ldexp(1.0 + frac, e - bias))
+    return np.array(out)
+
+
+def encode_fp6(v, fmt):
+    """float array -> FP6 codes (0..63, sign bit 5): nearest magnitude, ties
+    to the even code, saturating at the largest magnitude."""
+    v = np.asarray(v, np.float64)
+    mags = _fp6_magnitudes(fmt)
+    a = np.minimum(np.abs(v), mags[-1])
+    hi = np.clip(np.searchsorted(mags, a), 1, 31)
+    lo = hi - 1
+    dlo, dhi = a - mags[lo], mags[hi] - a
+    code = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(hi % 2 == 0, hi, lo)))
+    return (code | (np.signbit(v).astype(np.int64) << 5)).astype(np.uint8)
+
+
+def pack_fp6(codes):
+    """rows x K codes -> rows x 3K/4 bytes: element k in bits 6k .. 6k+5 of
+    the row's little-endian bit string."""
+    c = np.asarray(codes, np.uint32)
+    w = c[:, 0::4] | (c[:, 1::4] << 6) | (c[:, 2::4] << 12) | (c[:, 3::4] << 18)
+    out = np.empty((c.shape[0], w.shape[1] * 3), np.uint8)
+    out[:, 0::3] = w & 255
+    out[:, 1::3] = (w >> 8) & 255
+    out[:, 2::3] = w >> 16
+    return out
+
+
+def unpack_fp6(packed):
+    p = np.asarray(packed, np.uint32)
+    w = p[:, 0::3] | (p[:, 1::3] << 8) | (p[:, 2::3] << 16)
+    out = np.empty((p.shape[0], w.shape[1] * 4), np.uint8)
+    for i in range(4):
+        out[:, i::4] = (w >> (6 * i)) & 63
+    return out
+
+
 def quantize(x, fmt):
     """float32 rows x K -> (codes, scales) per the OCP MX conversion rule."""
     x = np.asarray(x, np.float32)
@@ -123,6 +178,8 @@ def quantize(x, fmt):
         codes = encode_e4m3(scaled)
     elif fmt == FMT_E5M2:
         codes = encode_e5m2(scaled)
+    elif fmt in (FMT_E2M3, FMT_E3M2):
+        codes = pack_fp6(encode_fp6(scaled, fmt))
     else:
         c = encode_e2m1(scaled)
         codes = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)

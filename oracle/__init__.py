@@ -31,7 +31,17 @@ import numpy as np
 FMT_E2M1 = 1
 FMT_E4M3 = 2
 FMT_E5M2 = 3
-_FORMATS = (FMT_E2M1, FMT_E4M3, FMT_E5M2)
+FMT_E2M3 = 4
+FMT_E3M2 = 5
+_FORMATS = (FMT_E2M1, FMT_E4M3, FMT_E5M2, FMT_E2M3, FMT_E3M2)
+
+
+def _row_bytes(fmt, K):
+    if fmt == FMT_E2M1:
+        return K // 2
+    if fmt in (FMT_E2M3, FMT_E3M2):
+        return K // 4 * 3
+    return K
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -84,8 +94,7 @@ def _check_shapes(fmt, A, As, B, Bs, K, fmt_b=None):
     fmt_b = fmt if fmt_b is None else fmt_b
     if fmt not in _FORMATS or fmt_b not in _FORMATS:
         raise ValueError("formats must be E2M1, E4M3 or E5M2 (any pair)")
-    rba = K // 2 if fmt == FMT_E2M1 else K
-    rbb = K // 2 if fmt_b == FMT_E2M1 else K
+    rba, rbb = _row_bytes(fmt, K), _row_bytes(fmt_b, K)
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != rba or B.shape[1] != rbb:
         raise ValueError("A and B must be 2-D with %d and %d bytes per row" % (rba, rbb))
     if As.shape != (A.shape[0], K // 32) or Bs.shape != (B.shape[0], K // 32):

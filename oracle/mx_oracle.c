@@ -67,6 +67,8 @@
 #define MXO_FMT_E2M1 1
 #define MXO_FMT_E4M3 2
 #define MXO_FMT_E5M2 3
+#define MXO_FMT_E2M3 4
+#define MXO_FMT_E3M2 5
 
 /* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.  Exponent
  * field 0 is subnormal: m * 2^-1.  No Inf, no NaN (OCP MX v1.0, FP4). */
@@ -100,6 +102,26 @@ double mxo_e5m2_value(unsigned code)
     return s ? -mag : mag;
 }
 
+/* FP6 E2M3: sign bit 5, exponent bits 4..3 (bias 1), mantissa bits 2..0.
+ * Exponent field 0 is subnormal: m/8.  No Inf, no NaN; largest 7.5 (OCP MX
+ * v1.0, FP6 E2M3). */
+double mxo_e2m3_value(unsigned code)
+{
+    unsigned s = (code >> 5) & 1u, e = (code >> 3) & 3u, m = code & 7u;
+    double mag = (e == 0) ? (double)m / 8.0 : ldexp(1.0 + (double)m / 8.0, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* FP6 E3M2: sign bit 5, exponent bits 4..2 (bias 3), mantissa bits 1..0.
+ * Exponent field 0 is subnormal: m/4 * 2^-2.  No Inf, no NaN; largest 28
+ * (OCP MX v1.0, FP6 E3M2). */
+double mxo_e3m2_value(unsigned code)
+{
+    unsigned s = (code >> 5) & 1u, e = (code >> 2) & 7u, m = code & 3u;
+    double mag = (e == 0) ? ldexp((double)m / 4.0, -2) : ldexp(1.0 + (double)m / 4.0, (int)e - 3);
+    return s ? -mag : mag;
+}
+
 /* E8M0 scale: 2^(byte - 127); byte 255 is NaN (OCP MX v1.0, E8M0). */
 double mxo_e8m0_value(unsigned byte)
 {
@@ -107,12 +129,21 @@ double mxo_e8m0_value(unsigned byte)
     return ldexp(1.0, (int)byte - 127);
 }
 
-/* Decode element k of one packed row into a double. */
+/* Decode element k of one packed row into a double.  FP6 rows are a
+ * little-endian bit string with element k in bits 6k .. 6k+5 (bit b is bit
+ * b % 8 of byte b / 8), four elements per three bytes. */
 static double decode_elem(int fmt, const uint8_t *row, int64_t k,
                           const double *t4, const double *t8)
 {
     if (fmt == MXO_FMT_E4M3) return t8[row[k]];
     if (fmt == MXO_FMT_E5M2) return mxo_e5m2_value(row[k]);
+    if (fmt == MXO_FMT_E2M3 || fmt == MXO_FMT_E3M2) {
+        const int64_t bit = 6 * k;
+        unsigned v = row[bit >> 3];
+        if ((bit & 7) > 2) v |= (unsigned)row[(bit >> 3) + 1] << 8;
+        const unsigned code = (v >> (bit & 7)) & 63u;
+        return fmt == MXO_FMT_E2M3 ? mxo_e2m3_value(code) : mxo_e3m2_value(code);
+    }
     uint8_t byte = row[k >> 1];
     return t4[(k & 1) ? (byte >> 4) : (byte & 15u)];
 }
@@ -126,7 +157,12 @@ static void make_tables(double t4[16], double t8[256], double pow2[509])
     for (int i = 0; i < 509; ++i) pow2[i] = ldexp(1.0, i - 254);
 }
 
-static int64_t row_bytes(int fmt, int64_t K) { return fmt == MXO_FMT_E2M1 ? K / 2 : K; }
+static int64_t row_bytes(int fmt, int64_t K)
+{
+    if (fmt == MXO_FMT_E2M1) return K / 2;
+    if (fmt == MXO_FMT_E2M3 || fmt == MXO_FMT_E3M2) return K / 4 * 3;
+    return K;
+}
 
 /* Exact block sums with an E5M2 operand: every finite E5M2, E4M3 or E2M1
  * value is an integer multiple of 2^-16 below 2^32 in those units, so each
@@ -211,8 +247,8 @@ int mxo_gemm_ab(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                 const int64_t *rows, int64_t nrows,
                 double *C, double *T, double *E, int nthreads)
 {
-    if (fmt_a != MXO_FMT_E2M1 && fmt_a != MXO_FMT_E4M3 && fmt_a != MXO_FMT_E5M2) return -1;
-    if (fmt_b != MXO_FMT_E2M1 && fmt_b != MXO_FMT_E4M3 && fmt_b != MXO_FMT_E5M2) return -1;
+    if (fmt_a < MXO_FMT_E2M1 || fmt_a > MXO_FMT_E3M2 || fmt_b < MXO_FMT_E2M1 || fmt_b > MXO_FMT_E3M2)
+        return -1;
     /* With an E5M2 operand a block sum can need more than 53 bits (E5M2 x
      * E4M3 products span 50 binades, E5M2 x E5M2 64), so it is taken in
      * 128-bit integers; every value of the three formats is a whole multiple

@@ -24,6 +24,7 @@ import mxinputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 E2M1, E4M3, E5M2 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2
+E2M3, E3M2 = mxinputs.FMT_E2M3, mxinputs.FMT_E3M2
 
 
 # --------------------------------------------------------------------------
@@ -55,10 +56,27 @@ def torch_e8m0():
     return torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
 
 
+def golden_fp6(fmt):
+    """The 64 FP6 values by code, from the OCP value list (codes 0..31) and
+    the sign bit (code | 32)."""
+    name = "e2m3" if fmt == E2M3 else "e3m2"
+    vals = np.zeros(64, np.float64)
+    with open(os.path.join(GOLDEN, "%s_values.txt" % name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()
+                vals[int(c)] = float(v)
+                vals[int(c) | 32] = -float(v)
+    return vals
+
+
 def decode_rows(fmt, packed):
     """uint8 operand rows -> float64 values with the independent tables."""
     if fmt == E2M1:
         return golden_e2m1()[mxinputs.unpack_e2m1(packed)]
+    if fmt in (E2M3, E3M2):
+        return golden_fp6(fmt)[mxinputs.unpack_fp6(packed)]
     if fmt == E5M2:
         return torch_e5m2()[np.asarray(packed, np.uint8)]
     return torch_e4m3()[np.asarray(packed, np.uint8)]
@@ -649,6 +667,61 @@ def pin_e5m2_pairs(orc):
     assert C[0, 0] == 2.0 ** -25, C[0, 0]
 
 
+def pin_fp6(orc):
+    """FP6 (E2M3, E3M2): every code's value against the OCP value lists; a
+    numpy matmul of operands decoded with those lists and the generator's own
+    unpacking; the bit position of every element of a 4-element, 3-byte
+    group (one-hot products at each k of a block); exact integers; and the
+    transpose symmetry."""
+    for fmt in (E2M3, E3M2):
+        g = golden_fp6(fmt)
+        got = np.array([orc.gemm(fmt, *_fp6_onehot(fmt, c, g), 32)[0][0, 0] for c in range(64)])
+        assert np.array_equal(got, g), (fmt, np.flatnonzero(got != g)[:5])
+        case = mxinputs.make_random(fmt, 24, 18, 512, seed=61)
+        A, As, B, Bs = case["A"], case["A_scale"], case["B"], case["B_scale"]
+        C, T = orc.gemm(fmt, A, As, B, Bs, 512)
+        assert np.all(np.abs(C - dequant(fmt, A, As) @ dequant(fmt, B, Bs).T) <= 1e-12 * T), fmt
+        Ct, Tt = orc.gemm(fmt, B, Bs, A, As, 512)
+        assert np.array_equal(C, Ct.T) and np.array_equal(T, Tt.T)
+        # one-hot at every position k of the first block: A_k = 1, B_k = 2
+        one, two = int(np.flatnonzero(g == 1.0)[0]), int(np.flatnonzero(g == 2.0)[0])
+        s = np.full((1, 1), 127, np.uint8)
+        for k in range(32):
+            ca = np.zeros((1, 32), np.uint8)
+            cb = np.zeros((1, 32), np.uint8)
+            ca[0, k], cb[0, k] = one, two
+            ca[0, (k + 1) % 32] = one                  # neighbour: A only, B zero there
+            C1, _ = orc.gemm(fmt, mxinputs.pack_fp6(ca), s, mxinputs.pack_fp6(cb), s, 32)
+            assert C1[0, 0] == 2.0, (fmt, k, C1[0, 0])
+            # the same against an E4M3 operand (2.0 = code 0x40), which fixes
+            # the FP6 element position on its own (a permutation applied to
+            # both FP6 operands would leave every block sum unchanged)
+            c8 = np.zeros((1, 32), np.uint8)
+            c8[0, k] = 0x40
+            C2, _ = orc.gemm(fmt, mxinputs.pack_fp6(ca), s, c8, s, 32, fmt_b=E4M3)
+            assert C2[0, 0] == 2.0, (fmt, k, C2[0, 0])
+        # integer-valued codes, scales 127: exact
+        ints = [c for c in range(64) if g[c] == np.round(g[c])]
+        rng = np.random.default_rng(7)
+        ia = rng.choice(ints, size=(6, 256))
+        ib = rng.choice(ints, size=(5, 256))
+        s = np.full((6, 8), 127, np.uint8)
+        Ci, _ = orc.gemm(fmt, mxinputs.pack_fp6(ia), s, mxinputs.pack_fp6(ib), s[:5], 256)
+        want = g[ia].astype(np.int64) @ g[ib].astype(np.int64).T
+        assert np.array_equal(Ci, want.astype(np.float64)), fmt
+
+
+def _fp6_onehot(fmt, code, g):
+    """A = [code, 0, ...], B = [1.0, 0, ...] (one 32-block, scale 127): C is
+    the value of the code."""
+    one = int(np.flatnonzero(g == 1.0)[0])
+    ca = np.zeros((1, 32), np.uint8)
+    cb = np.zeros((1, 32), np.uint8)
+    ca[0, 0], cb[0, 0] = code, one
+    s = np.full((1, 1), 127, np.uint8)
+    return mxinputs.pack_fp6(ca), s, mxinputs.pack_fp6(cb), s
+
+
 def pin_bf16(orc):
     """BF16 dense GEMM: the decode against torch's bfloat16 (every pattern);
     a numpy matmul of torch-decoded values; exact rationals on a tiny case;
@@ -713,5 +786,5 @@ ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e5m2_vs_torch,
             pin_quantize_e2m1_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
-            pin_grouped, pin_mixed_formats, pin_e5m2, pin_e5m2_pairs, pin_bf16,
+            pin_grouped, pin_mixed_formats, pin_e5m2, pin_e5m2_pairs, pin_fp6, pin_bf16,
             pin_grouped_bf16]

@@ -67,6 +67,12 @@ MUTANTS = [
     ("bf16_last_k", "for (int64_t k = 0; k < K; ++k) {\n                c += a[k] * b[k];",
      "for (int64_t k = 0; k < K - 1; ++k) {\n                c += a[k] * b[k];"),
     ("mixed_same_format_entry", "return mxo_gemm_ab(fmt, fmt, M,", "return mxo_gemm_ab(fmt, MXO_FMT_E4M3, M,"),
+    # FP6 elements.
+    ("e2m3_bias", "ldexp(1.0 + (double)m / 8.0, (int)e - 1);\n    return s ? -mag : mag;\n}\n\n/* FP6 E3M2",
+     "ldexp(1.0 + (double)m / 8.0, (int)e - 2);\n    return s ? -mag : mag;\n}\n\n/* FP6 E3M2"),
+    ("e3m2_subnormal", "ldexp((double)m / 4.0, -2)", "ldexp((double)m / 4.0, -3)"),
+    ("fp6_bit_offset", "const int64_t bit = 6 * k;", "const int64_t bit = 6 * (k ^ 1);"),
+    ("fp6_high_byte_dropped", "if ((bit & 7) > 2) v |=", "if ((bit & 7) > 4) v |="),
     # The quantizer.
     ("q_e4m3_emax", "const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;",
      "const int emax = e2m1 ? 2 : e5m2 ? 15 : 7;"),
