@@ -52,10 +52,17 @@ extern "C" {
 #endif
 
 /* Element formats: MXFP4 = E2M1; MXFP8 = E4M3, or its other OCP encoding
- * E5M2 (wider range: 2^-16 .. 57344, with infinities and NaNs).  E5M2 is
- * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any of the
- * three) and mx_quantize; the grouped GEMMs take E2M1 and E4M3. */
-enum { MX_FMT_E2M1 = 1, MX_FMT_E4M3 = 2, MX_FMT_E5M2 = 3 };
+ * E5M2 (wider range: 2^-16 .. 57344, with infinities and NaNs); MXFP6 =
+ * E2M3 (largest 7.5) or E3M2 (largest 28), no infinities or NaNs.  E5M2 is
+ * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any of
+ * E2M1, E4M3, E5M2) and mx_quantize; the FP6 formats by mx_gemm,
+ * mx_gemm_tile and mx_gemm_mixed (with the same FP6 format only); the
+ * grouped GEMMs take E2M1 and E4M3.
+ * FP6 rows are K*3/4 bytes: a little-endian bit string with element k in
+ * bits 6k .. 6k+5 (bit b is bit b % 8 of byte b / 8), four elements in
+ * three bytes (OCP MX v1.0 fixes the element encoding; this packing is this
+ * library's). */
+enum { MX_FMT_E2M1 = 1, MX_FMT_E4M3 = 2, MX_FMT_E5M2 = 3, MX_FMT_E2M3 = 4, MX_FMT_E3M2 = 5 };
 
 /* Output element types. */
 enum { MX_OUT_FP32 = 1, MX_OUT_BF16 = 2 };

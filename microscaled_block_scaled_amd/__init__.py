@@ -33,6 +33,8 @@ import os
 FMT_E2M1 = 1
 FMT_E4M3 = 2
 FMT_E5M2 = 3
+FMT_E2M3 = 4          # MXFP6, packed 4 elements per 3 bytes
+FMT_E3M2 = 5
 OUT_FP32 = 1
 OUT_BF16 = 2
 MAX_DIM = 1 << 30     # largest M or N
@@ -205,6 +207,15 @@ def _as_u8(t, name):
     return t
 
 
+def _k_of(fmt, row_bytes):
+    """K-values in an operand row of row_bytes bytes."""
+    if fmt == FMT_E2M1:
+        return row_bytes * 2
+    if fmt in (FMT_E2M3, FMT_E3M2):
+        return row_bytes // 3 * 4
+    return row_bytes
+
+
 def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
             tile=None, split_k=0, fmt_b=None):
     """C = A * B^T for MX-quantized A (M x K) and B (N x K); see module doc.
@@ -216,14 +227,15 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
     if out_dtype is None:
         out_dtype = torch.bfloat16
     fmt_b = fmt if fmt_b is None else fmt_b
-    if fmt not in (FMT_E2M1, FMT_E4M3, FMT_E5M2) or fmt_b not in (FMT_E2M1, FMT_E4M3, FMT_E5M2):
-        raise ValueError("fmt and fmt_b must be FMT_E2M1, FMT_E4M3 or FMT_E5M2")
+    fmts = (FMT_E2M1, FMT_E4M3, FMT_E5M2, FMT_E2M3, FMT_E3M2)
+    if fmt not in fmts or fmt_b not in fmts:
+        raise ValueError("fmt and fmt_b must be one of the MX element formats")
     code, tdt = _out_code(out_dtype)
     a, b = _as_u8(a, "a"), _as_u8(b, "b")
     a_scale, b_scale = _as_u8(a_scale, "a_scale"), _as_u8(b_scale, "b_scale")
     M, N = a.shape[0], b.shape[0]
-    K = a.shape[1] * (2 if fmt == FMT_E2M1 else 1)
-    if b.shape[1] * (2 if fmt_b == FMT_E2M1 else 1) != K:
+    K = _k_of(fmt, a.shape[1])
+    if _k_of(fmt_b, b.shape[1]) != K:
         raise ValueError("a and b disagree on K")
     if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (N, K // 32):
         raise ValueError("scales must be (rows, K/32) = (%d, %d) and (%d, %d)"

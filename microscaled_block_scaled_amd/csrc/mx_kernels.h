@@ -51,12 +51,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 enum { FP4 = 1, FP8 = 2, BF8 = 3 };   // equal to MX_FMT_E2M1 / MX_FMT_E4M3 / MX_FMT_E5M2
 enum { B16 = 4 };                     // dense BF16 elements, no scales (B16 pairs with B16 only)
+enum { F6E2 = 5, F6E3 = 6 };          // FP6 E2M3 / E3M2 (MX_FMT_E2M3 / MX_FMT_E3M2 on the host)
+template <int F> struct is_fp6 { static constexpr bool value = F == F6E2 || F == F6E3; };
 enum { OF32 = 1, OBF16 = 2 };   // equal to MX_OUT_FP32 / MX_OUT_BF16
 
 // Format selector of the scaled MFMA (cbsz for A, blgp for B): 0 E4M3,
-// 1 E5M2, 4 E2M1.  E4M3 and E5M2 share one byte-per-element layout.
+// 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1.  E4M3 and E5M2 share one byte-per-element
+// layout.  FP6 operands, measured on the device like the others: lane
+// (r, g) holds K-values 32g .. 32g+31 as a 192-bit string in its first six
+// dwords, element i in bits 6i .. 6i+5.
 template <int FMT> struct mfma_fmt {
-    static constexpr int sel = (FMT == FP4) ? 4 : (FMT == BF8) ? 1 : 0;
+    static constexpr int sel = (FMT == FP4) ? 4 : (FMT == BF8) ? 1 : (FMT == F6E2) ? 2
+                             : (FMT == F6E3) ? 3 : 0;
 };
 
 // A slab is a run of K-values of every row of the A and B tiles: 256 when
@@ -74,12 +80,13 @@ template <int FA, int FB> struct slab {
     static constexpr int steps = kvals / kstep;      // 4, 2 or 4
     static constexpr int sbytes = scaled ? kvals / 32 : 0;   // 8, 4 or none
     // bytes of one row of an operand of format F in a slab
-    template <int F> static constexpr int row_bytes = (F == FP4) ? kvals / 2 : (F == B16) ? 2 * kvals : kvals;
+    template <int F> static constexpr int row_bytes =
+        (F == FP4) ? kvals / 2 : (F == B16) ? 2 * kvals : is_fp6<F>::value ? kvals / 4 * 3 : kvals;
 };
 // Bytes of k consecutive elements of format F.
 template <int F> __device__ __forceinline__ int64_t kbytes(int64_t k)
 {
-    return (F == FP4) ? k / 2 : (F == B16) ? 2 * k : k;
+    return (F == FP4) ? k / 2 : (F == B16) ? 2 * k : is_fp6<F>::value ? k / 4 * 3 : k;
 }
 
 // FP32 -> BF16 bits, round to nearest even (NaN stays NaN): one gfx950
@@ -100,7 +107,15 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // mod 4 among 16, get 4 distinct values, so 8 or 16 consecutive rows reading
 // one chunk again touch distinct banks.  Depends on r mod 16 only.
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-template <int RB> __device__ __forceinline__ int swz_row(int r) { return RB == 128 ? swz(r) : swz64(r); }
+// FP6 slab rows (96 bytes) are not swizzled.
+template <int RB> __device__ __forceinline__ int swz_row(int r)
+{
+    return RB == 128 ? swz(r) : RB == 64 ? swz64(r) : 0;
+}
+// Rows per copy instruction for slab rows of RB bytes: 1024 / RB for 128-
+// and 64-byte rows (64 lanes x 16 bytes); 8 for 96-byte FP6 rows, copied by
+// lanes 0..47 (6 chunks per row), the other 16 lanes idle.
+template <int RB> struct copy_rows { static constexpr int value = RB == 96 ? 8 : 1024 / RB; };
 
 template <int FA, int FB>
 __device__ __forceinline__ v16f mma(const v8i &a, const v8i &b, v16f acc, int sa, int sb)
@@ -114,6 +129,20 @@ __device__ __forceinline__ v16f mma(const v4i &a, const v4i &b, v16f acc, int, i
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
                                                   __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
+}
+
+// An FP6 operand fragment: 24 bytes (32 elements) from LDS, 8-byte aligned,
+// by three 8-byte reads, into the first six dwords of the MFMA operand.
+template <typename V>
+__device__ __forceinline__ V fp6_frag(const uint8_t *p)
+{
+    V v{};
+    if constexpr (sizeof(V) == 32) {
+        const uint2 *q = (const uint2 *)p;
+        const uint2 q0 = q[0], q1 = q[1], q2 = q[2];
+        v = V{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, 0, 0};
+    }
+    return v;
 }
 
 // Direct HBM -> LDS copies (gfx950 global_load_lds): lane l of the wave
@@ -250,7 +279,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int DATA = BM * RA + BN * RB;                // element bytes per slab
     constexpr int NSI = SCALED ? (ROWS + 63) / 64 : 0;     // scale copy instructions
     constexpr int SBUF = NSI * 64 * 16;                    // one scale buffer
-    constexpr int RPCA = 1024 / RA, RPCB = 1024 / RB;      // rows per copy instruction
+    constexpr int RPCA = copy_rows<RA>::value, RPCB = copy_rows<RB>::value;   // rows per copy instruction
     static_assert(S >= 2 && S - 1 <= PS, "one period of scale lookahead covers the ring");
     static_assert(BM % RPCA == 0 && BN % RPCB == 0, "rows per copy instruction");
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be 32-aligned");
@@ -341,7 +370,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         const uint32_t rb32 = (uint32_t)rowb;
         return CopyGeo{crow, (uint32_t)crow * rb32,
                        (uint32_t)(cpc ^ swz_row<R>(crow)) << 4,
-                       (uint32_t)(cpc ^ swz_row<R>(crow + 1024 / R)) << 4, rb32};
+                       (uint32_t)(cpc ^ swz_row<R>(crow + copy_rows<R>::value)) << 4, rb32};
     };
     const CopyGeo ga = copy_geo(std::integral_constant<int, RA>{}, rowba);
     const CopyGeo gb = copy_geo(std::integral_constant<int, RB>{}, rowbb);
@@ -368,13 +397,15 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPCA - 1);
             const uint32_t ch = min((RA == 128 && (i & 1)) ? ga.ch1 : ga.ch0, cmaxa);
-            g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * 1024);
+            if (RA != 96 || lane < 48)
+                g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * RPCA * RA);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
             const int i = min(wave + u * NW, BN / RPCB - 1);
             const uint32_t ch = min((RB == 128 && (i & 1)) ? gb.ch1 : gb.ch0, cmaxb);
-            g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * RA + i * 1024);
+            if (RB != 96 || lane < 48)
+                g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * RA + i * RPCB * RB);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
@@ -432,8 +463,14 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     struct Src { int data, scale, a0, a1, b0, b1; };
     auto chunk_offs = [&](auto fc, int p, int swl, int &o0, int &o1) {
         // Step p of a slab: E4M3 / E5M2 chunks 4p+g and 4p+2+g of a 128-byte
-        // row, E2M1 chunk 2p+g (of a 128- or a 64-byte row), BF16 chunk 2p+g.
+        // row, E2M1 chunk 2p+g (of a 128- or a 64-byte row), BF16 chunk 2p+g;
+        // FP6: 24 bytes at byte 48p+24g of a 96-byte row.
         constexpr int F = decltype(fc)::value;
+        if constexpr (is_fp6<F>::value) {
+            o0 = 48 * p + 24 * g;
+            o1 = 0;
+            return;
+        }
         const int c0 = (F == FP4 || F == B16) ? 2 * p + g : 4 * p + g;
         o0 = (c0 ^ swl) << 4;
         o1 = ((c0 + 2) ^ swl) << 4;
@@ -457,6 +494,11 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         constexpr bool IA = decltype(ia)::value;
         constexpr int F = IA ? FA : FB, R = IA ? RA : RB;
         const uint8_t *rp = smem + s.data + off + f * 32 * R;
+        if constexpr (is_fp6<F>::value) {
+            v = fp6_frag<fv>(rp + (IA ? s.a0 : s.b0));
+            sv = smem[s.scale + soff + f * 32 * 16];
+            return;
+        }
         const v4i lo = *(const v4i *)(rp + (IA ? s.a0 : s.b0));
         if constexpr (!SCALED) {
             v = lo;
@@ -498,8 +540,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             // LDS reads per fragment: data (2 for E4M3 / E5M2, 1 for E2M1
             // and BF16) + scale (none for BF16)
             constexpr int FRF = ROLL_A ? FA : FB, FDF = ROLL_A ? FB : FA;
-            constexpr int NRR = !SCALED ? 1 : (FRF != FP4) ? 3 : 2;
-            constexpr int NRD = !SCALED ? 1 : (FDF != FP4) ? 3 : 2;
+            constexpr int NRR = !SCALED ? 1 : is_fp6<FRF>::value ? 4 : (FRF != FP4) ? 3 : 2;
+            constexpr int NRD = !SCALED ? 1 : is_fp6<FDF>::value ? 4 : (FDF != FP4) ? 3 : 2;
 #pragma unroll
             for (int d = 0; d < FD; ++d) {
                 if constexpr (ROLL_A)

@@ -21,7 +21,7 @@ constexpr int kMaxDevices = 64;
 
 int check_args(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype)
 {
-    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3 && fmt != MX_FMT_E5M2) return MX_ERR_FORMAT;
+    if (fmt < MX_FMT_E2M1 || fmt > MX_FMT_E3M2) return MX_ERR_FORMAT;
     if (out_dtype != MX_OUT_FP32 && out_dtype != MX_OUT_BF16) return MX_ERR_OUT_DTYPE;
     // K a multiple of 128 (FlyDSL article, "API compatibility is not
     // universal input coverage").
@@ -281,6 +281,10 @@ int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, 
     const int o = out_dtype;
     if (!scaled)
         launched = launch<mx::B16, mx::B16>(plan, o, A, nullptr, B, nullptr, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E2M3)                       // checked: fmt_b is E2M3 too
+        launched = launch<mx::F6E2, mx::F6E2>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (fmt_a == MX_FMT_E3M2)                       // checked: fmt_b is E3M2 too
+        launched = launch<mx::F6E3, mx::F6E3>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E2M1 && fmt_b == MX_FMT_E2M1)
         launched = launch<mx::FP4, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
@@ -376,7 +380,11 @@ extern "C" int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t
 {
     int rc = check_args(fmt_a, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
-    if (fmt_b != MX_FMT_E2M1 && fmt_b != MX_FMT_E4M3 && fmt_b != MX_FMT_E5M2) return MX_ERR_FORMAT;
+    if (fmt_b < MX_FMT_E2M1 || fmt_b > MX_FMT_E3M2) return MX_ERR_FORMAT;
+    // FP6 pairs with the same FP6 format only.
+    const bool fp6_a = fmt_a == MX_FMT_E2M3 || fmt_a == MX_FMT_E3M2;
+    const bool fp6_b = fmt_b == MX_FMT_E2M3 || fmt_b == MX_FMT_E3M2;
+    if ((fp6_a || fp6_b) && fmt_a != fmt_b) return MX_ERR_FORMAT;
     if (split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
     mx_plan_t plan;
     if (tile_m == 0 && tile_n == 0) {
@@ -526,7 +534,8 @@ int grouped_plan(int fmt, int64_t groups, const int64_t *group_rows, int64_t N, 
     int rc = fmt == kFmtBF16 ? check_args_bf16(1, N, K, out_dtype)
                              : check_args(fmt, 1, N, K, out_dtype);   // format, output, N, K
     if (rc != MX_OK) return rc;
-    if (fmt == MX_FMT_E5M2) return MX_ERR_FORMAT;            // grouped: E2M1, E4M3 and BF16
+    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3 && fmt != kFmtBF16)
+        return MX_ERR_FORMAT;                                // grouped: E2M1, E4M3 and BF16
     if (groups < 1 || groups > MX_MAX_GROUPS || groups * N > MX_MAX_DIM) return MX_ERR_SHAPE;
     if (!group_rows || !plan) return MX_ERR_NULL;
     int64_t total = 0, maxm = 0;

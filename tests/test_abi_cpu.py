@@ -54,7 +54,7 @@ def test_strerror_covers_codes():
 
 @pytest.mark.parametrize("fmt,M,N,K,out,code", [
     (0, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
-    (4, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
+    (6, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
     (1, 16, 16, 128, 0, mxg.MX_ERR_OUT_DTYPE),
     (2, 16, 16, 128, 7, mxg.MX_ERR_OUT_DTYPE),
     (1, 0, 16, 128, 1, mxg.MX_ERR_SHAPE),
@@ -450,3 +450,28 @@ def test_grouped_mixed_argument_errors():
     assert call(2, 1, ptrs=(good, None, good, good, good)) == mxg.MX_ERR_NULL
     assert call(1, 2, ptrs=(good, good, good + 8, good, good)) == mxg.MX_ERR_ALIGN
     assert call(2, 1) == mxg.MX_ERR_NO_DEVICE or __import__("torch").cuda.device_count() > 0
+
+
+def test_fp6_accepted_where_documented():
+    L = mxg.lib()
+    good = 1 << 20
+    args = (good,) * 5
+    p = mxg.MxPlan()
+    for f in (mxg.FMT_E2M3, mxg.FMT_E3M2):
+        assert L.mx_gemm_plan(f, 64, 64, 256, 2, ctypes.byref(p)) == mxg.MX_OK
+        # FP6 pairs with the same FP6 format only
+        for g in (1, 2, 3, 4 if f == 5 else 5):
+            assert L.mx_gemm_mixed(f, g, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+            assert L.mx_gemm_mixed(g, f, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+        # not in the grouped GEMMs or the quantizer
+        assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_FORMAT
+        assert L.mx_quantize(f, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
+    # the shim derives K from 3K/4-byte rows
+    import torch
+    a = torch.zeros((4, 96), dtype=torch.uint8)
+    s = torch.zeros((4, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError):          # shapes fine (K = 128), but not on the GPU
+        mxg.mx_gemm(a, s, a, s, mxg.FMT_E2M3)
+    with pytest.raises(ValueError):          # K mismatch against a 128-byte E4M3 row
+        mxg.mx_gemm(a, s, torch.zeros((4, 128), dtype=torch.uint8), s, mxg.FMT_E2M3,
+                    fmt_b=mxg.FMT_E4M3)
