@@ -330,20 +330,24 @@ def bench_grouped(steps, warmup, fmt):
 
 
 # Other element formats, BF16 out: mixed "W4A8" (A E4M3 activations, B E2M1
-# weights) on the fused-QKV shape and the 70B down projection at batch 8,
-# E5M2 for both operands, and E4M3 x E5M2, on the fused-QKV shape.
+# weights) on the fused-QKV shape and the 70B down projection at batch 8;
+# E5M2 for both operands, E4M3 x E5M2, and the two FP6 formats on the
+# fused-QKV shape.
 MIXED_WORKLOADS = {
     "w4a8_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
     "w4a8_llama70b_down_m8": (8, 8192, 28672, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
     "mxfp8_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E5M2, mxinputs.FMT_E5M2),
     "mxfp8_e4m3_x_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2),
+    "mxfp6_e2m3_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E2M3, mxinputs.FMT_E2M3),
+    "mxfp6_e3m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E3M2, mxinputs.FMT_E3M2),
 }
 
 
 def bench_mixed(steps, warmup, name):
-    """A GEMM in another format pair (mx_gemm_mixed or E5M2 mx_gemm).  The
-    MFMA peak taken is the MXFP8 one (an 8-bit operand runs at the 8-bit
-    rate)."""
+    """A GEMM in another format pair (mx_gemm_mixed, or one format through
+    mx_gemm).  The MFMA peak taken is the MXFP8 one when an operand has 8-bit
+    elements (the instruction then runs at the 8-bit rate), else the
+    MXFP4/MXFP6 one."""
     import torch
     import microscaled_block_scaled_amd as mxg
     M, N, K, fa, fb = MIXED_WORKLOADS[name]
@@ -374,7 +378,8 @@ def bench_mixed(steps, warmup, name):
     flops = 2.0 * M * N * K
     nbytes = (M * mxinputs.row_bytes(fa, K) + N * mxinputs.row_bytes(fb, K)
               + (M + N) * (K // 32) + M * N * 2)
-    peak = PEAK_TFLOPS[mxinputs.FMT_E4M3]
+    eight_bit = {mxinputs.FMT_E4M3, mxinputs.FMT_E5M2} & {fa, fb}
+    peak = PEAK_TFLOPS[mxinputs.FMT_E4M3 if eight_bit else mxinputs.FMT_E2M1]
     p = mxg.plan(fa, M, N, K, out)
     plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
         p["variant"], p["tile_m"], p["tile_n"], p["split_k"], p["workgroups"])
@@ -390,7 +395,7 @@ def bench_mixed(steps, warmup, name):
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)
     tflops = flops * steps / wall / 1e12
-    return {"metric": "MX GEMM TFLOPS (other formats) and % of MI355X dense MXFP8 MFMA peak",
+    return {"metric": "MX GEMM TFLOPS (other formats) and % of MI355X dense MX MFMA peak",
             "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
