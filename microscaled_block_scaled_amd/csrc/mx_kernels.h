@@ -114,8 +114,18 @@ template <int RB> __device__ __forceinline__ int swz_row(int r)
 }
 // Rows per copy instruction for slab rows of RB bytes: 1024 / RB for 128-
 // and 64-byte rows (64 lanes x 16 bytes); 8 for 96-byte FP6 rows, copied by
-// lanes 0..47 (6 chunks per row), the other 16 lanes idle.
+// lanes 0..47 (6 chunks per row).  An FP6 group of 8 rows takes a 1024-byte
+// LDS block, rows 96 bytes apart and 256 bytes of padding, into which lanes
+// 48..63 copy duplicate chunks, so the copies need no branch (the K loop
+// stays one basic block).  So every format's LDS layout has 1024 bytes per
+// copy instruction, and an FP6 row takes 128 LDS bytes on average.
 template <int RB> struct copy_rows { static constexpr int value = RB == 96 ? 8 : 1024 / RB; };
+template <int RB> struct lds_pitch { static constexpr int value = RB == 96 ? 128 : RB; };
+// LDS offset of row r of an operand tile with slab rows of RB bytes.
+template <int RB> __device__ __forceinline__ int lds_row(int r)
+{
+    return RB == 96 ? (r >> 3) * 1024 + (r & 7) * 96 : r * RB;
+}
 
 template <int FA, int FB>
 __device__ __forceinline__ v16f mma(const v8i &a, const v8i &b, v16f acc, int sa, int sb)
@@ -131,18 +141,13 @@ __device__ __forceinline__ v16f mma(const v4i &a, const v4i &b, v16f acc, int, i
                                                   __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
 }
 
-// An FP6 operand fragment: 24 bytes (32 elements) from LDS, 8-byte aligned,
-// by three 8-byte reads, into the first six dwords of the MFMA operand.
+// An FP6 operand fragment: the 24 bytes (32 elements) read from LDS as three
+// 8-byte words go to the first six dwords of the MFMA operand.
 template <typename V>
-__device__ __forceinline__ V fp6_frag(const uint8_t *p)
+__device__ __forceinline__ void fp6_frag(V &v, uint2 q0, uint2 q1, uint2 q2)
 {
-    V v{};
-    if constexpr (sizeof(V) == 32) {
-        const uint2 *q = (const uint2 *)p;
-        const uint2 q0 = q[0], q1 = q[1], q2 = q[2];
+    if constexpr (sizeof(V) == 32)
         v = V{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, 0, 0};
-    }
-    return v;
 }
 
 // Direct HBM -> LDS copies (gfx950 global_load_lds): lane l of the wave
@@ -276,7 +281,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int RA = SL::template row_bytes<FA>;         // slab row bytes, A and B
     constexpr int RB = SL::template row_bytes<FB>;
     constexpr int ROWS = BM + BN;
-    constexpr int DATA = BM * RA + BN * RB;                // element bytes per slab
+    constexpr int LA = lds_pitch<RA>::value, LB = lds_pitch<RB>::value;   // LDS bytes per row
+    constexpr int DATA = BM * LA + BN * LB;                // LDS bytes per slab
     constexpr int NSI = SCALED ? (ROWS + 63) / 64 : 0;     // scale copy instructions
     constexpr int SBUF = NSI * 64 * 16;                    // one scale buffer
     constexpr int RPCA = copy_rows<RA>::value, RPCB = copy_rows<RB>::value;   // rows per copy instruction
@@ -397,15 +403,13 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPCA - 1);
             const uint32_t ch = min((RA == 128 && (i & 1)) ? ga.ch1 : ga.ch0, cmaxa);
-            if (RA != 96 || lane < 48)
-                g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * RPCA * RA);
+            g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * 1024);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
             const int i = min(wave + u * NW, BN / RPCB - 1);
             const uint32_t ch = min((RB == 128 && (i & 1)) ? gb.ch1 : gb.ch0, cmaxb);
-            if (RB != 96 || lane < 48)
-                g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * RA + i * RPCB * RB);
+            g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * LA + i * 1024);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
@@ -434,8 +438,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // swz(r) = swz(lr) (WTM and 32i are multiples of 16), so fragment i is the
     // lane's offset plus the constant 32*R*i.
     const int swla = swz_row<RA>(lr), swlb = swz_row<RB>(lr);
-    const int a_off = (wm * WTM + lr) * RA;
-    const int b_off = BM * RA + (wn * WTN + lr) * RB;
+    const int a_off = wm * WTM * LA + lds_row<RA>(lr);
+    const int b_off = BM * LA + wn * WTN * LB + lds_row<RB>(lr);
     const int sa_off = (wm * WTM + lr) * 16;
     const int sb_off = (BM + wn * WTN + lr) * 16;
 
@@ -492,10 +496,12 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // a scale byte.
     auto frag = [&](auto ia, const Src &s, int off, int soff, int f, fv &v, int &sv) {
         constexpr bool IA = decltype(ia)::value;
-        constexpr int F = IA ? FA : FB, R = IA ? RA : RB;
-        const uint8_t *rp = smem + s.data + off + f * 32 * R;
+        constexpr int F = IA ? FA : FB, L = IA ? LA : LB;     // 32 rows take 32 * L LDS bytes
+        const uint8_t *rp = smem + s.data + off + f * 32 * L;
         if constexpr (is_fp6<F>::value) {
-            v = fp6_frag<fv>(rp + (IA ? s.a0 : s.b0));
+            // three 8-byte reads (the 24 bytes are 8-byte aligned)
+            const uint8_t *q = rp + (IA ? s.a0 : s.b0);
+            fp6_frag(v, *(const uint2 *)q, *(const uint2 *)(q + 8), *(const uint2 *)(q + 16));
             sv = smem[s.scale + soff + f * 32 * 16];
             return;
         }
