@@ -114,17 +114,19 @@ template <int RB> __device__ __forceinline__ int swz_row(int r)
 }
 // Rows per copy instruction for slab rows of RB bytes: 1024 / RB for 128-
 // and 64-byte rows (64 lanes x 16 bytes); 8 for 96-byte FP6 rows, copied by
-// lanes 0..47 (6 chunks per row).  An FP6 group of 8 rows takes a 1024-byte
-// LDS block, rows 96 bytes apart and 256 bytes of padding, into which lanes
-// 48..63 copy duplicate chunks, so the copies need no branch (the K loop
-// stays one basic block).  So every format's LDS layout has 1024 bytes per
-// copy instruction, and an FP6 row takes 128 LDS bytes on average.
+// lanes 0..47 (6 chunks per row).  An FP6 group of 8 rows takes a 1040-byte
+// LDS block: the rows, 96 bytes apart, then padding into which lanes 48..63
+// copy duplicate chunks, so the copies need no branch (the K loop stays one
+// basic block).  The 16 bytes beyond 1024 shift each group's rows by 16
+// bytes of bank offset against the previous group's, so two groups read by
+// the same 16 lanes use different banks (8 rows of one group, 96 bytes
+// apart, already do).  An FP6 row takes 130 LDS bytes on average.
 template <int RB> struct copy_rows { static constexpr int value = RB == 96 ? 8 : 1024 / RB; };
-template <int RB> struct lds_pitch { static constexpr int value = RB == 96 ? 128 : RB; };
+template <int RB> struct lds_pitch { static constexpr int value = RB == 96 ? 130 : RB; };
 // LDS offset of row r of an operand tile with slab rows of RB bytes.
 template <int RB> __device__ __forceinline__ int lds_row(int r)
 {
-    return RB == 96 ? (r >> 3) * 1024 + (r & 7) * 96 : r * RB;
+    return RB == 96 ? (r >> 3) * 1040 + (r & 7) * 96 : r * RB;
 }
 
 template <int FA, int FB>
@@ -403,13 +405,13 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPCA - 1);
             const uint32_t ch = min((RA == 128 && (i & 1)) ? ga.ch1 : ga.ch0, cmaxa);
-            g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * 1024);
+            g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * RPCA * LA);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
             const int i = min(wave + u * NW, BN / RPCB - 1);
             const uint32_t ch = min((RB == 128 && (i & 1)) ? gb.ch1 : gb.ch0, cmaxb);
-            g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * LA + i * 1024);
+            g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * LA + i * RPCB * LB);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
