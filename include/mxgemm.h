@@ -1,5 +1,7 @@
 /*
- * mxgemm.h -- C ABI of the MI355X (gfx950) MX block-scaled NT GEMM.
+ * mxgemm.h -- C ABI of the MI355X (gfx950) MX block-scaled NT GEMM, its
+ * grouped (mixture-of-experts) form, MX quantization, and a dense BF16 GEMM
+ * on the same kernels.
  *
  * The operation (FlyDSL summary pages, section "API compatibility is not
  * universal input coverage"; AI-compiler digest 2026-10-22, item 1

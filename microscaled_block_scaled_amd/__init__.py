@@ -8,8 +8,10 @@ raise.
     C = mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=torch.bfloat16)
 
 a: (M, K/2) uint8 for MXFP4 (E2M1, two elements per byte, element 2i in the
-   low nibble), or (M, K) uint8 / float8_e4m3fn for MXFP8 (E4M3; or E5M2,
-   FMT_E5M2, as uint8 / float8_e5m2);
+   low nibble), (M, K) uint8 / float8_e4m3fn for MXFP8 (E4M3; or E5M2,
+   FMT_E5M2, as uint8 / float8_e5m2), or (M, 3K/4) uint8 for MXFP6 (FMT_E2M3,
+   FMT_E3M2; element k in bits 6k .. 6k+5 of the row); ``fmt_b`` gives B its
+   own format;
 b: (N, ...) likewise; a_scale: (M, K/32) uint8 E8M0; b_scale: (N, K/32).
 Returns C = A * B^T, (M, N), float32 or bfloat16.
 

@@ -1,4 +1,6 @@
-// mx_kernels.h -- gfx950 device code for the MX block-scaled NT GEMM.
+// mx_kernels.h -- gfx950 device code for the MX block-scaled NT GEMM (E2M1,
+// E4M3, E5M2 and FP6 elements, one format per operand), the same tile kernel
+// on dense BF16 operands, and the split-K reduction.
 //
 // C[m][n] = sum_b 2^(sA[m][b]+sB[n][b]-254) * sum_{j<32} A[m][32b+j]*B[n][32b+j]
 // with FP32 accumulation (the MX scaled GEMM of the FlyDSL article: E8M0 scale
