@@ -59,7 +59,8 @@ extern "C" {
  * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any of
  * E2M1, E4M3, E5M2) and mx_quantize; the FP6 formats by mx_gemm,
  * mx_gemm_tile and mx_gemm_mixed (with the same FP6 format only); the
- * grouped GEMMs take E2M1 and E4M3.
+ * grouped GEMMs take the same formats and pairs as mx_gemm and
+ * mx_gemm_mixed.
  * FP6 rows are K*3/4 bytes: a little-endian bit string with element k in
  * bits 6k .. 6k+5 (bit b is bit b % 8 of byte b / 8), four elements in
  * three bytes (OCP MX v1.0 fixes the element encoding; this packing is this
@@ -286,10 +287,11 @@ int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
 
 /*
  * mx_gemm_grouped with the weights in their own format: A (and A_scale) in
- * fmt_a, every B_g (and B_scale) in fmt_b, each MX_FMT_E2M1 or MX_FMT_E4M3
- * (E4M3 activations with E2M1 expert weights is the usual serving layout of
- * a mixture-of-experts layer; the block dot product is mx_gemm_mixed's).
- * A's rows are K or K/2 bytes as fmt_a says, B's as fmt_b says; everything
+ * fmt_a, every B_g (and B_scale) in fmt_b: the pairs mx_gemm_mixed takes
+ * (any two of E2M1, E4M3 and E5M2, or one FP6 format for both; E4M3
+ * activations with E2M1 expert weights is the usual serving layout of a
+ * mixture-of-experts layer; the block dot product is mx_gemm_mixed's).
+ * A's rows are as long as fmt_a says, B's as fmt_b says; everything
  * else as for mx_gemm_grouped, whose plan (mx_gemm_grouped_plan with fmt_a)
  * describes the launch.  With fmt_a == fmt_b it is mx_gemm_grouped.
  */

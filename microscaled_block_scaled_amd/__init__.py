@@ -394,14 +394,15 @@ def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out
     """C_g = A_g * B_g^T for consecutive row groups of a (group_rows[g] rows
     each, summing to a's row count; zeros allowed) and the G = len(group_rows)
     weights stacked in b, (G*N, K) in mx_gemm's operand layout.  ``fmt_b``
-    gives the weights their own format (E4M3 x E2M1 or the reverse).
+    gives the weights their own format (the pairs mx_gemm accepts).
     Returns (sum(group_rows), N)."""
     import torch
     if out_dtype is None:
         out_dtype = torch.bfloat16
     fmt_b = fmt if fmt_b is None else fmt_b
-    if fmt not in (FMT_E2M1, FMT_E4M3) or fmt_b not in (FMT_E2M1, FMT_E4M3):
-        raise ValueError("fmt and fmt_b must be FMT_E2M1 or FMT_E4M3")
+    fmts = (FMT_E2M1, FMT_E4M3, FMT_E5M2, FMT_E2M3, FMT_E3M2)
+    if fmt not in fmts or fmt_b not in fmts:
+        raise ValueError("fmt and fmt_b must be one of the MX element formats")
     code, tdt = _out_code(out_dtype)
     rows = [int(r) for r in group_rows]
     G = len(rows)
@@ -415,8 +416,8 @@ def mx_gemm_grouped(a, a_scale, b, b_scale, group_rows, fmt, out_dtype=None, out
     if b.shape[0] % G != 0:
         raise ValueError("b's rows are not a multiple of the group count")
     N = b.shape[0] // G
-    K = a.shape[1] * (2 if fmt == FMT_E2M1 else 1)
-    if b.shape[1] * (2 if fmt_b == FMT_E2M1 else 1) != K:
+    K = _k_of(fmt, a.shape[1])
+    if _k_of(fmt_b, b.shape[1]) != K:
         raise ValueError("a and b disagree on K")
     if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (G * N, K // 32):
         raise ValueError("scales must be (rows, K/32)")

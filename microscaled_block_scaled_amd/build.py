@@ -9,7 +9,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "mxgemm.hip")]
+# Two translation units compiled side by side, then linked.
+SOURCES = [os.path.join(CSRC, "mxgemm.hip"), os.path.join(CSRC, "mxgrouped.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
           [os.path.join(ROOT, "include", "mxgemm.h")]
 
@@ -22,18 +23,35 @@ FLAGS = [
 ]
 
 
+def _run(cmd):
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(procs, what):
+    for proc in procs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            raise RuntimeError("hipcc failed building %s" % what)
+        yield out
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    objs = [LIB + ".%d.o" % i for i in range(len(SOURCES))]
+    cmds = [[HIPCC] + [f for f in FLAGS if f != "-shared"] + ["-c", src, "-o", obj]
+            for src, obj in zip(SOURCES, objs)]
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if proc.returncode != 0:
-        sys.stderr.write(proc.stdout)
-        raise RuntimeError("hipcc failed building libmxgemm.so")
-    if verbose and proc.stdout.strip():
+        for cmd in cmds + [link]:
+            print(" ".join(cmd), flush=True)
+    outs = list(_finish([_run(c) for c in cmds], "libmxgemm.so"))
+    outs += list(_finish([_run(link)], "libmxgemm.so"))
+    for obj in objs:
+        os.remove(obj)
+    if verbose:
         # hipcc's host pass warns that it does not know the packed-fp32 feature.
-        lines = [l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l]
+        lines = [l for out in outs for l in out.splitlines() if "packed-fp32-ops" not in l]
         if lines:
             print("\n".join(lines))
     os.replace(tmp, LIB)

@@ -343,8 +343,17 @@ def test_e5m2_accepted_where_documented():
         assert L.mx_gemm_mixed(fa, fb, 16, 16, 128, *args, 2, 0, 0, 0, None) \
             == mxg.MX_ERR_NO_DEVICE, (fa, fb)
     assert L.mx_gemm_mixed(3, 4, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-    # the grouped GEMM takes E2M1 / E4M3 only; the quantizer takes E5M2 too
-    assert _grouped(3, [4], 16, 128) == mxg.MX_ERR_FORMAT
+    # the grouped GEMMs take every MX format and the pairs mx_gemm_mixed takes
+    for f in (3, 4, 5):
+        assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_NO_DEVICE, f
+    arr = (ctypes.c_int64 * 2)(4, 0)
+    for fa, fb in ((3, 2), (2, 3), (3, 1), (1, 3), (3, 3)):
+        assert L.mx_gemm_grouped_mixed(fa, fb, 2, arr, 16, 128, *args, 2, None) \
+            == mxg.MX_ERR_NO_DEVICE, (fa, fb)
+    for fa, fb in ((4, 2), (1, 5), (4, 5), (5, 4), (3, 6), (0, 1)):
+        assert L.mx_gemm_grouped_mixed(fa, fb, 2, arr, 16, 128, *args, 2, None) \
+            == mxg.MX_ERR_FORMAT, (fa, fb)
+    # the quantizer takes E5M2 too
     assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_NO_DEVICE \
         or __import__("torch").cuda.device_count() > 0
     assert L.mx_quantize(4, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
@@ -444,7 +453,7 @@ def test_grouped_mixed_argument_errors():
     L = mxg.lib()
     call = lambda fa, fb, K=128, ptrs=(good,) * 5: L.mx_gemm_grouped_mixed(
         fa, fb, 2, arr, 16, K, *ptrs, 2, None)
-    for fa, fb in ((2, 3), (3, 1), (0, 1), (2, 9), (0x100, 0x100)):
+    for fa, fb in ((2, 4), (5, 1), (0, 1), (2, 9), (0x100, 0x100)):
         assert call(fa, fb) == mxg.MX_ERR_FORMAT, (fa, fb)
     assert call(2, 1, K=96) == mxg.MX_ERR_SHAPE
     assert call(2, 1, ptrs=(good, None, good, good, good)) == mxg.MX_ERR_NULL
@@ -463,8 +472,8 @@ def test_fp6_accepted_where_documented():
         for g in (1, 2, 3, 4 if f == 5 else 5):
             assert L.mx_gemm_mixed(f, g, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
             assert L.mx_gemm_mixed(g, f, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-        # not in the grouped GEMMs or the quantizer
-        assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_FORMAT
+        # in the grouped GEMM (argument checks pass: no device here), not the quantizer
+        assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_NO_DEVICE
         assert L.mx_quantize(f, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
     # the shim derives K from 3K/4-byte rows
     import torch
