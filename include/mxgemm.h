@@ -56,11 +56,11 @@ extern "C" {
 /* Element formats: MXFP4 = E2M1; MXFP8 = E4M3, or its other OCP encoding
  * E5M2 (wider range: 2^-16 .. 57344, with infinities and NaNs); MXFP6 =
  * E2M3 (largest 7.5) or E3M2 (largest 28), no infinities or NaNs.  E5M2 is
- * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any of
- * E2M1, E4M3, E5M2) and mx_quantize; the FP6 formats by mx_gemm,
- * mx_gemm_tile and mx_gemm_mixed (with the same FP6 format only); the
- * grouped GEMMs take the same formats and pairs as mx_gemm and
- * mx_gemm_mixed.
+ * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any
+ * format) and mx_quantize; the FP6 formats by mx_gemm, mx_gemm_tile and
+ * mx_gemm_mixed (paired with any format); the grouped GEMMs take every
+ * format, any two of E2M1, E4M3 and E5M2, and an FP6 format only with
+ * itself.
  * FP6 rows are K*3/4 bytes: a little-endian bit string with element k in
  * bits 6k .. 6k+5 (bit b is bit b % 8 of byte b / 8), four elements in
  * three bytes (OCP MX v1.0 fixes the element encoding; this packing is this
@@ -204,13 +204,14 @@ int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
 
 /*
  * MX GEMM with A and B in different element formats: fmt_a for A, fmt_b for
- * B, each MX_FMT_E2M1, MX_FMT_E4M3 or MX_FMT_E5M2, in any pair (A E4M3 with
- * B E2M1 is the usual "W4A8" serving layout; E4M3 with E5M2 pairs the two
- * MXFP8 encodings).  The block dot product is the one of mx_gemm with
+ * B, each any MX_FMT_* code, in any pair (A E4M3 with B E2M1 is the usual
+ * "W4A8" serving layout; E4M3 with E5M2 pairs the two MXFP8 encodings; FP6
+ * pairs with the 4- and 8-bit formats and with the other FP6 format).  The
+ * block dot product is the one of mx_gemm with
  * each operand decoded in its own format (the OCP MX v1.0 dot product does
  * not require equal formats; the pages' "broader low precision" outlook, and
  * gfx950's scaled MFMA takes a format per operand).  A is M x K in fmt_a's
- * layout (K or K/2 bytes per row), B is N x K in fmt_b's; scales, C, the
+ * layout (K, K/2 or 3K/4 bytes per row), B is N x K in fmt_b's; scales, C, the
  * output types, alignment, errors and asynchrony as for mx_gemm.
  * tile_m = tile_n = 0 takes the plan's tile (the plan depends on M, N and K
  * only, so mx_gemm_plan describes it); otherwise (tile_m, tile_n) must be one

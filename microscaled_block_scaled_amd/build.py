@@ -9,8 +9,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Two translation units compiled side by side, then linked.
-SOURCES = [os.path.join(CSRC, "mxgemm.hip"), os.path.join(CSRC, "mxgrouped.hip")]
+# Translation units compiled side by side, then linked.
+SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "mxgrouped.hip", "mxfp6pairs.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
           [os.path.join(ROOT, "include", "mxgemm.h")]
 

@@ -1,0 +1,89 @@
+// mx_launch.h -- launches of the tile kernel for one format pair: the tile
+// shape from the plan, the split-K slices and their in-order reduction.
+// Shared by mxgemm.hip and mxfp6pairs.hip (the pairs of an FP6 format with
+// another format, compiled as a translation unit of their own).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "mxgemm.h"
+#include "mx_kernels.h"
+#include "mx_host.h"
+
+namespace mxhost {
+
+// Split-K slices are whole 512-K scale periods.
+inline constexpr int64_t kPeriodK = 512;
+
+inline int64_t slice_k(int64_t K, int split) { return cdiv(cdiv(K, split), kPeriodK) * kPeriodK; }
+
+// FP32 elements per split-K plane (a multiple of 4 keeps planes 16-byte aligned).
+inline int64_t plane_of(int64_t M, int64_t N) { return cdiv(M * N, 64) * 64; }
+
+inline bool is_fp6_fmt(int fmt) { return fmt == MX_FMT_E2M3 || fmt == MX_FMT_E3M2; }
+
+template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>
+void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
+                int64_t M, int64_t N, int64_t K, int split, float *W, hipStream_t stream)
+{
+    const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
+    const int gm = 4;
+    const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
+    if (split == 1) {
+        hipLaunchKernelGGL((mx::tile_kernel<FA, FB, OUT, BM, BN, WGM, WGN, S>), dim3(grid),
+                           dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
+                           (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, C,
+                           (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)K, (int64_t)0);
+        return;
+    }
+    const int64_t plane = plane_of(M, N);
+    hipLaunchKernelGGL((mx::tile_kernel<FA, FB, mx::OF32, BM, BN, WGM, WGN, S>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
+                       (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, (void *)W,
+                       (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)slice_k(K, split),
+                       plane);
+    hipLaunchKernelGGL((mx::splitk_reduce<OUT>), dim3((unsigned)cdiv(M * N, 1024)), dim3(256),
+                       0, stream, (const float *)W, C, M * N, plane, split);
+}
+
+template <int FA, int FB, int OUT>
+bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
+                 const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
+                 hipStream_t stream)
+{
+#define MX_CFG(BM_, BN_, WM_, WN_, S_)                                                    \
+    if (p.tile_m == BM_ && p.tile_n == BN_ && p.threads == WM_ * WN_ * 64) {             \
+        launch_cfg<FA, FB, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, M, N, K,          \
+                                                        p.split_k, W, stream);             \
+        return true;                                                                      \
+    }
+    MX_CFG(256, 256, 4, 2, 2)
+    MX_CFG(256, 192, 4, 2, 2)
+    MX_CFG(256, 160, 4, 1, 2)
+    MX_CFG(256, 128, 4, 2, 3)
+    MX_CFG(128, 128, 2, 2, 3)
+    MX_CFG(64, 256, 1, 8, 3)
+#undef MX_CFG
+    return false;
+}
+
+// Dispatch on the output type for formats (FA, FB).
+template <int FA, int FB>
+bool launch(const mx_plan_t &p, int out_dtype, const void *A, const void *As, const void *B,
+            const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
+            hipStream_t stream)
+{
+    return out_dtype == MX_OUT_FP32
+        ? launch_tile<FA, FB, mx::OF32>(p, A, As, B, Bs, C, M, N, K, W, stream)
+        : launch_tile<FA, FB, mx::OBF16>(p, A, As, B, Bs, C, M, N, K, W, stream);
+}
+
+// The tile kernel for fmt_a x fmt_b where one is an FP6 format and the pair
+// is not one FP6 format twice (defined in mxfp6pairs.hip).  W is the split-K
+// workspace of the plan.  Returns false if the plan's tile is not compiled.
+bool launch_fp6_pair(int fmt_a, int fmt_b, const mx_plan_t &p, int out_dtype, const void *A,
+                     const void *As, const void *B, const void *Bs, void *C, int64_t M,
+                     int64_t N, int64_t K, float *W, hipStream_t stream);
+
+}  // namespace mxhost

@@ -1,0 +1,36 @@
+// mxfp6pairs.hip -- the tile kernel for an FP6 format (E2M3, E3M2) paired
+// with another MX format (E2M1, E4M3, E5M2 or the other FP6 format).  Each
+// operand keeps its own slab layout and MFMA format selector; the pairs are
+// compiled here, beside mxgemm.hip, so the two build in parallel.
+#include "mx_launch.h"
+
+namespace mxhost {
+
+bool launch_fp6_pair(int fmt_a, int fmt_b, const mx_plan_t &p, int o, const void *A,
+                     const void *As, const void *B, const void *Bs, void *C, int64_t M,
+                     int64_t N, int64_t K, float *W, hipStream_t s)
+{
+#define MX_P(FA_, FB_) launch<FA_, FB_>(p, o, A, As, B, Bs, C, M, N, K, W, s)
+    if (fmt_a == MX_FMT_E2M3 || fmt_a == MX_FMT_E3M2) {
+        const bool e2 = fmt_a == MX_FMT_E2M3;
+        switch (fmt_b) {
+        case MX_FMT_E2M1: return e2 ? MX_P(mx::F6E2, mx::FP4) : MX_P(mx::F6E3, mx::FP4);
+        case MX_FMT_E4M3: return e2 ? MX_P(mx::F6E2, mx::FP8) : MX_P(mx::F6E3, mx::FP8);
+        case MX_FMT_E5M2: return e2 ? MX_P(mx::F6E2, mx::BF8) : MX_P(mx::F6E3, mx::BF8);
+        case MX_FMT_E2M3: return e2 ? false : MX_P(mx::F6E3, mx::F6E2);
+        case MX_FMT_E3M2: return e2 ? MX_P(mx::F6E2, mx::F6E3) : false;
+        default: return false;
+        }
+    }
+    const bool e2 = fmt_b == MX_FMT_E2M3;
+    if (fmt_b != MX_FMT_E2M3 && fmt_b != MX_FMT_E3M2) return false;
+    switch (fmt_a) {
+    case MX_FMT_E2M1: return e2 ? MX_P(mx::FP4, mx::F6E2) : MX_P(mx::FP4, mx::F6E3);
+    case MX_FMT_E4M3: return e2 ? MX_P(mx::FP8, mx::F6E2) : MX_P(mx::FP8, mx::F6E3);
+    case MX_FMT_E5M2: return e2 ? MX_P(mx::BF8, mx::F6E2) : MX_P(mx::BF8, mx::F6E3);
+    default: return false;
+    }
+#undef MX_P
+}
+
+}  // namespace mxhost

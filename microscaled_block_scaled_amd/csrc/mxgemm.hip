@@ -14,6 +14,7 @@
 #include "mx_kernels.h"
 #include "mx_quant.h"
 #include "mx_host.h"
+#include "mx_launch.h"
 
 using namespace mxhost;
 
@@ -27,9 +28,6 @@ namespace {
 // keeps at least kMinSliceK of K.
 constexpr int kMaxSplit = MX_MAX_SPLIT_K;
 constexpr int64_t kMinSliceK = 2048;
-constexpr int64_t kPeriodK = 512;
-
-int64_t slice_k(int64_t K, int split) { return cdiv(cdiv(K, split), kPeriodK) * kPeriodK; }
 
 // Measured on MI355X: 256-row tiles split until the grid fills the CUs once;
 // the 64-row tile (small M, B streamed from memory) is fastest at about half
@@ -41,9 +39,6 @@ int choose_split(const TileCfg &c, int64_t tiles, int64_t K)
     while (s < kMaxSplit && tiles * 2 * s <= target && K / (2 * s) >= kMinSliceK) s *= 2;
     return (int)cdiv(K, slice_k(K, s));        // slices actually needed
 }
-
-// FP32 elements per split-K plane (a multiple of 4 keeps planes 16-byte aligned).
-int64_t plane_of(int64_t M, int64_t N) { return cdiv(M * N, 64) * 64; }
 
 // Pick the tile (and split) whose grid fills whole waves of CUs best,
 // weighting away the padding in partial tiles; ties go to the larger tile
@@ -107,62 +102,6 @@ int find_tile(int tile_m, int tile_n)
 }
 
 // workspace W and the reduction kernel then produces C.
-template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>
-void launch_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
-                int64_t M, int64_t N, int64_t K, int split, float *W, hipStream_t stream)
-{
-    const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
-    const int gm = 4;
-    const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
-    if (split == 1) {
-        hipLaunchKernelGGL((mx::tile_kernel<FA, FB, OUT, BM, BN, WGM, WGN, S>), dim3(grid),
-                           dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
-                           (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, C,
-                           (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)K, (int64_t)0);
-        return;
-    }
-    const int64_t plane = plane_of(M, N);
-    hipLaunchKernelGGL((mx::tile_kernel<FA, FB, mx::OF32, BM, BN, WGM, WGN, S>), dim3(grid),
-                       dim3(WGM * WGN * 64), 0, stream, (const uint8_t *)A,
-                       (const uint8_t *)As, (const uint8_t *)B, (const uint8_t *)Bs, (void *)W,
-                       (int)M, (int)N, (int)K, tiles_m, tiles_n, gm, (int)slice_k(K, split),
-                       plane);
-    hipLaunchKernelGGL((mx::splitk_reduce<OUT>), dim3((unsigned)cdiv(M * N, 1024)), dim3(256),
-                       0, stream, (const float *)W, C, M * N, plane, split);
-}
-
-template <int FA, int FB, int OUT>
-bool launch_tile(const mx_plan_t &p, const void *A, const void *As, const void *B,
-                 const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
-                 hipStream_t stream)
-{
-#define MX_CFG(BM_, BN_, WM_, WN_, S_)                                                    \
-    if (p.tile_m == BM_ && p.tile_n == BN_ && p.threads == WM_ * WN_ * 64) {             \
-        launch_cfg<FA, FB, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, M, N, K,          \
-                                                        p.split_k, W, stream);             \
-        return true;                                                                      \
-    }
-    MX_CFG(256, 256, 4, 2, 2)
-    MX_CFG(256, 192, 4, 2, 2)
-    MX_CFG(256, 160, 4, 1, 2)
-    MX_CFG(256, 128, 4, 2, 3)
-    MX_CFG(128, 128, 2, 2, 3)
-    MX_CFG(64, 256, 1, 8, 3)
-#undef MX_CFG
-    return false;
-}
-
-// Dispatch on the output type for formats (FA, FB).
-template <int FA, int FB>
-bool launch(const mx_plan_t &p, int out_dtype, const void *A, const void *As, const void *B,
-            const void *Bs, void *C, int64_t M, int64_t N, int64_t K, float *W,
-            hipStream_t stream)
-{
-    return out_dtype == MX_OUT_FP32
-        ? launch_tile<FA, FB, mx::OF32>(p, A, As, B, Bs, C, M, N, K, W, stream)
-        : launch_tile<FA, FB, mx::OBF16>(p, A, As, B, Bs, C, M, N, K, W, stream);
-}
-
 // Split-K workspace, one per (device, stream), grown on demand with the
 // stream-ordered allocator and kept until the process exits, so repeated
 // calls do not allocate.  g_ws_mu is held from the lookup until both
@@ -216,10 +155,13 @@ int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, 
     const int o = out_dtype;
     if (!scaled)
         launched = launch<mx::B16, mx::B16>(plan, o, A, nullptr, B, nullptr, C, M, N, K, W, s);
-    else if (fmt_a == MX_FMT_E2M3)                       // checked: fmt_b is E2M3 too
+    else if (fmt_a == MX_FMT_E2M3 && fmt_b == MX_FMT_E2M3)
         launched = launch<mx::F6E2, mx::F6E2>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
-    else if (fmt_a == MX_FMT_E3M2)                       // checked: fmt_b is E3M2 too
+    else if (fmt_a == MX_FMT_E3M2 && fmt_b == MX_FMT_E3M2)
         launched = launch<mx::F6E3, mx::F6E3>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
+    else if (is_fp6_fmt(fmt_a) || is_fp6_fmt(fmt_b))     // FP6 with another format
+        launched = launch_fp6_pair(fmt_a, fmt_b, plan, o, A, A_scale, B, B_scale, C, M, N, K, W,
+                                   s);
     else if (fmt_a == MX_FMT_E2M1 && fmt_b == MX_FMT_E2M1)
         launched = launch<mx::FP4, mx::FP4>(plan, o, A, A_scale, B, B_scale, C, M, N, K, W, s);
     else if (fmt_a == MX_FMT_E4M3 && fmt_b == MX_FMT_E4M3)
@@ -315,11 +257,7 @@ extern "C" int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t
 {
     int rc = check_args(fmt_a, M, N, K, out_dtype);
     if (rc != MX_OK) return rc;
-    if (fmt_b < MX_FMT_E2M1 || fmt_b > MX_FMT_E3M2) return MX_ERR_FORMAT;
-    // FP6 pairs with the same FP6 format only.
-    const bool fp6_a = fmt_a == MX_FMT_E2M3 || fmt_a == MX_FMT_E3M2;
-    const bool fp6_b = fmt_b == MX_FMT_E2M3 || fmt_b == MX_FMT_E3M2;
-    if ((fp6_a || fp6_b) && fmt_a != fmt_b) return MX_ERR_FORMAT;
+    if (fmt_b < MX_FMT_E2M1 || fmt_b > MX_FMT_E3M2) return MX_ERR_FORMAT;   // any pair
     if (split_k < 0 || split_k > kMaxSplit) return MX_ERR_SHAPE;
     mx_plan_t plan;
     if (tile_m == 0 && tile_n == 0) {

@@ -342,8 +342,8 @@ def test_e5m2_accepted_where_documented():
     for fa, fb in ((3, 2), (2, 3), (3, 1), (1, 3)):
         assert L.mx_gemm_mixed(fa, fb, 16, 16, 128, *args, 2, 0, 0, 0, None) \
             == mxg.MX_ERR_NO_DEVICE, (fa, fb)
-    assert L.mx_gemm_mixed(3, 4, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-    # the grouped GEMMs take every MX format and the pairs mx_gemm_mixed takes
+    assert L.mx_gemm_mixed(3, 6, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
+    # the grouped GEMMs take every MX format, any pair of the 4- and 8-bit ones
     for f in (3, 4, 5):
         assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_NO_DEVICE, f
     arr = (ctypes.c_int64 * 2)(4, 0)
@@ -468,10 +468,14 @@ def test_fp6_accepted_where_documented():
     p = mxg.MxPlan()
     for f in (mxg.FMT_E2M3, mxg.FMT_E3M2):
         assert L.mx_gemm_plan(f, 64, 64, 256, 2, ctypes.byref(p)) == mxg.MX_OK
-        # FP6 pairs with the same FP6 format only
-        for g in (1, 2, 3, 4 if f == 5 else 5):
+        # FP6 pairs with every MX format (argument checks pass: no device here)
+        for g in (1, 2, 3, 4, 5):
+            assert L.mx_gemm_mixed(f, g, 16, 16, 128, *args, 2, 0, 0, 0, None) \
+                == mxg.MX_ERR_NO_DEVICE, (f, g)
+            assert L.mx_gemm_mixed(g, f, 16, 16, 128, *args, 2, 0, 0, 0, None) \
+                == mxg.MX_ERR_NO_DEVICE, (g, f)
+        for g in (0, 6):
             assert L.mx_gemm_mixed(f, g, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-            assert L.mx_gemm_mixed(g, f, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
         # in the grouped GEMM (argument checks pass: no device here), not the quantizer
         assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_NO_DEVICE
         assert L.mx_quantize(f, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
