@@ -59,8 +59,7 @@ extern "C" {
  * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any
  * format) and mx_quantize; the FP6 formats by mx_gemm, mx_gemm_tile and
  * mx_gemm_mixed (paired with any format); the grouped GEMMs take every
- * format, any two of E2M1, E4M3 and E5M2, and an FP6 format only with
- * itself.
+ * format and every pair.
  * FP6 rows are K*3/4 bytes: a little-endian bit string with element k in
  * bits 6k .. 6k+5 (bit b is bit b % 8 of byte b / 8), four elements in
  * three bytes (OCP MX v1.0 fixes the element encoding; this packing is this
@@ -289,7 +288,7 @@ int mx_gemm_grouped(int fmt, int64_t groups, const int64_t *group_rows,
 /*
  * mx_gemm_grouped with the weights in their own format: A (and A_scale) in
  * fmt_a, every B_g (and B_scale) in fmt_b: the pairs mx_gemm_mixed takes
- * (any two of E2M1, E4M3 and E5M2, or one FP6 format for both; E4M3
+ * (any two MX formats; E4M3
  * activations with E2M1 expert weights is the usual serving layout of a
  * mixture-of-experts layer; the block dot product is mx_gemm_mixed's).
  * A's rows are as long as fmt_a says, B's as fmt_b says; everything

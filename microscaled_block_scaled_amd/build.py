@@ -10,7 +10,8 @@ LIB = os.path.join(HERE, "libmxgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Translation units compiled side by side, then linked.
-SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "mxgrouped.hip", "mxfp6pairs.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "mxgrouped.hip", "mxfp6pairs.hip",
+                                               "mxgrouped_fp6.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
           [os.path.join(ROOT, "include", "mxgemm.h")]
 

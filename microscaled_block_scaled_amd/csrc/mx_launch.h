@@ -1,7 +1,8 @@
 // mx_launch.h -- launches of the tile kernel for one format pair: the tile
-// shape from the plan, the split-K slices and their in-order reduction.
-// Shared by mxgemm.hip and mxfp6pairs.hip (the pairs of an FP6 format with
-// another format, compiled as a translation unit of their own).
+// shape from the plan, the split-K slices and their in-order reduction, and
+// the grouped launches.  Shared by mxgemm.hip, mxgrouped.hip and the units
+// that hold the pairs of an FP6 format with another format (mxfp6pairs.hip,
+// mxgrouped_fp6.hip), compiled as translation units of their own.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -85,5 +86,46 @@ bool launch(const mx_plan_t &p, int out_dtype, const void *A, const void *As, co
 bool launch_fp6_pair(int fmt_a, int fmt_b, const mx_plan_t &p, int out_dtype, const void *A,
                      const void *As, const void *B, const void *Bs, void *C, int64_t M,
                      int64_t N, int64_t K, float *W, hipStream_t stream);
+
+// Grouped launches: one tile shape (kTiles[t]) for every group, the group
+// table in the kernel arguments, no K split.
+template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>
+void launch_grouped_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
+                        int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t stream)
+{
+    const int tiles_n = (int)cdiv(N, BN);
+    hipLaunchKernelGGL((mx::tile_kernel<FA, FB, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
+                       dim3((unsigned)gt.tile_start[gt.n]), dim3(WGM * WGN * 64), 0, stream,
+                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
+                       (const uint8_t *)Bs, C, 0, (int)N, (int)K, 0, tiles_n, 4, (int)K,
+                       (int64_t)0, gt);
+}
+
+template <int FA, int FB, int OUT>
+bool launch_grouped(int t, const void *A, const void *As, const void *B, const void *Bs,
+                    void *C, int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t s)
+{
+    const TileCfg &c = kTiles[t];
+#define MX_GCFG(BM_, BN_, WM_, WN_, S_)                                                   \
+    if (c.bm == BM_ && c.bn == BN_ && c.wgm == WM_ && c.wgn == WN_) {                    \
+        launch_grouped_cfg<FA, FB, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, N, K, gt, s); \
+        return true;                                                                      \
+    }
+    MX_GCFG(256, 256, 4, 2, 2)
+    MX_GCFG(256, 192, 4, 2, 2)
+    MX_GCFG(256, 160, 4, 1, 2)
+    MX_GCFG(256, 128, 4, 2, 3)
+    MX_GCFG(128, 128, 2, 2, 3)
+    MX_GCFG(64, 256, 1, 8, 3)
+#undef MX_GCFG
+    return false;
+}
+
+// The grouped tile kernel for fmt_a x fmt_b where one is an FP6 format and
+// the pair is not one FP6 format twice (defined in mxgrouped_fp6.hip).
+// Returns false if tile t is not compiled.
+bool launch_grouped_fp6_pair(int fmt_a, int fmt_b, int t, bool f32, const void *A,
+                             const void *As, const void *B, const void *Bs, void *C, int64_t N,
+                             int64_t K, const mx::GroupTable &gt, hipStream_t stream);
 
 }  // namespace mxhost

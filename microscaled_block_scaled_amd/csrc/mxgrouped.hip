@@ -10,6 +10,7 @@
 #include "mxgemm.h"
 #include "mx_kernels.h"
 #include "mx_host.h"
+#include "mx_launch.h"
 
 using namespace mxhost;
 
@@ -38,38 +39,6 @@ int choose_tile_grouped(const int64_t *rows, int64_t groups, int64_t N, int64_t 
         if (eff > best_eff + 1e-9) { best_eff = eff; best = t; }
     }
     return best;
-}
-
-template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>
-void launch_grouped_cfg(const void *A, const void *As, const void *B, const void *Bs, void *C,
-                        int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t stream)
-{
-    const int tiles_n = (int)cdiv(N, BN);
-    hipLaunchKernelGGL((mx::tile_kernel<FA, FB, OUT, BM, BN, WGM, WGN, S, mx::GroupTable>),
-                       dim3((unsigned)gt.tile_start[gt.n]), dim3(WGM * WGN * 64), 0, stream,
-                       (const uint8_t *)A, (const uint8_t *)As, (const uint8_t *)B,
-                       (const uint8_t *)Bs, C, 0, (int)N, (int)K, 0, tiles_n, 4, (int)K,
-                       (int64_t)0, gt);
-}
-
-template <int FA, int FB, int OUT>
-bool launch_grouped(int t, const void *A, const void *As, const void *B, const void *Bs,
-                    void *C, int64_t N, int64_t K, const mx::GroupTable &gt, hipStream_t s)
-{
-    const TileCfg &c = kTiles[t];
-#define MX_GCFG(BM_, BN_, WM_, WN_, S_)                                                   \
-    if (c.bm == BM_ && c.bn == BN_ && c.wgm == WM_ && c.wgn == WN_) {                    \
-        launch_grouped_cfg<FA, FB, OUT, BM_, BN_, WM_, WN_, S_>(A, As, B, Bs, C, N, K, gt, s); \
-        return true;                                                                      \
-    }
-    MX_GCFG(256, 256, 4, 2, 2)
-    MX_GCFG(256, 192, 4, 2, 2)
-    MX_GCFG(256, 160, 4, 1, 2)
-    MX_GCFG(256, 128, 4, 2, 3)
-    MX_GCFG(128, 128, 2, 2, 3)
-    MX_GCFG(64, 256, 1, 8, 3)
-#undef MX_GCFG
-    return false;
 }
 
 }  // namespace
@@ -129,8 +98,7 @@ extern "C" int mx_gemm_grouped_plan(int fmt, int64_t groups, const int64_t *grou
 
 namespace {
 
-// Grouped GEMM with A in fmt and B in fmt_b: any pair of MX_FMT_E2M1,
-// MX_FMT_E4M3 and MX_FMT_E5M2, both operands in the same FP6 format, or
+// Grouped GEMM with A in fmt and B in fmt_b: any pair of MX formats, or
 // fmt = fmt_b = kFmtBF16 with no scale arrays.
 int run_grouped(int fmt, int fmt_b, int64_t groups, const int64_t *group_rows, int64_t N,
                 int64_t K, const void *A, const void *A_scale, const void *B,
@@ -144,8 +112,7 @@ int run_grouped(int fmt, int fmt_b, int64_t groups, const int64_t *group_rows, i
     const bool fp6a = fmt == MX_FMT_E2M3 || fmt == MX_FMT_E3M2;
     const bool fp6b = fmt_b == MX_FMT_E2M3 || fmt_b == MX_FMT_E3M2;
     if ((fmt == kFmtBF16) != (fmt_b == kFmtBF16) ||
-        (fmt_b != kFmtBF16 && check_args(fmt_b, 1, N, K, out_dtype) != MX_OK) ||
-        ((fp6a || fp6b) && fmt != fmt_b))
+        (fmt_b != kFmtBF16 && check_args(fmt_b, 1, N, K, out_dtype) != MX_OK))
         return MX_ERR_FORMAT;
     if (plan.workgroups == 0) return MX_OK;                 // no rows: nothing to compute
     const bool scaled = fmt != kFmtBF16;
@@ -165,10 +132,13 @@ int run_grouped(int fmt, int fmt_b, int64_t groups, const int64_t *group_rows, i
          : launch_grouped<FA_, FB_, mx::OBF16>(t, A, A_scale, B, B_scale, C, N, K, gt, s))
     if (fmt == kFmtBF16)
         launched = MX_GRUN(mx::B16, mx::B16);
-    else if (fmt == MX_FMT_E2M3)
+    else if (fmt == MX_FMT_E2M3 && fmt_b == MX_FMT_E2M3)
         launched = MX_GRUN(mx::F6E2, mx::F6E2);
-    else if (fmt == MX_FMT_E3M2)
+    else if (fmt == MX_FMT_E3M2 && fmt_b == MX_FMT_E3M2)
         launched = MX_GRUN(mx::F6E3, mx::F6E3);
+    else if (fp6a || fp6b)                                         // FP6 with another format
+        launched = launch_grouped_fp6_pair(fmt, fmt_b, t, f32, A, A_scale, B, B_scale, C, N, K,
+                                           gt, s);
     else if (fmt == MX_FMT_E2M1)
         launched = fmt_b == MX_FMT_E2M1 ? MX_GRUN(mx::FP4, mx::FP4)
                  : fmt_b == MX_FMT_E4M3 ? MX_GRUN(mx::FP4, mx::FP8)

@@ -343,14 +343,14 @@ def test_e5m2_accepted_where_documented():
         assert L.mx_gemm_mixed(fa, fb, 16, 16, 128, *args, 2, 0, 0, 0, None) \
             == mxg.MX_ERR_NO_DEVICE, (fa, fb)
     assert L.mx_gemm_mixed(3, 6, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-    # the grouped GEMMs take every MX format, any pair of the 4- and 8-bit ones
+    # the grouped GEMMs take every MX format and every pair of them
     for f in (3, 4, 5):
         assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_NO_DEVICE, f
     arr = (ctypes.c_int64 * 2)(4, 0)
-    for fa, fb in ((3, 2), (2, 3), (3, 1), (1, 3), (3, 3)):
+    for fa, fb in ((3, 2), (2, 3), (3, 1), (1, 3), (3, 3), (4, 2), (1, 5), (4, 5), (5, 4)):
         assert L.mx_gemm_grouped_mixed(fa, fb, 2, arr, 16, 128, *args, 2, None) \
             == mxg.MX_ERR_NO_DEVICE, (fa, fb)
-    for fa, fb in ((4, 2), (1, 5), (4, 5), (5, 4), (3, 6), (0, 1)):
+    for fa, fb in ((3, 6), (0, 1), (6, 4)):
         assert L.mx_gemm_grouped_mixed(fa, fb, 2, arr, 16, 128, *args, 2, None) \
             == mxg.MX_ERR_FORMAT, (fa, fb)
     # the quantizer takes E5M2 too
@@ -453,7 +453,7 @@ def test_grouped_mixed_argument_errors():
     L = mxg.lib()
     call = lambda fa, fb, K=128, ptrs=(good,) * 5: L.mx_gemm_grouped_mixed(
         fa, fb, 2, arr, 16, K, *ptrs, 2, None)
-    for fa, fb in ((2, 4), (5, 1), (0, 1), (2, 9), (0x100, 0x100)):
+    for fa, fb in ((2, 6), (6, 1), (0, 1), (2, 9), (0x100, 0x100)):
         assert call(fa, fb) == mxg.MX_ERR_FORMAT, (fa, fb)
     assert call(2, 1, K=96) == mxg.MX_ERR_SHAPE
     assert call(2, 1, ptrs=(good, None, good, good, good)) == mxg.MX_ERR_NULL

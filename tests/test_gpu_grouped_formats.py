@@ -1,6 +1,7 @@
 """GPU parity of the grouped MX GEMM in the formats beyond E2M1 / E4M3: E5M2
 with itself and paired with E4M3 or E2M1 either way round, and each FP6
-format (E2M3, E3M2) with itself, against the oracle's grouped GEMM, through
+format (E2M3, E3M2) with itself, the other FP6 format, E2M1, E4M3 or E5M2
+either way round, against the oracle's grouped GEMM, through
 the C ABI: uneven, empty and single-row groups, ragged N and K, both output
 types, a full-size expert layer on sampled rows, and one group equal bit for
 bit to the dense GEMM on the same tile.
@@ -20,8 +21,10 @@ pytestmark = pytest.mark.gpu
 E2M1, E4M3, E5M2 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2
 E2M3, E3M2 = mxinputs.FMT_E2M3, mxinputs.FMT_E3M2
 F32, BF16 = mxinputs.OUT_FP32, mxinputs.OUT_BF16
-PAIRS = [(E5M2, E5M2), (E4M3, E5M2), (E5M2, E4M3), (E2M1, E5M2), (E5M2, E2M1),
-         (E2M3, E2M3), (E3M2, E3M2)]
+PAIRS = ([(E5M2, E5M2), (E4M3, E5M2), (E5M2, E4M3), (E2M1, E5M2), (E5M2, E2M1),
+          (E2M3, E2M3), (E3M2, E3M2), (E2M3, E3M2), (E3M2, E2M3)] +
+         [(f6, g) for f6 in (E2M3, E3M2) for g in (E2M1, E4M3, E5M2)] +
+         [(g, f6) for f6 in (E2M3, E3M2) for g in (E2M1, E4M3, E5M2)])
 PAIR_IDS = ["%s_x_%s" % (mxinputs.fmt_name(a), mxinputs.fmt_name(b)) for a, b in PAIRS]
 EXPERT_ROWS = [704, 320, 512, 896, 128, 640, 448, 448]
 
