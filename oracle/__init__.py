@@ -261,12 +261,13 @@ class Oracle:
     def quantize(self, fmt, X):
         """MX-quantize X (rows x K, values exactly representable in float64,
         K a multiple of 32) -> (codes, scales) uint8 arrays: codes rows x K
-        (E4M3, E5M2) or rows x K/2 (E2M1), scales rows x K/32."""
+        (E4M3, E5M2), rows x K/2 (E2M1) or rows x 3K/4 (E2M3, E3M2), scales
+        rows x K/32."""
         X = np.ascontiguousarray(X, dtype=np.float64)
         if X.ndim != 2 or X.shape[1] % 32:
             raise ValueError("X must be 2-D with a multiple of 32 columns")
         rows, K = X.shape
-        Q = np.zeros((rows, K // 2 if fmt == FMT_E2M1 else K), np.uint8)
+        Q = np.zeros((rows, _row_bytes(fmt, K)), np.uint8)
         S = np.zeros((rows, K // 32), np.uint8)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         rc = self.lib.mxo_quantize(int(fmt), rows, K, X.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),

@@ -348,11 +348,12 @@ int mxo_gemm(int fmt, int64_t M, int64_t N, int64_t K,
  * per block of 32 consecutive values x_j along K,
  *   amax = max_j |x_j|
  *   X    = floor(log2 amax) - emax   (emax: exponent of the element format's
- *                                     largest normal, 2 for E2M1, 8 for E4M3)
+ *                                     largest normal: 2 for E2M1 and E2M3,
+ *                                     8 for E4M3, 15 for E5M2, 4 for E3M2)
  *   s    = X + 127 clamped to [0, 254]   (the E8M0 byte; s = 0 if amax = 0)
  *   P_j  = x_j * 2^(127 - s) rounded to the nearest element value, ties to
  *          the even code (even last mantissa bit), magnitudes above the
- *          format's largest (6, 448) saturating to it; the sign bit is x_j's
+ *          format's largest (6, 448, 57344, 7.5, 28) saturating to it; the sign bit is x_j's
  *          sign, also when the magnitude rounds to zero.
  * A block holding a NaN or an infinity gets s = 255 (E8M0 NaN) and every
  * element code 0.
@@ -380,20 +381,27 @@ static unsigned encode_magnitude(double a, int man, int bias, double maxv)
 
 /* Quantize X (rows x K doubles, each an exact FP32 or BF16 value; K a
  * multiple of 32) to Q (rows x K bytes for E4M3 / E5M2, rows x K/2 for E2M1, element
- * 2i in the low nibble) and S (rows x K/32 E8M0 bytes).  Returns 0, or -1 on
+ * 2i in the low nibble, rows x 3K/4 for E2M3 / E3M2, element k at bits
+ * 6k .. 6k+5) and S (rows x K/32 E8M0 bytes).  Returns 0, or -1 on
  * an argument the rule does not cover. */
 int mxo_quantize(int fmt, int64_t rows, int64_t K, const double *X, uint8_t *Q, uint8_t *S)
 {
-    if (fmt != MXO_FMT_E2M1 && fmt != MXO_FMT_E4M3 && fmt != MXO_FMT_E5M2) return -1;
+    if (fmt < MXO_FMT_E2M1 || fmt > MXO_FMT_E3M2) return -1;
     if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
-    /* emax = exponent of the largest normal value: 6 = 1.5 * 2^2,
-     * 448 = 1.75 * 2^8, 57344 = 1.75 * 2^15. */
-    const int e2m1 = fmt == MXO_FMT_E2M1, e5m2 = fmt == MXO_FMT_E5M2;
-    const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;
-    const int man = e2m1 ? 1 : e5m2 ? 2 : 3;
-    const int bias = e2m1 ? 1 : e5m2 ? 15 : 7;
-    const double maxv = e2m1 ? 6.0 : e5m2 ? 57344.0 : 448.0;
-    const unsigned sign_bit = e2m1 ? 8u : 128u;
+    /* Per format (OCP MX v1.0 element formats): emax = exponent of the
+     * largest normal value (6 = 1.5 * 2^2, 448 = 1.75 * 2^8, 57344 =
+     * 1.75 * 2^15, 7.5 = 1.875 * 2^2, 28 = 1.75 * 2^4), mantissa bits,
+     * exponent bias, largest magnitude and the sign bit of a code. */
+    static const int emax_of[6] = {0, 2, 8, 15, 2, 4};
+    static const int man_of[6] = {0, 1, 3, 2, 3, 2};
+    static const int bias_of[6] = {0, 1, 7, 15, 1, 3};
+    static const double maxv_of[6] = {0, 6.0, 448.0, 57344.0, 7.5, 28.0};
+    static const unsigned sign_of[6] = {0, 8u, 128u, 128u, 32u, 32u};
+    const int e2m1 = fmt == MXO_FMT_E2M1;
+    const int fp6 = fmt == MXO_FMT_E2M3 || fmt == MXO_FMT_E3M2;
+    const int emax = emax_of[fmt], man = man_of[fmt], bias = bias_of[fmt];
+    const double maxv = maxv_of[fmt];
+    const unsigned sign_bit = sign_of[fmt];
     const int64_t nb = K / 32, rb = row_bytes(fmt, K);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
@@ -424,7 +432,16 @@ int mxo_quantize(int fmt, int64_t rows, int64_t K, const double *X, uint8_t *Q, 
                     if (signbit(x[j])) code |= sign_bit;
                 }
                 const int64_t k = 32 * b + j;
-                if (!e2m1) {
+                if (fp6) {
+                    /* element k is bits 6k .. 6k+5 of the row's little-endian
+                     * bit string: set each bit on its own */
+                    for (int i = 0; i < 6; ++i) {
+                        const int64_t bit = 6 * k + i;
+                        uint8_t *byte = &Q[r * rb + (bit >> 3)];
+                        const uint8_t m = (uint8_t)(1u << (bit & 7));
+                        *byte = (uint8_t)(((code >> i) & 1u) ? (*byte | m) : (*byte & ~m));
+                    }
+                } else if (!e2m1) {
                     Q[r * rb + k] = (uint8_t)code;
                 } else {
                     uint8_t *byte = &Q[r * rb + (k >> 1)];

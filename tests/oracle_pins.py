@@ -468,6 +468,38 @@ def pin_quantize_e2m1_bruteforce(orc):
         assert c == want, "E2M1 code for %r: got %d want %d" % (x, c, want)
 
 
+def pin_quantize_fp6_bruteforce(orc):
+    """FP6 elements (E2M3, E3M2): with amax equal to the format's largest
+    value (7.5, 28) the shared exponent is 0, so each code must be the
+    nearest value of the OCP list (tests/golden), ties to the code with an
+    even last bit, sign from the value, unpacked by the input generator's
+    own FP6 unpacking.  Above the largest value within the top binade the
+    code saturates, and the scale byte follows emax 2 / 4."""
+    for fmt, maxv, top in ((E2M3, 7.5, 7.9), (E3M2, 28.0, 31.5)):
+        g = golden_fp6(fmt)
+        mags = g[:32]
+        vals = _sweep_values(maxv, [abs(x) for x in mags])
+        X = _blocks_with_amax(vals, maxv)
+        Q, S = orc.quantize(fmt, X)
+        assert Q.shape == (1, X.shape[1] // 4 * 3)
+        assert (S == 127).all(), "fmt %d scale byte for amax %g must be 127" % (fmt, maxv)
+        codes = mxinputs.unpack_fp6(Q)[0]
+        for x, c in zip(X[0], codes):
+            d = np.abs(mags - abs(x))
+            best = np.flatnonzero(d == d.min())
+            want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            want |= 32 if np.signbit(x) else 0
+            assert c == want, "fmt %d code for %r: got %d want %d" % (fmt, x, c, want)
+        # saturation in the top binade, both signs
+        X = _blocks_with_amax(np.array([top, (maxv + top) / 2, -top]), top)
+        Q, S = orc.quantize(fmt, X)
+        assert S[0, 0] == 127, S[0, 0]
+        assert list(mxinputs.unpack_fp6(Q)[0][:4]) == [31, 31, 31, 63]
+        # emax: amax 1.0 gives byte 127 - emax
+        X = _blocks_with_amax(np.array([0.25]), 1.0)
+        assert orc.quantize(fmt, X)[1][0, 0] == 127 - (2 if fmt == E2M3 else 4)
+
+
 def pin_quantize_scale_rule(orc):
     """Scale bytes: floor(log2 amax) from Python's frexp, minus emax, plus
     127, clamped to [0, 254]; 0 for an all-zero block.  amax ranges over
@@ -784,7 +816,7 @@ ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_bruteforce, pin_integer_exact, pin_scale_shift, pin_numpy_matmul,
             pin_symmetry, pin_zero_and_onehot, pin_nan, pin_row_subset,
             pin_group_bound, pin_quantize_e4m3_vs_torch, pin_quantize_e5m2_vs_torch,
-            pin_quantize_e2m1_bruteforce,
+            pin_quantize_e2m1_bruteforce, pin_quantize_fp6_bruteforce,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
             pin_grouped, pin_mixed_formats, pin_e5m2, pin_e5m2_pairs, pin_fp6, pin_bf16,
             pin_grouped_bf16]

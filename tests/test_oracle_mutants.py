@@ -55,10 +55,8 @@ MUTANTS = [
     ("e5m2_subnormal", "ldexp((double)m / 4.0, -14)", "ldexp((double)m / 4.0, -15)"),
     ("e5m2_inf_as_nan", "mag = (m == 0) ? INFINITY : NAN;", "mag = NAN;"),
     ("e5m2_double_sums", "if (exact128) block_exact(", "if (0) block_exact("),
-    ("e5m2_quant_emax", "const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;",
-     "const int emax = e2m1 ? 2 : e5m2 ? 14 : 8;"),
-    ("e5m2_quant_bias", "const int bias = e2m1 ? 1 : e5m2 ? 15 : 7;",
-     "const int bias = e2m1 ? 1 : e5m2 ? 16 : 7;"),
+    ("e5m2_quant_emax", "emax_of[6] = {0, 2, 8, 15, 2, 4};", "emax_of[6] = {0, 2, 8, 14, 2, 4};"),
+    ("e5m2_quant_bias", "bias_of[6] = {0, 1, 7, 15, 1, 3};", "bias_of[6] = {0, 1, 7, 16, 1, 3};"),
     ("e5m2_pair_double_sums", "const int exact128 = fmt_a == MXO_FMT_E5M2 || fmt_b == MXO_FMT_E5M2;",
      "const int exact128 = fmt_a == MXO_FMT_E5M2 && fmt_b == MXO_FMT_E5M2;"),
     # BF16 GEMM.
@@ -74,8 +72,12 @@ MUTANTS = [
     ("fp6_bit_offset", "const int64_t bit = 6 * k;", "const int64_t bit = 6 * (k ^ 1);"),
     ("fp6_high_byte_dropped", "if ((bit & 7) > 2) v |=", "if ((bit & 7) > 4) v |="),
     # The quantizer.
-    ("q_e4m3_emax", "const int emax = e2m1 ? 2 : e5m2 ? 15 : 8;",
-     "const int emax = e2m1 ? 2 : e5m2 ? 15 : 7;"),
+    ("q_e4m3_emax", "emax_of[6] = {0, 2, 8, 15, 2, 4};", "emax_of[6] = {0, 2, 7, 15, 2, 4};"),
+    ("q_e3m2_emax", "emax_of[6] = {0, 2, 8, 15, 2, 4};", "emax_of[6] = {0, 2, 8, 15, 2, 3};"),
+    ("q_e2m3_bias", "bias_of[6] = {0, 1, 7, 15, 1, 3};", "bias_of[6] = {0, 1, 7, 15, 2, 3};"),
+    ("q_e3m2_max", "maxv_of[6] = {0, 6.0, 448.0, 57344.0, 7.5, 28.0};",
+     "maxv_of[6] = {0, 6.0, 448.0, 57344.0, 7.5, 24.0};"),
+    ("q_fp6_bit_order", "const int64_t bit = 6 * k + i;", "const int64_t bit = 6 * k + 5 - i;"),
     ("q_ties_away", "nearbyint(a / quantum)", "round(a / quantum)"),
     ("q_no_saturation", "if (a > maxv) a = maxv;", ""),
     ("q_negative_zero", "if (signbit(x[j])) code |= sign_bit;",
