@@ -56,10 +56,8 @@ extern "C" {
 /* Element formats: MXFP4 = E2M1; MXFP8 = E4M3, or its other OCP encoding
  * E5M2 (wider range: 2^-16 .. 57344, with infinities and NaNs); MXFP6 =
  * E2M3 (largest 7.5) or E3M2 (largest 28), no infinities or NaNs.  E5M2 is
- * accepted by mx_gemm, mx_gemm_tile, mx_gemm_mixed (paired with any
- * format) and mx_quantize; the FP6 formats by mx_gemm, mx_gemm_tile and
- * mx_gemm_mixed (paired with any format); the grouped GEMMs take every
- * format and every pair.
+ * accepted, like the FP6 formats, by mx_gemm, mx_gemm_tile, mx_gemm_mixed
+ * (paired with any format), the grouped GEMMs (any pair) and mx_quantize.
  * FP6 rows are K*3/4 bytes: a little-endian bit string with element k in
  * bits 6k .. 6k+5 (bit b is bit b % 8 of byte b / 8), four elements in
  * three bytes (OCP MX v1.0 fixes the element encoding; this packing is this
@@ -180,19 +178,21 @@ int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
  * already in this form, section "Performance numbers need their
  * baselines"); per block of 32 consecutive values x along K:
  *   X = floor(log2 max|x|) - emax      (emax = 2 for E2M1, 8 for E4M3,
- *                                       15 for E5M2)
+ *                                       15 for E5M2, 2 for E2M3, 4 for E3M2)
  *   scale byte = X + 127, clamped to [0, 254]; 0 for an all-zero block
  *   element    = x * 2^(127 - scale byte) rounded to the nearest element
  *                value (ties to the code with an even last bit), magnitudes
- *                above 6 (E2M1) / 448 (E4M3) / 57344 (E5M2) saturating,
+ *                above 6 (E2M1) / 448 (E4M3) / 57344 (E5M2) / 7.5 (E2M3) /
+ *                28 (E3M2) saturating,
  *                sign kept
  *   a block holding a NaN or an infinity: scale byte 255, element codes 0.
- *   fmt        MX_FMT_E2M1, MX_FMT_E4M3 or MX_FMT_E5M2
+ *   fmt        any MX_FMT_* code
  *   in_dtype   MX_IN_FP32 or MX_IN_BF16
  *   rows, K    rows >= 1, K >= 32, K % 32 == 0, both <= MX_MAX_DIM
  *   X          device pointer, 16-byte aligned
  *   Q          device pointer, 8-byte aligned: rows x K bytes (E4M3, E5M2)
  *              or rows x K/2 bytes (E2M1, element 2i in the low nibble)
+ *              or rows x 3K/4 bytes (E2M3, E3M2, the FP6 bit string)
  *   Q_scale    device pointer: rows x K/32 bytes
  *   stream     hipStream_t, or NULL
  * Returns MX_OK or a negative MX_ERR_* code; errors and asynchrony as for

@@ -336,7 +336,8 @@ def quantize_ptr(fmt, in_dtype, rows, K, X, Q, Q_scale, stream=0):
 def mx_quantize(x, fmt, stream=None):
     """MX-quantize x (rows x K float32 or bfloat16 on the GPU, K a multiple of
     32) -> (q, q_scale) uint8 tensors in mx_gemm's operand layout: q is
-    rows x K (E4M3) or rows x K/2 (E2M1), q_scale rows x K/32."""
+    rows x K (E4M3, E5M2), rows x K/2 (E2M1) or rows x 3K/4 (E2M3, E3M2),
+    q_scale rows x K/32."""
     import torch
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D torch.Tensor")
@@ -348,10 +349,11 @@ def mx_quantize(x, fmt, stream=None):
         raise ValueError("x must be float32 or bfloat16")
     if not x.is_contiguous() or not x.is_cuda:
         raise ValueError("x must be a contiguous GPU tensor")
-    if fmt not in (FMT_E2M1, FMT_E4M3, FMT_E5M2):
-        raise ValueError("fmt must be FMT_E2M1, FMT_E4M3 or FMT_E5M2")
+    if fmt not in (FMT_E2M1, FMT_E4M3, FMT_E5M2, FMT_E2M3, FMT_E3M2):
+        raise ValueError("fmt must be one of the MX element formats")
     rows, K = x.shape
-    q = torch.empty((rows, K // 2 if fmt == FMT_E2M1 else K), dtype=torch.uint8, device=x.device)
+    rb = K // 2 if fmt == FMT_E2M1 else K // 4 * 3 if fmt in (FMT_E2M3, FMT_E3M2) else K
+    q = torch.empty((rows, rb), dtype=torch.uint8, device=x.device)
     qs = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream

@@ -13,6 +13,7 @@
 #include "mxgemm.h"
 #include "mx_kernels.h"
 #include "mx_quant.h"
+#include "mx_quant6.h"
 #include "mx_host.h"
 #include "mx_launch.h"
 
@@ -304,7 +305,7 @@ extern "C" int mx_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, cons
 extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
                            const void *X, void *Q, void *Q_scale, void *stream)
 {
-    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3 && fmt != MX_FMT_E5M2) return MX_ERR_FORMAT;
+    if (fmt < MX_FMT_E2M1 || fmt > MX_FMT_E3M2) return MX_ERR_FORMAT;
     if (in_dtype != MX_IN_FP32 && in_dtype != MX_IN_BF16) return MX_ERR_IN_DTYPE;
     if (rows < 1 || K < 32 || K % 32 != 0 || rows > MX_MAX_DIM || K > MX_MAX_DIM)
         return MX_ERR_SHAPE;
@@ -330,11 +331,21 @@ extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
             hipLaunchKernelGGL((mx::quantize_kernel<mx::FP8, mx::IN_F32>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
         else
             hipLaunchKernelGGL((mx::quantize_kernel<mx::FP8, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
-    } else {
+    } else if (fmt == MX_FMT_E5M2) {
         if (in_dtype == MX_IN_FP32)
             hipLaunchKernelGGL((mx::quantize_kernel<mx::BF8, mx::IN_F32>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
         else
             hipLaunchKernelGGL((mx::quantize_kernel<mx::BF8, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+    } else if (fmt == MX_FMT_E2M3) {
+        if (in_dtype == MX_IN_FP32)
+            hipLaunchKernelGGL((mx::quantize6_kernel<mx::F6E2, mx::IN_F32>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+        else
+            hipLaunchKernelGGL((mx::quantize6_kernel<mx::F6E2, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+    } else {
+        if (in_dtype == MX_IN_FP32)
+            hipLaunchKernelGGL((mx::quantize6_kernel<mx::F6E3, mx::IN_F32>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
+        else
+            hipLaunchKernelGGL((mx::quantize6_kernel<mx::F6E3, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
     }
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }

@@ -196,7 +196,7 @@ def test_python_shim_rejects_bad_tensors():
 
 
 @pytest.mark.parametrize("fmt,ind,rows,K,code", [
-    (4, 1, 4, 64, mxg.MX_ERR_FORMAT),
+    (6, 1, 4, 64, mxg.MX_ERR_FORMAT),
     (1, 3, 4, 64, mxg.MX_ERR_IN_DTYPE),
     (2, 0, 4, 64, mxg.MX_ERR_IN_DTYPE),
     (1, 1, 0, 64, mxg.MX_ERR_SHAPE),
@@ -356,7 +356,7 @@ def test_e5m2_accepted_where_documented():
     # the quantizer takes E5M2 too
     assert L.mx_quantize(3, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_NO_DEVICE \
         or __import__("torch").cuda.device_count() > 0
-    assert L.mx_quantize(4, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
+    assert L.mx_quantize(6, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
 
 
 def test_bf16_argument_errors():
@@ -476,9 +476,9 @@ def test_fp6_accepted_where_documented():
                 == mxg.MX_ERR_NO_DEVICE, (g, f)
         for g in (0, 6):
             assert L.mx_gemm_mixed(f, g, 16, 16, 128, *args, 2, 0, 0, 0, None) == mxg.MX_ERR_FORMAT
-        # in the grouped GEMM (argument checks pass: no device here), not the quantizer
+        # in the grouped GEMM and the quantizer (argument checks pass: no device here)
         assert _grouped(f, [4], 16, 128) == mxg.MX_ERR_NO_DEVICE
-        assert L.mx_quantize(f, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_FORMAT
+        assert L.mx_quantize(f, 1, 4, 64, good, good, good, None) == mxg.MX_ERR_NO_DEVICE
     # the shim derives K from 3K/4-byte rows
     import torch
     a = torch.zeros((4, 96), dtype=torch.uint8)

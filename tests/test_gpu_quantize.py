@@ -11,7 +11,9 @@ from gpu_util import log
 pytestmark = pytest.mark.gpu
 
 E2M1, E4M3, E5M2 = mxinputs.FMT_E2M1, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2
-FMTS, FMT_IDS = [E2M1, E4M3, E5M2], ["e2m1", "e4m3", "e5m2"]
+E2M3, E3M2 = mxinputs.FMT_E2M3, mxinputs.FMT_E3M2
+FMTS = [E2M1, E4M3, E5M2, E2M3, E3M2]
+FMT_IDS = ["e2m1", "e4m3", "e5m2", "e2m3", "e3m2"]
 
 
 def _gpu(x, fmt):
@@ -61,8 +63,10 @@ def test_quantize_edge_values(fmt, dtype):
     with either sign, FP32 and BF16 subnormal and huge block maxima, and
     blocks holding a NaN or an infinity."""
     import torch
-    top = {E2M1: 6.0, E4M3: 448.0, E5M2: 57344.0}[fmt]
-    if fmt == E2M1:
+    top = {E2M1: 6.0, E4M3: 448.0, E5M2: 57344.0, E2M3: 7.5, E3M2: 28.0}[fmt]
+    if fmt in (E2M3, E3M2):                 # the 32 FP6 magnitudes by code
+        grid = np.asarray(mxinputs._fp6_magnitudes(fmt), np.float64)
+    elif fmt == E2M1:
         grid = oracle.tables()[0][:8]
     elif fmt == E4M3:
         grid = np.abs(oracle.tables()[1][:127])
@@ -92,11 +96,15 @@ def test_quantize_edge_values(fmt, dtype):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_quantize_full_size(fmt):
-    """The 8B-Llama fused-QKV operands (2048 + 6144 rows, K = 4096) from FP32."""
+    """The 8B-Llama fused-QKV operands (2048 + 6144 rows, K = 4096) from FP32.
+    The FP6 formats store 3 (FP32 input) or 6 (BF16 input) bytes per lane;
+    both are run here at full size."""
     import torch
     x = _random(8192, 4096, 99 + fmt, torch.float32)
     log("quantize full size fmt=%d" % fmt)
     _check(x, fmt, "full size")
+    if fmt in (E2M3, E3M2):
+        _check(x.to(torch.bfloat16), fmt, "full size bf16")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
@@ -112,5 +120,11 @@ def test_quantize_then_gemm(fmt):
     torch.cuda.synchronize()
     case = dict(fmt=fmt, M=300, N=200, K=1024, A=qa.cpu().numpy(), A_scale=sa.cpu().numpy(),
                 B=qb.cpu().numpy(), B_scale=sb.cpu().numpy())
-    res, *_ = check_against_oracle(case, mxinputs.OUT_FP32, C=C)
+    if fmt in (E2M3, E3M2):
+        # FP6: judged with the oracle's group term E, as the FP6 GEMM tests do
+        Cref, T, E = oracle.gemm(fmt, case["A"], case["A_scale"], case["B"], case["B_scale"],
+                                 1024, group_bound=True)
+        res = oracle.compare(C.double().cpu().numpy(), Cref, T, False, E)
+    else:
+        res, *_ = check_against_oracle(case, mxinputs.OUT_FP32, C=C)
     assert res["n_bad"] == 0, res
