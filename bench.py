@@ -42,6 +42,7 @@ CSRC = os.path.join(ROOT, "microscaled_block_scaled_amd", "csrc")
 # device code is stale.
 GEMM_SOURCES = [os.path.join(CSRC, "mx_kernels.h")]
 QUANT_SOURCES = [os.path.join(CSRC, "mx_quant.h")]
+QUANT6_SOURCES = [os.path.join(CSRC, "mx_quant.h"), os.path.join(CSRC, "mx_quant6.h")]
 
 
 def algorithmic_bytes(fmt, M, N, K, out):
@@ -202,7 +203,8 @@ def bench_quantize(steps, warmup, fmt, in_dtype):
     x = torch.randn((rows, K), generator=g, dtype=torch.float32)
     tdt = torch.float32 if in_dtype == mxg.IN_FP32 else torch.bfloat16
     x = x.to(tdt).to(dev)
-    q = torch.empty((rows, K // 2 if fmt == mxinputs.FMT_E2M1 else K), dtype=torch.uint8, device=dev)
+    q = torch.empty((rows, mxinputs.row_bytes(fmt, K)), dtype=torch.uint8, device=dev)
+    srcs = QUANT6_SOURCES if fmt in (mxinputs.FMT_E2M3, mxinputs.FMT_E3M2) else QUANT_SOURCES
     qs = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     args = (fmt, in_dtype, rows, K, x.data_ptr(), q.data_ptr(), qs.data_ptr(), stream.cuda_stream)
@@ -228,12 +230,12 @@ def bench_quantize(steps, warmup, fmt, in_dtype):
             "dtype": "f32" if in_dtype == mxg.IN_FP32 else "bf16", "data": "synthetic",
             "config": {"workload": "quantize_%s_from_%s_8192x4096" % (
                 mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
-                "rows": rows, "K": K, "kernel_source_sha256": kernel_source_hash(QUANT_SOURCES)},
+                "rows": rows, "K": K, "kernel_source_sha256": kernel_source_hash(srcs)},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("quantize_%s_from_%s_8192x4096" % (
                              mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
-                             QUANT_SOURCES),
+                             srcs),
                          "algorithmic_bytes": nbytes,
                          "launch_us": round(launch_s * 1e6, 2)}}
 
@@ -594,7 +596,8 @@ def main():
         copy_calibration()
         return
     if a.quantize:
-        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, mxinputs.FMT_E5M2):
+        for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, mxinputs.FMT_E5M2, mxinputs.FMT_E2M3,
+                    mxinputs.FMT_E3M2):
             for ind in (1, 2):
                 print(json.dumps(bench_quantize(a.steps, a.warmup, fmt, ind)), flush=True)
         return
