@@ -38,8 +38,12 @@ __device__ __forceinline__ uint32_t fp6_code(float y)
 
 // One lane holds V = 4 (FP32 input) or 8 (BF16 input) consecutive values of
 // a block, LPB = 32 / V lanes per block, grid-stride over blocks as
-// quantize_kernel.  Each lane stores its 3 bytes as single bytes (V = 4) or
-// its 6 bytes as three 16-bit words (V = 8, at an even offset).
+// quantize_kernel.  A lane's codes are 3 (V = 4) or 6 (V = 8) bytes, so 4 or
+// 2 lanes make 12 bytes, three whole dwords, which those lanes store after
+// one DPP move brings each the neighbour's bits it needs.  The lanes of a
+// hardware quad always hold one block (LPB is 8 or 4, blocks start at lane
+// multiples of LPB), so they run the same loop trips and the DPP sources
+// are active.
 template <int F, int IN>
 __global__ void __launch_bounds__(256)
 quantize6_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *__restrict__ S,
@@ -85,17 +89,27 @@ quantize6_kernel(const void *__restrict__ X, uint8_t *__restrict__ Q, uint8_t *_
                 w[j] |= fp6_code<F>(ldexpf(v[4 * j + i], 127 - s)) << (6 * i);
             if (bad) w[j] = 0;
         }
-        uint8_t *q = Q + b * 24 + sub * (V / 4) * 3;
         if (V == 4) {
-            q[0] = (uint8_t)w[0];
-            q[1] = (uint8_t)(w[0] >> 8);
-            q[2] = (uint8_t)(w[0] >> 16);
+            // quad lane r < 3 stores dword r of the quad's 12 bytes: its own
+            // bytes from byte r on, then the next lane's (quad_perm 1,2,3,3)
+            const int r = sub & 3;
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[0], 0xF9, 0xF, 0xF, false);
+            if (r < 3)
+                *(uint32_t *)(Q + b * 24 + (sub >> 2) * 12 + 4 * r) =
+                    (w[0] >> (8 * r)) | (nb << (24 - 8 * r));
         } else {
-            const uint32_t hi = w[V / 4 - 1];
-            uint16_t *q16 = (uint16_t *)q;
-            q16[0] = (uint16_t)w[0];
-            q16[1] = (uint16_t)((w[0] >> 16) | (hi << 8));
-            q16[2] = (uint16_t)(hi >> 8);
+            // lane pair (A0 A1 | B0 B1, 3 bytes each): the even lane stores
+            // A0 A1[0] and A1[1..2] B0[0..1], the odd lane B0[2] B1; the even
+            // lane takes B0 from its neighbour (quad_perm 1,1,3,3)
+            const uint32_t w1 = w[V / 4 - 1];
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[0], 0xF5, 0xF, 0xF, false);
+            uint32_t *q32 = (uint32_t *)(Q + b * 24 + (sub >> 1) * 12);
+            if ((sub & 1) == 0) {
+                q32[0] = w[0] | (w1 << 24);
+                q32[1] = (w1 >> 8) | (nb << 16);
+            } else {
+                q32[2] = (w[0] >> 16) | (w1 << 8);
+            }
         }
     }
 }
