@@ -5,15 +5,19 @@ One step = one mx_gemm call (C = A * B^T, MX block-scaled) over a synthetic,
 already-quantized workload resident in HBM; quantization is outside the
 timed region, as in the measurements the FlyDSL article reports (section
 "Performance numbers need their baselines").  The default workload is the
-MXFP8 Llama-3.1-8B fused-QKV projection, M=2048, N=6144, K=4096, BF16 out.
+largest one: the MXFP4 Llama-3.3-70B MLP down projection at M=2048
+(N=8192, K=28672, BF16 out, 962 GFLOP per call).
 
-Prints one JSON line: whole-job TFLOP/s over exactly --steps timed steps,
-the dominant kernel's roofline position (achieved vs the MI355X dense MX
-MFMA peak, from HIP events around every launch on the launch stream), and
-the CPU oracle's rate on a bounded row sample of the same workload.
+Prints one JSON line: whole-job TFLOP/s over exactly --steps timed steps
+(cycling through operand copies, so no step finds its data in the
+last-level cache), the kernel's roofline position from the cold median of
+60 launches each timed alone (HIP events on the launch stream) against the
+MI355X dense MX MFMA peak and against the measured MFMA ceiling of the same
+device, and the CPU oracle's rate on a bounded row sample of the workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
-    python bench.py --cold [--all]    (per-launch cold-cache timing)
+    python bench.py --cold [--all]    (per-launch cold-cache timing only)
+    python bench.py --ceiling         (the MFMA ceiling of both formats)
     python bench.py --quantize | --grouped | --mixed | --bf16
         (the quantizer / grouped GEMM / mixed-format GEMM / dense BF16 GEMM)
 """
@@ -30,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 import mxinputs  # noqa: E402
 
-DEFAULT_WORKLOAD = "mxfp8_llama8b_qkv"
+DEFAULT_WORKLOAD = "mxfp4_llama70b_down_m2048"
 METRIC = "MX GEMM TFLOPS and % of MI355X dense MXFP4/MXFP8 MFMA peak per shape"
 # MI355X published dense peaks: MXFP4 10.1 PFLOP/s, MXFP8 5.0 PFLOP/s; HBM3E 8 TB/s.
 PEAK_TFLOPS = {mxinputs.FMT_E2M1: 10100.0, mxinputs.FMT_E4M3: 5000.0}
@@ -91,32 +95,95 @@ def cpu_threads():
     return max(1, min(16, n))
 
 
-def cpu_baseline(case, target_s=12.0):
-    """The CPU oracle on a row sample of the same workload (all N columns)."""
+def host_cores():
+    """(cores this process may run on, cores the host reports)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return usable, os.cpu_count() or usable
+
+
+def cpu_baseline(case, target_s=10.0, single_s=6.0):
+    """The CPU oracle on a row sample of the same workload (all N columns):
+    about target_s seconds on up to 16 threads, then about single_s seconds
+    on one thread."""
     import numpy as np
     import oracle
     threads = cpu_threads()
     M, N, K, fmt = case["M"], case["N"], case["K"], case["fmt"]
 
-    def run(rows):
+    def run(rows, nthreads):
         t0 = time.perf_counter()
         oracle.gemm(fmt, case["A"], case["A_scale"], case["B"], case["B_scale"], K,
-                    rows=rows, threads=threads)
+                    rows=rows, threads=nthreads)
         return time.perf_counter() - t0
 
-    r0 = min(M, 4)
-    t0 = run(np.arange(r0))
-    nrows = int(max(r0, min(M, r0 * target_s / max(t0, 1e-6))))
-    rows = np.linspace(0, M - 1, nrows).astype(np.int64)
-    t = run(rows)
-    flops = 2.0 * nrows * N * K
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+    def sample(nthreads, budget):
+        r0 = min(M, max(1, nthreads // 4))
+        t0 = run(np.arange(r0), nthreads)
+        nrows = int(max(r0, min(M, r0 * budget / max(t0, 1e-6))))
+        rows = np.linspace(0, M - 1, nrows).astype(np.int64)
+        return nrows, run(rows, nthreads)
+
+    nrows, t = sample(threads, target_s)
+    n1, t1 = sample(1, single_s)
+    usable, reported = host_cores()
+    flop_row = 2.0 * N * K
+    return {"value": round(nrows * flop_row / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d rows of A (all %d columns, K=%d), %.1f s on %d threads"
-                      % (nrows, M, N, K, t, threads)}
+            "sample": "%d of %d rows of A (all %d columns, K=%d), %.1f s on %d threads; "
+                      "single thread: %d rows in %.1f s" % (nrows, M, N, K, t, threads, n1, t1),
+            "single_thread_value": round(n1 * flop_row / t1 / 1e12, 6),
+            "host_cores_usable": usable, "host_cores_reported": reported}
 
 
-def bench_one(name, steps, warmup, with_cpu):
+def mfma_ceiling(fmt, target_s=0.05, reps=3):
+    """The block-scaled MFMA's sustained rate on this device with no memory
+    traffic (mx_mfma_ceiling, the tile kernel's launch shape), on random and
+    on constant operands: TFLOP/s, median of `reps` launches of about
+    target_s seconds each, after one warm-up launch."""
+    import torch
+    import microscaled_block_scaled_amd as mxg
+    dev = torch.device("cuda", 0)
+    out = torch.empty(mxg.CEILING_WORKGROUPS * mxg.CEILING_THREADS, dtype=torch.float32,
+                      device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nominal = PEAK_TFLOPS[fmt] * 1e12
+    steps = int(target_s * nominal / mxg.ceiling_flops(1)) // 2 * 2
+    res = {}
+    for random_data in (1, 0):
+        ts = []
+        for i in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = mxg.ceiling_ptr(fmt, steps, random_data, out.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("mx_mfma_ceiling failed: %s" % mxg.strerror(rc))
+            e1.record(stream)
+            e1.synchronize()
+            if i:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        ts.sort()
+        res["random" if random_data else "constant"] = round(
+            mxg.ceiling_flops(steps) / ts[len(ts) // 2] / 1e12, 1)
+    return res
+
+
+def _percentiles(ts):
+    ts = sorted(ts)
+    q = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
+    return {"median_us": round(q(0.5), 2), "p10_us": round(q(0.1), 2), "p90_us": round(q(0.9), 2)}
+
+
+def bench_one(name, steps, warmup, with_cpu, cold_launches=60, with_ceiling=True):
+    """One workload.  The timed region is `steps` back-to-back mx_gemm calls
+    cycling through enough copies of the operands and output that no call
+    finds its data in the 256 MB last-level cache (each copy was last
+    touched at least 768 MB of traffic earlier).  Then, for the roofline,
+    `cold_launches` calls each timed alone between its own event pair after
+    a 512 MiB read that evicts the caches (median, p10, p90), and the same
+    with no eviction (warm)."""
     import torch
     import microscaled_block_scaled_amd as mxg
 
@@ -124,54 +191,88 @@ def bench_one(name, steps, warmup, with_cpu):
     fmt, M, N, K, out = case["fmt"], case["M"], case["N"], case["K"], case["out"]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
-    C = torch.empty((M, N), dtype=torch.float32 if out == mxinputs.OUT_FP32 else torch.bfloat16,
-                    device=dev)
+    tdt = torch.float32 if out == mxinputs.OUT_FP32 else torch.bfloat16
+    nbytes = algorithmic_bytes(fmt, M, N, K, out)
+    ncopies = max(2, min(64, -(-(768 << 20) // nbytes)))
+    host = [torch.from_numpy(case[k]) for k in ("A", "A_scale", "B", "B_scale")]
+    sets = []
+    for _ in range(ncopies):
+        A, As, B, Bs = (h.to(dev) for h in host)
+        C = torch.empty((M, N), dtype=tdt, device=dev)
+        sets.append((A, As, B, Bs, C))
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    args = (fmt, M, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
-            C.data_ptr(), out, sh)
+    argsets = [(fmt, M, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
+                C.data_ptr(), out, sh) for (A, As, B, Bs, C) in sets]
 
-    def step():
-        rc = mxg.gemm_ptr(*args)
+    def call(i):
+        rc = mxg.gemm_ptr(*argsets[i % ncopies])
         if rc != 0:
             raise RuntimeError("mx_gemm failed: %s" % mxg.strerror(rc))
 
-    for _ in range(warmup):
-        step()
-    # One HIP event pair on the launch stream brackets the timed launches:
-    # their span / steps is the average launch duration (kernel time plus any
-    # gap between back-to-back launches).
+    for i in range(warmup):
+        call(i)
+    # The timed region: an event pair on the launch stream around the same
+    # launches gives their average duration too.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        call(i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    avg_launch_s = e0.elapsed_time(e1) / steps / 1e3
+    rotating_us = e0.elapsed_time(e1) / steps * 1e3
+
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev).view(torch.float32)
+
+    def per_launch(evict):
+        ts = []
+        for i in range(5 + cold_launches):
+            if evict:
+                flush.amax()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call(0)
+            b.record(stream)
+            b.synchronize()
+            if i >= 5:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return _percentiles(ts)
+
+    cold, warm = per_launch(True), per_launch(False)
+    del flush
+    ceiling = mfma_ceiling(fmt) if with_ceiling else None
 
     flops = 2.0 * M * N * K
-    nbytes = algorithmic_bytes(fmt, M, N, K, out)
     tflops = flops * steps / wall / 1e12
     bound = "mfma" if flops / nbytes >= RIDGE[fmt] else "hbm"
     plan = mxg.plan(fmt, M, N, K, out)
     plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
         plan["variant"], plan["tile_m"], plan["tile_n"], plan["split_k"], plan["workgroups"])
     traffic = measured_traffic(name, GEMM_SOURCES, plan_str)
+    launch_s = cold["median_us"] * 1e-6
     if bound == "mfma":
-        achieved = flops / avg_launch_s / 1e12
+        achieved = flops / launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[fmt],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[fmt], 4)}
     else:
-        achieved = nbytes / avg_launch_s / 1e9
+        achieved = nbytes / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = traffic
     roof["algorithmic_bytes"] = nbytes
-    roof["launch_us"] = round(avg_launch_s * 1e6, 2)
+    roof["launch_us"] = cold["median_us"]
+    roof["timing"] = "cold median of %d launches, each alone after a 512 MiB cache-evicting read" \
+        % cold_launches
+    roof["cold"] = cold
+    roof["warm"] = warm
+    roof["rotating_avg_us"] = round(rotating_us, 2)
+    roof["mfma_ceiling_tflops"] = ceiling
+    roof["tflops"] = round(flops / launch_s / 1e12, 2)
+    roof["frac_of_measured_ceiling"] = (round(flops / launch_s / 1e12 / ceiling["random"], 4)
+                                        if ceiling else None)
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
@@ -182,7 +283,7 @@ def bench_one(name, steps, warmup, with_cpu):
                    "format": mxinputs.fmt_name(fmt),
                    "out": "fp32" if out == mxinputs.OUT_FP32 else "bf16",
                    "accumulate": "fp32", "peak_frac": round(tflops / PEAK_TFLOPS[fmt], 4),
-                   "plan": plan_str,
+                   "plan": plan_str, "operand_copies": ncopies,
                    "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
         "roofline": roof,
     }
@@ -567,12 +668,16 @@ def bench_bf16(steps, warmup, name, with_cpu):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(mxinputs.CONFIGS))
     ap.add_argument("--all", action="store_true",
                     help="one line per workload (no CPU baseline except the default one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-launches", type=int, default=60,
+                    help="launches timed alone for the cold / warm medians (at least 3)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the MFMA-ceiling measurement (frac_of_measured_ceiling null)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--quantize", action="store_true",
@@ -586,6 +691,8 @@ def main():
                     help="time the other formats (A E4M3 x B E2M1; E5M2) instead")
     ap.add_argument("--bf16", action="store_true",
                     help="time the dense BF16 GEMM (mx_gemm_bf16) instead")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the MFMA ceiling (mx_mfma_ceiling) of both formats")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
@@ -594,6 +701,16 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.ceiling:
+        import microscaled_block_scaled_amd as mxg
+        for fmt in (mxinputs.FMT_E2M1, mxinputs.FMT_E4M3):
+            c = mfma_ceiling(fmt)
+            print(json.dumps({"mfma_ceiling": mxinputs.fmt_name(fmt), "unit": "TFLOP/s",
+                              "random": c["random"], "constant": c["constant"],
+                              "datasheet_peak": PEAK_TFLOPS[fmt],
+                              "launch": "%d workgroups x %d threads" % (
+                                  mxg.CEILING_WORKGROUPS, mxg.CEILING_THREADS)}), flush=True)
         return
     if a.quantize:
         for fmt in (mxinputs.FMT_E4M3, mxinputs.FMT_E2M1, mxinputs.FMT_E5M2, mxinputs.FMT_E2M3,
@@ -625,7 +742,8 @@ def main():
         if a.all else [a.workload]
     for name in names:
         with_cpu = (not a.no_cpu_baseline) and name == a.workload
-        print(json.dumps(bench_one(name, a.steps, a.warmup, with_cpu)), flush=True)
+        print(json.dumps(bench_one(name, a.steps, a.warmup, with_cpu,
+                                   max(3, a.cold_launches), not a.no_ceiling)), flush=True)
 
 
 if __name__ == "__main__":

@@ -337,6 +337,32 @@ int mx_gemm_grouped_bf16(int64_t groups, const int64_t *group_rows, int64_t N, i
 int mx_gemm_grouped_bf16_plan(int64_t groups, const int64_t *group_rows, int64_t N,
                               int64_t K, int out_dtype, mx_plan_t *plan);
 
+/* Launch shape of mx_mfma_ceiling: the tile kernel's (one 512-thread
+ * workgroup per compute unit of the MI355X). */
+#define MX_CEILING_WORKGROUPS 256
+#define MX_CEILING_THREADS 512
+
+/*
+ * Measurement, not part of the GEMM: the rate at which the current device
+ * sustains the block-scaled matrix instruction with no memory traffic, to
+ * set a GEMM's measured rate against (the datasheet peak assumes the top
+ * clock, which the power limit may not allow).  Every wave of
+ * MX_CEILING_WORKGROUPS x MX_CEILING_THREADS threads keeps a 2 x 4 grid of
+ * 32x32 FP32 accumulators and runs `steps` K-steps of 8 instructions (K 64
+ * each, 2*32*32*64 FLOPs each) on register-resident operands: two operand
+ * sets alternating step by step, hashed ("random_data" non-zero; E4M3 NaN
+ * codes replaced) or constant.  Total FLOPs =
+ * MX_CEILING_WORKGROUPS * MX_CEILING_THREADS / 64 * steps * 8 * 131072.
+ *   fmt     MX_FMT_E2M1 or MX_FMT_E4M3 (both operands)
+ *   steps   even, 2 .. 2^30
+ *   out     device memory for MX_CEILING_WORKGROUPS * MX_CEILING_THREADS
+ *           floats, 4-byte aligned; receives each lane's accumulator sum (a
+ *           value with no meaning, written so that no work is dead code)
+ * Returns MX_OK or MX_ERR_FORMAT / MX_ERR_SHAPE / MX_ERR_NULL / MX_ERR_ALIGN
+ * / a device error; asynchronous on `stream` like mx_gemm.
+ */
+int mx_mfma_ceiling(int fmt, int64_t steps, int random_data, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,6 +131,8 @@ def lib():
     L.mx_gemm_grouped.restype = ctypes.c_int
     L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
                                   vp, vp, vp, ctypes.c_int, vp]
+    L.mx_mfma_ceiling.restype = ctypes.c_int
+    L.mx_mfma_ceiling.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp]
     _lib = L
     return L
 
@@ -325,6 +327,22 @@ def mx_gemm_bf16(a, b, out_dtype=None, out=None, stream=None, tile=None, split_k
     if rc != MX_OK:
         _raise(rc)
     return out
+
+
+# Launch shape and work of mx_mfma_ceiling (include/mxgemm.h).
+CEILING_WORKGROUPS = 256
+CEILING_THREADS = 512
+
+
+def ceiling_flops(steps):
+    """FLOPs of one mx_mfma_ceiling launch of `steps` K-steps."""
+    return CEILING_WORKGROUPS * CEILING_THREADS // 64 * steps * 8 * 2 * 32 * 32 * 64
+
+
+def ceiling_ptr(fmt, steps, random_data, out, stream=0):
+    """Raw entry point of mx_mfma_ceiling (a measurement kernel): status code."""
+    return lib().mx_mfma_ceiling(int(fmt), int(steps), int(bool(random_data)), out,
+                                 stream or None)
 
 
 def quantize_ptr(fmt, in_dtype, rows, K, X, Q, Q_scale, stream=0):

@@ -131,14 +131,17 @@ template <int RB> __device__ __forceinline__ int lds_row(int r)
     return RB == 96 ? (r >> 3) * 1040 + (r & 7) * 96 : r * RB;
 }
 
-template <int FA, int FB>
+// The scale operands are 32-bit registers holding four E8M0 bytes; op_sel
+// OPS picks byte OPS of each (measured on the device: op_sel i applies byte i,
+// for A and for B alike).
+template <int FA, int FB, int OPS>
 __device__ __forceinline__ v16f mma(const v8i &a, const v8i &b, v16f acc, int sa, int sb)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        a, b, acc, mfma_fmt<FA>::sel, mfma_fmt<FB>::sel, 0, sa, 0, sb);
+        a, b, acc, mfma_fmt<FA>::sel, mfma_fmt<FB>::sel, OPS, sa, OPS, sb);
 }
 // Dense BF16: 16 bytes (8 values) per lane and operand, no scales.
-template <int FA, int FB>
+template <int FA, int FB, int OPS>
 __device__ __forceinline__ v16f mma(const v4i &a, const v4i &b, v16f acc, int, int)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
@@ -154,17 +157,28 @@ __device__ __forceinline__ void fp6_frag(V &v, uint2 q0, uint2 q1, uint2 q2)
         v = V{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, 0, 0};
 }
 
-// Direct HBM -> LDS copies (gfx950 global_load_lds): lane l of the wave
-// writes its `size` bytes to lds + l * size; `lds` must be wave-uniform.
+// Direct HBM -> LDS copies: buffer_load_dwordx4 with the lds bit (the gfx950
+// form moves 16 bytes per lane).  Lane l of the wave writes its 16 bytes to
+// lds + l * 16; `lds` must be wave-uniform.  The source is a buffer resource
+// (wave-uniform 64-bit base) plus a 32-bit per-lane byte offset.  The buffer
+// form, rather than global_load_lds, matters for scheduling: the compiler
+// counts a global (FLAT-encoded) LDS copy as both a memory and an LDS access
+// and then waits for every outstanding LDS read (lgkmcnt(0)) before any use
+// of one, while with buffer copies in flight it waits only for the read it
+// needs.  num_records is the largest value, so no access is range-checked
+// (every offset the kernel forms lies inside its operand).
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Word 3 of a gfx9 buffer descriptor: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ __forceinline__ void g2l_16(const void *src, void *lds)
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, kRsrcWord3);
 }
-__device__ __forceinline__ void g2l_4(const void *src, void *lds)
+__device__ __forceinline__ void b2l_16(rsrc_t src, uint32_t off, void *lds)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)lds, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's memory loads are outstanding (loads
@@ -244,7 +258,7 @@ __device__ __forceinline__ void static_for(F &&f)
 // E2M1).  K is walked in slabs of 128 or 256 K-values of every A and B row
 // (see slab<>).  The LDS holds a ring of S slabs (2 or 3, as the tile's LDS footprint allows) and two scale
 // buffers:
-//   * slab k+S-1 is copied HBM -> LDS directly (global_load_lds, no register
+//   * slab k+S-1 is copied HBM -> LDS directly (buffer loads into LDS, no register
 //     staging) into the ring slot that slab k-1 has just vacated, so S-1
 //     slabs of copies are in flight while slab k is multiplied -- the
 //     consumed part of the LDS tile is refilled as soon as it is free;
@@ -301,7 +315,10 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     typedef typename std::conditional<OUT == OF32, float, uint16_t>::type otype;
     constexpr int OS = sizeof(otype);
     constexpr int PITCH = WTN * OS + 16;                   // staging row pitch, bytes
-    constexpr int RING = S * DATA + 2 * SBUF;
+    // (+16: a half-period read of the last row of a short, shifted last
+    // period may run up to 12 bytes past its buffer; those bytes belong to
+    // steps that do not exist)
+    constexpr int RING = S * DATA + 2 * SBUF + 16;
     constexpr int SMEM = RING > NW * 32 * PITCH ? RING : NW * 32 * PITCH;
     static_assert(SMEM <= 163840, "LDS budget");
 
@@ -402,18 +419,18 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         // into the row.  (With 64-byte slab rows every slab is whole.)
         const uint32_t cmaxa = (uint32_t)(rowla - 16 - koffa);
         const uint32_t cmaxb = (uint32_t)(rowlb - 16 - koffb);
-        const uint8_t *const Ak = At + koffa, *const Bk = Bt + koffb;
+        const rsrc_t Ak = make_rsrc(At + koffa), Bk = make_rsrc(Bt + koffb);
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPCA - 1);
             const uint32_t ch = min((RA == 128 && (i & 1)) ? ga.ch1 : ga.ch0, cmaxa);
-            g2l_16(Ak + (row_off(ga, i * RPCA, last_a) + ch), base + i * RPCA * LA);
+            b2l_16(Ak, row_off(ga, i * RPCA, last_a) + ch, base + i * RPCA * LA);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
             const int i = min(wave + u * NW, BN / RPCB - 1);
             const uint32_t ch = min((RB == 128 && (i & 1)) ? gb.ch1 : gb.ch0, cmaxb);
-            g2l_16(Bk + (row_off(gb, i * RPCB, last_b) + ch), base + BM * LA + i * RPCB * LB);
+            b2l_16(Bk, row_off(gb, i * RPCB, last_b) + ch, base + BM * LA + i * RPCB * LB);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
@@ -432,8 +449,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             const int i = min(wave + u * NW, NSI - 1);
             const bool in_a = i * 64 < BM;
             const int row = min(i * 64 + lane - (in_a ? 0 : BM), in_a ? last_a : last_b);
-            const uint8_t *const src = (in_a ? Ast : Bst) + soff;
-            g2l_16(src + (uint32_t)row * (uint32_t)sps, sbase + buf * SBUF + i * 1024);
+            const rsrc_t src = make_rsrc((in_a ? Ast : Bst) + soff);
+            b2l_16(src, (uint32_t)row * (uint32_t)sps, sbase + buf * SBUF + i * 1024);
         }
     };
 
@@ -458,16 +475,27 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int r_off = ROLL_A ? a_off : b_off, d_off = ROLL_A ? b_off : a_off;
     const int rs_off = ROLL_A ? sa_off : sb_off, ds_off = ROLL_A ? sb_off : sa_off;
     // Fragment registers: 8 dwords for the scaled MFMA (E2M1 uses the low
-    // 4), 4 for BF16.
+    // 4), 4 for BF16.  When both operands are E2M1 (4-dword fragments) the
+    // rolled operand is double-buffered too (R2): then every fragment of the
+    // next step is read right after the step's first MFMAs, a whole step
+    // ahead of its use, and the burst of reads that all waves issue at once
+    // has a step to drain through the LDS.
+    constexpr bool R2 = FA == FP4 && FB == FP4;
     typedef typename std::conditional<SCALED, v8i, v4i>::type fv;
-    fv fr[FR], fd[2][FD];
-    int fsr[FR] = {}, fsd[2][FD] = {};                     // scale bytes (unused for BF16)
+    fv fr[R2 ? 2 : 1][FR], fd[2][FD];
+    // Scale registers (unused for BF16).  A period's 8 steps fall in two
+    // halves of 4; for each half a fragment's lane holds the 4 scale bytes of
+    // its steps in one register, byte i for the half's step i, applied by
+    // the MFMA's op_sel.  The rolled operand reloads its register with the
+    // fragment that opens a half; the D operand keeps one register per half
+    // parity, since its next half is read while the current one is in use.
+    int fsr[R2 ? 2 : 1][FR] = {}, fsd[2][FD] = {};
 
     // Where one step's operands are: ring slot `slot`, pass p of the slab,
     // scale buffer `sbuf`, slab `kp` within its scale period, and the scale
     // byte shift of a short last period.  Data chunk offsets (per operand)
-    // and the scale byte are per lane (they depend on the lane group g and
-    // the swizzle).
+    // are per lane (they depend on the lane group g and the swizzle); the
+    // scale offset is that of the step's half-period.
     struct Src { int data, scale, a0, a1, b0, b1; };
     auto chunk_offs = [&](auto fc, int p, int swl, int &o0, int &o1) {
         // Step p of a slab: E4M3 / E5M2 chunks 4p+g and 4p+2+g of a 128-byte
@@ -486,7 +514,11 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     auto src_of = [&](int slot, int p, int sbuf, int kp, int shift) {
         Src r;
         r.data = slot * DATA;
-        r.scale = S * DATA + sbuf * SBUF + kp * SBS + 2 * p + g + shift;   // scale block 2p+g of the slab
+        // Step j = kp*HS + p of the period (0..7) reads scale block 2j + g,
+        // byte shift + 2j + g of its row in the buffer (the shift, a multiple
+        // of 4, only in a short last period).  Its half j/4 starts at byte
+        // shift + 8*(j/4), a 4-byte boundary.
+        r.scale = S * DATA + sbuf * SBUF + shift + 8 * ((kp * HS + p) >> 2);
         chunk_offs(std::integral_constant<int, FA>{}, p, swla, r.a0, r.a1);
         chunk_offs(std::integral_constant<int, FB>{}, p, swlb, r.b0, r.b1);
         return r;
@@ -496,9 +528,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                    c ? x.a1 : y.a1, c ? x.b0 : y.b0, c ? x.b1 : y.b1};
     };
     // Fragment f of operand A (ia true) or B, whose lane rows start at LDS
-    // offset `off` (scale rows at `soff`): 16 (E2M1) or 32 (E4M3) bytes and
-    // a scale byte.
-    auto frag = [&](auto ia, const Src &s, int off, int soff, int f, fv &v, int &sv) {
+    // offset `off`: 16 (E2M1), 24 (FP6) or 32 (E4M3) bytes.
+    auto frag = [&](auto ia, const Src &s, int off, int f, fv &v) {
         constexpr bool IA = decltype(ia)::value;
         constexpr int F = IA ? FA : FB, L = IA ? LA : LB;     // 32 rows take 32 * L LDS bytes
         const uint8_t *rp = smem + s.data + off + f * 32 * L;
@@ -506,29 +537,44 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             // three 8-byte reads (the 24 bytes are 8-byte aligned)
             const uint8_t *q = rp + (IA ? s.a0 : s.b0);
             fp6_frag(v, *(const uint2 *)q, *(const uint2 *)(q + 8), *(const uint2 *)(q + 16));
-            sv = smem[s.scale + soff + f * 32 * 16];
             return;
         }
         const v4i lo = *(const v4i *)(rp + (IA ? s.a0 : s.b0));
         if constexpr (!SCALED) {
             v = lo;
+        } else if constexpr (F != FP4) {
+            const v4i hi = *(const v4i *)(rp + (IA ? s.a1 : s.b1));
+            v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         } else {
-            if constexpr (F != FP4) {
-                const v4i hi = *(const v4i *)(rp + (IA ? s.a1 : s.b1));
-                v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                v = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-            }
-            sv = smem[s.scale + soff + f * 32 * 16];
+            v = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+        }
+    };
+    // The scale register of fragment f (scale rows at LDS offset `soff`) for
+    // the half-period at s.scale: the row's 8 bytes there (two 4-byte reads,
+    // merged into one ds_read2_b32) hold blocks 2i + g' of steps i = 0..3 for
+    // both lane groups g'; one v_perm_b32 keeps this lane group's four, in
+    // step order.
+    const uint32_t psel = g ? 0x07050301u : 0x06040200u;
+    auto frag_scale = [&](const Src &s, int soff, int f, int &sv) {
+        if constexpr (SCALED) {
+            const uint8_t *q = smem + s.scale + soff + f * 32 * 16;
+            const uint32_t w0 = *(const uint32_t *)q, w1 = *(const uint32_t *)(q + 4);
+            sv = (int)__builtin_amdgcn_perm(w1, w0, psel);
         }
     };
     const std::integral_constant<bool, ROLL_A> is_r{};       // the rolled operand is A?
     const std::integral_constant<bool, !ROLL_A> is_d{};
-    auto load_all = [&](const Src &s, int set) {
+    auto load_all = [&](const Src &s) {
 #pragma unroll
-        for (int f = 0; f < FR; ++f) frag(is_r, s, r_off, rs_off, f, fr[f], fsr[f]);
+        for (int f = 0; f < FR; ++f) {
+            frag(is_r, s, r_off, f, fr[0][f]);
+            frag_scale(s, rs_off, f, fsr[0][f]);
+        }
 #pragma unroll
-        for (int f = 0; f < FD; ++f) frag(is_d, s, d_off, ds_off, f, fd[set][f], fsd[set][f]);
+        for (int f = 0; f < FD; ++f) {
+            frag(is_d, s, d_off, f, fd[0][f]);
+            frag_scale(s, ds_off, f, fsd[0][f]);
+        }
     };
 
     v16f acc[FM][FN];
@@ -540,31 +586,59 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // Multiply one step (operands fr and fd[cur]) and read the next step's
-    // operands from `nx`: rolled fragment o right after its FD MFMAs, and the
-    // D fragments spread over the FR groups.  The scheduling groups keep each
-    // rolled reload behind the MFMAs that read the old value.
-    auto step = [&](int cur, const Src &nx) {
+    // operands from `nx`: rolled fragment o right after its FD MFMAs, and
+    // the D fragments spread over the first half of the groups.  The first
+    // MFMAs of the next step then read registers loaded at least half a step
+    // earlier, so the LDS latency stays hidden even when the wave runs alone
+    // on its SIMD (its partner parked at the slab barrier).  (All D reads in
+    // the first group would spill on the 256x256 E4M3 tile.)  The scheduling
+    // groups keep each rolled reload behind the MFMAs that read the old
+    // value.
+    // Step q (a compile-time index: the steps of a trip are unrolled, and a
+    // trip starts at a period start, so q % 8 is the step within its period)
+    // multiplies with register set q & 1 and scale byte q % 4 of the
+    // half-period q / 4; the next step opens a half when (q + 1) % 4 == 0,
+    // and then its fragments bring their scale registers along.
+    constexpr int DH = R2 ? 1 : (FR + 1) / 2;              // groups that read D
+    auto step = [&](auto qc, const Src &nx) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int cur = q & 1, OPS = SCALED ? q % 4 : 0;
+        constexpr bool NEWHALF = SCALED && (q + 1) % 4 == 0;
+        constexpr int hc = (q / 4) & 1, hn = ((q + 1) / 4) & 1;   // half parities
+        constexpr int rc = R2 ? cur : 0, rn = R2 ? cur ^ 1 : 0;   // rolled register sets
+        constexpr int sc = R2 ? hc : 0, sn = R2 ? hn : 0;         // rolled scale sets
         static_for<FR>([&](auto oc) {
             constexpr int o = decltype(oc)::value;
-            constexpr int d0 = o * FD / FR, d1 = (o + 1) * FD / FR;
-            // LDS reads per fragment: data (2 for E4M3 / E5M2, 1 for E2M1
-            // and BF16) + scale (none for BF16)
+            constexpr int d0 = o < DH ? o * FD / DH : FD, d1 = o < DH ? (o + 1) * FD / DH : FD;
+            // rolled fragments read after this group: fragment o (R2: all of
+            // them after the first group)
+            constexpr int r0 = R2 ? (o == 0 ? 0 : FR) : o, r1 = R2 ? (o == 0 ? FR : FR) : o + 1;
+            // LDS reads per fragment: data (2 for E4M3 / E5M2, 3 for FP6, 1
+            // for E2M1 and BF16), + 1 for a scale register
             constexpr int FRF = ROLL_A ? FA : FB, FDF = ROLL_A ? FB : FA;
-            constexpr int NRR = !SCALED ? 1 : is_fp6<FRF>::value ? 4 : (FRF != FP4) ? 3 : 2;
-            constexpr int NRD = !SCALED ? 1 : is_fp6<FDF>::value ? 4 : (FDF != FP4) ? 3 : 2;
+            constexpr int NRR = (is_fp6<FRF>::value ? 3 : (FRF == FP4 || FRF == B16) ? 1 : 2) + NEWHALF;
+            constexpr int NRD = (is_fp6<FDF>::value ? 3 : (FDF == FP4 || FDF == B16) ? 1 : 2) + NEWHALF;
 #pragma unroll
             for (int d = 0; d < FD; ++d) {
                 if constexpr (ROLL_A)
-                    acc[o][d] = mma<FA, FB>(fr[o], fd[cur][d], acc[o][d], fsr[o], fsd[cur][d]);
+                    acc[o][d] = mma<FA, FB, OPS>(fr[rc][o], fd[cur][d], acc[o][d], fsr[sc][o],
+                                                 fsd[hc][d]);
                 else
-                    acc[d][o] = mma<FA, FB>(fd[cur][d], fr[o], acc[d][o], fsd[cur][d], fsr[o]);
+                    acc[d][o] = mma<FA, FB, OPS>(fd[cur][d], fr[rc][o], acc[d][o], fsd[hc][d],
+                                                 fsr[sc][o]);
             }
-            frag(is_r, nx, r_off, rs_off, o, fr[o], fsr[o]);
 #pragma unroll
-            for (int d = d0; d < d1; ++d)
-                frag(is_d, nx, d_off, ds_off, d, fd[cur ^ 1][d], fsd[cur ^ 1][d]);
+            for (int r = r0; r < r1; ++r) {
+                frag(is_r, nx, r_off, r, fr[rn][r]);
+                if constexpr (NEWHALF) frag_scale(nx, rs_off, r, fsr[sn][r]);
+            }
+#pragma unroll
+            for (int d = d0; d < d1; ++d) {
+                frag(is_d, nx, d_off, d, fd[cur ^ 1][d]);
+                if constexpr (NEWHALF) frag_scale(nx, ds_off, d, fsd[hn][d]);
+            }
             __builtin_amdgcn_sched_group_barrier(0x008, FD, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NRR + NRD * (d1 - d0), 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRR * (r1 - r0) + NRD * (d1 - d0), 0);
         });
     };
 
@@ -618,7 +692,7 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     if (!short_rows) issue_scales(1, 1);
     issue(S - 1, S - 1);
     Src cur = src_of(0, 0, 0, 0, shift_of(0));
-    load_all(cur, 0);
+    load_all(cur);
 
     // Main loop: one trip = TS slabs (a multiple of the ring depth and of
     // the scale period) = TS*HS steps, so register set, ring slot, pass and
@@ -629,37 +703,38 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int TS = std::lcm(PS, S);       // k0 is a multiple of PS: kq % PS is global
     static_assert(TS % PS == 0 && TS % S == 0, "trip covers whole periods and rings");
     constexpr int TRIP = TS * HS;
+    static_assert(!SCALED || TRIP % 8 == 0, "a trip is whole scale periods of 8 steps");
     int t0 = 0;
     for (; t0 + TRIP < nsteps; t0 += TRIP) {
         const int k0 = t0 / HS;                       // first slab of the trip
-#pragma unroll
-        for (int q = 0; q < TRIP; ++q) {
-            const int kq = (q + 1) / HS;              // slab of step q+1 within the trip
+        static_for<TRIP>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int kq = (q + 1) / HS;          // slab of step q+1 within the trip
             const int per = (k0 + kq) / PS;           // its scale period
-            if ((q + 1) % HS == 0)
+            if constexpr ((q + 1) % HS == 0)
                 open(k0 + kq, (kq + S - 1) % S, kq % PS == 0, (per + 1) & 1);
             cur = src_of(kq % S, (q + 1) % HS, per & 1, kq % PS, shift_of(k0 + kq));
-            step(q & 1, cur);
-        }
+            step(qc, cur);
+        });
     }
     // Last trip: steps t0 .. nsteps-1 (1 to TRIP of them).  After the last
     // step the "next" operands are re-read from the last step's place (in
     // range, never used), which keeps the step code free of branches.
     {
         const int k0 = t0 / HS;
-#pragma unroll
-        for (int q = 0; q < TRIP; ++q) {
+        static_for<TRIP>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
             if (t0 + q < nsteps) {
-                const int kq = (q + 1) / HS;
+                constexpr int kq = (q + 1) / HS;
                 const int per = (k0 + kq) / PS;
                 const bool more = t0 + q + 1 < nsteps;
-                if (more && (q + 1) % HS == 0)
+                if ((q + 1) % HS == 0 && more)
                     open_guarded(k0 + kq, (kq + S - 1) % S, kq % PS == 0, (per + 1) & 1);
                 cur = sel(more, src_of(kq % S, (q + 1) % HS, per & 1, kq % PS, shift_of(k0 + kq)),
                           cur);
-                step(q & 1, cur);
+                step(qc, cur);
             }
-        }
+        });
     }
 
     // No copy may still be in flight, and every wave must be done reading the

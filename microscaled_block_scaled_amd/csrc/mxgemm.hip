@@ -14,6 +14,7 @@
 #include "mx_kernels.h"
 #include "mx_quant.h"
 #include "mx_quant6.h"
+#include "mx_ceiling.h"
 #include "mx_host.h"
 #include "mx_launch.h"
 
@@ -347,5 +348,26 @@ extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
         else
             hipLaunchKernelGGL((mx::quantize6_kernel<mx::F6E3, mx::IN_BF16>), dim3(grid), dim3(256), 0, s, X, q, qs, nblocks);
     }
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+extern "C" int mx_mfma_ceiling(int fmt, int64_t steps, int random_data, float *out,
+                               void *stream)
+{
+    if (fmt != MX_FMT_E2M1 && fmt != MX_FMT_E4M3) return MX_ERR_FORMAT;
+    if (steps < 2 || steps % 2 != 0 || steps > ((int64_t)1 << 30)) return MX_ERR_SHAPE;
+    if (!out) return MX_ERR_NULL;
+    if (!aligned(out, 4)) return MX_ERR_ALIGN;
+    int dev = -1;
+    const int rc = device_ready(&dev);
+    if (rc != MX_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (fmt == MX_FMT_E2M1)
+        hipLaunchKernelGGL(mx::mfma_ceiling_kernel<mx::FP4>, dim3(MX_CEILING_WORKGROUPS),
+                           dim3(MX_CEILING_THREADS), 0, s, out, (int)steps, random_data);
+    else
+        hipLaunchKernelGGL(mx::mfma_ceiling_kernel<mx::FP8>, dim3(MX_CEILING_WORKGROUPS),
+                           dim3(MX_CEILING_THREADS), 0, s, out, (int)steps, random_data);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }

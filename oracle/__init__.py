@@ -329,7 +329,9 @@ def tables():
 
 
 def bf16_ulp(x):
-    """Spacing of bfloat16 numbers in the binade of each |x| (float64 array)."""
+    """Spacing of bfloat16 numbers in the binade of each |x| (float64 array):
+    2^(max(floor(log2|x|), -126) - 7), and 2^-133 (the subnormal spacing)
+    for x = 0."""
     x = np.abs(np.asarray(x, np.float64))
     _, e = np.frexp(x)                       # x = f * 2^e, f in [0.5, 1)
     expo = np.maximum(e - 1, -126)           # floor(log2 |x|), clamped
@@ -338,7 +340,8 @@ def bf16_ulp(x):
 
 
 def bound(C, T, out_is_bf16, E=None):
-    """Allowed |gpu - C| per element."""
+    """Allowed |gpu - C| per element: 1e-5 * T, plus one bfloat16 ulp of C
+    for BF16 output, plus E when given."""
     b = REL_TOL * np.asarray(T, np.float64)
     if E is not None:
         b = b + np.asarray(E, np.float64)
@@ -347,23 +350,55 @@ def bound(C, T, out_is_bf16, E=None):
     return b
 
 
+def round_to_output(C, out_is_bf16):
+    """C (float64) as the output type holds it: rounded to float32 (nearest
+    even), then for BF16 output to bfloat16 (nearest even, from the float32
+    bits, as the device converts its FP32 accumulator).  Values beyond the
+    type's range become infinities; NaN stays NaN.  Returned as float64."""
+    C = np.asarray(C, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        c32 = C.astype(np.float32)
+    if out_is_bf16:
+        bits = c32.view(np.uint32).astype(np.uint64)
+        rnd = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+        finite = np.isfinite(c32)
+        bits = np.where(finite, rnd, bits & 0xFFFF0000).astype(np.uint32)
+        c32 = bits.view(np.float32)
+    return c32.astype(np.float64)
+
+
 def compare(gpu, C, T, out_is_bf16, E=None):
-    """Per-element acceptance.  Returns a dict with the worst error/bound
-    ratio, the number of failing elements, the first failing index (or None)
-    and, when E is given, how many elements exceed the plain bound (without
-    E) and the worst ratio against it."""
+    """Per-element acceptance.
+
+    An element whose oracle value is NaN must be NaN on the GPU, and one
+    whose value the output type cannot hold (it rounds to an infinity) must
+    be that infinity; every other element must be finite and meet
+    |gpu - C| <= bound(C, T, out_is_bf16, E) (with T == 0 and FP32 output
+    that is an exact zero; +0 and -0 are equal).  Returns a dict with the
+    worst error/bound ratio over the finite elements, the number of failing
+    elements and the first failing index (or None); when E is given, also how
+    many elements fail the plain bound (without E) and the worst ratio
+    against it."""
     g = np.asarray(gpu, np.float64)
     C = np.asarray(C, np.float64)
     if g.shape != C.shape:
         raise ValueError("shape mismatch %s vs %s" % (g.shape, C.shape))
-    err = np.abs(g - C)
+    ref = round_to_output(C, out_is_bf16)
+    cnan = np.isnan(C)
+    cinf = ~cnan & np.isinf(ref)
+    special = cnan | cinf
+    special_bad = special & ~np.where(cnan, np.isnan(g), g == ref)
+    with np.errstate(invalid="ignore"):
+        err = np.where(special, 0.0, np.abs(g - np.where(special, 0.0, C)))
 
     def judge(lim):
+        lim = np.where(special, 0.0, lim)
         # A zero limit (T == 0, FP32 output) demands an exact zero.
         with np.errstate(divide="ignore", invalid="ignore"):
             ratio = np.where(lim > 0, err / lim, np.where(err == 0, 0.0, np.inf))
-        bad = ~(err <= lim)
-        return (float(np.max(ratio)) if ratio.size else 0.0), bad
+        bad = special_bad | (~special & ~(err <= lim))
+        finite = ratio[~special]
+        return (float(np.max(finite)) if finite.size else 0.0), bad
 
     worst, bad = judge(bound(C, T, out_is_bf16, E))
     nbad = int(bad.sum())

@@ -27,3 +27,17 @@ def orc():
         from oracle import build
         build.build()
     return oracle.default()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Per GPU test file: how many elements the plain 1e-5 * T bound judged,
+    how many missed it, and the worst ratio (tests/gpu_util.py)."""
+    gu = sys.modules.get("gpu_util")
+    if gu is None or not gu.PLAIN_STATS:
+        return
+    terminalreporter.write_sep("-", "plain-bound tally per file")
+    for f, st in sorted(gu.PLAIN_STATS.items()):
+        terminalreporter.write_line(
+            "%-34s elements %10d  beyond plain %6d  worst plain ratio %.3g%s" % (
+                f, st["elements"], st["beyond_plain"], st["worst_plain_ratio"],
+                "  (group term allowed)" if st["group_term"] else ""))

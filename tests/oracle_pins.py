@@ -820,3 +820,115 @@ ALL_PINS = [pin_e4m3_table, pin_e2m1_table, pin_e8m0, pin_worked_examples,
             pin_quantize_scale_rule, pin_quantize_nonfinite, pin_quantize_roundtrip,
             pin_grouped, pin_mixed_formats, pin_e5m2, pin_e5m2_pairs, pin_fp6, pin_bf16,
             pin_grouped_bf16]
+
+
+# --------------------------------------------------------------------------
+# The acceptance helpers: oracle.bf16_ulp, bound, round_to_output and compare.
+# Each pin takes a namespace holding those four functions (the oracle module,
+# or a copy with a planted mistake) and checks them against torch's bfloat16
+# and float32 conversions and against cases worked out by hand.
+
+def _torch_bf16_values(bits):
+    import torch
+    return torch.from_numpy(np.asarray(bits, np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def pin_bf16_ulp(h):
+    """bf16_ulp(x) is the spacing to the next bfloat16 number up, for every
+    positive finite bfloat16 value below the largest (subnormals included),
+    for its negation, and for values between two bfloat16 numbers."""
+    bits = np.arange(1, 0x7F7F, dtype=np.int64)
+    v = _torch_bf16_values(bits)
+    spacing = _torch_bf16_values(bits + 1) - v
+    assert np.array_equal(h.bf16_ulp(v), spacing)
+    assert np.array_equal(h.bf16_ulp(-v), spacing)
+    assert np.array_equal(h.bf16_ulp((v + (v + spacing)) / 2), spacing)
+    assert h.bf16_ulp(np.array([0.0]))[0] == spacing[0] == 2.0 ** -133
+    # the largest finite bfloat16, (2 - 2^-7) * 2^127, is in the binade of 2^127
+    assert h.bf16_ulp(np.array([_torch_bf16_values([0x7F7F])[0]]))[0] == 2.0 ** 120
+
+
+def pin_round_to_output(h):
+    """round_to_output equals torch's float64 -> float32 conversion, and for
+    BF16 output torch's float32 -> bfloat16 conversion of that, over
+    magnitudes from below the bfloat16 subnormals to beyond float32's range,
+    exact ties, the bfloat16 overflow threshold and NaN."""
+    import torch
+    r = np.random.default_rng(7)
+    x = np.ldexp(r.uniform(1.0, 2.0, 4000), r.integers(-150, 130, 4000))
+    x *= np.where(r.random(4000) < 0.5, -1.0, 1.0)
+    ties = np.ldexp(1.0 + (2 * r.integers(0, 128, 200) + 1) / 256.0, r.integers(-120, 120, 200))
+    big = np.array([3.3895313892515355e+38, 3.3961775292304740e+38, 3.39617753e38,
+                    3.4e38, 3.5e38, 1e39, -1e39, 2.0 ** -149, 2.0 ** -150, 0.0, -0.0])
+    x = np.concatenate([x, ties, -ties, big])
+    t32 = torch.from_numpy(x).to(torch.float32)
+    assert np.array_equal(h.round_to_output(x, False), t32.double().numpy())
+    assert np.array_equal(h.round_to_output(x, True), t32.to(torch.bfloat16).double().numpy())
+    assert np.isnan(h.round_to_output(np.array([np.nan]), True)).all()
+    assert np.isnan(h.round_to_output(np.array([np.nan]), False)).all()
+
+
+def pin_bound(h):
+    """bound = 1e-5 * T (FP32 out), + E when given, + one bfloat16 ulp of C
+    for BF16 out; ulps from hand: 0 -> 2^-133, 1 -> 2^-7, -3 -> 2^-6,
+    2^-130 -> 2^-133 (subnormal), 1e30 (2^99.66) -> 2^92."""
+    C = np.array([0.0, 1.0, -3.0, 2.0 ** -130, 1e30])
+    T = np.array([0.0, 1.0, 5.0, 2.0 ** -130, 2e30])
+    E = np.array([0.5, 0.0, 2.0, 0.0, 1e20])
+    ulp = np.array([2.0 ** -133, 2.0 ** -7, 2.0 ** -6, 2.0 ** -133, 2.0 ** 92])
+    assert np.array_equal(h.bound(C, T, False), 1e-5 * T)
+    assert np.array_equal(h.bound(C, T, False, E), 1e-5 * T + E)
+    assert np.array_equal(h.bound(C, T, True), 1e-5 * T + ulp)
+    assert np.array_equal(h.bound(C, T, True, E), 1e-5 * T + E + ulp)
+
+
+def pin_compare(h):
+    """compare() on cases worked out by hand: errors exactly at the bound
+    pass and the next double above it fails; T = 0 demands an exact zero
+    (FP32) or at most the bfloat16 subnormal spacing (BF16); +0 equals -0; E
+    counts only when given, and n_plain_bad counts what passes only thanks
+    to it; NaN must meet NaN; a value beyond the output type's range must
+    meet the infinity of its sign; the worst ratio and the first failing
+    index are reported."""
+    def one(g, c, t, bf16, e=None):
+        return h.compare(np.array([g]), np.array([c]), np.array([t]), bf16,
+                         None if e is None else np.array([e]))
+    lim = 1e-5 * 2.0 ** 20                       # exact: a power-of-two multiple
+    assert one(lim, 0.0, 2.0 ** 20, False)["n_bad"] == 0
+    assert one(np.nextafter(lim, np.inf), 0.0, 2.0 ** 20, False)["n_bad"] == 1
+    assert one(-lim, 0.0, 2.0 ** 20, False)["n_bad"] == 0
+    assert one(0.0, 0.0, 0.0, False)["n_bad"] == 0
+    assert one(-0.0, 0.0, 0.0, False)["n_bad"] == 0
+    r = one(2.0 ** -149, 0.0, 0.0, False)
+    assert r["n_bad"] == 1 and r["max_ratio"] == float("inf")
+    assert one(2.0 ** -133, 0.0, 0.0, True)["n_bad"] == 0
+    assert one(2.0 ** -132, 0.0, 0.0, True)["n_bad"] == 1
+    assert one(1.0 + 2.0 ** -7, 1.0, 0.0, True)["n_bad"] == 0
+    assert one(1.0 + 2.0 ** -6, 1.0, 0.0, True)["n_bad"] == 1
+    assert one(1.0 + 2.0 ** -7, 1.0, 0.0, False)["n_bad"] == 1
+    r = one(0.5, 0.0, 0.0, False, 0.5)
+    assert r["n_bad"] == 0 and r["n_plain_bad"] == 1
+    assert one(0.5, 0.0, 0.0, False)["n_bad"] == 1
+    assert one(0.5, 0.0, 0.0, False, 0.25)["n_bad"] == 1
+    nan, inf = float("nan"), float("inf")
+    assert one(nan, nan, 1.0, False)["n_bad"] == 0
+    assert one(nan, nan, 1.0, True)["n_bad"] == 0
+    assert one(1.0, nan, 1.0, False)["n_bad"] == 1
+    assert one(nan, 1.0, 1.0, False)["n_bad"] == 1
+    assert one(inf, 1e39, 1e39, False)["n_bad"] == 0
+    assert one(-inf, -1e39, 1e39, False)["n_bad"] == 0
+    assert one(-inf, 1e39, 1e39, False)["n_bad"] == 1
+    assert one(3.4028234663852886e38, 1e39, 1e39, False)["n_bad"] == 1
+    assert one(inf, 1.0, 1.0, False)["n_bad"] == 1
+    assert one(inf, 3.4e38, 3.4e38, True)["n_bad"] == 0     # above bfloat16's largest
+    assert one(inf, 3.4e38, 3.4e38, False)["n_bad"] == 1    # float32 still holds it
+    g = np.array([1.0, 2.0, 3.0, 4.0 + 1e-3, 5.0])
+    C = np.array([1.0, 2.0 + 0.5e-5, 3.0, 4.0, 5.0])
+    r = h.compare(g, C, np.ones(5), False)
+    assert r["n_bad"] == 1 and r["first_bad"] == (3,)
+    assert abs(r["max_ratio"] - 100.0) < 1e-6
+    r = h.compare(g[:3], C[:3], np.ones(3), False)
+    assert r["n_bad"] == 0 and abs(r["max_ratio"] - 0.5) < 1e-6
+
+
+HELPER_PINS = [pin_bf16_ulp, pin_round_to_output, pin_bound, pin_compare]

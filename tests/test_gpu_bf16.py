@@ -12,7 +12,7 @@ import pytest
 import microscaled_block_scaled_amd as mxg
 import mxinputs
 import oracle
-from gpu_util import host64, log, sample_rows
+from gpu_util import acceptance, host64, log, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -39,8 +39,7 @@ def _check(A, B, out, C, rows=None, what=""):
     g = host64(C)
     if rows is not None:
         g = g[np.asarray(rows)]
-    r = oracle.compare(g, Cref, T, out == BF16)
-    log("  %s: worst err/bound %.3g" % (what, r["max_ratio"]))
+    r = acceptance(g, Cref, T, out == BF16, what=what)
     assert r["n_bad"] == 0, "%s: %d bad, worst ratio %.3g at %s" % (
         what, r["n_bad"], r["max_ratio"], r["first_bad"])
 

@@ -12,7 +12,7 @@ import pytest
 import microscaled_block_scaled_amd as mxg
 import mxinputs
 import oracle
-from gpu_util import host64, log, sample_rows
+from gpu_util import acceptance, host64, log, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -30,15 +30,13 @@ def _run(case, out, tile=None, split_k=0):
     return C
 
 
-def _check(case, out, C, rows=None, what=""):
+def _check(case, out, C, rows=None, what="", group_term=False):
     Cref, T, E = oracle.gemm(E5M2, case["A"], case["A_scale"], case["B"], case["B_scale"],
                              case["K"], rows=rows, group_bound=True)
     g = host64(C)
     if rows is not None:
         g = g[np.asarray(rows)]
-    r = oracle.compare(g, Cref, T, out == BF16, E)
-    if "n_plain_bad" in r:
-        log("  %s: %d elements beyond 1e-5*T alone" % (what, r["n_plain_bad"]))
+    r = acceptance(g, Cref, T, out == BF16, E, group_term, what)
     assert r["n_bad"] == 0, "%s: %d bad, worst ratio %.3g at %s" % (
         what, r["n_bad"], r["max_ratio"], r["first_bad"])
 
@@ -72,11 +70,13 @@ def test_e5m2_every_tile(tile, split):
 
 def test_e5m2_wide_scales():
     """Scale bytes drawn over a wide range, so blocks of very different
-    magnitude meet in one sum."""
+    magnitude meet in one sum.  One block then dominates most outputs, so
+    the error of its groups of 8 is not averaged over many blocks: the bound
+    adds the oracle's group term (deliberately wide-range input)."""
     case = mxinputs.make_random(E5M2, 96, 80, 1024, seed=8, scale_lo=90, scale_hi=160)
     log("e5m2 wide scales")
     for out in (F32, BF16):
-        _check(case, out, _run(case, out), what="wide scales")
+        _check(case, out, _run(case, out), what="wide scales", group_term=True)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1000, 8192), (8, 8192, 4096)])

@@ -13,7 +13,7 @@ import pytest
 import microscaled_block_scaled_amd as mxg
 import mxinputs
 import oracle
-from gpu_util import host64, log, sample_rows
+from gpu_util import acceptance, host64, log, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -41,16 +41,14 @@ def _run(case, out, tile=None, split_k=0):
     return C
 
 
-def _check(case, out, C, rows=None, what=""):
+def _check(case, out, C, rows=None, what="", group_term=False):
     Cref, T, E = oracle.gemm(case["fa"], case["A"], case["A_scale"], case["B"],
                              case["B_scale"], case["K"], rows=rows, group_bound=True,
                              fmt_b=case["fb"])
     g = host64(C)
     if rows is not None:
         g = g[np.asarray(rows)]
-    r = oracle.compare(g, Cref, T, out == BF16, E)
-    if "n_plain_bad" in r:
-        log("  %s: %d elements beyond 1e-5*T alone" % (what, r["n_plain_bad"]))
+    r = acceptance(g, Cref, T, out == BF16, E, group_term, what)
     assert r["n_bad"] == 0, "%s: %d bad, worst ratio %.3g at %s" % (
         what, r["n_bad"], r["max_ratio"], r["first_bad"])
 
@@ -64,7 +62,9 @@ TAIL_SHAPES = [(1, 1, 128), (33, 255, 128), (255, 257, 384), (130, 7, 640), (64,
 def test_e5m2_pair_tails(fa, fb, M, N, K, out):
     log("e5m2 pair %d x %d out=%d M=%d N=%d K=%d" % (fa, fb, out, M, N, K))
     case = _case(fa, fb, M, N, K, seed=M + 2 * N + K + fa)
-    _check(case, out, _run(case, out), what="tails")
+    # K = 128 is four blocks: the group error of an 8-bit operand is then not
+    # averaged over many blocks (the only shape here that needs the group term)
+    _check(case, out, _run(case, out), what="tails", group_term=K == 128)
 
 
 @pytest.mark.parametrize("split", [1, 3], ids=["nosplit", "split3"])

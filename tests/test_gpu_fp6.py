@@ -12,7 +12,7 @@ import pytest
 import microscaled_block_scaled_amd as mxg
 import mxinputs
 import oracle
-from gpu_util import host64, log, sample_rows
+from gpu_util import acceptance, host64, log, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -32,15 +32,13 @@ def _run(case, out, tile=None, split_k=0):
     return C
 
 
-def _check(case, out, C, rows=None, what=""):
+def _check(case, out, C, rows=None, what="", group_term=False):
     Cref, T, E = oracle.gemm(case["fmt"], case["A"], case["A_scale"], case["B"],
                              case["B_scale"], case["K"], rows=rows, group_bound=True)
     g = host64(C)
     if rows is not None:
         g = g[np.asarray(rows)]
-    r = oracle.compare(g, Cref, T, out == BF16, E)
-    log("  %s: worst err/bound %.3g, %d beyond 1e-5*T alone" % (
-        what, r["max_ratio"], r.get("n_plain_bad", 0)))
+    r = acceptance(g, Cref, T, out == BF16, E, group_term, what)
     assert r["n_bad"] == 0, "%s: %d bad, worst ratio %.3g at %s" % (
         what, r["n_bad"], r["max_ratio"], r["first_bad"])
 
@@ -81,9 +79,11 @@ def test_fp6_small_m_full_size_and_scales(fmt):
     C = _run(case, BF16)
     assert torch.equal(C, _run(case, BF16))
     _check(case, BF16, C, rows=sample_rows(2048, n=32), what="full size")
+    # deliberately wide-range scales: one block dominates most outputs, so
+    # the bound adds the oracle's group term
     case = mxinputs.make_random(fmt, 96, 80, 1024, seed=8, scale_lo=90, scale_hi=160)
     for out in (F32, BF16):
-        _check(case, out, _run(case, out), what="wide scales")
+        _check(case, out, _run(case, out), what="wide scales", group_term=True)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=IDS)

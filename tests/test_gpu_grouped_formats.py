@@ -14,7 +14,7 @@ import pytest
 import microscaled_block_scaled_amd as mxg
 import mxinputs
 import oracle
-from gpu_util import host64, log
+from gpu_util import acceptance, host64, log
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +59,7 @@ def _check(case, out, C, pick=None):
     g = host64(C)
     if pick is not None:
         g = g[np.asarray(pick)]
-    r = oracle.compare(g, Cref, T, out == BF16, E)
-    log("  worst err/bound %.3g" % r["max_ratio"])
+    r = acceptance(g, Cref, T, out == BF16, E, what="grouped formats")
     assert r["n_bad"] == 0, "%d bad, worst ratio %.3g at %s" % (
         r["n_bad"], r["max_ratio"], r["first_bad"])
 

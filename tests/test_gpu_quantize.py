@@ -111,7 +111,7 @@ def test_quantize_full_size(fmt):
 def test_quantize_then_gemm(fmt):
     """Operands quantized on the GPU feed mx_gemm directly."""
     import torch
-    from gpu_util import check_against_oracle
+    from gpu_util import acceptance, check_against_oracle
     a = _random(300, 1024, 5, torch.float32)
     b = _random(200, 1024, 6, torch.bfloat16)
     qa, sa = mxg.mx_quantize(a, fmt)
@@ -124,7 +124,7 @@ def test_quantize_then_gemm(fmt):
         # FP6: judged with the oracle's group term E, as the FP6 GEMM tests do
         Cref, T, E = oracle.gemm(fmt, case["A"], case["A_scale"], case["B"], case["B_scale"],
                                  1024, group_bound=True)
-        res = oracle.compare(C.double().cpu().numpy(), Cref, T, False, E)
+        res = acceptance(C.double().cpu().numpy(), Cref, T, False, E, what="quantize then gemm")
     else:
         res, *_ = check_against_oracle(case, mxinputs.OUT_FP32, C=C)
     assert res["n_bad"] == 0, res

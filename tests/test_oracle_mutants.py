@@ -169,3 +169,67 @@ def test_pins_catch_grouped_bf16_mutant(name, old, new):
     mut.gemm_grouped_bf16 = ns["gemm_grouped_bf16"].__get__(mut)
     with pytest.raises((AssertionError, ValueError)):
         oracle_pins.pin_grouped_bf16(mut)
+
+
+# Mistakes planted in the acceptance helpers (oracle/__init__.py): a looser
+# bfloat16 ulp, the wrong subnormal spacing or clamp, a doubled tolerance,
+# the ulp term added to FP32 output, a loose comparison, NaN or infinities
+# accepted whatever the device returned, round-half-up instead of
+# round-to-even in the BF16 conversion, and E leaking into the plain count.
+HELPER_MUTANTS = [
+    ("ulp_one_bit_loose", "ulp = np.ldexp(1.0, expo - 7)", "ulp = np.ldexp(1.0, expo - 6)"),
+    ("ulp_clamp", "expo = np.maximum(e - 1, -126)", "expo = np.maximum(e - 1, -127)"),
+    ("ulp_zero", "np.ldexp(1.0, -133), ulp)", "np.ldexp(1.0, -132), ulp)"),
+    ("ulp_binade", "expo = np.maximum(e - 1, -126)", "expo = np.maximum(e, -126)"),
+    ("tolerance_doubled", "b = REL_TOL * np.asarray(T, np.float64)",
+     "b = 2 * REL_TOL * np.asarray(T, np.float64)"),
+    ("ulp_for_fp32", "    if out_is_bf16:\n        b = b + bf16_ulp(C)",
+     "    if True:\n        b = b + bf16_ulp(C)"),
+    ("loose_compare", "bad = special_bad | (~special & ~(err <= lim))",
+     "bad = special_bad | (~special & (err > 2 * lim))"),
+    ("nan_accepts_anything", "np.where(cnan, np.isnan(g), g == ref)",
+     "np.where(cnan, True, g == ref)"),
+    ("inf_sign_ignored", "np.where(cnan, np.isnan(g), g == ref)",
+     "np.where(cnan, np.isnan(g), np.isinf(g))"),
+    ("bf16_round_half_up", "rnd = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000",
+     "rnd = (bits + 0x8000) & 0xFFFF0000"),
+    ("bf16_truncates", "rnd = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000",
+     "rnd = bits & 0xFFFF0000"),
+    ("plain_count_with_e", "pw, pbad = judge(bound(C, T, out_is_bf16))",
+     "pw, pbad = judge(bound(C, T, out_is_bf16, E))"),
+    ("zero_limit_lenient", "np.where(err == 0, 0.0, np.inf))", "np.where(err == 0, 0.0, 0.0))"),
+]
+
+
+def _helper_namespace(old=None, new=None):
+    import inspect
+    import types
+
+    import numpy as np
+    src = "\n\n".join(inspect.getsource(f) for f in (oracle.bf16_ulp, oracle.bound,
+                                                      oracle.round_to_output, oracle.compare))
+    if old is not None:
+        assert old in src, old
+        src = src.replace(old, new, 1)
+    ns = {"np": np, "REL_TOL": oracle.REL_TOL}
+    exec(src, ns)
+    return types.SimpleNamespace(**{k: ns[k] for k in ("bf16_ulp", "bound", "round_to_output",
+                                                        "compare")})
+
+
+def test_helper_namespace_unmutated_passes():
+    h = _helper_namespace()
+    for pin in oracle_pins.HELPER_PINS:
+        pin(h)
+
+
+@pytest.mark.parametrize("name,old,new", HELPER_MUTANTS, ids=[m[0] for m in HELPER_MUTANTS])
+def test_pins_catch_helper_mutant(name, old, new):
+    h = _helper_namespace(old, new)
+    caught = []
+    for pin in oracle_pins.HELPER_PINS:
+        try:
+            pin(h)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin caught helper mutant %s" % name
