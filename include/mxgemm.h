@@ -41,8 +41,17 @@
  * Thread safety.  Calls may be made concurrently from several host threads
  * and streams.  The library keeps read-only per-device state, set up once per
  * device on first use, and, for split-K calls (see mx_plan_t), one workspace
- * per (device, stream), grown on demand and held until the process exits;
- * split-K calls on one stream are serialised while they are enqueued.
+ * per (device, stream handle).  Lifetime of a workspace: it is allocated on
+ * that stream with hipMallocAsync the first time a call there needs one,
+ * replaced (freed and reallocated on the stream) when a call needs more, and
+ * otherwise held, at the largest size a call on that stream has needed,
+ * until the process exits -- destroying the stream does not free it.  Calls
+ * on one stream are ordered by the stream; calls on different streams use
+ * different workspaces; split-K calls on one stream from several host threads
+ * are serialised while they are enqueued.  One precondition follows: a
+ * stream must have finished its split-K calls (hipStreamSynchronize) before
+ * it is destroyed, because a stream created later may receive the same
+ * handle and would then share that workspace with the still-running calls.
  */
 #ifndef MXGEMM_H
 #define MXGEMM_H
@@ -96,7 +105,8 @@ enum { MX_IN_FP32 = 1, MX_IN_BF16 = 2 };
 
 /*
  * C = A * B^T with MX block scaling, enqueued on `stream`.
- *   fmt        MX_FMT_E2M1 or MX_FMT_E4M3 (A and B share the format)
+ *   fmt        any MX_FMT_* code (A and B share the format; mx_gemm_mixed
+ *              takes one per operand)
  *   M, N, K    sizes; K a multiple of 128, at most MX_MAX_K
  *   A, B       packed elements (layout above), 16-byte aligned device pointers
  *   A_scale,
@@ -120,9 +130,8 @@ const char *mx_strerror(int code);
  * C, staging A and B through LDS.  Small M uses a 64-row tile.  When the
  * tiles cannot fill the GPU and K is long, each workgroup takes one of
  * split_k K-slices and writes FP32 partial results to a workspace that a
- * second kernel adds in slice order (workspace_bytes, taken from the
- * library's per-stream workspace, allocated with hipMallocAsync on the
- * caller's stream the first time a call needs more).
+ * second kernel adds in slice order (workspace_bytes of the stream's
+ * workspace, see "Thread safety" above).
  */
 enum { MX_VARIANT_TILE = 1 };
 
@@ -145,6 +154,14 @@ typedef struct {
  */
 int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype,
                  mx_plan_t *plan);
+
+/*
+ * Test hook: the next `count` calls of mx_gemm and its variants that need a
+ * split-K workspace fail as if obtaining it had failed: they return
+ * MX_ERR_ALLOC and launch nothing.  count <= 0 clears it.  For exercising
+ * the MX_ERR_ALLOC path only.
+ */
+void mx_debug_fail_allocations(int count);
 
 /*
  * The output tile shapes the library has kernels for.  Writes up to

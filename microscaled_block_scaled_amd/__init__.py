@@ -131,6 +131,8 @@ def lib():
     L.mx_gemm_grouped.restype = ctypes.c_int
     L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
                                   vp, vp, vp, ctypes.c_int, vp]
+    L.mx_debug_fail_allocations.restype = None
+    L.mx_debug_fail_allocations.argtypes = [ctypes.c_int]
     L.mx_mfma_ceiling.restype = ctypes.c_int
     L.mx_mfma_ceiling.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp]
     _lib = L
@@ -211,13 +213,29 @@ def _as_u8(t, name):
     return t
 
 
-def _k_of(fmt, row_bytes):
-    """K-values in an operand row of row_bytes bytes."""
+def _row_bytes(fmt, K):
+    """Bytes of an operand row of K values in format fmt."""
     if fmt == FMT_E2M1:
-        return row_bytes * 2
+        return K // 2
     if fmt in (FMT_E2M3, FMT_E3M2):
-        return row_bytes // 3 * 4
-    return row_bytes
+        return K // 4 * 3
+    return K
+
+
+def _k_of(fmt, row_bytes):
+    """K-values in an operand row of row_bytes bytes; raises ValueError when
+    no K has rows of exactly that length (an FP6 row must be a multiple of 3
+    bytes, an E2M1 row any length)."""
+    if fmt == FMT_E2M1:
+        K = row_bytes * 2
+    elif fmt in (FMT_E2M3, FMT_E3M2):
+        K = row_bytes // 3 * 4
+    else:
+        K = row_bytes
+    if _row_bytes(fmt, K) != row_bytes:
+        raise ValueError("a row of %d bytes holds no whole number of format-%d elements "
+                         "(FP6 rows are 3*K/4 bytes)" % (row_bytes, fmt))
+    return K
 
 
 def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
@@ -327,6 +345,11 @@ def mx_gemm_bf16(a, b, out_dtype=None, out=None, stream=None, tile=None, split_k
     if rc != MX_OK:
         _raise(rc)
     return out
+
+
+def debug_fail_allocations(count):
+    """Test hook: the next `count` split-K workspace allocations fail."""
+    lib().mx_debug_fail_allocations(int(count))
 
 
 # Launch shape and work of mx_mfma_ceiling (include/mxgemm.h).

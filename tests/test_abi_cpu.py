@@ -488,3 +488,15 @@ def test_fp6_accepted_where_documented():
     with pytest.raises(ValueError):          # K mismatch against a 128-byte E4M3 row
         mxg.mx_gemm(a, s, torch.zeros((4, 128), dtype=torch.uint8), s, mxg.FMT_E2M3,
                     fmt_b=mxg.FMT_E4M3)
+
+
+def test_operand_row_length_must_hold_whole_elements():
+    """K is inferred from an operand's row length: an FP6 row must be exactly
+    3*K/4 bytes (97 bytes is refused, not read as K = 128)."""
+    assert mxg._k_of(mxg.FMT_E2M3, 96) == 128
+    assert mxg._k_of(mxg.FMT_E3M2, 3 * 1024 // 4) == 1024
+    assert mxg._k_of(mxg.FMT_E2M1, 64) == 128 and mxg._k_of(mxg.FMT_E4M3, 128) == 128
+    for fmt in (mxg.FMT_E2M3, mxg.FMT_E3M2):
+        for rb in (97, 98, 1):
+            with pytest.raises(ValueError):
+                mxg._k_of(fmt, rb)
