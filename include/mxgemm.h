@@ -91,7 +91,9 @@ enum {
     MX_ERR_ARCH = -7,       /* the current device is not gfx950               */
     MX_ERR_ALLOC = -8,      /* split-K workspace allocation failed            */
     MX_ERR_LAUNCH = -9,     /* a kernel launch failed                         */
-    MX_ERR_IN_DTYPE = -10   /* in_dtype is not MX_IN_FP32 / MX_IN_BF16       */
+    MX_ERR_IN_DTYPE = -10,  /* in_dtype is not MX_IN_FP32 / MX_IN_BF16       */
+    MX_ERR_SCRATCH = -11    /* mx_gemm_noalloc: the problem's split-K workspace
+                               exceeds MX_NOALLOC_SCRATCH_BYTES               */
 };
 
 /* Input element types of mx_quantize. */
@@ -131,7 +133,8 @@ const char *mx_strerror(int code);
  * tiles cannot fill the GPU and K is long, each workgroup takes one of
  * split_k K-slices and writes FP32 partial results to a workspace that a
  * second kernel adds in slice order (workspace_bytes of the stream's
- * workspace, see "Thread safety" above).
+ * workspace, see "Thread safety" above; mx_gemm_noalloc uses a fixed scratch
+ * instead).
  */
 enum { MX_VARIANT_TILE = 1 };
 
@@ -154,6 +157,33 @@ typedef struct {
  */
 int mx_gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype,
                  mx_plan_t *plan);
+
+/*
+ * mx_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, plan, kernels, errors and results (bit for bit) as mx_gemm;
+ * the only difference is where a split-K call keeps its FP32 partial planes.
+ * Instead of allocating them, it uses a fixed scratch array in device memory
+ * of MX_NOALLOC_SCRATCH_BYTES, one per device, which the library holds from
+ * its first call on that device until the process ends.  It calls no
+ * allocator at all (no hipMalloc, hipMallocAsync, hipFree or library routine
+ * that allocates).
+ *   Returns MX_ERR_SCRATCH, before any HIP call, when the plan's
+ *   workspace_bytes (mx_gemm_plan) exceeds MX_NOALLOC_SCRATCH_BYTES: e.g.
+ *   M = 256, N = 8192, K = 28672 (4 K-slices) needs exactly 32 MiB and runs;
+ *   M = 512, N = 6144, K = 28672 (4 slices of 12 MiB) is refused.  Problems
+ *   the plan does not split need no scratch and have no limit.
+ * Every call on one device shares that device's scratch, and it keeps what
+ * the last call wrote (each split-K call writes every element it reads, so
+ * nothing needs clearing): two calls that overlap in time on one device --
+ * on different streams, or from different host threads without stream
+ * ordering between them -- race on it and may return wrong results.
+ */
+#define MX_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+int mx_gemm_noalloc(int fmt, int64_t M, int64_t N, int64_t K,
+                    const void *A, const void *A_scale,
+                    const void *B, const void *B_scale,
+                    void *C, int out_dtype, void *stream);
 
 /*
  * Test hook: the next `count` calls of mx_gemm and its variants that need a

@@ -57,12 +57,14 @@ MX_ERR_ARCH = -7
 MX_ERR_ALLOC = -8
 MX_ERR_LAUNCH = -9
 MX_ERR_IN_DTYPE = -10
+MX_ERR_SCRATCH = -11
+NOALLOC_SCRATCH_BYTES = 32 << 20   # mx_gemm_noalloc's fixed split-K scratch per device
 
 IN_FP32 = 1
 IN_BF16 = 2
 
 _VALUE_ERRORS = (MX_ERR_FORMAT, MX_ERR_OUT_DTYPE, MX_ERR_SHAPE, MX_ERR_NULL, MX_ERR_ALIGN,
-                 MX_ERR_IN_DTYPE)
+                 MX_ERR_IN_DTYPE, MX_ERR_SCRATCH)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxgemm.so")
 _lib = None
@@ -131,6 +133,9 @@ def lib():
     L.mx_gemm_grouped.restype = ctypes.c_int
     L.mx_gemm_grouped.argtypes = [ctypes.c_int, i64, ctypes.POINTER(i64), i64, i64, vp, vp,
                                   vp, vp, vp, ctypes.c_int, vp]
+    L.mx_gemm_noalloc.restype = ctypes.c_int
+    L.mx_gemm_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp,
+                                  ctypes.c_int, vp]
     L.mx_debug_fail_allocations.restype = None
     L.mx_debug_fail_allocations.argtypes = [ctypes.c_int]
     L.mx_mfma_ceiling.restype = ctypes.c_int
@@ -345,6 +350,14 @@ def mx_gemm_bf16(a, b, out_dtype=None, out=None, stream=None, tile=None, split_k
     if rc != MX_OK:
         _raise(rc)
     return out
+
+
+def gemm_noalloc_ptr(fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream=0):
+    """Raw entry point of mx_gemm_noalloc (no allocation: split-K planes in
+    the library's fixed per-device scratch): integer device addresses,
+    returns the status code."""
+    return lib().mx_gemm_noalloc(int(fmt), int(M), int(N), int(K), A, A_scale, B, B_scale, C,
+                                 int(out_dtype), stream or None)
 
 
 def debug_fail_allocations(count):

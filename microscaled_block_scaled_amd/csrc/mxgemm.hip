@@ -146,16 +146,46 @@ bool fail_injected()
     return false;
 }
 
-// Checks that need no device, then the device check, then the launch.
+// The split-K scratch of mx_gemm_noalloc: a fixed array in device memory,
+// one per device the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address on each device is looked up once, with that device current, and
+// only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = (size_t)MX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch[kMaxDevices];
+int g_scratch_rc[kMaxDevices];
+
+int device_scratch(int dev, void **ptr)
+{
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            g_scratch_rc[dev] = MX_ERR_LAUNCH;
+            return;
+        }
+        g_scratch[dev] = p;
+        g_scratch_rc[dev] = MX_OK;
+    });
+    *ptr = g_scratch[dev];
+    return g_scratch_rc[dev];
+}
+
+// Checks that need no device, then the device check, then the launch.  With
+// noalloc the split-K workspace is the device's fixed scratch instead of a
+// stream-ordered allocation.
 int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
              const void *A, const void *A_scale, const void *B, const void *B_scale,
-             void *C, int out_dtype, void *stream)
+             void *C, int out_dtype, void *stream, bool noalloc = false)
 {
     const bool scaled = fmt_a != kFmtBF16;
     if (!A || !B || !C || (scaled && (!A_scale || !B_scale))) return MX_ERR_NULL;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) ||
         (scaled && (!aligned(A_scale, 4) || !aligned(B_scale, 4))))
         return MX_ERR_ALIGN;
+    if (noalloc && plan.workspace_bytes > (int64_t)kScratchBytes) return MX_ERR_SCRATCH;
     int dev = -1;
     int rc = device_ready(&dev);
     if (rc != MX_OK) return rc;
@@ -165,9 +195,16 @@ int run_plan(const mx_plan_t &plan, int fmt_a, int fmt_b, int64_t M, int64_t N, 
     float *W = nullptr;
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     if (plan.workspace_bytes > 0) {
-        ws_lock.lock();
-        W = fail_injected() ? nullptr : stream_workspace(dev, s, (size_t)plan.workspace_bytes);
-        if (!W) return MX_ERR_ALLOC;
+        if (noalloc) {
+            void *p = nullptr;
+            rc = device_scratch(dev, &p);
+            if (rc != MX_OK) return rc;
+            W = (float *)p;
+        } else {
+            ws_lock.lock();
+            W = fail_injected() ? nullptr : stream_workspace(dev, s, (size_t)plan.workspace_bytes);
+            if (!W) return MX_ERR_ALLOC;
+        }
     }
     bool launched;
     const int o = out_dtype;
@@ -219,6 +256,8 @@ extern "C" const char *mx_strerror(int code)
     case MX_ERR_ALLOC: return "workspace allocation failed";
     case MX_ERR_LAUNCH: return "kernel launch failed";
     case MX_ERR_IN_DTYPE: return "unsupported input type (expected MX_IN_FP32 or MX_IN_BF16)";
+    case MX_ERR_SCRATCH: return "split-K workspace larger than the fixed scratch of the "
+                                "no-allocation entry point (MX_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
     }
 }
@@ -249,6 +288,17 @@ extern "C" int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
     int rc = make_plan(fmt, M, N, K, out_dtype, &plan);
     if (rc != MX_OK) return rc;
     return run_plan(plan, fmt, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream);
+}
+
+extern "C" int mx_gemm_noalloc(int fmt, int64_t M, int64_t N, int64_t K,
+                               const void *A, const void *A_scale,
+                               const void *B, const void *B_scale,
+                               void *C, int out_dtype, void *stream)
+{
+    mx_plan_t plan;
+    int rc = make_plan(fmt, M, N, K, out_dtype, &plan);
+    if (rc != MX_OK) return rc;
+    return run_plan(plan, fmt, fmt, M, N, K, A, A_scale, B, B_scale, C, out_dtype, stream, true);
 }
 
 extern "C" void mx_debug_fail_allocations(int count)

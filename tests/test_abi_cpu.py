@@ -46,7 +46,7 @@ def test_header_constants_match_binding():
 
 
 def test_strerror_covers_codes():
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         s = mxg.strerror(code)
         assert s and s != "unknown error code", code
     assert mxg.strerror(5) == "unknown error code"
@@ -488,6 +488,35 @@ def test_fp6_accepted_where_documented():
     with pytest.raises(ValueError):          # K mismatch against a 128-byte E4M3 row
         mxg.mx_gemm(a, s, torch.zeros((4, 128), dtype=torch.uint8), s, mxg.FMT_E2M3,
                     fmt_b=mxg.FMT_E4M3)
+
+
+@pytest.mark.parametrize("fmt,M,N,K,out,code", [
+    (0, 16, 16, 128, 1, mxg.MX_ERR_FORMAT),
+    (1, 16, 16, 128, 0, mxg.MX_ERR_OUT_DTYPE),
+    (1, 16, 16, 64, 1, mxg.MX_ERR_SHAPE),
+    (2, 16, 16, (1 << 24) + 128, 2, mxg.MX_ERR_SHAPE),
+])
+def test_noalloc_argument_errors(fmt, M, N, K, out, code):
+    """mx_gemm_noalloc checks its arguments as mx_gemm does, before any HIP call."""
+    L = mxg.lib()
+    assert L.mx_gemm_noalloc(fmt, M, N, K, None, None, None, None, None, out, None) == code
+
+
+def test_noalloc_rejects_workspace_beyond_scratch():
+    """A problem whose split-K planes exceed the fixed scratch is refused with
+    MX_ERR_SCRATCH before any HIP call (the pointers are never touched: any
+    16-byte aligned values will do); one that fits, or needs no split, is
+    not refused for its size."""
+    L = mxg.lib()
+    big = (2, 512, 6144, 28672)             # 256x192 tiles, split 4: 4 planes of 12 MiB
+    p = mxg.plan(*big, out_dtype=2)
+    assert p["workspace_bytes"] > mxg.NOALLOC_SCRATCH_BYTES, p
+    fake = 1 << 20
+    assert L.mx_gemm_noalloc(big[0], big[1], big[2], big[3], fake, fake, fake, fake, fake, 2,
+                             None) == mxg.MX_ERR_SCRATCH
+    fits = mxg.plan(2, 256, 8192, 28672, out_dtype=2)
+    assert 0 < fits["workspace_bytes"] <= mxg.NOALLOC_SCRATCH_BYTES, fits
+    assert "scratch" in mxg.strerror(mxg.MX_ERR_SCRATCH)
 
 
 def test_operand_row_length_must_hold_whole_elements():
