@@ -16,7 +16,6 @@ MI355X dense MX MFMA peak and against the measured MFMA ceiling of the same
 device, and the CPU oracle's rate on a bounded row sample of the workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
-    python bench.py --cold [--all]    (per-launch cold-cache timing only)
     python bench.py --ceiling         (the MFMA ceiling of both formats)
     python bench.py --quantize | --grouped | --mixed | --bf16
         (the quantizer / grouped GEMM / mixed-format GEMM / dense BF16 GEMM)
@@ -228,10 +227,15 @@ def bench_one(name, steps, warmup, with_cpu, cold_launches=60, with_ceiling=True
     flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev).view(torch.float32)
 
     def per_launch(evict):
+        # The stream is kept busy (the evicting read, or an untimed call on
+        # the same operands) while the event pair and the timed call are
+        # enqueued, so the host's launch latency stays outside the pair.
         ts = []
         for i in range(5 + cold_launches):
             if evict:
                 flush.amax()
+            else:
+                call(0)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             call(0)
@@ -512,58 +516,6 @@ def bench_mixed(steps, warmup, name):
             "roofline": roof}
 
 
-def bench_cold(name, launches=60, warmup=10):
-    """Cold-cache timing of one workload: before every launch a 512 MiB
-    device read (a max-reduction) evicts A, B and C from the L2s and the
-    256 MB last-level cache, and each launch is timed alone between its own
-    event pair on the launch stream.  The eviction reads, so it leaves clean
-    lines behind: a write would leave dirty ones, and the launch would then
-    pay for their write-back (a plain row reduction over 235 MB measured
-    2.4 TB/s after a write flush, 4.8 after a read flush).  Reports the
-    median and the 10th / 90th percentiles, and the same warm (no eviction)."""
-    import torch
-    import microscaled_block_scaled_amd as mxg
-    case = mxinputs.make_case(name)
-    fmt, M, N, K, out = case["fmt"], case["M"], case["N"], case["K"], case["out"]
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    A, As, B, Bs = (torch.from_numpy(case[k]).to(dev) for k in ("A", "A_scale", "B", "B_scale"))
-    C = torch.empty((M, N), dtype=torch.float32 if out == mxinputs.OUT_FP32 else torch.bfloat16,
-                    device=dev)
-    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev).view(torch.float32)
-    stream = torch.cuda.current_stream(dev)
-    args = (fmt, M, N, K, A.data_ptr(), As.data_ptr(), B.data_ptr(), Bs.data_ptr(),
-            C.data_ptr(), out, stream.cuda_stream)
-
-    def timed(evict):
-        ts = []
-        for i in range(warmup + launches):
-            if evict:
-                flush.amax()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            if mxg.gemm_ptr(*args) != 0:
-                raise RuntimeError("mx_gemm failed")
-            e1.record(stream)
-            e1.synchronize()
-            if i >= warmup:
-                ts.append(e0.elapsed_time(e1) * 1e3)
-        ts.sort()
-        q = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
-        return {"median_us": round(q(0.5), 2), "p10_us": round(q(0.1), 2),
-                "p90_us": round(q(0.9), 2)}
-
-    flops = 2.0 * M * N * K
-    nbytes = algorithmic_bytes(fmt, M, N, K, out)
-    res = {"workload": name, "launches": launches, "cold": timed(True), "warm": timed(False)}
-    for k in ("cold", "warm"):
-        t = res[k]["median_us"] * 1e-6
-        res[k]["tflops"] = round(flops / t / 1e12, 1)
-        res[k]["hbm_gbs"] = round(nbytes / t / 1e9, 1)
-    return res
-
-
 def copy_calibration(nbytes=256 << 20, reps=3):
     """A plain device copy of known size, for scaling the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the GEMM kernels."""
@@ -684,9 +636,6 @@ def main():
                     help="time mx_quantize (both formats, FP32 and BF16 input) instead")
     ap.add_argument("--grouped", action="store_true",
                     help="time the grouped GEMM (eight uneven experts; MXFP8, MXFP4, BF16) instead")
-    ap.add_argument("--cold", action="store_true",
-                    help="per-launch cold-cache and warm timings (median, p10, p90) of "
-                         "--workload, or of every workload with --all")
     ap.add_argument("--mixed", action="store_true",
                     help="time the other formats (A E4M3 x B E2M1; E5M2) instead")
     ap.add_argument("--bf16", action="store_true",
@@ -717,12 +666,6 @@ def main():
                     mxinputs.FMT_E3M2):
             for ind in (1, 2):
                 print(json.dumps(bench_quantize(a.steps, a.warmup, fmt, ind)), flush=True)
-        return
-    if a.cold:
-        names = sorted(mxinputs.CONFIGS, key=lambda n: (mxinputs.CONFIGS[n]["index"], n)) \
-            if a.all else [a.workload]
-        for name in names:
-            print(json.dumps(bench_cold(name)), flush=True)
         return
     if a.mixed:
         for name in MIXED_WORKLOADS:
