@@ -86,7 +86,11 @@ void fill_plan(int t, int64_t M, int64_t N, int64_t K, mx_plan_t *p, int split_r
     p->threads = c.wgm * c.wgn * 64;
     p->lds_bytes = 0;
     p->workgroups = tiles * p->split_k;
-    p->workspace_bytes = p->split_k > 1 ? p->split_k * plane_of(M, N) * 4 : 0;
+    // Planes only for grids the kernels take (callers refuse larger ones):
+    // with at most 2^31 workgroups of at most 256 x 256 outputs, M * N <= 2^47
+    // and the byte count cannot overflow.
+    p->workspace_bytes = p->split_k > 1 && p->workgroups <= kMaxGrid
+        ? p->split_k * plane_of(M, N) * 4 : 0;
 }
 
 int make_plan(int fmt, int64_t M, int64_t N, int64_t K, int out_dtype, mx_plan_t *p)

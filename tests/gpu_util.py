@@ -53,7 +53,7 @@ def _caller_file():
 
 
 def acceptance(g, Cref, T, out_is_bf16, E=None, group_term=False, what=""):
-    """North_star's rule, element by element: |gpu - C| <= 1e-5 * T, plus
+    """The acceptance rule, element by element: |gpu - C| <= 1e-5 * T, plus
     one bfloat16 ulp of C for BF16 output (NaN and out-of-range values as
     oracle.compare says).
 
