@@ -16,7 +16,7 @@ MI355X dense MX MFMA peak and against the measured MFMA ceiling of the same
 device, and the CPU oracle's rate on a bounded row sample of the workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
-    python bench.py --ceiling         (the MFMA ceiling of both formats)
+    python bench.py --ceiling         (the HBM read ceiling, the MFMA ceiling of both formats)
     python bench.py --quantize | --grouped | --mixed | --bf16
         (the quantizer / grouped GEMM / mixed-format GEMM / dense BF16 GEMM)
 """
@@ -169,6 +169,57 @@ def mfma_ceiling(fmt, target_s=0.05, reps=3):
     return res
 
 
+_HBM_CEILING = []
+
+
+def hbm_ceiling(nbytes=1 << 30, reps=5):
+    """The rate at which this device streams HBM into the CUs
+    (mx_hbm_read_ceiling, a plain read of every byte): GB/s, median of
+    `reps` launches over one of two 1 GiB buffers, alternated so that the
+    buffer read is never in the 256 MB last-level cache.  Each launch is
+    timed alone, with the stream kept busy by an untimed launch on the other
+    buffer while its event pair is enqueued.  Measured once per process."""
+    if _HBM_CEILING:
+        return _HBM_CEILING[0]
+    import torch
+    import microscaled_block_scaled_amd as mxg
+    dev = torch.device("cuda", 0)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    out = torch.empty(mxg.HBM_CEILING_WORKGROUPS * mxg.HBM_CEILING_THREADS, dtype=torch.int32,
+                      device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(buf):
+        rc = mxg.hbm_ceiling_ptr(buf.data_ptr(), nbytes, out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError("mx_hbm_read_ceiling failed: %s" % mxg.strerror(rc))
+
+    ts = []
+    for i in range(reps + 1):
+        launch(bufs[(i + 1) % 2])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch(bufs[i % 2])
+        e1.record(stream)
+        e1.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1) / 1e3)
+    del bufs
+    ts.sort()
+    _HBM_CEILING.append(round(nbytes / ts[len(ts) // 2] / 1e9, 1))
+    return _HBM_CEILING[0]
+
+
+def hbm_fields(roof):
+    """For an HBM-bound line: the measured read ceiling and the fraction of it
+    reached."""
+    if roof["bound"] == "hbm":
+        hbm = hbm_ceiling()
+        roof["hbm_read_ceiling_gbs"] = hbm
+        roof["frac_of_measured_hbm"] = round(roof["achieved"] / hbm, 4)
+    return roof
+
+
 def _percentiles(ts):
     ts = sorted(ts)
     q = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
@@ -277,6 +328,8 @@ def bench_one(name, steps, warmup, with_cpu, cold_launches=60, with_ceiling=True
     roof["tflops"] = round(flops / launch_s / 1e12, 2)
     roof["frac_of_measured_ceiling"] = (round(flops / launch_s / 1e12 / ceiling["random"], 4)
                                         if ceiling else None)
+    if with_ceiling:
+        hbm_fields(roof)
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 5),
@@ -336,13 +389,13 @@ def bench_quantize(steps, warmup, fmt, in_dtype):
             "config": {"workload": "quantize_%s_from_%s_8192x4096" % (
                 mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
                 "rows": rows, "K": K, "kernel_source_sha256": kernel_source_hash(srcs)},
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("quantize_%s_from_%s_8192x4096" % (
-                             mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"),
-                             srcs),
-                         "algorithmic_bytes": nbytes,
-                         "launch_us": round(launch_s * 1e6, 2)}}
+            "roofline": hbm_fields({
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("quantize_%s_from_%s_8192x4096" % (
+                    mxinputs.fmt_name(fmt), "f32" if in_dtype == mxg.IN_FP32 else "bf16"), srcs),
+                "algorithmic_bytes": nbytes,
+                "launch_us": round(launch_s * 1e6, 2)})}
 
 
 # Eight experts of a mixture-of-experts layer: token counts of one 4096-token
@@ -418,6 +471,7 @@ def bench_grouped(steps, warmup, fmt):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(workload, GEMM_SOURCES, plan_str)
+    hbm_fields(roof)
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)
     tflops = flops * steps / wall / 1e12
@@ -499,6 +553,7 @@ def bench_mixed(steps, warmup, name):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(name, GEMM_SOURCES, plan_str)
+    hbm_fields(roof)
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)
     tflops = flops * steps / wall / 1e12
@@ -584,6 +639,7 @@ def bench_bf16(steps, warmup, name, with_cpu):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(name, GEMM_SOURCES, plan_str)
+    hbm_fields(roof)
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)
     tflops = flops * steps / wall / 1e12
@@ -629,7 +685,8 @@ def main():
     ap.add_argument("--cold-launches", type=int, default=60,
                     help="launches timed alone for the cold / warm medians (at least 3)")
     ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the MFMA-ceiling measurement (frac_of_measured_ceiling null)")
+                    help="skip the ceiling measurements (frac_of_measured_ceiling and "
+                         "frac_of_measured_hbm null)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--quantize", action="store_true",
@@ -641,7 +698,9 @@ def main():
     ap.add_argument("--bf16", action="store_true",
                     help="time the dense BF16 GEMM (mx_gemm_bf16) instead")
     ap.add_argument("--ceiling", action="store_true",
-                    help="only measure the MFMA ceiling (mx_mfma_ceiling) of both formats")
+                    help="only measure the device's ceilings: HBM streaming read "
+                         "(mx_hbm_read_ceiling) and the MFMA rate of both formats "
+                         "(mx_mfma_ceiling)")
     a = ap.parse_args()
     if a.gpus != 1:
         sys.stderr.write("bench.py runs on exactly one GPU: the MX GEMM path has no "
@@ -653,6 +712,10 @@ def main():
         return
     if a.ceiling:
         import microscaled_block_scaled_amd as mxg
+        print(json.dumps({"hbm_read_ceiling": "1 GiB buffers", "unit": "GB/s",
+                          "value": hbm_ceiling(), "datasheet_peak": PEAK_HBM_GBS,
+                          "launch": "%d workgroups x %d threads" % (
+                              mxg.HBM_CEILING_WORKGROUPS, mxg.HBM_CEILING_THREADS)}), flush=True)
         for fmt in (mxinputs.FMT_E2M1, mxinputs.FMT_E4M3):
             c = mfma_ceiling(fmt)
             print(json.dumps({"mfma_ceiling": mxinputs.fmt_name(fmt), "unit": "TFLOP/s",

@@ -410,6 +410,29 @@ int mx_gemm_grouped_bf16_plan(int64_t groups, const int64_t *group_rows, int64_t
  */
 int mx_mfma_ceiling(int fmt, int64_t steps, int random_data, float *out, void *stream);
 
+/* Launch shape of mx_hbm_read_ceiling: two 256-thread workgroups per CU. */
+#define MX_HBM_CEILING_WORKGROUPS 512
+#define MX_HBM_CEILING_THREADS 256
+
+/*
+ * Measurement only, not part of the GEMM: reads `bytes` of device memory at
+ * src once, as a plain streaming kernel does.  The buffer is cut into
+ * MX_HBM_CEILING_WORKGROUPS contiguous ranges of ceil(bytes/16 /
+ * MX_HBM_CEILING_WORKGROUPS) 16-byte chunks (the last ones shorter or
+ * empty); thread t of workgroup w folds with XOR the chunks t, t + 256, ...
+ * of range w, and writes its fold to out[256 w + t] (out holds
+ * MX_HBM_CEILING_WORKGROUPS * MX_HBM_CEILING_THREADS 32-bit words,
+ * caller-owned device memory).  Loads carry the nontemporal hint.  Timing
+ * it over a buffer larger than the last-level cache gives the rate at which
+ * this device actually delivers HBM data to the CUs, the practical bound of
+ * the memory-bound GEMM shapes (the FlyDSL article, "Performance numbers need
+ * their baselines": a rate means little without its baseline).  bytes is a
+ * positive multiple of 16; src is 16-byte aligned, out 4-byte aligned.
+ * Enqueued on `stream`, asynchronous.  Returns MX_OK, MX_ERR_NULL,
+ * MX_ERR_SHAPE, MX_ERR_ALIGN, a device error or MX_ERR_LAUNCH.
+ */
+int mx_hbm_read_ceiling(const void *src, int64_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,6 +140,8 @@ def lib():
     L.mx_debug_fail_allocations.argtypes = [ctypes.c_int]
     L.mx_mfma_ceiling.restype = ctypes.c_int
     L.mx_mfma_ceiling.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp]
+    L.mx_hbm_read_ceiling.restype = ctypes.c_int
+    L.mx_hbm_read_ceiling.argtypes = [vp, i64, vp, vp]
     _lib = L
     return L
 
@@ -379,6 +381,16 @@ def ceiling_ptr(fmt, steps, random_data, out, stream=0):
     """Raw entry point of mx_mfma_ceiling (a measurement kernel): status code."""
     return lib().mx_mfma_ceiling(int(fmt), int(steps), int(bool(random_data)), out,
                                  stream or None)
+
+
+# Launch shape of mx_hbm_read_ceiling (include/mxgemm.h).
+HBM_CEILING_WORKGROUPS = 512
+HBM_CEILING_THREADS = 256
+
+
+def hbm_ceiling_ptr(src, nbytes, out, stream=0):
+    """Raw entry point of mx_hbm_read_ceiling (a measurement kernel): status code."""
+    return lib().mx_hbm_read_ceiling(src, int(nbytes), out, stream or None)
 
 
 def quantize_ptr(fmt, in_dtype, rows, K, X, Q, Q_scale, stream=0):

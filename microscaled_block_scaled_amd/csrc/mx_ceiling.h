@@ -1,9 +1,13 @@
-// mx_ceiling.h -- a measurement kernel, not part of the GEMM: the rate at
-// which this device sustains the block-scaled MFMA with no memory traffic at
-// all, in the tile kernel's launch shape (one 512-thread workgroup per CU,
-// two waves per SIMD).  It bounds what any GEMM kernel can reach on the same
-// data: the datasheet peak assumes the matrix units run at the top clock,
-// which the power limit does not allow when the operands are random.
+// mx_ceiling.h -- measurement kernels, not part of the GEMM.
+//   * mfma_ceiling_kernel: the rate at which this device sustains the
+//     block-scaled MFMA with no memory traffic at all, in the tile kernel's
+//     launch shape (one 512-thread workgroup per CU, two waves per SIMD).  It
+//     bounds what any GEMM kernel can reach on the same data: the datasheet
+//     peak assumes the matrix units run at the top clock, which the power
+//     limit does not allow when the operands are random.
+//   * hbm_read_kernel: the rate at which this device streams a buffer from
+//     HBM into the CUs, the practical bound of the memory-bound shapes (the
+//     datasheet's 8 TB/s is the interface's raw rate).
 #pragma once
 
 #include "mx_kernels.h"
@@ -86,6 +90,32 @@ __global__ void __launch_bounds__(512) mfma_ceiling_kernel(float *out, int steps
 #pragma unroll
             for (int e = 0; e < 16; ++e) r += acc[i][j][e];
     out[gid] = r;
+}
+
+// Workgroup w reads the w-th of gridDim.x contiguous ranges of the buffer
+// (ceil(n / gridDim.x) 16-byte chunks each, the last ones shorter or empty):
+// its 256 threads read 256 consecutive chunks per step, eight steps' loads in
+// flight, with the nontemporal hint (measured on MI355X: about 6.9 TB/s with
+// it over 1 GiB, 6.1 without, 5.3 for a grid-strided walk).  Thread t folds
+// (XOR) the chunks it read, those at t, t + 256, ... from the range's start,
+// and writes the fold to out[global thread index], so no load is dead code.
+__global__ void __launch_bounds__(256) hbm_read_kernel(const v4i *__restrict__ src, int64_t n,
+                                                       uint32_t *__restrict__ out)
+{
+    constexpr int U = 8;
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = min((int64_t)blockIdx.x * per, n), b1 = min(b0 + per, n);
+    v4i x = {0, 0, 0, 0};
+    int64_t i = b0 + threadIdx.x;
+    for (; i + (U - 1) * 256 < b1; i += U * 256) {
+        v4i v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < U; ++u) x ^= v[u];
+    }
+    for (; i < b1; i += 256) x ^= __builtin_nontemporal_load(src + i);
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = (uint32_t)(x[0] ^ x[1] ^ x[2] ^ x[3]);
 }
 
 }  // namespace mx

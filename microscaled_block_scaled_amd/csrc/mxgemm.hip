@@ -426,6 +426,21 @@ extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
+extern "C" int mx_hbm_read_ceiling(const void *src, int64_t bytes, uint32_t *out, void *stream)
+{
+    if (!src || !out) return MX_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0) return MX_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(out, 4)) return MX_ERR_ALIGN;
+    int dev = -1;
+    const int rc = device_ready(&dev);
+    if (rc != MX_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(mx::hbm_read_kernel, dim3(MX_HBM_CEILING_WORKGROUPS),
+                       dim3(MX_HBM_CEILING_THREADS), 0, s, (const mx::v4i *)src, bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
 extern "C" int mx_mfma_ceiling(int fmt, int64_t steps, int random_data, float *out,
                                void *stream)
 {

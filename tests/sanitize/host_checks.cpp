@@ -163,6 +163,15 @@ int main()
         CHECK(mx_gemm_grouped(1, 2, g0, 64, 128, nullptr, nullptr, nullptr, nullptr, nullptr, 2,
                               nullptr) == MX_OK);
     }
+    CHECK(mx_hbm_read_ceiling(nullptr, 1024, reinterpret_cast<uint32_t *>(fake), nullptr) ==
+          MX_ERR_NULL);
+    for (int64_t bytes : {(int64_t)-16, (int64_t)0, (int64_t)8, (int64_t)1000})
+        CHECK(mx_hbm_read_ceiling(fake, bytes, reinterpret_cast<uint32_t *>(fake), nullptr) ==
+              MX_ERR_SHAPE);
+    CHECK(mx_hbm_read_ceiling(fake + 8, 1024, reinterpret_cast<uint32_t *>(fake), nullptr) ==
+          MX_ERR_ALIGN);
+    CHECK(mx_hbm_read_ceiling(fake, 1024, reinterpret_cast<uint32_t *>(fake), nullptr) ==
+          MX_ERR_NO_DEVICE);
     mx_debug_fail_allocations(-3);
     mx_debug_fail_allocations(2);
     mx_debug_fail_allocations(0);

@@ -529,3 +529,15 @@ def test_operand_row_length_must_hold_whole_elements():
         for rb in (97, 98, 1):
             with pytest.raises(ValueError):
                 mxg._k_of(fmt, rb)
+
+
+def test_hbm_read_ceiling_argument_errors():
+    """mx_hbm_read_ceiling checks its arguments before any HIP call."""
+    L = mxg.lib()
+    fake = 1 << 20
+    assert L.mx_hbm_read_ceiling(None, 1024, fake, None) == mxg.MX_ERR_NULL
+    assert L.mx_hbm_read_ceiling(fake, 1024, None, None) == mxg.MX_ERR_NULL
+    for nbytes in (-16, 0, 8, 1000):
+        assert L.mx_hbm_read_ceiling(fake, nbytes, fake, None) == mxg.MX_ERR_SHAPE
+    assert L.mx_hbm_read_ceiling(fake + 8, 1024, fake, None) == mxg.MX_ERR_ALIGN
+    assert L.mx_hbm_read_ceiling(fake, 1024, fake + 2, None) == mxg.MX_ERR_ALIGN
