@@ -165,20 +165,28 @@ __device__ __forceinline__ void fp6_frag(V &v, uint2 q0, uint2 q1, uint2 q2)
 // counts a global (FLAT-encoded) LDS copy as both a memory and an LDS access
 // and then waits for every outstanding LDS read (lgkmcnt(0)) before any use
 // of one, while with buffer copies in flight it waits only for the read it
-// needs.  num_records is the largest value, so no access is range-checked
-// (every offset the kernel forms lies inside its operand).
+// needs.  The descriptor's num_records bounds the offsets: a copy at or past
+// it is not fetched (the hardware's range check returns zeros), which is how
+// the rows of a partial tile beyond the matrix's last row cost no memory
+// traffic (their results are never stored).  num_records -1 checks nothing.
+// AUX is the cache policy: 0 the default, kStream the nontemporal hint for
+// data read once (measured: it raises a plain streaming read over 1 GiB from
+// 6.1 to 6.9 TB/s on MI355X).
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // Word 3 of a gfx9 buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kStream = 2;   // the nt bit of the cache-policy operand
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base)
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_records)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, kRsrcWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)num_records,
+                                             kRsrcWord3);
 }
+template <int AUX = 0>
 __device__ __forceinline__ void b2l_16(rsrc_t src, uint32_t off, void *lds)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)lds, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)lds, 16, off, 0, 0, AUX);
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's memory loads are outstanding (loads
@@ -376,15 +384,25 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int nsteps = klen / SL::kstep;
 
     // Copy addresses are a wave-uniform base (scalar registers) plus a 32-bit
-    // per-lane offset, which stays below 256 rows * rowb < 2^32 for K <= 2^24.
-    // Rows past the end of the matrix are clamped to its last row (their
-    // results are never stored).
+    // per-lane offset, which stays below 256 rows * rowb <= 2^32 for K <= 2^24.
+    // In a tile that runs past the matrix's last row, the copies of the rows
+    // beyond it fall outside their descriptor's num_records and are not
+    // fetched (their results are never stored).
     static_assert(BM % 64 == 0, "copy geometry");
     const uint8_t *const At = A + (int64_t)m0 * rowba + kboffa;
     const uint8_t *const Bt = B + (int64_t)n0 * rowbb + kboffb;
     const uint8_t *const Ast = As + (int64_t)m0 * sps + kb / 32;
     const uint8_t *const Bst = Bs + (int64_t)n0 * sps + kb / 32;
     const int last_a = min(BM, M - m0) - 1, last_b = min(BN, N - n0) - 1;   // last row in the tile
+    // Bytes of a partial tile's rows from a copy base `skip` bytes into the
+    // first row (whole tiles: no range check).  Below 2^32: at most 255 rows.
+    auto extent = [](int last, int rows, int64_t rowb, int64_t skip) -> uint32_t {
+        return last + 1 == rows ? 0xffffffffu : (uint32_t)((last + 1) * rowb - skip);
+    };
+    // B is streamed once per tile when every tile column has a single row
+    // tile (the short tiles serve M <= their height): it takes the
+    // nontemporal hint there.
+    constexpr int AUXB = BM <= 128 ? kStream : 0;
     // Per operand (slab row bytes R, rows per copy instruction 1024/R): lane
     // l copies chunk l % (R/16) of row l / (R/16) of a block of rows, into
     // LDS chunk cpc of that row, which holds global chunk cpc ^ swz(row).
@@ -401,9 +419,15 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     };
     const CopyGeo ga = copy_geo(std::integral_constant<int, RA>{}, rowba);
     const CopyGeo gb = copy_geo(std::integral_constant<int, RB>{}, rowbb);
-    auto row_off = [&](const CopyGeo &c, int r0, int last) -> uint32_t {   // r0: first row of the block
-        return (r0 + c.crow <= last) ? (uint32_t)r0 * c.rowb32 + c.lane_row
-                                     : (uint32_t)last * c.rowb32;
+    // Byte offset of this lane's row in the block of rows starting at r0.
+    // FP6 lanes 48..63 name rows 8..10 of their 8-row block (their chunks
+    // land in padding nobody reads): in a tile's last block those rows lie
+    // past the tile, so every row is clamped to the tile's last one
+    // (`rows` - 1), which is inside the matrix when the tile is whole and
+    // past num_records (not fetched) when it is not.
+    auto row_off = [&](const CopyGeo &c, int r0, int rows) -> uint32_t {
+        return (r0 + c.crow < rows) ? (uint32_t)r0 * c.rowb32 + c.lane_row
+                                    : (uint32_t)(rows - 1) * c.rowb32;
     };
 
     // Copy slab k into ring slot `slot`.  Branch-free: every wave issues the
@@ -419,18 +443,19 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         // into the row.  (With 64-byte slab rows every slab is whole.)
         const uint32_t cmaxa = (uint32_t)(rowla - 16 - koffa);
         const uint32_t cmaxb = (uint32_t)(rowlb - 16 - koffb);
-        const rsrc_t Ak = make_rsrc(At + koffa), Bk = make_rsrc(Bt + koffb);
+        const rsrc_t Ak = make_rsrc(At + koffa, extent(last_a, BM, rowba, kboffa + koffa));
+        const rsrc_t Bk = make_rsrc(Bt + koffb, extent(last_b, BN, rowbb, kboffb + koffb));
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPCA - 1);
             const uint32_t ch = min((RA == 128 && (i & 1)) ? ga.ch1 : ga.ch0, cmaxa);
-            b2l_16(Ak, row_off(ga, i * RPCA, last_a) + ch, base + i * RPCA * LA);
+            b2l_16(Ak, row_off(ga, i * RPCA, BM) + ch, base + i * RPCA * LA);
         }
 #pragma unroll
         for (int u = 0; u < CPB; ++u) {
             const int i = min(wave + u * NW, BN / RPCB - 1);
             const uint32_t ch = min((RB == 128 && (i & 1)) ? gb.ch1 : gb.ch0, cmaxb);
-            b2l_16(Bk, row_off(gb, i * RPCB, last_b) + ch, base + BM * LA + i * RPCB * LB);
+            b2l_16<AUXB>(Bk, row_off(gb, i * RPCB, BN) + ch, base + BM * LA + i * RPCB * LB);
         }
     };
     // Copy scale period p (16 bytes of every row) into scale buffer `buf`;
@@ -448,8 +473,12 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         for (int u = 0; u < CPS; ++u) {
             const int i = min(wave + u * NW, NSI - 1);
             const bool in_a = i * 64 < BM;
-            const int row = min(i * 64 + lane - (in_a ? 0 : BM), in_a ? last_a : last_b);
-            const rsrc_t src = make_rsrc((in_a ? Ast : Bst) + soff);
+            const int row = i * 64 + lane - (in_a ? 0 : BM);
+            // (exact extents even for whole tiles: the last instruction's B
+            // rows may run past BN)
+            const int last = in_a ? last_a : last_b;
+            const rsrc_t src = make_rsrc((in_a ? Ast : Bst) + soff,
+                                         (uint32_t)((last + 1) * sps - kb / 32 - soff));
             b2l_16(src, (uint32_t)row * (uint32_t)sps, sbase + buf * SBUF + i * 1024);
         }
     };
