@@ -394,11 +394,14 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *const Ast = As + (int64_t)m0 * sps + kb / 32;
     const uint8_t *const Bst = Bs + (int64_t)n0 * sps + kb / 32;
     const int last_a = min(BM, M - m0) - 1, last_b = min(BN, N - n0) - 1;   // last row in the tile
-    // Bytes of a partial tile's rows from a copy base `skip` bytes into the
-    // first row (whole tiles: no range check).  Below 2^32: at most 255 rows.
-    auto extent = [](int last, int rows, int64_t rowb, int64_t skip) -> uint32_t {
-        return last + 1 == rows ? 0xffffffffu : (uint32_t)((last + 1) * rowb - skip);
-    };
+    // num_records of the copies: a partial tile's rows counted from the
+    // slice's first byte (below 2^32: at most 255 rows), less the slab's
+    // offset in issue(); whole tiles are not range-checked.  (Computed once
+    // here: forming the 64-bit product per slab raised the mixed-format
+    // kernels from 192 VGPRs to 256 and spills.)
+    const bool whole_a = last_a + 1 == BM, whole_b = last_b + 1 == BN;
+    const uint32_t ext_a = whole_a ? 0xffffffffu : (uint32_t)((last_a + 1) * rowba - kboffa);
+    const uint32_t ext_b = whole_b ? 0xffffffffu : (uint32_t)((last_b + 1) * rowbb - kboffb);
     // B is streamed once per tile when every tile column has a single row
     // tile (the short tiles serve M <= their height): it takes the
     // nontemporal hint there.
@@ -443,8 +446,8 @@ tile_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         // into the row.  (With 64-byte slab rows every slab is whole.)
         const uint32_t cmaxa = (uint32_t)(rowla - 16 - koffa);
         const uint32_t cmaxb = (uint32_t)(rowlb - 16 - koffb);
-        const rsrc_t Ak = make_rsrc(At + koffa, extent(last_a, BM, rowba, kboffa + koffa));
-        const rsrc_t Bk = make_rsrc(Bt + koffb, extent(last_b, BN, rowbb, kboffb + koffb));
+        const rsrc_t Ak = make_rsrc(At + koffa, whole_a ? ext_a : ext_a - (uint32_t)koffa);
+        const rsrc_t Bk = make_rsrc(Bt + koffb, whole_b ? ext_b : ext_b - (uint32_t)koffb);
 #pragma unroll
         for (int u = 0; u < CPA; ++u) {
             const int i = min(wave + u * NW, BM / RPCA - 1);
