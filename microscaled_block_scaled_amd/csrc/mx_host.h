@@ -45,6 +45,13 @@ inline constexpr TileCfg kTiles[] = {
     {128, 128, 2, 2, 3}, {64, 256, 1, 8, 3},
 };
 inline constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+// Relative speed per CU of a tile shape on MFMA-bound work, for the plans.
+// The 256-row tile with four waves (one per SIMD) leaves each SIMD's LDS and
+// barrier latency uncovered: measured on MI355X, 2048 x 5120 x 25600 MXFP4
+// took 192 us on 256x160 tiles (256 workgroups) and 170 us on 256x192 tiles
+// with 40 of 256 CUs idle, i.e. 0.73 of the 8-wave tile's rate per CU.
+inline double tile_speed(const TileCfg &c) { return c.bm == 256 && c.wgm * c.wgn == 4 ? 0.73 : 1.0; }
 inline constexpr int kCUs = 256;   // MI355X compute units: one 256-row tile per CU per wave
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

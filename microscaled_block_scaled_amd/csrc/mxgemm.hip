@@ -65,7 +65,8 @@ int choose_tile(int64_t M, int64_t N, int64_t K)
         // A split costs a workspace round trip of one FP32 plane per slice:
         // on a tie, fewer slices win.
         const int64_t split = wgs / tiles;
-        const double eff = fill * useful * (split > 1 ? 1.0 - 0.01 * (double)split : 1.0);
+        const double eff = fill * useful * tile_speed(c) *
+                           (split > 1 ? 1.0 - 0.01 * (double)split : 1.0);
         if (eff > best_eff + 1e-9) { best_eff = eff; best = t; }
     }
     return best;
