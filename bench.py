@@ -44,6 +44,7 @@ CSRC = os.path.join(ROOT, "microscaled_block_scaled_amd", "csrc")
 # The device code of each kernel family: a counter summary taken on other
 # device code is stale.
 GEMM_SOURCES = [os.path.join(CSRC, "mx_kernels.h")]
+DECODE_SOURCES = GEMM_SOURCES + [os.path.join(CSRC, "mx_decode.h")]
 QUANT_SOURCES = [os.path.join(CSRC, "mx_quant.h")]
 QUANT6_SOURCES = [os.path.join(CSRC, "mx_quant.h"), os.path.join(CSRC, "mx_quant6.h")]
 
@@ -61,6 +62,13 @@ def kernel_source_hash(sources=None):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def gemm_sources(plan):
+    """The device code a GEMM plan runs: the tile kernel, or the decode kernel
+    (which also uses the tile kernel's helpers)."""
+    import microscaled_block_scaled_amd as mxg
+    return DECODE_SOURCES if plan["variant"] == mxg.VARIANT_DECODE else GEMM_SOURCES
 
 
 def measured_traffic(workload, sources=None, plan=None):
@@ -306,7 +314,7 @@ def bench_one(name, steps, warmup, with_cpu, cold_launches=60, with_ceiling=True
     plan = mxg.plan(fmt, M, N, K, out)
     plan_str = "variant %d tile %dx%d split %d, %d workgroups" % (
         plan["variant"], plan["tile_m"], plan["tile_n"], plan["split_k"], plan["workgroups"])
-    traffic = measured_traffic(name, GEMM_SOURCES, plan_str)
+    traffic = measured_traffic(name, gemm_sources(plan), plan_str)
     launch_s = cold["median_us"] * 1e-6
     if bound == "mfma":
         achieved = flops / launch_s / 1e12
@@ -552,7 +560,7 @@ def bench_mixed(steps, warmup, name):
         achieved = nbytes / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(name, GEMM_SOURCES, plan_str)
+    roof["traffic"] = measured_traffic(name, gemm_sources(p), plan_str)
     hbm_fields(roof)
     roof["algorithmic_bytes"] = nbytes
     roof["launch_us"] = round(launch_s * 1e6, 2)

@@ -127,16 +127,25 @@ int mx_gemm(int fmt, int64_t M, int64_t N, int64_t K,
 const char *mx_strerror(int code);
 
 /*
- * Kernel variants a plan can choose.  There is one: every problem runs the
- * tiled kernel, in which each workgroup computes one tile_m x tile_n tile of
- * C, staging A and B through LDS.  Small M uses a 64-row tile.  When the
- * tiles cannot fill the GPU and K is long, each workgroup takes one of
- * split_k K-slices and writes FP32 partial results to a workspace that a
- * second kernel adds in slice order (workspace_bytes of the stream's
- * workspace, see "Thread safety" above; mx_gemm_noalloc uses a fixed scratch
- * instead).
+ * Kernel variants a plan can choose.
+ * MX_VARIANT_TILE: the tiled kernel, in which each workgroup computes one
+ *   tile_m x tile_n tile of C, staging A and B through LDS.  Small M uses a
+ *   128- or 64-row tile.  When the tiles cannot fill the GPU and K is long,
+ *   each workgroup takes one of split_k K-slices and writes FP32 partial
+ *   results to a workspace that a second kernel adds in slice order
+ *   (workspace_bytes of the stream's workspace, see "Thread safety" above;
+ *   mx_gemm_noalloc uses a fixed scratch instead).
+ * MX_VARIANT_DECODE: the decode kernel, for M <= MX_DECODE_TILE rows with
+ *   both operands E2M1, E4M3 or E5M2 and K >= 512.  Each workgroup computes
+ *   MX_DECODE_TILE columns of C for all M rows; its four waves take four
+ *   K-ranges of whole 512-K periods and add their partial sums in LDS in a
+ *   fixed order.  tile_m = tile_n = MX_DECODE_TILE, split_k = 1, no
+ *   workspace.  The plan takes it where it streams B faster than the tiled
+ *   kernel; mx_gemm_tile and mx_gemm_mixed run it when asked for the tile
+ *   (MX_DECODE_TILE, MX_DECODE_TILE).
  */
-enum { MX_VARIANT_TILE = 1 };
+enum { MX_VARIANT_TILE = 1, MX_VARIANT_DECODE = 2 };
+#define MX_DECODE_TILE 32
 
 /* How mx_gemm would run a problem (filled by mx_gemm_plan). */
 typedef struct {
@@ -205,10 +214,12 @@ int mx_tile_shapes(int *pairs, int max_pairs);
  * caller instead of the plan: (tile_m, tile_n) must be one of the shapes
  * mx_tile_shapes lists, and split_k is 0 (the plan's choice) or 1 ..
  * MX_MAX_SPLIT_K (K is then cut into that many slices of whole 512-K
- * periods, or fewer when K is short); otherwise MX_ERR_SHAPE.  Everything
- * else -- arguments, layouts, errors, results -- is as for mx_gemm.  It
- * exists so that every kernel configuration can be exercised (and timed) on
- * any problem size.
+ * periods, or fewer when K is short); otherwise MX_ERR_SHAPE.  The tile
+ * (MX_DECODE_TILE, MX_DECODE_TILE) runs the decode kernel (MX_VARIANT_DECODE)
+ * instead: it needs fmt E2M1, E4M3 or E5M2, M <= MX_DECODE_TILE, K >= 512 and
+ * split_k 0 or 1, else MX_ERR_SHAPE.  Everything else -- arguments, layouts,
+ * errors, results -- is as for mx_gemm.  It exists so that every kernel
+ * configuration can be exercised (and timed) on any problem size.
  */
 #define MX_MAX_SPLIT_K 8
 int mx_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K,
@@ -259,10 +270,13 @@ int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
  * gfx950's scaled MFMA takes a format per operand).  A is M x K in fmt_a's
  * layout (K, K/2 or 3K/4 bytes per row), B is N x K in fmt_b's; scales, C, the
  * output types, alignment, errors and asynchrony as for mx_gemm.
- * tile_m = tile_n = 0 takes the plan's tile (the plan depends on M, N and K
- * only, so mx_gemm_plan describes it); otherwise (tile_m, tile_n) must be one
- * of mx_tile_shapes.  split_k as for mx_gemm_tile (0: the plan's).  With
- * fmt_a == fmt_b the result equals mx_gemm's / mx_gemm_tile's bit for bit.
+ * tile_m = tile_n = 0 takes the plan's tile (the plan depends on M, N and K,
+ * and on whether both formats are E2M1, E4M3 or E5M2, which the decode
+ * kernel needs: mx_gemm_plan with either format describes it when both are,
+ * and with an FP6 format when one is); otherwise (tile_m, tile_n) must be
+ * one of mx_tile_shapes, or the decode tile under mx_gemm_tile's conditions.
+ * split_k as for mx_gemm_tile (0: the plan's).  With fmt_a == fmt_b the
+ * result equals mx_gemm's / mx_gemm_tile's bit for bit.
  */
 int mx_gemm_mixed(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                   const void *A, const void *A_scale,

@@ -45,6 +45,8 @@ MAX_K_BF16 = 1 << 23  # largest K of the dense BF16 GEMM
 MAX_SPLIT_K = 8       # largest forced K split (mx_gemm_tile)
 MAX_GROUPS = 256      # most groups of mx_gemm_grouped
 VARIANT_TILE = 1
+VARIANT_DECODE = 2    # the decode kernel: M <= DECODE_TILE rows, E2M1 / E4M3 / E5M2
+DECODE_TILE = 32      # its tile: DECODE_TILE columns of C (all M rows) per workgroup
 
 MX_OK = 0
 MX_ERR_FORMAT = -1
@@ -251,7 +253,9 @@ def mx_gemm(a, a_scale, b, b_scale, fmt, out_dtype=None, out=None, stream=None,
     ``fmt`` is the element format of A, and of B unless ``fmt_b`` gives B
     another one (E4M3 x E2M1 and the reverse).  ``tile=(tile_m, tile_n)``
     forces one of ``tile_shapes()``, and with it ``split_k`` the number of K
-    slices (0: the plan's choice)."""
+    slices (0: the plan's choice); ``tile=(DECODE_TILE, DECODE_TILE)`` forces
+    the decode kernel (M <= DECODE_TILE, E2M1 / E4M3 / E5M2, K >= 512, no
+    split)."""
     import torch
     if out_dtype is None:
         out_dtype = torch.bfloat16

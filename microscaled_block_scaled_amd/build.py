@@ -11,7 +11,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Translation units compiled side by side, then linked.
 SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "mxgrouped.hip", "mxfp6pairs.hip",
-                                               "mxgrouped_fp6.hip")]
+                                               "mxgrouped_fp6.hip", "mxdecode.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
           [os.path.join(ROOT, "include", "mxgemm.h")]
 

@@ -87,6 +87,23 @@ bool launch_fp6_pair(int fmt_a, int fmt_b, const mx_plan_t &p, int out_dtype, co
                      const void *As, const void *B, const void *Bs, void *C, int64_t M,
                      int64_t N, int64_t K, float *W, hipStream_t stream);
 
+// The decode kernel's problems: both operands E2M1, E4M3 or E5M2, M <= 32
+// rows, and K >= 512 (a whole scale period per row, which the kernel's
+// scale loads read).
+inline bool decode_fits(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K)
+{
+    auto mx8 = [](int f) { return f == MX_FMT_E2M1 || f == MX_FMT_E4M3 || f == MX_FMT_E5M2; };
+    return mx8(fmt_a) && mx8(fmt_b) && M >= 1 && M <= MX_DECODE_TILE && N >= 1 &&
+           K >= kPeriodK && K % 128 == 0;
+}
+
+// The decode kernel for fmt_a x fmt_b (defined in mxdecode.hip): one
+// workgroup per MX_DECODE_TILE columns of C.  Returns false if the problem
+// is not one decode_fits accepts.
+bool launch_decode(int fmt_a, int fmt_b, int out_dtype, const void *A, const void *As,
+                   const void *B, const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
+                   hipStream_t s);
+
 // Grouped launches: one tile shape (kTiles[t]) for every group, the group
 // table in the kernel arguments, no K split.
 template <int FA, int FB, int OUT, int BM, int BN, int WGM, int WGN, int S>

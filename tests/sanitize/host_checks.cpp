@@ -35,9 +35,17 @@ static const int64_t kKs[] = {-128, 0, 16, 64, 100, 128, 256, 384, 512, 640, 204
                               ((int64_t)1 << 24) + 128};
 
 // A plan's arithmetic: whole tiles, slices of whole 512-K periods covering K
-// with none empty, workspace of split_k planes.
-static void check_plan(const mx_plan_t &p, int64_t M, int64_t N, int64_t K)
+// with none empty, workspace of split_k planes; or the decode kernel, only
+// for M <= MX_DECODE_TILE, K >= 512 and formats other than FP6 (fp6 true).
+static void check_plan(const mx_plan_t &p, int64_t M, int64_t N, int64_t K, bool fp6 = false)
 {
+    if (p.variant == MX_VARIANT_DECODE) {
+        CHECK(!fp6 && M >= 1 && M <= MX_DECODE_TILE && K >= 512);
+        CHECK(p.tile_m == MX_DECODE_TILE && p.tile_n == MX_DECODE_TILE && p.split_k == 1);
+        CHECK(p.threads == 256 && p.workspace_bytes == 0);
+        CHECK(p.workgroups == cdiv(N, MX_DECODE_TILE));
+        return;
+    }
     CHECK(p.variant == MX_VARIANT_TILE);
     CHECK(p.tile_m > 0 && p.tile_n > 0 && p.threads > 0 && p.threads <= 1024);
     CHECK(p.split_k >= 1 && p.split_k <= MX_MAX_SPLIT_K);
@@ -68,7 +76,7 @@ int main()
 
     // Plans: MX formats (and codes around them), both output types (and bad
     // ones), every M, N, K of the grid.
-    int planned = 0;
+    int planned = 0, decode = 0;
     for (int fmt = -1; fmt <= 7; ++fmt)
         for (int out = 0; out <= 3; ++out)
             for (int64_t M : kDims)
@@ -79,11 +87,12 @@ int main()
                         const int rc = mx_gemm_plan(fmt, M, N, K, out, &p);
                         CHECK(rc <= 0 && rc >= MX_ERR_SCRATCH);
                         if (rc == MX_OK) {
-                            check_plan(p, M, N, K);
+                            check_plan(p, M, N, K, fmt == MX_FMT_E2M3 || fmt == MX_FMT_E3M2);
                             ++planned;
+                            decode += p.variant == MX_VARIANT_DECODE;
                         }
                     }
-    CHECK(planned > 1000);
+    CHECK(planned > 1000 && decode > 100);
     CHECK(mx_gemm_plan(1, 8, 8, 128, 2, nullptr) == MX_ERR_NULL);
 
     for (int out = 0; out <= 3; ++out)
@@ -93,14 +102,17 @@ int main()
                     mx_plan_t p;
                     const int rc = mx_gemm_bf16_plan(M, N, K, out, &p);
                     CHECK(rc <= 0);
-                    if (rc == MX_OK) check_plan(p, M, N, K);
+                    if (rc == MX_OK) check_plan(p, M, N, K, true);
                 }
 
-    // Forced tiles and splits: every tile shape, splits 0..MX_MAX_SPLIT_K and
-    // beyond, on shapes up to the limits.  Null operands: the call returns
-    // after planning, before any HIP call.
-    for (int t = 0; t <= nt; ++t) {
-        const int bm = t < nt ? pairs[2 * t] : 100, bn = t < nt ? pairs[2 * t + 1] : 100;
+    // Forced tiles and splits: every tile shape, the decode tile, the plan's
+    // choice (0, 0) and an unknown tile, splits 0..MX_MAX_SPLIT_K and beyond,
+    // on shapes up to the limits.  Null operands: the call returns after
+    // planning, before any HIP call.
+    const int extra[][2] = {{100, 100}, {MX_DECODE_TILE, MX_DECODE_TILE}, {0, 0}};
+    for (int t = 0; t < nt + 3; ++t) {
+        const int bm = t < nt ? pairs[2 * t] : extra[t - nt][0];
+        const int bn = t < nt ? pairs[2 * t + 1] : extra[t - nt][1];
         for (int split = -1; split <= MX_MAX_SPLIT_K + 1; ++split)
             for (int64_t M : kDims)
                 for (int64_t N : kDims)

@@ -43,6 +43,8 @@ def test_header_constants_match_binding():
         == mxg.MAX_K_BF16.bit_length() - 1
     assert int(re.search(r"#define MX_MAX_SPLIT_K (\d+)", src).group(1)) == mxg.MAX_SPLIT_K
     assert int(re.search(r"#define MX_MAX_GROUPS (\d+)", src).group(1)) == mxg.MAX_GROUPS
+    assert int(re.search(r"#define MX_DECODE_TILE (\d+)", src).group(1)) == mxg.DECODE_TILE
+    assert consts["MX_VARIANT_DECODE"] == mxg.VARIANT_DECODE
 
 
 def test_strerror_covers_codes():
@@ -141,8 +143,8 @@ def test_plan_shapes():
         mxg.plan(mxg.FMT_E4M3, 16, 16, 100)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (32, 100, 4096), (64, 8192, 28672),
-                                   (33, 28672, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 28672), (32, 100, 16384), (64, 8192, 28672),
+                                   (33, 28672, 4096), (8, 28672, 1024)])
 def test_plan_small_m_uses_short_tile(M, N, K):
     for fmt in (mxg.FMT_E2M1, mxg.FMT_E4M3):
         p = mxg.plan(fmt, M, N, K)
@@ -156,6 +158,67 @@ def test_plan_small_m_uses_short_tile(M, N, K):
         assert p["workgroups"] <= cap or p["split_k"] == 1
         if tiles <= 64 and K >= 8192:
             assert p["split_k"] > 1 and p["workspace_bytes"] > 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (8, 8192, 28672), (32, 8192, 4096),
+                                   (16, 14336, 4096), (5, 8161, 2048), (8, 6144, 28672),
+                                   (32, 100, 512), (1, 16384, 8192), (8, 28672, 28672),
+                                   (16, 3072, 14336), (1, 12288, 1024)])
+def test_plan_decode(M, N, K):
+    """M <= 32 and K >= 512 within the measured limits (rounds of 256
+    decode workgroups, K, M): the decode variant, for each of E2M1, E4M3
+    and E5M2."""
+    for fmt in (mxg.FMT_E2M1, mxg.FMT_E4M3, mxg.FMT_E5M2):
+        p = mxg.plan(fmt, M, N, K)
+        assert p["variant"] == mxg.VARIANT_DECODE, (fmt, p)
+        assert (p["tile_m"], p["tile_n"]) == (mxg.DECODE_TILE, mxg.DECODE_TILE)
+        assert p["split_k"] == 1 and p["workspace_bytes"] == 0 and p["threads"] == 256
+        assert p["workgroups"] == -(-N // mxg.DECODE_TILE)
+    # FP6 has no decode kernel: the tiled one
+    for fmt in (mxg.FMT_E2M3, mxg.FMT_E3M2):
+        assert mxg.plan(fmt, M, N, K)["variant"] == mxg.VARIANT_TILE
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 8192, 28672), (8, 4096, 28672), (8, 28672, 4096),
+                                   (16, 8192, 28672), (1, 16385, 2048), (8, 8192, 384),
+                                   (1, 32769, 28672), (16, 12288, 8192), (1, 12320, 1024)])
+def test_plan_decode_not_taken(M, N, K):
+    """M > 32; K >= 16384 with fewer than 160 decode workgroups (N = 4096);
+    more than 4 rounds of 256 workgroups, more than 2 at K < 6144 or more
+    than 1.5 at K <= 1024; M > 8 with K > 14336, or with more than one round
+    at K >= 6144; K < 512: the tiled kernel."""
+    assert mxg.plan(mxg.FMT_E4M3, M, N, K)["variant"] == mxg.VARIANT_TILE
+
+
+def test_forced_decode_tile_errors():
+    """The decode tile forced through mx_gemm_tile / mx_gemm_mixed /
+    mx_gemm_bf16: refused (before any HIP call) for FP6, BF16, M > 32,
+    K < 512 or a split; accepted otherwise (then stopped by a NULL pointer,
+    or by the missing device)."""
+    L = mxg.lib()
+    good = 1 << 20
+    D = mxg.DECODE_TILE
+    for fmt in (mxg.FMT_E2M3, mxg.FMT_E3M2):
+        assert L.mx_gemm_tile(fmt, 8, 64, 512, good, good, good, good, good, 2, D, D, 0,
+                              None) == mxg.MX_ERR_SHAPE
+    for M, K, split in ((33, 512, 0), (8, 384, 0), (8, 128, 1), (8, 512, 2)):
+        assert L.mx_gemm_tile(2, M, 64, K, good, good, good, good, good, 2, D, D, split,
+                              None) == mxg.MX_ERR_SHAPE, (M, K, split)
+    for fa, fb in ((mxg.FMT_E4M3, mxg.FMT_E2M3), (mxg.FMT_E3M2, mxg.FMT_E2M1)):
+        assert L.mx_gemm_mixed(fa, fb, 8, 64, 512, good, good, good, good, good, 2, D, D, 0,
+                               None) == mxg.MX_ERR_SHAPE
+    assert L.mx_gemm_bf16(8, 64, 512, good, good, good, 2, D, D, 0, None) == mxg.MX_ERR_SHAPE
+    for fmt in (mxg.FMT_E2M1, mxg.FMT_E4M3, mxg.FMT_E5M2):
+        for split in (0, 1):
+            assert L.mx_gemm_tile(fmt, 32, 64, 512, None, good, good, good, good, 2, D, D,
+                                  split, None) == mxg.MX_ERR_NULL
+    for fa, fb in ((mxg.FMT_E4M3, mxg.FMT_E2M1), (mxg.FMT_E2M1, mxg.FMT_E5M2)):
+        assert L.mx_gemm_mixed(fa, fb, 1, 1, 640, good, good, None, good, good, 2, D, D, 0,
+                               None) == mxg.MX_ERR_NULL
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert L.mx_gemm_tile(2, 8, 64, 512, good, good, good, good, good, 2, D, D, 0,
+                              None) == mxg.MX_ERR_NO_DEVICE
 
 
 def test_plan_split_k():
@@ -386,10 +449,14 @@ def test_bf16_argument_errors():
 
 def test_bf16_plan_matches_mx_plan():
     """The BF16 GEMM runs on the tile kernels with the MX GEMM's tile and
-    split choice (both depend on M, N and K only)."""
+    split choice (both depend on M, N and K only), as the FP6 formats do;
+    where the MX plan takes the decode kernel, which has no BF16 form, BF16
+    stays on the tiled kernel."""
     for M, N, K in ((2048, 6144, 4096), (8, 8192, 28672), (256, 28672, 4096),
                     (2048, 5120, 25600), (1, 1, 128)):
-        assert mxg.plan_bf16(M, N, K) == mxg.plan(mxg.FMT_E4M3, M, N, K)
+        assert mxg.plan_bf16(M, N, K) == mxg.plan(mxg.FMT_E2M3, M, N, K)
+    assert mxg.plan(mxg.FMT_E4M3, 8, 8192, 28672)["variant"] == mxg.VARIANT_DECODE
+    assert mxg.plan_bf16(8, 8192, 28672)["variant"] == mxg.VARIANT_TILE
     p = mxg.plan_bf16(5, 7, 48)
     assert p["split_k"] == 1 and p["workgroups"] >= 1
 

@@ -155,3 +155,130 @@ def test_model_reports_unclamped_fp6_padding_lanes():
     unclamped = (r0 + crow) * rowb
     assert ((n0 * rowb + unclamped + 16) > N * rowb).any()
     assert not check(F6E2, F6E2, 128, 128, 2, 2, 8, N, 4096, 4096)
+
+
+# --------------------------------------------------------------------------
+# The decode kernel (csrc/mx_decode.h): 4 waves per workgroup, each a K-range
+# of whole 512-K periods, a private ring of S slabs of 32 A rows and 32 B
+# rows, every slab position of every period issuing its copies (past the
+# range with num_records 0), and 16-byte scale loads per lane row, two
+# periods ahead, never crossing a row.
+DECODE_LDS, DECODE_ROWS, DECODE_WAVES = 163840, 32, 4
+
+
+def decode_geo(fa, fb):
+    """(rows of A staged, copies per slab, ring depth) of the decode kernel."""
+    kv = kvals(fa, fb)
+    RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
+    MA = DECODE_ROWS
+    ncopy = MA * RA // 1024 + DECODE_ROWS * RB // 1024
+    slot = MA * RA + DECODE_ROWS * RB
+    return MA, ncopy, min(DECODE_LDS // (DECODE_WAVES * slot), 2 + 63 // ncopy)
+
+
+def decode_operand(R, rowb, rows_real, koff, cmax, records, size, base, live, need_bytes,
+                   staged=DECODE_ROWS):
+    """One slab position's copies of one operand (`staged` rows)."""
+    RPC = 1024 // R
+    i, lane = np.meshgrid(np.arange(staged // RPC), np.arange(64), indexing="ij")
+    row = i * RPC + lane // (R // 16)
+    cpc = lane % (R // 16)
+    ch = np.minimum(cpc * 16, cmax)               # the swizzle permutes chunks within a row
+    off = row * rowb + ch
+    assert (off < 2 ** 32).all()
+    fetched = off + 16 <= records
+    inside = (base + off >= 0) & (base + off + 16 <= size)
+    ok = bool(inside[fetched].all())
+    if not live:
+        return ok and not fetched.any(), True
+    needed = (row < rows_real) & (cpc * 16 < need_bytes)
+    return ok, bool(fetched[needed].all())
+
+
+def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
+    """Problems of the decode kernel's loads for one problem; the two flags
+    turn off the scale window's clamp into the row and the zero num_records
+    of copies past the range (for the model's own tests)."""
+    kv = kvals(fa, fb)
+    RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
+    MA, ncopy, S = decode_geo(fa, fb)
+    PS = 512 // kv
+    L = max(2, -(-(S - 1) // PS))                    # periods of scale loads in flight
+    assert (S - 2) * ncopy <= 63 and DECODE_WAVES * S * (MA * RA + DECODE_ROWS * RB) <= DECODE_LDS
+    rowba, rowbb = kbytes(fa, K), kbytes(fb, K)
+    sps = K // 32
+    per_w = -(-(K // 128) // (4 * DECODE_WAVES))
+    problems = []
+    for n0 in sorted({0, (-(-N // DECODE_ROWS) - 1) * DECODE_ROWS}):
+        rows_b = min(DECODE_ROWS, N - n0)
+        for wave in range(DECODE_WAVES):
+            kb = min(wave * per_w * 512, K)
+            klen = min(per_w * 512, K - kb)
+            nslab = -(-klen // kv)
+            if nslab == 0:
+                continue
+            nper = -(-klen // 512)
+            trips = -(-nper // L) * L                   # L periods per trip
+            kboffa, kboffb = kbytes(fa, kb), kbytes(fb, kb)
+            rowla, rowlb = kbytes(fa, klen), kbytes(fb, klen)
+            exta, extb = M * rowba - kboffa, rows_b * rowbb - kboffb
+            positions = list(range(S - 1)) + [q * PS + kp + S - 1 for q in range(trips)
+                                              for kp in range(PS)]
+            for k in positions:
+                live = k < nslab
+                kc = min(k, nslab - 1)
+                koffa, koffb = kc * RA, kc * RB
+                for name, args in (
+                        ("A", (RA, rowba, M, koffa, rowla - 16 - koffa,
+                               exta - koffa if live or not idle_records else 0, M * rowba,
+                               kboffa + koffa, live, rowla - koffa, MA)),
+                        ("B", (RB, rowbb, rows_b, koffb, rowlb - 16 - koffb,
+                               extb - koffb if live or not idle_records else 0, N * rowbb,
+                               n0 * rowbb + kboffb + koffb, live, rowlb - koffb))):
+                    ok, need = decode_operand(*args)
+                    if not ok or not need:
+                        problems.append((name, n0, wave, k, ok, need))
+            # scale loads: periods 0 .. trips + L - 1, clamped to the last
+            lr = np.arange(DECODE_ROWS)
+            for q in range(trips + L):
+                qc = min(q, nper - 1)
+                blk = kb // 32 + 16 * qc
+                at = min(blk, sps - 16) if clamp_scales else blk
+                nblk = min(16, klen // 32 - 16 * qc)
+                if at < 0 or not (at <= blk and blk + nblk <= at + 16) or (blk - at) % 4:
+                    problems.append(("scale window", n0, wave, q))
+                off = lr * sps + at
+                for name, rows, base, size in (("As", M, 0, M * sps),
+                                               ("Bs", rows_b, n0 * sps, N * sps)):
+                    fetched = off + 16 <= rows * sps
+                    inside = base + off + 16 <= size
+                    in_row = off + 16 <= (lr + 1) * sps
+                    if not (inside[fetched].all() and in_row.all() and fetched[lr < rows].all()):
+                        problems.append((name, n0, wave, q))
+    return problems
+
+
+DECODE_FORMATS = [FP4, FP8, BF8]
+
+
+@pytest.mark.parametrize("fa,fb", [(a, b) for a in DECODE_FORMATS for b in DECODE_FORMATS])
+def test_decode_copies_stay_inside_their_operands(fa, fb):
+    shapes = [(1, 1, 512), (8, 8192, 28672), (32, 203, 640), (5, 100, 1664), (17, 64, 3200),
+              (32, 8161, 2048), (3, 40, 1152), (32, 96, 8192 + 384), (2, 33, 4096 + 128),
+              (9, 40, 2560), (16, 70, 1152)]
+    bad = []
+    for M, N, K in shapes:
+        bad += [((M, N, K), prob) for prob in decode_check(fa, fb, M, N, K)]
+    assert not bad, bad[:5]
+
+
+def test_decode_model_reports_planted_mistakes():
+    """The model itself: a short last period loaded from its own start (not
+    16 bytes before the row's end) reads across into the next row, and past
+    the last row of the scale array; copies past the range with a live
+    num_records fetch what the kernel never reads."""
+    assert not decode_check(FP4, FP4, 5, 100, 1664)
+    assert any(p[0] in ("As", "Bs") for p in decode_check(FP4, FP4, 5, 100, 1664,
+                                                          clamp_scales=False))
+    assert any(p[0] in ("A", "B") for p in decode_check(FP8, FP8, 8, 64, 4096 + 128,
+                                                        idle_records=False))

@@ -81,7 +81,7 @@ def test_e5m2_pair_every_tile(fa, fb, tile, split):
 
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=PAIR_IDS)
 def test_e5m2_pair_small_m_and_full_size(fa, fb):
-    """8 rows against a 70B-down-shaped weight (split-K plan), and the
+    """8 rows against a 70B-down-shaped weight (the decode kernel), and the
     fused-QKV shape on sampled rows, bit-identical on a rerun."""
     import torch
     case = _case(fa, fb, 8, 8192, 4096, seed=70 + fa)

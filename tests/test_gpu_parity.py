@@ -61,12 +61,16 @@ SMALL_M_SHAPES = [(1, 32, 128), (8, 97, 1152), (32, 64, 3968), (33, 40, 640),
 @pytest.mark.parametrize("out", [F32, BF16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", SMALL_M_SHAPES)
 def test_small_m(tile, fmt, out, M, N, K):
-    """Small M runs a short tile, 128x128 or 64x256 (rows past M read row
-    M-1, never stored), with split-K when the grid is small and K long (the
-    last shapes): the plan's pick and each short tile forced, at its planned
-    split."""
+    """Small M runs the decode kernel (M <= 32, K >= 512, and for K > 8192
+    also M <= 8 and enough columns) or a short tile, 128x128 or 64x256 (rows
+    past M not fetched, never stored), with split-K when the grid is small
+    and K long (the last shape): the plan's pick and each short tile forced,
+    at its planned split."""
     p = mxg.plan(fmt, M, N, K, out)
-    assert p["tile_m"] in (64, 128), p
+    if p["variant"] == mxg.VARIANT_DECODE:
+        assert M <= mxg.DECODE_TILE and K >= 512, p
+    else:
+        assert p["tile_m"] in (64, 128), p
     case = mxinputs.make_random(fmt, M, N, K, seed=1000 + M * 3 + N + K)
     log("small M fmt=%d out=%d M=%d N=%d K=%d tile=%s plan split=%d"
         % (fmt, out, M, N, K, tile, p["split_k"]))
