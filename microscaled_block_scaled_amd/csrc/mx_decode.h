@@ -38,17 +38,25 @@ __device__ __forceinline__ void wait_vm_lds()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
-// Slab geometry of the decode kernel for formats (FA, FB).  (Staging only
-// the A rows of one copy instruction when M <= 8, for a ring of 8 slabs of
-// B instead of 5, measured no faster on MI355X: at M = 8, N = 8192,
-// K = 28672 the same time within 1 %, and up to 18 % slower for E2M1 with
-// K <= 4096.)
-template <int FA, int FB>
+// Slab geometry of the decode kernel for formats (FA, FB): the tile
+// kernel's slabs (128 K-values, 256 when both operands are E2M1), 32 rows
+// of A and 32 of B.  WIDE is for an E4M3 / E5M2 A with an E2M1 B and M <= 8
+// (8-bit activations, 4-bit weights): 256-K slabs, so that each B row of a
+// slab is one whole 128-byte line (with 128-K slabs it is half of one,
+// and the line's other half is fetched again), A rows of 256 bytes, and
+// only the 8 A rows of two copy instructions staged, which keeps the ring
+// 6 slabs deep.  (Staging 8 A rows in the other geometries too, for a ring
+// of 8 slabs instead of 5, measured no faster on MI355X: at M = 8,
+// N = 8192, K = 28672 the same time within 1 %, and up to 18 % slower for
+// E2M1 with K <= 4096.)
+template <int FA, int FB, bool WIDE = false>
 struct decode_geo {
     using SL = slab<FA, FB>;
-    static constexpr int RA = SL::template row_bytes<FA>;   // slab row bytes: 128 or 64
-    static constexpr int RB = SL::template row_bytes<FB>;
-    static constexpr int MA = kDecodeRows;                    // rows of A staged
+    static_assert(!WIDE || (FB == FP4 && FA != FP4), "the wide slabs pair an 8-bit A with an E2M1 B");
+    static constexpr int KS = WIDE ? 256 : SL::kvals;          // K-values per slab
+    static constexpr int RA = WIDE ? 256 : SL::template row_bytes<FA>;   // slab row bytes
+    static constexpr int RB = WIDE ? 128 : SL::template row_bytes<FB>;
+    static constexpr int MA = WIDE ? 8 : kDecodeRows;         // rows of A staged
     static constexpr int NCOPY = MA * RA / 1024 + kDecodeRows * RB / 1024;   // copies per slab
     static constexpr int SLOT = MA * RA + kDecodeRows * RB;   // LDS bytes per slab
     // ring depth: as many slabs as the LDS holds, within the wait's count
@@ -60,18 +68,27 @@ struct decode_geo {
     static constexpr int SMEM = kDecodeWaves * WAVE_LDS;
 };
 
-template <int FA, int FB, int OUT>
+// LDS swizzle of a slab row of R bytes: the tile kernel's for 128- and
+// 64-byte rows; for 256-byte rows (16 chunks) chunk c of row r is stored at
+// chunk c ^ (r mod 16), so 16 rows reading one chunk touch 16 distinct
+// 16-byte bank groups.
+template <int R> __device__ __forceinline__ int decode_swz(int r)
+{
+    return R == 256 ? (r & 15) : swz_row<R>(r);
+}
+
+template <int FA, int FB, int OUT, bool WIDE>
 __global__ void __launch_bounds__(kDecodeWaves * 64)
 decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
               const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs, void *__restrict__ C,
               int M, int N, int K)
 {
     using SL = slab<FA, FB>;
-    using G = decode_geo<FA, FB>;
+    using G = decode_geo<FA, FB, WIDE>;
     static_assert(SL::scaled && !is_fp6<FA>::value && !is_fp6<FB>::value,
                   "E2M1, E4M3 and E5M2 operands");
-    constexpr int KS = SL::kvals;                    // K-values per slab: 128 or 256
-    constexpr int HS = SL::steps;                    // 64-K MFMA steps per slab: 2 or 4
+    constexpr int KS = G::KS;                        // K-values per slab: 128 or 256
+    constexpr int HS = KS / 64;                      // 64-K MFMA steps per slab: 2 or 4
     constexpr int PS = 512 / KS;                     // slabs per scale period
     constexpr int RA = G::RA, RB = G::RB, MA = G::MA;
     constexpr int RPCA = 1024 / RA, RPCB = 1024 / RB;             // rows per copy instruction
@@ -132,13 +149,13 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
 #pragma unroll
         for (int i = 0; i < CPA; ++i) {
             const int row = i * RPCA + crowa;
-            const uint32_t ch = min((uint32_t)(cpca ^ swz_row<RA>(row)) << 4, cmaxa);
+            const uint32_t ch = min((uint32_t)(cpca ^ decode_swz<RA>(row)) << 4, cmaxa);
             b2l_16(Ak, (uint32_t)row * (uint32_t)rowba + ch, dst + i * 1024);
         }
 #pragma unroll
         for (int i = 0; i < CPB; ++i) {
             const int row = i * RPCB + crowb;
-            const uint32_t ch = min((uint32_t)(cpcb ^ swz_row<RB>(row)) << 4, cmaxb);
+            const uint32_t ch = min((uint32_t)(cpcb ^ decode_swz<RB>(row)) << 4, cmaxb);
             b2l_16<kStream>(Bk, (uint32_t)row * (uint32_t)rowbb + ch,
                             dst + MA * RA + i * 1024);
         }
@@ -174,13 +191,15 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         }
     };
 
-    // Fragment of step p of a slab for lane row lr (32 slab rows of R bytes
-    // at `rows`): E4M3 / E5M2 chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g.
-    auto frag = [&](auto fc, const uint8_t *rows, int p, v8i &v) {
-        constexpr int F = decltype(fc)::value;
-        constexpr int R = F == FP4 && !(FA == FP4 && FB == FP4) ? 64 : 128;
-        const int sw = swz_row<R>(lr);
-        const uint8_t *rp = rows + lr * R;
+    // Fragment of step p of a slab for lane row lr, from NR staged rows of R
+    // bytes at `rows` (with NR = 8, the A rows of the wide slabs, lane row lr
+    // reads row lr % 8; only rows below M <= 8 are stored): E4M3 / E5M2
+    // chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g.
+    auto frag = [&](auto fc, auto rc, auto nc, const uint8_t *rows, int p, v8i &v) {
+        constexpr int F = decltype(fc)::value, R = decltype(rc)::value, NR = decltype(nc)::value;
+        const int r = lr % NR;
+        const int sw = decode_swz<R>(r);
+        const uint8_t *rp = rows + r * R;
         const int c0 = F == FP4 ? 2 * p + g : 4 * p + g;
         const v4i lo = *(const v4i *)(rp + ((c0 ^ sw) << 4));
         if constexpr (F == FP4) {
@@ -190,7 +209,8 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
             v = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     };
-    static_assert(RA == (FA == FP4 && FB != FP4 ? 64 : 128) && RB == (FB == FP4 && FA != FP4 ? 64 : 128),
+    static_assert(WIDE || (RA == (FA == FP4 && FB != FP4 ? 64 : 128) &&
+                           RB == (FB == FP4 && FA != FP4 ? 64 : 128)),
                   "slab rows as the fragment reads assume");
 
     v16f acc;
@@ -226,8 +246,10 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                     constexpr int p = decltype(pc)::value, s = kp * HS + p;
                     if (HS == 2 || k * HS + p < nsteps) {
                         v8i a, b;
-                        frag(std::integral_constant<int, FA>{}, slot, p, a);
-                        frag(std::integral_constant<int, FB>{}, slot + MA * RA, p, b);
+                        frag(std::integral_constant<int, FA>{}, std::integral_constant<int, RA>{},
+                             std::integral_constant<int, MA>{}, slot, p, a);
+                        frag(std::integral_constant<int, FB>{}, std::integral_constant<int, RB>{},
+                             std::integral_constant<int, kDecodeRows>{}, slot + MA * RA, p, b);
                         acc = mma<FA, FB, 2 * (s & 1)>(a, b, acc, sa[s >> 1], sb[s >> 1]);
                     }
                 });

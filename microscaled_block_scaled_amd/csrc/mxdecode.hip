@@ -17,12 +17,25 @@ void go(int out_dtype, const void *A, const void *As, const void *B, const void 
     const dim3 grid((unsigned)cdiv(N, MX_DECODE_TILE)), block(mx::kDecodeWaves * 64);
     const uint8_t *a = (const uint8_t *)A, *as = (const uint8_t *)As;
     const uint8_t *b = (const uint8_t *)B, *bs = (const uint8_t *)Bs;
-    if (out_dtype == MX_OUT_FP32)
-        hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OF32>), grid, block, 0, s, a, as, b, bs,
-                           C, (int)M, (int)N, (int)K);
+    const bool f32 = out_dtype == MX_OUT_FP32;
+    // An 8-bit A with an E2M1 B and at most 8 rows: the wide slabs
+    if constexpr (FB == mx::FP4 && FA != mx::FP4) {
+        if (M <= mx::decode_geo<FA, FB, true>::MA) {
+            if (f32)
+                hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OF32, true>), grid, block, 0, s,
+                                   a, as, b, bs, C, (int)M, (int)N, (int)K);
+            else
+                hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OBF16, true>), grid, block, 0, s,
+                                   a, as, b, bs, C, (int)M, (int)N, (int)K);
+            return;
+        }
+    }
+    if (f32)
+        hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OF32, false>), grid, block, 0, s, a, as,
+                           b, bs, C, (int)M, (int)N, (int)K);
     else
-        hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OBF16>), grid, block, 0, s, a, as, b,
-                           bs, C, (int)M, (int)N, (int)K);
+        hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OBF16, false>), grid, block, 0, s, a,
+                           as, b, bs, C, (int)M, (int)N, (int)K);
 }
 
 int kernel_fmt(int fmt)

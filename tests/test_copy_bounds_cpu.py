@@ -166,14 +166,20 @@ def test_model_reports_unclamped_fp6_padding_lanes():
 DECODE_LDS, DECODE_ROWS, DECODE_WAVES = 163840, 32, 4
 
 
-def decode_geo(fa, fb):
-    """(rows of A staged, copies per slab, ring depth) of the decode kernel."""
-    kv = kvals(fa, fb)
+def decode_wide(fa, fb, M):
+    """The wide slabs: an 8-bit A with an E2M1 B and M <= 8."""
+    return fb == FP4 and fa != FP4 and M <= 8
+
+
+def decode_geo(fa, fb, wide=False):
+    """(K-values per slab, A and B slab row bytes, rows of A staged, copies
+    per slab, ring depth) of the decode kernel."""
+    kv = 256 if wide else kvals(fa, fb)
     RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
-    MA = DECODE_ROWS
+    MA = 8 if wide else DECODE_ROWS
     ncopy = MA * RA // 1024 + DECODE_ROWS * RB // 1024
     slot = MA * RA + DECODE_ROWS * RB
-    return MA, ncopy, min(DECODE_LDS // (DECODE_WAVES * slot), 2 + 63 // ncopy)
+    return kv, RA, RB, MA, ncopy, min(DECODE_LDS // (DECODE_WAVES * slot), 2 + 63 // ncopy)
 
 
 def decode_operand(R, rowb, rows_real, koff, cmax, records, size, base, live, need_bytes,
@@ -199,9 +205,7 @@ def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
     """Problems of the decode kernel's loads for one problem; the two flags
     turn off the scale window's clamp into the row and the zero num_records
     of copies past the range (for the model's own tests)."""
-    kv = kvals(fa, fb)
-    RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
-    MA, ncopy, S = decode_geo(fa, fb)
+    kv, RA, RB, MA, ncopy, S = decode_geo(fa, fb, decode_wide(fa, fb, M))
     PS = 512 // kv
     L = max(2, -(-(S - 1) // PS))                    # periods of scale loads in flight
     assert (S - 2) * ncopy <= 63 and DECODE_WAVES * S * (MA * RA + DECODE_ROWS * RB) <= DECODE_LDS

@@ -2,7 +2,8 @@
 columns of C, its four waves on four K-ranges, partial tiles added in LDS)
 against the oracle, through the C ABI: every pair of E2M1, E4M3 and E5M2
 on ragged shapes (short last periods, half E2M1 slabs, waves with empty
-K-ranges, N tails), every M from 1 to 32, exact integers, NaN rows,
+K-ranges, N tails), every M from 1 to 32 (also for the 8-bit x E2M1 pairs,
+whose M <= 8 runs the wide slabs), exact integers, NaN rows,
 stores confined to C, the plan's shapes equal to the forced kernel bit for
 bit, repeatability, and the no-allocation entry point.
 
@@ -87,6 +88,18 @@ def test_decode_every_m(fmt):
         log("decode every M fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
         case = _case(fmt, fmt, M, N, K, seed=500 + M)
         _check(case, F32, _run(case, F32), what="every M, M=%d" % M)
+
+
+@pytest.mark.parametrize("fa", [E4M3, E5M2], ids=["e4m3", "e5m2"])
+def test_decode_w4a8_every_m(fa):
+    """An 8-bit A with an E2M1 B, every row count 1 .. 32: M <= 8 runs the
+    wide slabs (256 K-values, 8 A rows staged), larger M the 128-K slabs.
+    K = 3200: a short last period and a half wide slab in the last wave."""
+    N, K = 140, 3200
+    for M in range(1, 33):
+        log("decode w4a8 every M fa=%d M=%d N=%d K=%d" % (fa, M, N, K))
+        case = _case(fa, E2M1, M, N, K, seed=550 + M)
+        _check(case, BF16, _run(case, BF16), what="w4a8 every M, M=%d" % M)
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=[NAMES[f] for f in FORMATS])
