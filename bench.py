@@ -349,7 +349,7 @@ def bench_one(name, steps, warmup, with_cpu, cold_launches=60, with_ceiling=True
                    "out": "fp32" if out == mxinputs.OUT_FP32 else "bf16",
                    "accumulate": "fp32", "peak_frac": round(tflops / PEAK_TFLOPS[fmt], 4),
                    "plan": plan_str, "operand_copies": ncopies,
-                   "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
+                   "kernel_source_sha256": kernel_source_hash(gemm_sources(plan))},
         "roofline": roof,
     }
     if with_cpu:
@@ -494,7 +494,7 @@ def bench_grouped(steps, warmup, fmt):
             "config": {"workload": workload, "group_rows": rows, "N": N, "K": K,
                        "format": fname, "out": "bf16",
                        "peak_frac": round(tflops / peak, 4), "plan": plan_str,
-                       "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
+                       "kernel_source_sha256": kernel_source_hash(gemm_sources(p))},
             "roofline": roof}
 
 
@@ -575,7 +575,7 @@ def bench_mixed(steps, warmup, name):
                        "format_a": mxinputs.fmt_name(fa), "format_b": mxinputs.fmt_name(fb),
                        "out": "bf16",
                        "peak_frac": round(tflops / peak, 4), "plan": plan_str,
-                       "kernel_source_sha256": kernel_source_hash(GEMM_SOURCES)},
+                       "kernel_source_sha256": kernel_source_hash(gemm_sources(p))},
             "roofline": roof}
 
 
