@@ -4,21 +4,27 @@
 // reads each weight byte once and does 2M FLOP per byte, far below the MFMA
 // ridge: its time is the time to stream B from HBM.
 //
-// Each workgroup computes one 32-column tile of C for all M rows.  Its four
-// waves take four consecutive K-ranges of whole 512-K scale periods, one
-// each, and at the end add their 32 x 32 FP32 partial tiles in LDS in wave
-// order (so the result does not depend on timing).  The tile kernel instead
-// splits K across workgroups, writes FP32 planes to memory and adds them in
-// a second kernel; here the only memory traffic is A, B, their scales and C.
+// C is cut into column groups of 32 columns (all M rows).  A workgroup of
+// four waves takes groups blockIdx.x, blockIdx.x + gridDim.x, ...; the grid
+// is at most one workgroup per CU.  Its four waves take four consecutive
+// K-ranges of whole 512-K scale periods, one each, and after each group add
+// their 32 x 32 FP32 partial tiles in LDS in wave order (so the result does
+// not depend on timing).  The tile kernel instead splits K across
+// workgroups, writes FP32 planes to memory and adds them in a second
+// kernel; here the only memory traffic is A, B, their scales and C.
 //
 // A wave works alone: a private ring of slabs in LDS (a slab holds 128 or
-// 256 K-values of the 32 A rows and 32 B rows, as in the tile kernel, with
-// the same XOR swizzle), filled by 16-byte buffer copies straight from HBM
-// and read back as MFMA fragments, with no workgroup barrier in the K loop.
-// Rows of A past M and of B past N lie past the copy descriptor's
-// num_records and are not fetched (their results are never stored).  B is
-// read once and carries the nontemporal hint.  Scale bytes are loaded into
-// registers, one period ahead.
+// 256 K-values of the staged A rows and 32 B rows, as in the tile kernel,
+// with the same XOR swizzle), filled by 16-byte buffer copies straight from
+// HBM and read back as MFMA fragments, with no workgroup barrier in the K
+// loop.  Its copies form one stream over all its groups: the first slabs of
+// the next group are in flight while a group's last slabs are multiplied
+// and its partial tiles are added, so a workgroup with several groups does
+// not refill its pipeline from empty for each.  Rows of A past M and of B
+// past N lie past the copy descriptor's num_records and are not fetched
+// (their results are never stored).  B is read once and carries the
+// nontemporal hint.  Scale bytes are loaded into registers, a few periods
+// ahead.
 #pragma once
 
 #include "mx_kernels.h"
@@ -28,6 +34,8 @@ namespace mx {
 constexpr int kDecodeWaves = 4;      // waves per workgroup, one K-range each
 constexpr int kDecodeRows = 32;      // columns of C per workgroup, and the most rows of A
 constexpr int kDecodeLds = 163840;   // LDS per workgroup: all of a CU's 160 KB
+// LDS for adding the waves' partial tiles: a 32 x 32 FP32 tile per wave.
+constexpr int kDecodeRed = kDecodeWaves * kDecodeRows * kDecodeRows * 4;
 
 // Wait until at most N of this wave's memory loads are outstanding and all
 // of its LDS reads are done (the ring slot about to be refilled was read by
@@ -59,13 +67,14 @@ struct decode_geo {
     static constexpr int MA = WIDE ? 8 : kDecodeRows;         // rows of A staged
     static constexpr int NCOPY = MA * RA / 1024 + kDecodeRows * RB / 1024;   // copies per slab
     static constexpr int SLOT = MA * RA + kDecodeRows * RB;   // LDS bytes per slab
-    // ring depth: as many slabs as the LDS holds, within the wait's count
-    // field ((S - 2) * NCOPY loads outstanding, at most 63)
-    static constexpr int S_LDS = kDecodeLds / (kDecodeWaves * SLOT);
+    // ring depth: as many slabs as the LDS beside the partial-tile area
+    // holds, within the wait's count field ((S - 2) * NCOPY loads
+    // outstanding, at most 63)
+    static constexpr int S_LDS = (kDecodeLds - kDecodeRed) / (kDecodeWaves * SLOT);
     static constexpr int S_CNT = 2 + 63 / NCOPY;
     static constexpr int S = S_LDS < S_CNT ? S_LDS : S_CNT;
     static constexpr int WAVE_LDS = S * SLOT;
-    static constexpr int SMEM = kDecodeWaves * WAVE_LDS;
+    static constexpr int SMEM = kDecodeWaves * WAVE_LDS + kDecodeRed;
 };
 
 // LDS swizzle of a slab row of R bytes: the tile kernel's for 128- and
@@ -98,17 +107,23 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     constexpr int S = G::S, SLOT = G::SLOT;
     static_assert(S >= 3 && (S - 2) * NCOPY <= 63, "ring depth and the vmcnt field");
     static_assert(G::SMEM <= kDecodeLds, "LDS budget");
-    static_assert(G::SMEM >= kDecodeWaves * 64 * 16 * 4, "the reduction reuses the rings");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[G::SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, g = lane >> 5;
-    const int n0 = blockIdx.x * kDecodeRows;
     uint8_t *const ring = smem + wave * G::WAVE_LDS;
+    float *const red = (float *)(smem + kDecodeWaves * G::WAVE_LDS);
 
-    // This wave's K-range [kb, kb + klen): whole 512-K periods, split as
-    // evenly as they go; the last wave's range ends at K (and may be empty).
+    // This workgroup's column groups: gi = 0 .. ng-1 is group
+    // blockIdx.x + gi * gridDim.x, columns n0 .. n0+31 of it.
+    const int ngroups = (N + kDecodeRows - 1) / kDecodeRows;
+    const int ng = (int)blockIdx.x < ngroups ? (ngroups - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    auto group_n0 = [&](int gi) { return ((int)blockIdx.x + gi * (int)gridDim.x) * kDecodeRows; };
+
+    // This wave's K-range [kb, kb + klen), the same for every group: whole
+    // 512-K periods, split as evenly as they go; the last wave's range ends
+    // at K (and may be empty).
     const int per_w = (K / 128 + 4 * kDecodeWaves - 1) / (4 * kDecodeWaves);
     const int kb = min(wave * per_w * 512, K), klen = min(per_w * 512, K - kb);
     const int nslab = (klen + KS - 1) / KS, nsteps = klen / 64, nper = (klen + 511) / 512;
@@ -116,7 +131,19 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int64_t kboffa = kbytes<FA>(kb), kboffb = kbytes<FB>(kb);
     const int64_t rowla = kbytes<FA>(klen), rowlb = kbytes<FB>(klen);
     const int sps = K / 32;                          // scale bytes per row
-    const int rows_b = min(kDecodeRows, N - n0);
+
+    // Scale registers: period q's bytes in (sa, sb), and the raw loads of
+    // the next L periods in a ring of L register sets, period q in set q % L.
+    // L periods of slab copies (at least S - 1 slab positions) separate a
+    // period's loads from their use, so waiting for them never stalls the
+    // copies in flight.
+    constexpr int L = (S - 1 + PS - 1) / PS;
+    // The stream: each group takes ppq periods (its range's, rounded up to
+    // whole trips of L) of PS slab positions; position j is slab j % ppg of
+    // group j / ppg.  Positions past a group's slabs, and past its last
+    // group, copy nothing and do no MFMA.
+    const int ppq = nslab > 0 ? (nper + L - 1) / L * L : 0;
+    const int ppg = ppq * PS;
 
     // Copy geometry (the tile kernel's): lane l copies chunk l % (R/16) of row
     // l / (R/16) of a block of rows into that chunk of the row's LDS copy,
@@ -124,25 +151,26 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int crowa = lane / (RA / 16), cpca = lane % (RA / 16);
     const int crowb = lane / (RB / 16), cpcb = lane % (RB / 16);
     const uint8_t *const Ab = A + kboffa;
-    const uint8_t *const Bb = B + (int64_t)n0 * rowbb + kboffb;
     // Extents from each copy base to the end of the last real row: copies of
     // rows at or past M (A) or N (B) are not fetched.  Under 2^32: at most 32
     // rows of at most 2^24 bytes.
     const uint32_t exta = (uint32_t)(M * rowba - kboffa);
-    const uint32_t extb = (uint32_t)(rows_b * rowbb - kboffb);
 
-    // Copy slab k of the range into ring slot k % S.  Every slab position
-    // issues the same copies, also past the last slab (then into the free
-    // slot, never read, with num_records 0: nothing is fetched), so that the
-    // count of loads in flight is the same on every path through the loop.
-    // When both operands are E2M1 and klen % 256 == 128 the last slab is
-    // half a slab: its chunk offsets are clamped into the range (those
-    // chunks are never read).
-    auto issue = [&](int k) {
-        uint8_t *const dst = ring + (k % S) * SLOT;
-        const bool live = k < nslab;
-        k = min(k, nslab - 1);
-        const uint32_t koffa = (uint32_t)k * RA, koffb = (uint32_t)k * RB;
+    // Copy stream position j into ring slot j % S.  Every position issues
+    // the same copies, also those with no slab (then with num_records 0:
+    // nothing is fetched), so that the count of loads in flight is the same
+    // on every path through the loop.  When both operands are E2M1 and
+    // klen % 256 == 128 the last slab is half a slab: its chunk offsets are
+    // clamped into the range (those chunks are never read).
+    auto issue = [&](int j) {
+        uint8_t *const dst = ring + (j % S) * SLOT;
+        const int gj = j / ppg, k = j - gj * ppg;
+        const bool live = gj < ng && k < nslab;
+        const int kc = min(k, nslab - 1);
+        const int n0 = group_n0(min(gj, ng - 1));
+        const uint32_t extb = (uint32_t)(min(kDecodeRows, N - n0) * rowbb - kboffb);
+        const uint8_t *const Bb = B + (int64_t)n0 * rowbb + kboffb;
+        const uint32_t koffa = (uint32_t)kc * RA, koffb = (uint32_t)kc * RB;
         const uint32_t cmaxa = (uint32_t)(rowla - 16) - koffa, cmaxb = (uint32_t)(rowlb - 16) - koffb;
         const rsrc_t Ak = make_rsrc(Ab + koffa, live ? exta - koffa : 0u);
         const rsrc_t Bk = make_rsrc(Bb + koffb, live ? extb - koffb : 0u);
@@ -161,26 +189,31 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         }
     };
 
-    // Scale bytes, several periods ahead.  load_scales fetches the 16 bytes of
-    // period q (blocks kb/32 + 16q ..) of A row lr and B row n0 + lr; a short
-    // last period is fetched as the 16 bytes that end at the row's end, so
-    // that no load crosses a row.  Rows past M (N) are past the descriptors'
-    // num_records: not fetched.  use_scales then rotates a short period back
-    // by whole dwords and shifts each dword right by 8g bits, so that this
-    // lane group's byte of step s (block 2s + g of the period) is byte
-    // 2(s % 2) of dword s / 2.  The empty asm pins that work, and with it the
-    // wait for the loads, to where use_scales is called (else the compiler
-    // may start it right after the loads and wait for them there).
+    // Scale bytes of stream period qg (period qg % ppq of group qg / ppq).
+    // load_scales fetches the 16 bytes of period q (blocks kb/32 + 16q ..)
+    // of A row lr and B row n0 + lr; a short last period is fetched as the
+    // 16 bytes that end at the row's end, so that no load crosses a row.
+    // Rows past M (N) are past the descriptors' num_records: not fetched.
+    // use_scales then rotates a short period back by whole dwords and shifts
+    // each dword right by 8g bits, so that this lane group's byte of step s
+    // (block 2s + g of the period) is byte 2(s % 2) of dword s / 2.  The
+    // empty asm pins that work, and with it the wait for the loads, to where
+    // use_scales is called (else the compiler may start it right after the
+    // loads and wait for them there).
     const rsrc_t Asr = make_rsrc(As, (uint32_t)(M * sps));
-    const rsrc_t Bsr = make_rsrc(Bs + (int64_t)n0 * sps, (uint32_t)(rows_b * sps));
     auto scale_at = [&](int q) { return min(kb / 32 + 16 * min(q, nper - 1), sps - 16); };
-    auto load_scales = [&](int q, v4i &ra, v4i &rb) {
+    auto load_scales = [&](int qg, v4i &ra, v4i &rb) {
+        const int gq = qg / ppq, q = qg - gq * ppq;
+        const int n0 = group_n0(min(gq, ng - 1));
+        const rsrc_t Bsr = make_rsrc(Bs + (int64_t)n0 * sps,
+                                     (uint32_t)(min(kDecodeRows, N - n0) * sps));
         const uint32_t off = (uint32_t)lr * (uint32_t)sps + (uint32_t)scale_at(q);
         ra = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(Asr, off, 0, 0));
         rb = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(Bsr, off, 0, 0));
     };
-    auto use_scales = [&](int q, v4i a, v4i b, v4i &sa, v4i &sb) {
+    auto use_scales = [&](int qg, v4i a, v4i b, v4i &sa, v4i &sb) {
         asm volatile("" : "+v"(a), "+v"(b));
+        const int q = qg % ppq;
         const int rot = (kb / 32 + 16 * min(q, nper - 1) - scale_at(q)) >> 2;
         if (rot & 1) { a = v4i{a[1], a[2], a[3], a[0]}; b = v4i{b[1], b[2], b[3], b[0]}; }
         if (rot & 2) { a = v4i{a[2], a[3], a[0], a[1]}; b = v4i{b[2], b[3], b[0], b[1]}; }
@@ -214,34 +247,26 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                   "slab rows as the fragment reads assume");
 
     v16f acc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-
-    // Scale registers: period q's bytes in (sa, sb), and the raw loads of
-    // the next L periods in a ring of L register sets, period q in set q % L.
-    // L periods of slab copies (at least S - 1 slab positions) separate a
-    // period's loads from their use, so waiting for them never stalls the
-    // copies in flight.
-    constexpr int L = (S - 1 + PS - 1) / PS > 2 ? (S - 1 + PS - 1) / PS : 2;
     v4i sa, sb, ra[L], rb[L];
 
-    // Period q, whose scales are set i = q % L: its slabs (every slab
-    // position issues its copies; slabs past the range do no MFMA), the
-    // loads of period q+L into set i (free since period q's scales were made
-    // current), and at its end period q+1's scales made current.
-    auto period = [&](auto ic, int q) {
+    // Stream period qg = gi * ppq + q (period q of group gi), whose scales
+    // are set i = q % L: its slabs, the loads of period qg + L into set i
+    // (free since period qg's scales were made current), and at its end
+    // period qg + 1's scales made current.
+    auto period = [&](auto ic, int gi, int q) {
         constexpr int i = decltype(ic)::value;
-        load_scales(q + L, ra[i], rb[i]);
+        const int qg = gi * ppq + q;
+        load_scales(qg + L, ra[i], rb[i]);
         static_for<PS>([&](auto kc) {
             constexpr int kp = decltype(kc)::value;
-            const int k = q * PS + kp;
-            // Slab k is in once at most the copies of the S - 2 slab
+            const int k = q * PS + kp, j = qg * PS + kp;
+            // Position j is in once at most the copies of the S - 2
             // positions issued after it are outstanding (the scale loads
             // issued since only make the wait stricter).
             wait_vm_lds<(S - 2) * NCOPY>();
-            issue(k + S - 1);                        // into the slot of slab k - 1
+            issue(j + S - 1);                        // into the slot of position j - 1
             if (k < nslab) {
-                const uint8_t *slot = ring + (k % S) * SLOT;
+                const uint8_t *slot = ring + (j % S) * SLOT;
                 static_for<HS>([&](auto pc) {
                     constexpr int p = decltype(pc)::value, s = kp * HS + p;
                     if (HS == 2 || k * HS + p < nsteps) {
@@ -255,45 +280,57 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                 });
             }
         });
-        use_scales(q + 1, ra[(i + 1) % L], rb[(i + 1) % L], sa, sb);
+        use_scales(qg + 1, ra[(i + 1) % L], rb[(i + 1) % L], sa, sb);
     };
 
-    if (nslab > 0) {
+    // Add the waves' partial tiles of group gi in wave order and store them.
+    // In the MFMA result lane (c, g) holds, in element e, row
+    // 8(e/4) + 4g + e%4 of column c; element e of lane l is kept at
+    // red[1024 w + 64 e + l].  The barriers order LDS only: the stream's
+    // copies into the rings stay in flight.
+    auto add_and_store = [&](int gi) {
+        const int n0 = group_n0(gi), rows_b = min(kDecodeRows, N - n0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[wave * 1024 + e * 64 + lane] = acc[e];
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < kDecodeRows * kDecodeRows / (kDecodeWaves * 64); ++q) {
+            const int m = q * 8 + (tid >> 5), c = tid & 31;
+            if (m >= M || c >= rows_b) continue;
+            const int at = ((m >> 3) * 4 + (m & 3)) * 64 + c + 32 * ((m >> 2) & 1);
+            float v = red[at];
+#pragma unroll
+            for (int w = 1; w < kDecodeWaves; ++w) v += red[w * 1024 + at];
+            if constexpr (OUT == OF32) ((float *)C)[(int64_t)m * N + n0 + c] = v;
+            else ((uint16_t *)C)[(int64_t)m * N + n0 + c] = f32_to_bf16(v);
+        }
+        lds_barrier();
+    };
+
+    if (ppg > 0) {
         static_for<L>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             load_scales(i, ra[i], rb[i]);
         });
 #pragma unroll
-        for (int k = 0; k < S - 1; ++k) issue(k);
+        for (int j = 0; j < S - 1; ++j) issue(j);
         use_scales(0, ra[0], rb[0], sa, sb);
-        // L periods per trip, so that the register sets keep their roles
-        // without a register move (a move of a load's result waits for the
-        // load).  The last trip may run up to L - 1 periods past the range:
-        // their slabs issue copies that fetch nothing and do no MFMA.
-        for (int q = 0; q < nper; q += L)
-            static_for<L>([&](auto ic) { period(ic, q + decltype(ic)::value); });
+        for (int gi = 0; gi < ng; ++gi) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+            // L periods per trip, so that the register sets keep their
+            // roles without a register move (a move of a load's result
+            // waits for the load).
+            for (int q = 0; q < ppq; q += L)
+                static_for<L>([&](auto ic) { period(ic, gi, q + decltype(ic)::value); });
+            add_and_store(gi);
+        }
+    } else {                                         // an empty K-range: zero partial tiles
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int gi = 0; gi < ng; ++gi) add_and_store(gi);
     }
-
-    // Add the waves' partial tiles in wave order.  In the MFMA result lane
-    // (c, g) holds, in element e, row 8(e/4) + 4g + e%4 of column c; element
-    // e of lane l is kept at red[1024 w + 64 e + l].
-    wait_vm0();
-    __syncthreads();
-    float *const red = (float *)smem;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[wave * 1024 + e * 64 + lane] = acc[e];
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kDecodeRows * kDecodeRows / (kDecodeWaves * 64); ++q) {
-        const int m = q * 8 + (tid >> 5), c = tid & 31;
-        if (m >= M || c >= rows_b) continue;
-        const int at = ((m >> 3) * 4 + (m & 3)) * 64 + c + 32 * ((m >> 2) & 1);
-        float v = red[at];
-#pragma unroll
-        for (int w = 1; w < kDecodeWaves; ++w) v += red[w * 1024 + at];
-        if constexpr (OUT == OF32) ((float *)C)[(int64_t)m * N + n0 + c] = v;
-        else ((uint16_t *)C)[(int64_t)m * N + n0 + c] = f32_to_bf16(v);
-    }
+    wait_vm0();                                      // the copies past the last group
 }
 
 }  // namespace mx

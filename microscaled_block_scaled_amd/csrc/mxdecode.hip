@@ -3,6 +3,8 @@
 // that the library builds in parallel.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "mx_decode.h"
 #include "mx_launch.h"
 
@@ -14,7 +16,9 @@ template <int FA, int FB>
 void go(int out_dtype, const void *A, const void *As, const void *B, const void *Bs, void *C,
         int64_t M, int64_t N, int64_t K, hipStream_t s)
 {
-    const dim3 grid((unsigned)cdiv(N, MX_DECODE_TILE)), block(mx::kDecodeWaves * 64);
+    // at most one workgroup per CU; each takes every gridDim-th column group
+    const dim3 grid((unsigned)std::min<int64_t>(cdiv(N, MX_DECODE_TILE), kCUs));
+    const dim3 block(mx::kDecodeWaves * 64);
     const uint8_t *a = (const uint8_t *)A, *as = (const uint8_t *)As;
     const uint8_t *b = (const uint8_t *)B, *bs = (const uint8_t *)Bs;
     const bool f32 = out_dtype == MX_OUT_FP32;

@@ -95,7 +95,8 @@ void fill_plan(int t, int64_t M, int64_t N, int64_t K, mx_plan_t *p, int split_r
         ? p->split_k * plane_of(M, N) * 4 : 0;
 }
 
-// Plan for the decode kernel: one workgroup per MX_DECODE_TILE columns.
+// Plan for the decode kernel: column groups of MX_DECODE_TILE columns, at
+// most one workgroup per CU, each taking every gridDim-th group.
 void fill_decode_plan(int64_t N, mx_plan_t *p)
 {
     memset(p, 0, sizeof(*p));
@@ -103,31 +104,34 @@ void fill_decode_plan(int64_t N, mx_plan_t *p)
     p->tile_m = p->tile_n = MX_DECODE_TILE;
     p->split_k = 1;
     p->threads = mx::kDecodeWaves * 64;
-    p->workgroups = cdiv(N, MX_DECODE_TILE);
+    p->workgroups = std::min<int64_t>(cdiv(N, MX_DECODE_TILE), kCUs);
 }
 
 // Whether the plan takes the decode kernel for a problem it can run.  The
-// decode kernel runs one workgroup per CU at a time (it takes all of a CU's
-// LDS), so its grid of ceil(N / 32) workgroups runs in rounds of 256.  The
+// decode kernel runs at most one workgroup per CU (it takes all of a CU's
+// LDS), each streaming every 256th column group of 32 columns.  The
 // thresholds were fitted to cold per-call times of both kernels on MI355X
-// over 360 problems (M = 1 .. 32, N = 2048 .. 28672, K = 512 .. 28672,
+// over 440 problems (M = 1 .. 32, N = 2048 .. 32768, K = 512 .. 28672,
 // E2M1 and E4M3): with them the plan reaches 0.995 of the faster kernel's
-// speed (geometric mean; worst 0.88), against 0.81 for the tiled kernel
-// alone.  The decode kernel loses
-//   * with more than four rounds, or more than two at K < 6144, or more
-//     than one and a half at K <= 1024 (each round refills the pipeline);
-//   * at K >= 16384 with under 5/8 of the CUs busy, where the tiled
-//     kernel's K split spreads the same bytes over more CUs;
-//   * for M > 8 at K > 14336, or with more than one round at K >= 6144:
-//     every workgroup reads all of A, 32 columns at a time.
-// M = 8, N = 8192, K = 28672 (one round): 1.08x E4M3, 1.13x E2M1.
+// speed (geometric mean; worst 0.80), against 0.81 for the tiled kernel
+// alone and 0.978 for the decode kernel alone.  The decode kernel loses
+//   * with more than 4 column groups per workgroup, or more than 2 at
+//     K < 1024, or more than 3 at K <= 1024 (its per-group work is short);
+//   * at K >= 16384 with fewer than 160 column groups, where the tiled
+//     kernel's K split spreads B over more CUs (N = 4096, K = 28672:
+//     0.76 - 1.0x);
+//   * for M > 16 at K > 14336, or with more than one group per workgroup
+//     at K = 14336: every workgroup reads all of A (M = 32, K = 28672:
+//     0.78 - 0.93x).
+// M = 8, N = 8192, K = 28672: 1.07x E4M3, 1.17x E2M1; N = 20480,
+// K = 4096: 1.2 - 1.4x.
 bool decode_preferred(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t wgs = cdiv(N, MX_DECODE_TILE);
-    if (wgs > 4 * kCUs || (wgs > 2 * kCUs && K < 6144)) return false;
-    if (K <= 1024 && wgs > kCUs * 3 / 2) return false;
+    const int64_t wgs = cdiv(N, MX_DECODE_TILE);    // column groups
+    if (wgs > 4 * kCUs || (wgs > 2 * kCUs && K < 1024)) return false;
+    if (K <= 1024 && wgs > 3 * kCUs) return false;
     if (K >= 16384 && wgs < kCUs * 5 / 8) return false;
-    if (M > 8 && (K > 14336 || (wgs > kCUs && K >= 6144))) return false;
+    if (M > 16 && (K > 14336 || (K >= 14336 && wgs > kCUs))) return false;
     return true;
 }
 

@@ -163,7 +163,8 @@ def test_plan_small_m_uses_short_tile(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (8, 8192, 28672), (32, 8192, 4096),
                                    (16, 14336, 4096), (5, 8161, 2048), (8, 6144, 28672),
                                    (32, 100, 512), (1, 16384, 8192), (8, 28672, 28672),
-                                   (16, 3072, 14336), (1, 12288, 1024)])
+                                   (16, 3072, 14336), (1, 12288, 1024), (8, 28672, 4096),
+                                   (16, 8192, 28672), (1, 32768, 2048), (32, 20480, 8192)])
 def test_plan_decode(M, N, K):
     """M <= 32 and K >= 512 within the measured limits (rounds of 256
     decode workgroups, K, M): the decode variant, for each of E2M1, E4M3
@@ -173,20 +174,21 @@ def test_plan_decode(M, N, K):
         assert p["variant"] == mxg.VARIANT_DECODE, (fmt, p)
         assert (p["tile_m"], p["tile_n"]) == (mxg.DECODE_TILE, mxg.DECODE_TILE)
         assert p["split_k"] == 1 and p["workspace_bytes"] == 0 and p["threads"] == 256
-        assert p["workgroups"] == -(-N // mxg.DECODE_TILE)
+        # at most one workgroup per CU, each taking every grid-th column group
+        assert p["workgroups"] == min(-(-N // mxg.DECODE_TILE), 256)
     # FP6 has no decode kernel: the tiled one
     for fmt in (mxg.FMT_E2M3, mxg.FMT_E3M2):
         assert mxg.plan(fmt, M, N, K)["variant"] == mxg.VARIANT_TILE
 
 
-@pytest.mark.parametrize("M,N,K", [(33, 8192, 28672), (8, 4096, 28672), (8, 28672, 4096),
-                                   (16, 8192, 28672), (1, 16385, 2048), (8, 8192, 384),
-                                   (1, 32769, 28672), (16, 12288, 8192), (1, 12320, 1024)])
+@pytest.mark.parametrize("M,N,K", [(33, 8192, 28672), (8, 4096, 28672), (17, 8192, 28672),
+                                   (1, 16385, 896), (8, 8192, 384), (1, 32769, 28672),
+                                   (24, 12288, 14336), (1, 24608, 1024)])
 def test_plan_decode_not_taken(M, N, K):
-    """M > 32; K >= 16384 with fewer than 160 decode workgroups (N = 4096);
-    more than 4 rounds of 256 workgroups, more than 2 at K < 6144 or more
-    than 1.5 at K <= 1024; M > 8 with K > 14336, or with more than one round
-    at K >= 6144; K < 512: the tiled kernel."""
+    """M > 32; K >= 16384 with fewer than 160 column groups (N = 4096); more
+    than 4 column groups per workgroup (N > 32768), more than 2 at K < 1024
+    or more than 3 at K <= 1024; M > 16 with K > 14336, or with more than
+    one group per workgroup at K = 14336; K < 512: the tiled kernel."""
     assert mxg.plan(mxg.FMT_E4M3, M, N, K)["variant"] == mxg.VARIANT_TILE
 
 

@@ -158,12 +158,15 @@ def test_model_reports_unclamped_fp6_padding_lanes():
 
 
 # --------------------------------------------------------------------------
-# The decode kernel (csrc/mx_decode.h): 4 waves per workgroup, each a K-range
-# of whole 512-K periods, a private ring of S slabs of 32 A rows and 32 B
-# rows, every slab position of every period issuing its copies (past the
-# range with num_records 0), and 16-byte scale loads per lane row, two
-# periods ahead, never crossing a row.
-DECODE_LDS, DECODE_ROWS, DECODE_WAVES = 163840, 32, 4
+# The decode kernel (csrc/mx_decode.h): a grid of at most 256 workgroups,
+# workgroup b taking column groups b, b + grid, ...; 4 waves per workgroup,
+# each a K-range of whole 512-K periods and a private ring of S slabs of the
+# staged A rows and 32 B rows; each wave's copies form one stream of slab
+# positions over all its groups (positions past a group's slabs, or past its
+# last group, copy with num_records 0), and 16-byte scale loads per lane
+# row, L periods ahead, never crossing a row.
+DECODE_LDS, DECODE_ROWS, DECODE_WAVES, DECODE_CUS = 163840, 32, 4, 256
+DECODE_RED = DECODE_WAVES * DECODE_ROWS * DECODE_ROWS * 4
 
 
 def decode_wide(fa, fb, M):
@@ -179,10 +182,11 @@ def decode_geo(fa, fb, wide=False):
     MA = 8 if wide else DECODE_ROWS
     ncopy = MA * RA // 1024 + DECODE_ROWS * RB // 1024
     slot = MA * RA + DECODE_ROWS * RB
-    return kv, RA, RB, MA, ncopy, min(DECODE_LDS // (DECODE_WAVES * slot), 2 + 63 // ncopy)
+    S = min((DECODE_LDS - DECODE_RED) // (DECODE_WAVES * slot), 2 + 63 // ncopy)
+    return kv, RA, RB, MA, ncopy, S
 
 
-def decode_operand(R, rowb, rows_real, koff, cmax, records, size, base, live, need_bytes,
+def decode_operand(R, rowb, rows_real, cmax, records, size, base, live, need_bytes,
                    staged=DECODE_ROWS):
     """One slab position's copies of one operand (`staged` rows)."""
     RPC = 1024 // R
@@ -202,19 +206,24 @@ def decode_operand(R, rowb, rows_real, koff, cmax, records, size, base, live, ne
 
 
 def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
-    """Problems of the decode kernel's loads for one problem; the two flags
-    turn off the scale window's clamp into the row and the zero num_records
-    of copies past the range (for the model's own tests)."""
+    """Problems of the decode kernel's loads for one problem, for the first
+    and the last workgroup; the two flags turn off the scale window's clamp
+    into the row and the zero num_records of copies with no slab (for the
+    model's own tests)."""
     kv, RA, RB, MA, ncopy, S = decode_geo(fa, fb, decode_wide(fa, fb, M))
     PS = 512 // kv
-    L = max(2, -(-(S - 1) // PS))                    # periods of scale loads in flight
-    assert (S - 2) * ncopy <= 63 and DECODE_WAVES * S * (MA * RA + DECODE_ROWS * RB) <= DECODE_LDS
+    L = -(-(S - 1) // PS)                            # periods of scale loads in flight
+    assert S >= 3 and (S - 2) * ncopy <= 63
+    assert DECODE_WAVES * S * (MA * RA + DECODE_ROWS * RB) + DECODE_RED <= DECODE_LDS
     rowba, rowbb = kbytes(fa, K), kbytes(fb, K)
     sps = K // 32
     per_w = -(-(K // 128) // (4 * DECODE_WAVES))
+    ngroups = -(-N // DECODE_ROWS)
+    grid = min(ngroups, DECODE_CUS)
     problems = []
-    for n0 in sorted({0, (-(-N // DECODE_ROWS) - 1) * DECODE_ROWS}):
-        rows_b = min(DECODE_ROWS, N - n0)
+    for b in sorted({0, grid - 1}):
+        ng = (ngroups - 1 - b) // grid + 1
+        group_n0 = lambda gi: (b + min(gi, ng - 1) * grid) * DECODE_ROWS
         for wave in range(DECODE_WAVES):
             kb = min(wave * per_w * 512, K)
             klen = min(per_w * 512, K - kb)
@@ -222,35 +231,48 @@ def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
             if nslab == 0:
                 continue
             nper = -(-klen // 512)
-            trips = -(-nper // L) * L                   # L periods per trip
+            ppq = -(-nper // L) * L                     # periods per group
+            ppg = ppq * PS                              # slab positions per group
             kboffa, kboffb = kbytes(fa, kb), kbytes(fb, kb)
             rowla, rowlb = kbytes(fa, klen), kbytes(fb, klen)
-            exta, extb = M * rowba - kboffa, rows_b * rowbb - kboffb
-            positions = list(range(S - 1)) + [q * PS + kp + S - 1 for q in range(trips)
-                                              for kp in range(PS)]
-            for k in positions:
-                live = k < nslab
+            exta = M * rowba - kboffa
+            # every position the stream issues: S - 1 ahead, then one per position
+            for j in range(ng * ppg + S - 1):
+                gj, k = divmod(j, ppg)
+                live = gj < ng and k < nslab
                 kc = min(k, nslab - 1)
+                n0 = group_n0(gj)
+                rows_b = min(DECODE_ROWS, N - n0)
+                extb = rows_b * rowbb - kboffb
                 koffa, koffb = kc * RA, kc * RB
+                # positions whose slab is read must be the group's first or last
+                # or a dummy one: check those (plus every dummy) to bound the work
+                if live and k not in (0, 1, nslab - 1) and gj not in (0, ng - 1):
+                    continue
                 for name, args in (
-                        ("A", (RA, rowba, M, koffa, rowla - 16 - koffa,
+                        ("A", (RA, rowba, M, rowla - 16 - koffa,
                                exta - koffa if live or not idle_records else 0, M * rowba,
                                kboffa + koffa, live, rowla - koffa, MA)),
-                        ("B", (RB, rowbb, rows_b, koffb, rowlb - 16 - koffb,
+                        ("B", (RB, rowbb, rows_b, rowlb - 16 - koffb,
                                extb - koffb if live or not idle_records else 0, N * rowbb,
                                n0 * rowbb + kboffb + koffb, live, rowlb - koffb))):
                     ok, need = decode_operand(*args)
                     if not ok or not need:
-                        problems.append((name, n0, wave, k, ok, need))
-            # scale loads: periods 0 .. trips + L - 1, clamped to the last
+                        problems.append((name, b, wave, j, ok, need))
+            # scale loads: stream periods 0 .. ng * ppq + L - 1
             lr = np.arange(DECODE_ROWS)
-            for q in range(trips + L):
+            for qg in range(ng * ppq + L):
+                gq, q = divmod(qg, ppq)
+                if 0 < gq < ng - 1 and 1 < q < nper - 1:
+                    continue
                 qc = min(q, nper - 1)
                 blk = kb // 32 + 16 * qc
                 at = min(blk, sps - 16) if clamp_scales else blk
                 nblk = min(16, klen // 32 - 16 * qc)
                 if at < 0 or not (at <= blk and blk + nblk <= at + 16) or (blk - at) % 4:
-                    problems.append(("scale window", n0, wave, q))
+                    problems.append(("scale window", b, wave, qg))
+                n0 = group_n0(gq)
+                rows_b = min(DECODE_ROWS, N - n0)
                 off = lr * sps + at
                 for name, rows, base, size in (("As", M, 0, M * sps),
                                                ("Bs", rows_b, n0 * sps, N * sps)):
@@ -258,7 +280,7 @@ def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
                     inside = base + off + 16 <= size
                     in_row = off + 16 <= (lr + 1) * sps
                     if not (inside[fetched].all() and in_row.all() and fetched[lr < rows].all()):
-                        problems.append((name, n0, wave, q))
+                        problems.append((name, b, wave, qg))
     return problems
 
 
@@ -269,7 +291,8 @@ DECODE_FORMATS = [FP4, FP8, BF8]
 def test_decode_copies_stay_inside_their_operands(fa, fb):
     shapes = [(1, 1, 512), (8, 8192, 28672), (32, 203, 640), (5, 100, 1664), (17, 64, 3200),
               (32, 8161, 2048), (3, 40, 1152), (32, 96, 8192 + 384), (2, 33, 4096 + 128),
-              (9, 40, 2560), (16, 70, 1152)]
+              (9, 40, 2560), (16, 70, 1152), (8, 28672, 4096), (4, 16417, 1664),
+              (32, 24607, 640)]
     bad = []
     for M, N, K in shapes:
         bad += [((M, N, K), prob) for prob in decode_check(fa, fb, M, N, K)]

@@ -3,7 +3,8 @@ columns of C, its four waves on four K-ranges, partial tiles added in LDS)
 against the oracle, through the C ABI: every pair of E2M1, E4M3 and E5M2
 on ragged shapes (short last periods, half E2M1 slabs, waves with empty
 K-ranges, N tails), every M from 1 to 32 (also for the 8-bit x E2M1 pairs,
-whose M <= 8 runs the wide slabs), exact integers, NaN rows,
+whose M <= 8 runs the wide slabs), more column groups than workgroups,
+exact integers, NaN rows,
 stores confined to C, the plan's shapes equal to the forced kernel bit for
 bit, repeatability, and the no-allocation entry point.
 
@@ -100,6 +101,18 @@ def test_decode_w4a8_every_m(fa):
         log("decode w4a8 every M fa=%d M=%d N=%d K=%d" % (fa, M, N, K))
         case = _case(fa, E2M1, M, N, K, seed=550 + M)
         _check(case, BF16, _run(case, BF16), what="w4a8 every M, M=%d" % M)
+
+
+@pytest.mark.parametrize("fa,fb", [(E2M1, E2M1), (E4M3, E4M3), (E4M3, E2M1)],
+                         ids=["e2m1", "e4m3", "w4a8"])
+@pytest.mark.parametrize("M,N,K", [(5, 20000, 1664), (32, 9000, 640), (8, 16417, 4224)])
+def test_decode_many_groups(fa, fb, M, N, K):
+    """More column groups than workgroups (at most 256): each workgroup's
+    copy stream runs on from one group into the next (2 to 3 groups each
+    here, the last one ragged), and every element matches the oracle."""
+    log("decode many groups fa=%d fb=%d M=%d N=%d K=%d" % (fa, fb, M, N, K))
+    case = _case(fa, fb, M, N, K, seed=M + N + K + fa)
+    _check(case, BF16, _run(case, BF16), what="many groups")
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=[NAMES[f] for f in FORMATS])
