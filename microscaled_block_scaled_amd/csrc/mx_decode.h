@@ -15,16 +15,18 @@
 //
 // A wave works alone: a private ring of slabs in LDS (a slab holds 128 or
 // 256 K-values of the staged A rows and 32 B rows, as in the tile kernel,
-// with the same XOR swizzle), filled by 16-byte buffer copies straight from
-// HBM and read back as MFMA fragments, with no workgroup barrier in the K
-// loop.  Its copies form one stream over all its groups: the first slabs of
-// the next group are in flight while a group's last slabs are multiplied
-// and its partial tiles are added, so a workgroup with several groups does
-// not refill its pipeline from empty for each.  Rows of A past M and of B
-// past N lie past the copy descriptor's num_records and are not fetched
-// (their results are never stored).  B is read once and carries the
-// nontemporal hint.  Scale bytes are loaded into registers, a few periods
-// ahead.
+// with the same XOR swizzle) and a few buffers of those rows' scale bytes,
+// one 512-K period each, filled by buffer copies straight from HBM and read
+// back as MFMA operands, with no workgroup barrier in the K loop.  Its
+// copies form
+// one stream over all its groups: the first slabs of the next group are in
+// flight while a group's last slabs are multiplied and its partial tiles
+// are added, so a workgroup with several groups does not refill its
+// pipeline from empty for each.  Every wait for memory is the one explicit
+// wait per slab: no load writes a register, so the compiler has nothing of
+// its own to wait for.  Rows of A past M and of B past N lie past the copy
+// descriptor's num_records and are not fetched (their results are never
+// stored).  B is read once and carries the nontemporal hint.
 #pragma once
 
 #include "mx_kernels.h"
@@ -52,28 +54,46 @@ __device__ __forceinline__ void wait_vm_lds()
 // (8-bit activations, 4-bit weights): 256-K slabs, so that each B row of a
 // slab is one whole 128-byte line (with 128-K slabs it is half of one,
 // and the line's other half is fetched again), A rows of 256 bytes, and
-// only the 8 A rows of two copy instructions staged, which keeps the ring
-// 6 slabs deep.  (Staging 8 A rows in the other geometries too, for a ring
-// of 8 slabs instead of 5, measured no faster on MI355X: at M = 8,
-// N = 8192, K = 28672 the same time within 1 %, and up to 18 % slower for
-// E2M1 with K <= 4096.)
+// only the 8 A rows of two copy instructions staged.  (Staging 8 A rows in
+// the other geometries too, for a deeper ring, measured no faster on
+// MI355X: at M = 8, N = 8192, K = 28672 the same time within 1 %, and up to
+// 18 % slower for E2M1 with K <= 4096.)
+//
+// Scale bytes are staged once per 512-K period, beside the ring: a period's
+// 16 bytes of each of the 32 A and 32 B rows (1 KB, four 4-byte copy
+// instructions) in one of R period buffers, issued with the period's first
+// slab.  They are read into registers when that slab is multiplied, and the
+// buffer is refilled R periods later, which the ring's lead of S - 1 slabs
+// must not reach: R * PS > S - 1, with PS slabs per period.
 template <int FA, int FB, bool WIDE = false>
 struct decode_geo {
     using SL = slab<FA, FB>;
     static_assert(!WIDE || (FB == FP4 && FA != FP4), "the wide slabs pair an 8-bit A with an E2M1 B");
     static constexpr int KS = WIDE ? 256 : SL::kvals;          // K-values per slab
+    static constexpr int PS = 512 / KS;                        // slabs per scale period
     static constexpr int RA = WIDE ? 256 : SL::template row_bytes<FA>;   // slab row bytes
     static constexpr int RB = WIDE ? 128 : SL::template row_bytes<FB>;
     static constexpr int MA = WIDE ? 8 : kDecodeRows;         // rows of A staged
-    static constexpr int NCOPY = MA * RA / 1024 + kDecodeRows * RB / 1024;   // copies per slab
     static constexpr int SLOT = MA * RA + kDecodeRows * RB;   // LDS bytes per slab
-    // ring depth: as many slabs as the LDS beside the partial-tile area
-    // holds, within the wait's count field ((S - 2) * NCOPY loads
-    // outstanding, at most 63)
-    static constexpr int S_LDS = (kDecodeLds - kDecodeRed) / (kDecodeWaves * SLOT);
-    static constexpr int S_CNT = 2 + 63 / NCOPY;
-    static constexpr int S = S_LDS < S_CNT ? S_LDS : S_CNT;
-    static constexpr int WAVE_LDS = S * SLOT;
+    static constexpr int NCOPY = SLOT / 1024;                 // copies per slab
+    static constexpr int NSC = 4;                             // scale copies per period
+    static constexpr int SCP = 1024;                          // LDS bytes per period buffer
+    static constexpr int bufs(int s) { return (s - 1) / PS + 1; }
+    // loads a slab's wait leaves outstanding: the next S - 2 positions'
+    // copies, the most scale copies among them
+    static constexpr int lead(int s) { return (s - 2) * NCOPY + NSC * ((s - 3 + PS) / PS); }
+    static constexpr int wave_lds(int s) { return s * SLOT + bufs(s) * SCP; }
+    // ring depth: the most slabs that fit in the LDS beside the partial-tile
+    // area, with a wait count that fits the vmcnt field (at most 63)
+    static constexpr int depth()
+    {
+        int s = 3;
+        while (kDecodeWaves * wave_lds(s + 1) + kDecodeRed <= kDecodeLds && lead(s + 1) <= 63) ++s;
+        return s;
+    }
+    static constexpr int S = depth();
+    static constexpr int R = bufs(S);
+    static constexpr int WAVE_LDS = wave_lds(S);
     static constexpr int SMEM = kDecodeWaves * WAVE_LDS + kDecodeRed;
 };
 
@@ -98,14 +118,15 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                   "E2M1, E4M3 and E5M2 operands");
     constexpr int KS = G::KS;                        // K-values per slab: 128 or 256
     constexpr int HS = KS / 64;                      // 64-K MFMA steps per slab: 2 or 4
-    constexpr int PS = 512 / KS;                     // slabs per scale period
+    constexpr int PS = G::PS;                        // slabs per scale period: 4 or 2
     constexpr int RA = G::RA, RB = G::RB, MA = G::MA;
     constexpr int RPCA = 1024 / RA, RPCB = 1024 / RB;             // rows per copy instruction
     constexpr int CPA = MA / RPCA, CPB = kDecodeRows / RPCB;      // copies per slab
     constexpr int NCOPY = G::NCOPY;
     static_assert(NCOPY == CPA + CPB, "copies per slab");
-    constexpr int S = G::S, SLOT = G::SLOT;
-    static_assert(S >= 3 && (S - 2) * NCOPY <= 63, "ring depth and the vmcnt field");
+    constexpr int S = G::S, SLOT = G::SLOT, R = G::R;
+    static_assert(S >= 3 && G::lead(S) <= 63, "ring depth and the vmcnt field");
+    static_assert(R * PS > S - 1, "a period buffer outlives its period's slabs");
     static_assert(G::SMEM <= kDecodeLds, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[G::SMEM];
 
@@ -113,6 +134,7 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, g = lane >> 5;
     uint8_t *const ring = smem + wave * G::WAVE_LDS;
+    uint8_t *const sring = ring + S * SLOT;          // the period buffers
     float *const red = (float *)(smem + kDecodeWaves * G::WAVE_LDS);
 
     // This workgroup's column groups: gi = 0 .. ng-1 is group
@@ -132,19 +154,6 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int64_t rowla = kbytes<FA>(klen), rowlb = kbytes<FB>(klen);
     const int sps = K / 32;                          // scale bytes per row
 
-    // Scale registers: period q's bytes in (sa, sb), and the raw loads of
-    // the next L periods in a ring of L register sets, period q in set q % L.
-    // L periods of slab copies (at least S - 1 slab positions) separate a
-    // period's loads from their use, so waiting for them never stalls the
-    // copies in flight.
-    constexpr int L = (S - 1 + PS - 1) / PS;
-    // The stream: each group takes ppq periods (its range's, rounded up to
-    // whole trips of L) of PS slab positions; position j is slab j % ppg of
-    // group j / ppg.  Positions past a group's slabs, and past its last
-    // group, copy nothing and do no MFMA.
-    const int ppq = nslab > 0 ? (nper + L - 1) / L * L : 0;
-    const int ppg = ppq * PS;
-
     // Copy geometry (the tile kernel's): lane l copies chunk l % (R/16) of row
     // l / (R/16) of a block of rows into that chunk of the row's LDS copy,
     // which holds global chunk (chunk ^ swizzle(row)).
@@ -156,15 +165,15 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // rows of at most 2^24 bytes.
     const uint32_t exta = (uint32_t)(M * rowba - kboffa);
 
-    // Copy stream position j into ring slot j % S.  Every position issues
-    // the same copies, also those with no slab (then with num_records 0:
-    // nothing is fetched), so that the count of loads in flight is the same
-    // on every path through the loop.  When both operands are E2M1 and
-    // klen % 256 == 128 the last slab is half a slab: its chunk offsets are
-    // clamped into the range (those chunks are never read).
-    auto issue = [&](int j) {
-        uint8_t *const dst = ring + (j % S) * SLOT;
-        const int gj = j / ppg, k = j - gj * ppg;
+    // Copy stream position (gj, k) -- slab position k of group gj -- into
+    // ring slot `slot`.  Every position issues the same copies, also those
+    // with no slab (then with num_records 0: nothing is fetched), so that
+    // the count of loads in flight is the same on every path through the
+    // loop.  When both operands are E2M1 and klen % 256 == 128 the last slab
+    // is half a slab: its chunk offsets are clamped into the range (those
+    // chunks are never read).
+    auto issue = [&](int gj, int k, int slot) {
+        uint8_t *const dst = ring + slot * SLOT;
         const bool live = gj < ng && k < nslab;
         const int kc = min(k, nslab - 1);
         const int n0 = group_n0(min(gj, ng - 1));
@@ -189,42 +198,28 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         }
     };
 
-    // Scale bytes of stream period qg (period qg % ppq of group qg / ppq).
-    // load_scales fetches the 16 bytes of period q (blocks kb/32 + 16q ..)
-    // of A row lr and B row n0 + lr; a short last period is fetched as the
-    // 16 bytes that end at the row's end, so that no load crosses a row.
-    // Rows past M (N) are past the descriptors' num_records: not fetched.
-    // use_scales then rotates a short period back by whole dwords and shifts
-    // each dword right by 8g bits, so that this lane group's byte of step s
-    // (block 2s + g of the period) is byte 2(s % 2) of dword s / 2.  The
-    // empty asm pins that work, and with it the wait for the loads, to where
-    // use_scales is called (else the compiler may start it right after the
-    // loads and wait for them there).
-    const rsrc_t Asr = make_rsrc(As, (uint32_t)(M * sps));
-    auto scale_at = [&](int q) { return min(kb / 32 + 16 * min(q, nper - 1), sps - 16); };
-    auto load_scales = [&](int qg, v4i &ra, v4i &rb) {
-        const int gq = qg / ppq, q = qg - gq * ppq;
-        const int n0 = group_n0(min(gq, ng - 1));
-        const rsrc_t Bsr = make_rsrc(Bs + (int64_t)n0 * sps,
-                                     (uint32_t)(min(kDecodeRows, N - n0) * sps));
-        const uint32_t off = (uint32_t)lr * (uint32_t)sps + (uint32_t)scale_at(q);
-        ra = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(Asr, off, 0, 0));
-        rb = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(Bsr, off, 0, 0));
-    };
-    auto use_scales = [&](int qg, v4i a, v4i b, v4i &sa, v4i &sb) {
-        asm volatile("" : "+v"(a), "+v"(b));
-        const int q = qg % ppq;
-        const int rot = (kb / 32 + 16 * min(q, nper - 1) - scale_at(q)) >> 2;
-        if (rot & 1) { a = v4i{a[1], a[2], a[3], a[0]}; b = v4i{b[1], b[2], b[3], b[0]}; }
-        if (rot & 2) { a = v4i{a[2], a[3], a[0], a[1]}; b = v4i{b[2], b[3], b[0], b[1]}; }
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            sa[d] = (int)((uint32_t)a[d] >> (8 * g));
-            sb[d] = (int)((uint32_t)b[d] >> (8 * g));
-        }
+    // Scale bytes of period q of group gj into period buffer `buf`: row r's
+    // 16 bytes of the period (blocks kb/32 + 16q ..) at 16r, A rows first,
+    // then B rows; lane l of copy i takes dword l % 4 of row 16i + l / 4.
+    // Each dword is checked on its own against num_records, which ends at
+    // the last real row: a short last period's dwords past the row are the
+    // next row's bytes, or not fetched, and are never read.
+    const uint32_t csoff = (uint32_t)(lane >> 2) * (uint32_t)sps + 4u * (uint32_t)(lane & 3);
+    auto issue_scales = [&](int gj, int q, int buf) {
+        uint8_t *const dst = sring + buf * G::SCP;
+        const bool live = gj < ng;
+        const int n0 = group_n0(min(gj, ng - 1));
+        const int kbs = kb / 32 + 16 * q;
+        const rsrc_t Ask = make_rsrc(As + kbs, live ? (uint32_t)(M * sps - kbs) : 0u);
+        const rsrc_t Bsk = make_rsrc(Bs + (int64_t)n0 * sps + kbs,
+                                     live ? (uint32_t)(min(kDecodeRows, N - n0) * sps - kbs) : 0u);
+        b2l_4(Ask, csoff, dst);
+        b2l_4(Ask, csoff + 16u * (uint32_t)sps, dst + 256);
+        b2l_4(Bsk, csoff, dst + 512);
+        b2l_4(Bsk, csoff + 16u * (uint32_t)sps, dst + 768);
     };
 
-    // Fragment of step p of a slab for lane row lr, from NR staged rows of R
+    // Operands of step p of a slab for lane row lr, from NR staged rows of R
     // bytes at `rows` (with NR = 8, the A rows of the wide slabs, lane row lr
     // reads row lr % 8; only rows below M <= 8 are stored): E4M3 / E5M2
     // chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g.
@@ -245,42 +240,46 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     static_assert(WIDE || (RA == (FA == FP4 && FB != FP4 ? 64 : 128) &&
                            RB == (FB == FP4 && FA != FP4 ? 64 : 128)),
                   "slab rows as the fragment reads assume");
+    // A period's scale bytes from its buffer, A row lr % MA and B row lr:
+    // step s of the period takes block 2s + g, byte 2(s % 2) + g of dword
+    // s / 2; shifted right by 8g it is byte 2(s % 2), which the MFMA's op_sel
+    // picks.  The two LDS reads are an asm block that waits for its own
+    // results: the compiler cannot tell the bytes they read from the LDS that
+    // the copies in flight are filling, and would wait for every one of those
+    // copies first.
+    auto scales = [&](const uint8_t *buf, v4i &sa, v4i &sb) {
+        const uint32_t la = lds_addr(buf + 16 * (lr % MA)), lb = lds_addr(buf + 512 + 16 * lr);
+        v4i x, y;
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(x), "=&v"(y) : "v"(la), "v"(lb) : "memory");
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            sa[d] = (int)((uint32_t)x[d] >> (8 * g));
+            sb[d] = (int)((uint32_t)y[d] >> (8 * g));
+        }
+    };
 
     v16f acc;
-    v4i sa, sb, ra[L], rb[L];
-
-    // Stream period qg = gi * ppq + q (period q of group gi), whose scales
-    // are set i = q % L: its slabs, the loads of period qg + L into set i
-    // (free since period qg's scales were made current), and at its end
-    // period qg + 1's scales made current.
-    auto period = [&](auto ic, int gi, int q) {
-        constexpr int i = decltype(ic)::value;
-        const int qg = gi * ppq + q;
-        load_scales(qg + L, ra[i], rb[i]);
-        static_for<PS>([&](auto kc) {
-            constexpr int kp = decltype(kc)::value;
-            const int k = q * PS + kp, j = qg * PS + kp;
-            // Position j is in once at most the copies of the S - 2
-            // positions issued after it are outstanding (the scale loads
-            // issued since only make the wait stricter).
-            wait_vm_lds<(S - 2) * NCOPY>();
-            issue(j + S - 1);                        // into the slot of position j - 1
-            if (k < nslab) {
-                const uint8_t *slot = ring + (j % S) * SLOT;
-                static_for<HS>([&](auto pc) {
-                    constexpr int p = decltype(pc)::value, s = kp * HS + p;
-                    if (HS == 2 || k * HS + p < nsteps) {
-                        v8i a, b;
-                        frag(std::integral_constant<int, FA>{}, std::integral_constant<int, RA>{},
-                             std::integral_constant<int, MA>{}, slot, p, a);
-                        frag(std::integral_constant<int, FB>{}, std::integral_constant<int, RB>{},
-                             std::integral_constant<int, kDecodeRows>{}, slot + MA * RA, p, b);
-                        acc = mma<FA, FB, 2 * (s & 1)>(a, b, acc, sa[s >> 1], sb[s >> 1]);
-                    }
-                });
-            }
-        });
-        use_scales(qg + 1, ra[(i + 1) % L], rb[(i + 1) % L], sa, sb);
+    v4i sa, sb;
+    // The stream: each group takes nper periods of PS slab positions;
+    // positions past a group's slabs, and past its last group, copy nothing
+    // and do no MFMA.  Its running position (uniform scalars, advanced by
+    // one at a time rather than divided out of a flat index): the next
+    // position to issue (group ig, position ik, ring slot islot, period
+    // buffer ibuf) and the ring slot and period buffer being multiplied
+    // (rslot, rbuf).
+    const int ppg = nslab > 0 ? nper * PS : 0;
+    int ig = 0, ik = 0, islot = 0, ibuf = 0, rslot = 0, rbuf = 0;
+    // FIRST: the position issued starts a period (a compile-time fact: the
+    // loop below is unrolled by the PS positions of a period).
+    auto issue_next = [&](auto fc) {
+        issue(ig, ik, islot);
+        if constexpr (decltype(fc)::value) {
+            issue_scales(ig, ik / PS, ibuf);
+            if (++ibuf == R) ibuf = 0;
+        }
+        if (++ik == ppg) { ik = 0; ++ig; }
+        if (++islot == S) islot = 0;
     };
 
     // Add the waves' partial tiles of group gi in wave order and store them.
@@ -307,27 +306,50 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
         lds_barrier();
     };
 
-    if (ppg > 0) {
-        static_for<L>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            load_scales(i, ra[i], rb[i]);
-        });
 #pragma unroll
-        for (int j = 0; j < S - 1; ++j) issue(j);
-        use_scales(0, ra[0], rb[0], sa, sb);
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (ppg > 0) {
+        static_for<S - 1>([&](auto jc) {
+            issue_next(std::bool_constant<decltype(jc)::value % PS == 0>{});
+        });
         for (int gi = 0; gi < ng; ++gi) {
+            for (int q = 0; q < nper; ++q) {
+                static_for<PS>([&](auto kc) {
+                    constexpr int kp = decltype(kc)::value;
+                    // Slab q*PS + kp is in once at most the loads of the S - 2
+                    // positions issued after it are outstanding: their slab
+                    // copies and the scale copies of the periods among them
+                    // that start (stores of C issued since only make the
+                    // wait stricter).
+                    wait_vm_lds<(S - 2) * NCOPY + G::NSC * ((kp + S - 2) / PS)>();
+                    issue_next(std::bool_constant<(kp + S - 1) % PS == 0>{});
+                    const uint8_t *const slot = ring + rslot * SLOT;
+                    if (++rslot == S) rslot = 0;
+                    if constexpr (kp == 0) {
+                        scales(sring + rbuf * G::SCP, sa, sb);
+                        if (++rbuf == R) rbuf = 0;
+                    }
+                    const int k = q * PS + kp;
+                    if (k < nslab) {
+                        static_for<HS>([&](auto pc) {
+                            constexpr int p = decltype(pc)::value, s = kp * HS + p;
+                            if (HS == 2 || k * HS + p < nsteps) {
+                                v8i a, b;
+                                frag(std::integral_constant<int, FA>{}, std::integral_constant<int, RA>{},
+                                     std::integral_constant<int, MA>{}, slot, p, a);
+                                frag(std::integral_constant<int, FB>{}, std::integral_constant<int, RB>{},
+                                     std::integral_constant<int, kDecodeRows>{}, slot + MA * RA, p, b);
+                                acc = mma<FA, FB, 2 * (s & 1)>(a, b, acc, sa[s >> 1], sb[s >> 1]);
+                            }
+                        });
+                    }
+                });
+            }
+            add_and_store(gi);
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-            // L periods per trip, so that the register sets keep their
-            // roles without a register move (a move of a load's result
-            // waits for the load).
-            for (int q = 0; q < ppq; q += L)
-                static_for<L>([&](auto ic) { period(ic, gi, q + decltype(ic)::value); });
-            add_and_store(gi);
         }
     } else {                                         // an empty K-range: zero partial tiles
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
         for (int gi = 0; gi < ng; ++gi) add_and_store(gi);
     }
     wait_vm0();                                      // the copies past the last group

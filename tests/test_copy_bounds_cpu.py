@@ -160,11 +160,12 @@ def test_model_reports_unclamped_fp6_padding_lanes():
 # --------------------------------------------------------------------------
 # The decode kernel (csrc/mx_decode.h): a grid of at most 256 workgroups,
 # workgroup b taking column groups b, b + grid, ...; 4 waves per workgroup,
-# each a K-range of whole 512-K periods and a private ring of S slabs of the
-# staged A rows and 32 B rows; each wave's copies form one stream of slab
-# positions over all its groups (positions past a group's slabs, or past its
-# last group, copy with num_records 0), and 16-byte scale loads per lane
-# row, L periods ahead, never crossing a row.
+# each a K-range of whole 512-K periods, a private ring of S slabs of the
+# staged A rows and 32 B rows, and R period buffers of those rows' scale
+# bytes; each wave's copies form one stream of slab positions over all its
+# groups, nper * PS positions per group (positions past a group's slabs, or
+# past its last group, copy with num_records 0), with four 4-byte scale
+# copies at each period's first position.
 DECODE_LDS, DECODE_ROWS, DECODE_WAVES, DECODE_CUS = 163840, 32, 4, 256
 DECODE_RED = DECODE_WAVES * DECODE_ROWS * DECODE_ROWS * 4
 
@@ -176,14 +177,22 @@ def decode_wide(fa, fb, M):
 
 def decode_geo(fa, fb, wide=False):
     """(K-values per slab, A and B slab row bytes, rows of A staged, copies
-    per slab, ring depth) of the decode kernel."""
+    per slab, ring depth, period buffers) of the decode kernel: the deepest
+    ring whose slabs and period buffers fit beside the partial tiles, with
+    a wait count (the next S - 2 positions' loads) within 63."""
     kv = 256 if wide else kvals(fa, fb)
     RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
     MA = 8 if wide else DECODE_ROWS
-    ncopy = MA * RA // 1024 + DECODE_ROWS * RB // 1024
     slot = MA * RA + DECODE_ROWS * RB
-    S = min((DECODE_LDS - DECODE_RED) // (DECODE_WAVES * slot), 2 + 63 // ncopy)
-    return kv, RA, RB, MA, ncopy, S
+    ncopy = slot // 1024
+    PS = 512 // kv
+    bufs = lambda s: (s - 1) // PS + 1
+    lead = lambda s: (s - 2) * ncopy + 4 * ((s - 3 + PS) // PS)
+    S = 3
+    while (DECODE_WAVES * ((S + 1) * slot + bufs(S + 1) * 1024) + DECODE_RED <= DECODE_LDS
+           and lead(S + 1) <= 63):
+        S += 1
+    return kv, RA, RB, MA, ncopy, S, bufs(S)
 
 
 def decode_operand(R, rowb, rows_real, cmax, records, size, base, live, need_bytes,
@@ -205,16 +214,32 @@ def decode_operand(R, rowb, rows_real, cmax, records, size, base, live, need_byt
     return ok, bool(fetched[needed].all())
 
 
-def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
+def decode_scales(sps, rows_real, kbs, records, size, base, live, nbytes):
+    """One period's scale copies of one operand: lane l of copy i takes
+    dword l % 4 of row 16i + l // 4, from the period's first scale byte
+    kbs.  Returns (every fetched dword inside the operand's scale array,
+    every dword the MFMAs read fetched)."""
+    i, lane = np.meshgrid(np.arange(2), np.arange(64), indexing="ij")
+    row, w = 16 * i + lane // 4, lane % 4
+    off = row * sps + 4 * w
+    fetched = off + 4 <= records
+    inside = (base + kbs + off >= 0) & (base + kbs + off + 4 <= size)
+    ok = bool(inside[fetched].all())
+    if not live:
+        return ok and not fetched.any(), True
+    needed = (row < rows_real) & (4 * w < nbytes)
+    return ok, bool(fetched[needed].all())
+
+
+def decode_check(fa, fb, M, N, K, scale_records_from_period=True, idle_records=True):
     """Problems of the decode kernel's loads for one problem, for the first
-    and the last workgroup; the two flags turn off the scale window's clamp
-    into the row and the zero num_records of copies with no slab (for the
-    model's own tests)."""
-    kv, RA, RB, MA, ncopy, S = decode_geo(fa, fb, decode_wide(fa, fb, M))
+    and the last workgroup; the two flags turn off the scale copies' extent
+    counted from the period's first scale byte and the zero num_records of
+    copies with no slab (for the model's own tests)."""
+    kv, RA, RB, MA, ncopy, S, R = decode_geo(fa, fb, decode_wide(fa, fb, M))
     PS = 512 // kv
-    L = -(-(S - 1) // PS)                            # periods of scale loads in flight
-    assert S >= 3 and (S - 2) * ncopy <= 63
-    assert DECODE_WAVES * S * (MA * RA + DECODE_ROWS * RB) + DECODE_RED <= DECODE_LDS
+    assert S >= 3 and (S - 2) * ncopy + 4 * ((S - 3 + PS) // PS) <= 63 and R * PS > S - 1
+    assert DECODE_WAVES * (S * (MA * RA + DECODE_ROWS * RB) + R * 1024) + DECODE_RED <= DECODE_LDS
     rowba, rowbb = kbytes(fa, K), kbytes(fb, K)
     sps = K // 32
     per_w = -(-(K // 128) // (4 * DECODE_WAVES))
@@ -231,8 +256,7 @@ def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
             if nslab == 0:
                 continue
             nper = -(-klen // 512)
-            ppq = -(-nper // L) * L                     # periods per group
-            ppg = ppq * PS                              # slab positions per group
+            ppg = nper * PS                             # slab positions per group
             kboffa, kboffb = kbytes(fa, kb), kbytes(fb, kb)
             rowla, rowlb = kbytes(fa, klen), kbytes(fb, klen)
             exta = M * rowba - kboffa
@@ -259,28 +283,20 @@ def decode_check(fa, fb, M, N, K, clamp_scales=True, idle_records=True):
                     ok, need = decode_operand(*args)
                     if not ok or not need:
                         problems.append((name, b, wave, j, ok, need))
-            # scale loads: stream periods 0 .. ng * ppq + L - 1
-            lr = np.arange(DECODE_ROWS)
-            for qg in range(ng * ppq + L):
-                gq, q = divmod(qg, ppq)
-                if 0 < gq < ng - 1 and 1 < q < nper - 1:
+                if k % PS:
                     continue
-                qc = min(q, nper - 1)
-                blk = kb // 32 + 16 * qc
-                at = min(blk, sps - 16) if clamp_scales else blk
-                nblk = min(16, klen // 32 - 16 * qc)
-                if at < 0 or not (at <= blk and blk + nblk <= at + 16) or (blk - at) % 4:
-                    problems.append(("scale window", b, wave, qg))
-                n0 = group_n0(gq)
-                rows_b = min(DECODE_ROWS, N - n0)
-                off = lr * sps + at
+                q = k // PS                               # the period this position starts
+                slive = gj < ng
+                kbs = kb // 32 + 16 * q
+                nbytes = min(512, klen - 512 * q) // 32   # scale bytes the period's steps read
                 for name, rows, base, size in (("As", M, 0, M * sps),
                                                ("Bs", rows_b, n0 * sps, N * sps)):
-                    fetched = off + 16 <= rows * sps
-                    inside = base + off + 16 <= size
-                    in_row = off + 16 <= (lr + 1) * sps
-                    if not (inside[fetched].all() and in_row.all() and fetched[lr < rows].all()):
-                        problems.append((name, b, wave, qg))
+                    rec = rows * sps - (kbs if scale_records_from_period else 0)
+                    ok, need = decode_scales(sps, rows, kbs,
+                                             rec if slive or not idle_records else 0,
+                                             size, base, slive, nbytes)
+                    if not ok or not need:
+                        problems.append((name, b, wave, j, ok, need))
     return problems
 
 
@@ -300,12 +316,12 @@ def test_decode_copies_stay_inside_their_operands(fa, fb):
 
 
 def test_decode_model_reports_planted_mistakes():
-    """The model itself: a short last period loaded from its own start (not
-    16 bytes before the row's end) reads across into the next row, and past
-    the last row of the scale array; copies past the range with a live
-    num_records fetch what the kernel never reads."""
+    """The model itself: scale copies whose extent is not counted from the
+    period's first scale byte read past the scale array (the dwords past
+    the last row's end in a short last period); copies past the range with
+    a live num_records fetch what the kernel never reads."""
     assert not decode_check(FP4, FP4, 5, 100, 1664)
     assert any(p[0] in ("As", "Bs") for p in decode_check(FP4, FP4, 5, 100, 1664,
-                                                          clamp_scales=False))
+                                                          scale_records_from_period=False))
     assert any(p[0] in ("A", "B") for p in decode_check(FP8, FP8, 8, 64, 4096 + 128,
                                                         idle_records=False))
