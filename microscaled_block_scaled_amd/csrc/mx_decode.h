@@ -48,6 +48,19 @@ __device__ __forceinline__ void wait_vm_lds()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
+// A buffer copy of 4 bytes per lane (b2l_16's form for dwords): lane l
+// writes lds + l * 4.
+__device__ __forceinline__ void b2l_4(rsrc_t src, uint32_t off, void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)lds, 4, off, 0, 0, 0);
+}
+
+// The 32-bit LDS address of a generic pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // Slab geometry of the decode kernel for formats (FA, FB): the tile
 // kernel's slabs (128 K-values, 256 when both operands are E2M1), 32 rows
 // of A and 32 of B.  WIDE is for an E4M3 / E5M2 A with an E2M1 B and M <= 8

@@ -188,16 +188,6 @@ __device__ __forceinline__ void b2l_16(rsrc_t src, uint32_t off, void *lds)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)lds, 16, off, 0, 0, AUX);
 }
-// The 32-bit LDS address of a generic pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-// The same copy of 4 bytes per lane: lane l writes lds + l * 4.
-__device__ __forceinline__ void b2l_4(rsrc_t src, uint32_t off, void *lds)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)lds, 4, off, 0, 0, 0);
-}
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's memory loads are outstanding (loads
 // retire in issue order).

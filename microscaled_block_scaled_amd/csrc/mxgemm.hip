@@ -111,27 +111,26 @@ void fill_decode_plan(int64_t N, mx_plan_t *p)
 // decode kernel runs at most one workgroup per CU (it takes all of a CU's
 // LDS), each streaming every 256th column group of 32 columns.  The
 // thresholds were fitted to cold per-call times of both kernels on MI355X
-// over 440 problems (M = 1 .. 32, N = 2048 .. 32768, K = 512 .. 28672,
-// E2M1 and E4M3): with them the plan reaches 0.995 of the faster kernel's
-// speed (geometric mean; worst 0.80), against 0.81 for the tiled kernel
-// alone and 0.978 for the decode kernel alone.  The decode kernel loses
-//   * with more than 4 column groups per workgroup, or more than 2 at
-//     K < 1024, or more than 3 at K <= 1024 (its per-group work is short);
-//   * at K >= 16384 with fewer than 160 column groups, where the tiled
-//     kernel's K split spreads B over more CUs (N = 4096, K = 28672:
-//     0.76 - 1.0x);
+// over 576 problems (M = 1 .. 32, N = 1024 .. 57344, K = 512 .. 28672,
+// E2M1 and E4M3): with them the plan reaches 0.996 of the faster kernel's
+// speed (geometric mean; worst 0.84), against 0.79 for the tiled kernel
+// alone and 0.976 for the decode kernel alone.  The decode kernel loses
+//   * at K < 1024 with more than 3 column groups per workgroup (N > 24576):
+//     its per-group work is short (0.9 - 0.95x);
+//   * at K >= 16384 with fewer than 160 column groups (N <= 5088), where
+//     the tiled kernel's K split spreads B over more CUs (N = 4096,
+//     K = 28672: 0.65 - 0.99x);
 //   * for M > 16 at K > 14336, or with more than one group per workgroup
-//     at K = 14336: every workgroup reads all of A (M = 32, K = 28672:
-//     0.78 - 0.93x).
-// M = 8, N = 8192, K = 28672: 1.07x E4M3, 1.17x E2M1; N = 20480,
-// K = 4096: 1.2 - 1.4x.
+//     at K = 14336: every workgroup reads all of A (M = 32, N = 57344,
+//     K = 28672: 0.85 - 0.95x).
+// M = 8, N = 8192, K = 28672: 1.09x E4M3, 1.12x E2M1; M = 8, N = 57344,
+// K = 8192: 1.26x, 1.30x.
 bool decode_preferred(int64_t M, int64_t N, int64_t K)
 {
     const int64_t wgs = cdiv(N, MX_DECODE_TILE);    // column groups
-    if (wgs > 4 * kCUs || (wgs > 2 * kCUs && K < 1024)) return false;
-    if (K <= 1024 && wgs > 3 * kCUs) return false;
+    if (K < 1024 && wgs > 3 * kCUs) return false;
     if (K >= 16384 && wgs < kCUs * 5 / 8) return false;
-    if (M > 16 && (K > 14336 || (K >= 14336 && wgs > kCUs))) return false;
+    if (M > 16 && K >= 14336 && (K > 14336 || wgs > kCUs)) return false;
     return true;
 }
 

@@ -144,7 +144,7 @@ def test_plan_shapes():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 28672), (32, 100, 16384), (64, 8192, 28672),
-                                   (33, 28672, 4096), (8, 28672, 1024)])
+                                   (33, 28672, 4096), (8, 28672, 512)])
 def test_plan_small_m_uses_short_tile(M, N, K):
     for fmt in (mxg.FMT_E2M1, mxg.FMT_E4M3):
         p = mxg.plan(fmt, M, N, K)
@@ -164,7 +164,9 @@ def test_plan_small_m_uses_short_tile(M, N, K):
                                    (16, 14336, 4096), (5, 8161, 2048), (8, 6144, 28672),
                                    (32, 100, 512), (1, 16384, 8192), (8, 28672, 28672),
                                    (16, 3072, 14336), (1, 12288, 1024), (8, 28672, 4096),
-                                   (16, 8192, 28672), (1, 32768, 2048), (32, 20480, 8192)])
+                                   (16, 8192, 28672), (1, 32768, 2048), (32, 20480, 8192),
+                                   (8, 57344, 8192), (1, 40960, 28672), (1, 24608, 1024),
+                                   (1, 16385, 896), (32, 57344, 4096)])
 def test_plan_decode(M, N, K):
     """M <= 32 and K >= 512 within the measured limits (rounds of 256
     decode workgroups, K, M): the decode variant, for each of E2M1, E4M3
@@ -182,13 +184,13 @@ def test_plan_decode(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(33, 8192, 28672), (8, 4096, 28672), (17, 8192, 28672),
-                                   (1, 16385, 896), (8, 8192, 384), (1, 32769, 28672),
-                                   (24, 12288, 14336), (1, 24608, 1024)])
+                                   (1, 24577, 896), (8, 8192, 384), (32, 57344, 28672),
+                                   (24, 12288, 14336), (1, 32768, 512), (1, 5088, 16384)])
 def test_plan_decode_not_taken(M, N, K):
-    """M > 32; K >= 16384 with fewer than 160 column groups (N = 4096); more
-    than 4 column groups per workgroup (N > 32768), more than 2 at K < 1024
-    or more than 3 at K <= 1024; M > 16 with K > 14336, or with more than
-    one group per workgroup at K = 14336; K < 512: the tiled kernel."""
+    """M > 32; K >= 16384 with fewer than 160 column groups (N <= 5088);
+    more than 3 column groups per workgroup at K < 1024 (N > 24576); M > 16
+    with K > 14336, or with more than one group per workgroup at
+    K = 14336; K < 512: the tiled kernel."""
     assert mxg.plan(mxg.FMT_E4M3, M, N, K)["variant"] == mxg.VARIANT_TILE
 
 
