@@ -136,11 +136,12 @@ const char *mx_strerror(int code);
  *   (workspace_bytes of the stream's workspace, see "Thread safety" above;
  *   mx_gemm_noalloc uses a fixed scratch instead).
  * MX_VARIANT_DECODE: the decode kernel, for M <= MX_DECODE_TILE rows with
- *   both operands E2M1, E4M3 or E5M2 and K >= 512.  Each workgroup computes
- *   MX_DECODE_TILE columns of C for all M rows; its four waves take four
- *   K-ranges of whole 512-K periods and add their partial sums in LDS in a
- *   fixed order.  tile_m = tile_n = MX_DECODE_TILE, split_k = 1, no
- *   workspace.  The plan takes it where it streams B faster than the tiled
+ *   both operands E2M1, E4M3 or E5M2 and K >= 512.  C is cut into groups
+ *   of MX_DECODE_TILE columns (all M rows); workgroups = min(groups, 256),
+ *   at most one per CU, and workgroup b computes groups b, b + workgroups,
+ *   ...; its four waves take four K-ranges of whole 512-K periods and add
+ *   their partial sums in LDS in a fixed order.  tile_m = tile_n =
+ *   MX_DECODE_TILE, split_k = 1, no workspace.  The plan takes it where it streams B faster than the tiled
  *   kernel; mx_gemm_tile and mx_gemm_mixed run it when asked for the tile
  *   (MX_DECODE_TILE, MX_DECODE_TILE).
  */
