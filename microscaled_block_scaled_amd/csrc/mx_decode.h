@@ -63,14 +63,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 
 // Slab geometry of the decode kernel for formats (FA, FB): the tile
 // kernel's slabs (128 K-values, 256 when both operands are E2M1), 32 rows
-// of A and 32 of B.  WIDE is for an E4M3 / E5M2 A with an E2M1 B and M <= 8
-// (8-bit activations, 4-bit weights): 256-K slabs, so that each B row of a
-// slab is one whole 128-byte line (with 128-K slabs it is half of one,
-// and the line's other half is fetched again), A rows of 256 bytes, and
-// only the 8 A rows of two copy instructions staged.  (Staging 8 A rows in
-// the other geometries too, for a deeper ring, measured no faster on
-// MI355X: at M = 8, N = 8192, K = 28672 the same time within 1 %, and up to
-// 18 % slower for E2M1 with K <= 4096.)
+// of A and 32 of B.  WA = 8 or 16 is for an E4M3 / E5M2 A with an E2M1 B
+// and M <= WA (8-bit activations, 4-bit weights): 256-K slabs, so that each
+// B row of a slab is one whole 128-byte line (with 128-K slabs it is half
+// of one, and the line's other half is fetched again), A rows of 256
+// bytes, and only WA A rows staged (2 or 4 copy instructions; 32 such rows
+// would leave room for fewer than 3 slabs).  (Staging 8 A rows in the
+// other geometries too, for a deeper ring, measured no faster on MI355X: at
+// M = 8, N = 8192, K = 28672 the same time within 1 %, and up to 18 %
+// slower for E2M1 with K <= 4096.)
 //
 // Scale bytes are staged once per 512-K period, beside the ring: a period's
 // 16 bytes of each of the 32 A and 32 B rows (1 KB, four 4-byte copy
@@ -78,15 +79,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // slab.  They are read into registers when that slab is multiplied, and the
 // buffer is refilled R periods later, which the ring's lead of S - 1 slabs
 // must not reach: R * PS > S - 1, with PS slabs per period.
-template <int FA, int FB, bool WIDE = false>
+template <int FA, int FB, int WA = 0>
 struct decode_geo {
+    static constexpr bool WIDE = WA != 0;
     using SL = slab<FA, FB>;
     static_assert(!WIDE || (FB == FP4 && FA != FP4), "the wide slabs pair an 8-bit A with an E2M1 B");
+    static_assert(WA == 0 || WA == 8 || WA == 16, "8 or 16 staged A rows");
     static constexpr int KS = WIDE ? 256 : SL::kvals;          // K-values per slab
     static constexpr int PS = 512 / KS;                        // slabs per scale period
     static constexpr int RA = WIDE ? 256 : SL::template row_bytes<FA>;   // slab row bytes
     static constexpr int RB = WIDE ? 128 : SL::template row_bytes<FB>;
-    static constexpr int MA = WIDE ? 8 : kDecodeRows;         // rows of A staged
+    static constexpr int MA = WIDE ? WA : kDecodeRows;        // rows of A staged
     static constexpr int SLOT = MA * RA + kDecodeRows * RB;   // LDS bytes per slab
     static constexpr int NCOPY = SLOT / 1024;                 // copies per slab
     static constexpr int NSC = 4;                             // scale copies per period
@@ -119,14 +122,15 @@ template <int R> __device__ __forceinline__ int decode_swz(int r)
     return R == 256 ? (r & 15) : swz_row<R>(r);
 }
 
-template <int FA, int FB, int OUT, bool WIDE>
+template <int FA, int FB, int OUT, int WA>
 __global__ void __launch_bounds__(kDecodeWaves * 64)
 decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
               const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs, void *__restrict__ C,
               int M, int N, int K)
 {
     using SL = slab<FA, FB>;
-    using G = decode_geo<FA, FB, WIDE>;
+    using G = decode_geo<FA, FB, WA>;
+    constexpr bool WIDE = G::WIDE;
     static_assert(SL::scaled && !is_fp6<FA>::value && !is_fp6<FB>::value,
                   "E2M1, E4M3 and E5M2 operands");
     constexpr int KS = G::KS;                        // K-values per slab: 128 or 256
@@ -233,8 +237,8 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     };
 
     // Operands of step p of a slab for lane row lr, from NR staged rows of R
-    // bytes at `rows` (with NR = 8, the A rows of the wide slabs, lane row lr
-    // reads row lr % 8; only rows below M <= 8 are stored): E4M3 / E5M2
+    // bytes at `rows` (with NR = 8 or 16, the A rows of the wide slabs, lane
+    // row lr reads row lr % NR; only rows below M <= NR are stored): E4M3 / E5M2
     // chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g.
     auto frag = [&](auto fc, auto rc, auto nc, const uint8_t *rows, int p, v8i &v) {
         constexpr int F = decltype(fc)::value, R = decltype(rc)::value, NR = decltype(nc)::value;

@@ -171,18 +171,21 @@ DECODE_RED = DECODE_WAVES * DECODE_ROWS * DECODE_ROWS * 4
 
 
 def decode_wide(fa, fb, M):
-    """The wide slabs: an 8-bit A with an E2M1 B and M <= 8."""
-    return fb == FP4 and fa != FP4 and M <= 8
+    """The A rows the wide slabs stage (0: not wide): an 8-bit A with an
+    E2M1 B, 8 rows for M <= 8 and 16 for M <= 16."""
+    if fb != FP4 or fa == FP4 or M > 16:
+        return 0
+    return 8 if M <= 8 else 16
 
 
-def decode_geo(fa, fb, wide=False):
+def decode_geo(fa, fb, wide=0):
     """(K-values per slab, A and B slab row bytes, rows of A staged, copies
     per slab, ring depth, period buffers) of the decode kernel: the deepest
     ring whose slabs and period buffers fit beside the partial tiles, with
     a wait count (the next S - 2 positions' loads) within 63."""
     kv = 256 if wide else kvals(fa, fb)
     RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
-    MA = 8 if wide else DECODE_ROWS
+    MA = wide if wide else DECODE_ROWS
     slot = MA * RA + DECODE_ROWS * RB
     ncopy = slot // 1024
     PS = 512 // kv
@@ -308,7 +311,7 @@ def test_decode_copies_stay_inside_their_operands(fa, fb):
     shapes = [(1, 1, 512), (8, 8192, 28672), (32, 203, 640), (5, 100, 1664), (17, 64, 3200),
               (32, 8161, 2048), (3, 40, 1152), (32, 96, 8192 + 384), (2, 33, 4096 + 128),
               (9, 40, 2560), (16, 70, 1152), (8, 28672, 4096), (4, 16417, 1664),
-              (32, 24607, 640)]
+              (32, 24607, 640), (12, 8200, 3200), (16, 16417, 4224)]
     bad = []
     for M, N, K in shapes:
         bad += [((M, N, K), prob) for prob in decode_check(fa, fb, M, N, K)]

@@ -3,7 +3,7 @@ columns of C, its four waves on four K-ranges, partial tiles added in LDS)
 against the oracle, through the C ABI: every pair of E2M1, E4M3 and E5M2
 on ragged shapes (short last periods, half E2M1 slabs, waves with empty
 K-ranges, N tails), every M from 1 to 32 (also for the 8-bit x E2M1 pairs,
-whose M <= 8 runs the wide slabs), more column groups than workgroups,
+whose M <= 16 runs the wide slabs), more column groups than workgroups,
 exact integers, NaN rows,
 stores confined to C, the plan's shapes equal to the forced kernel bit for
 bit, repeatability, and the no-allocation entry point.
@@ -93,8 +93,8 @@ def test_decode_every_m(fmt):
 
 @pytest.mark.parametrize("fa", [E4M3, E5M2], ids=["e4m3", "e5m2"])
 def test_decode_w4a8_every_m(fa):
-    """An 8-bit A with an E2M1 B, every row count 1 .. 32: M <= 8 runs the
-    wide slabs (256 K-values, 8 A rows staged), larger M the 128-K slabs.
+    """An 8-bit A with an E2M1 B, every row count 1 .. 32: M <= 16 runs the
+    wide slabs (256 K-values, 8 or 16 A rows staged), larger M the 128-K slabs.
     K = 3200: a short last period and a half wide slab in the last wave."""
     N, K = 140, 3200
     for M in range(1, 33):
@@ -105,7 +105,8 @@ def test_decode_w4a8_every_m(fa):
 
 @pytest.mark.parametrize("fa,fb", [(E2M1, E2M1), (E4M3, E4M3), (E4M3, E2M1)],
                          ids=["e2m1", "e4m3", "w4a8"])
-@pytest.mark.parametrize("M,N,K", [(5, 20000, 1664), (32, 9000, 640), (8, 16417, 4224)])
+@pytest.mark.parametrize("M,N,K", [(5, 20000, 1664), (32, 9000, 640), (8, 16417, 4224),
+                                   (13, 16417, 3200)])
 def test_decode_many_groups(fa, fb, M, N, K):
     """More column groups than workgroups (at most 256): each workgroup's
     copy stream runs on from one group into the next (2 to 3 groups each
