@@ -1,8 +1,8 @@
 """GPU parity at the size limits of the C ABI: the largest K (MX_MAX_K = 2^24)
 with 256-row tiles, where a lane's 32-bit copy offset (row within the tile
 times the row pitch) comes within 2^24 of 2^32, for MXFP8 (K bytes per row)
-and MXFP4; and the largest dense-BF16 K (2^23, 2K bytes per row).  Checked
-on sampled rows of both row tiles against the oracle."""
+and MXFP4; the same K on the decode kernel; and the largest dense-BF16 K
+(2^23, 2K bytes per row).  Checked on sampled rows against the oracle."""
 import numpy as np
 import pytest
 
@@ -63,3 +63,26 @@ def test_largest_k_bf16():
     got = host64(C)[rows]
     log("  max |diff| %g" % np.max(np.abs(got - want)))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E2M1], ids=["e4m3", "e2m1"])
+def test_largest_k_decode(fmt):
+    """The decode kernel (forced tile 32 x 32) at the largest K: 32 rows of
+    A, so its copy extents reach 32 rows of 2^24 (E4M3) bytes, each wave's
+    K-range is 2^22 values long, and N = 40 gives a ragged second column
+    group; sampled rows against the oracle."""
+    import torch
+    M, N, K = 32, 40, mxg.MAX_K
+    log("largest K decode fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
+    rng = np.random.default_rng(4048 + fmt)
+    A, B = _codes(rng, fmt, M, K), _codes(rng, fmt, N, K)
+    As = rng.integers(120, 135, size=(M, K // 32), dtype=np.uint8)
+    Bs = rng.integers(120, 135, size=(N, K // 32), dtype=np.uint8)
+    d = [torch.from_numpy(x).cuda() for x in (A, As, B, Bs)]
+    C = mxg.mx_gemm(d[0], d[1], d[2], d[3], fmt, out_dtype=torch.float32,
+                    tile=(mxg.DECODE_TILE, mxg.DECODE_TILE))
+    torch.cuda.synchronize()
+    rows = [0, 17, 31]
+    Cref, T, E = oracle.gemm(fmt, A, As, B, Bs, K, rows=rows, group_bound=True)
+    r = acceptance(host64(C)[rows], Cref, T, False, E, what="largest K decode")
+    assert r["n_bad"] == 0, r
