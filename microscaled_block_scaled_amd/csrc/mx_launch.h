@@ -88,8 +88,9 @@ bool launch_fp6_pair(int fmt_a, int fmt_b, const mx_plan_t &p, int out_dtype, co
                      int64_t N, int64_t K, float *W, hipStream_t stream);
 
 // The decode kernel's problems: both operands E2M1, E4M3 or E5M2, M <= 32
-// rows, and K >= 512 (a whole scale period per row, which the kernel's
-// scale loads read).
+// rows, and K >= 512 and a multiple of 128 (whole slabs of the 8-bit
+// operands; the shapes it is tested and timed on -- shorter K is a GEMM
+// the tiled kernel runs in a few microseconds).
 inline bool decode_fits(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K)
 {
     auto mx8 = [](int f) { return f == MX_FMT_E2M1 || f == MX_FMT_E4M3 || f == MX_FMT_E5M2; };
