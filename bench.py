@@ -499,12 +499,16 @@ def bench_grouped(steps, warmup, fmt):
 
 
 # Other element formats, BF16 out: mixed "W4A8" (A E4M3 activations, B E2M1
-# weights) on the fused-QKV shape and the 70B down projection at batch 8;
+# weights) on the fused-QKV shape and the 70B down and gate-up projections
+# at batch 8;
 # E5M2 for both operands, E4M3 x E5M2, and the two FP6 formats on the
 # fused-QKV shape.
 MIXED_WORKLOADS = {
     "w4a8_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
     "w4a8_llama70b_down_m8": (8, 8192, 28672, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
+    # the gate and up projections of the same layer (N = 2 x 28672, K = 8192):
+    # 1792 column groups of the decode kernel, 7 per workgroup
+    "w4a8_llama70b_gateup_m8": (8, 57344, 8192, mxinputs.FMT_E4M3, mxinputs.FMT_E2M1),
     "mxfp8_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E5M2, mxinputs.FMT_E5M2),
     "mxfp8_e4m3_x_e5m2_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E4M3, mxinputs.FMT_E5M2),
     "mxfp6_e2m3_llama8b_qkv": (2048, 6144, 4096, mxinputs.FMT_E2M3, mxinputs.FMT_E2M3),
