@@ -18,11 +18,10 @@
 // with the same XOR swizzle) and a few buffers of those rows' scale bytes,
 // one 512-K period each, filled by buffer copies straight from HBM and read
 // back as MFMA operands, with no workgroup barrier in the K loop.  Its
-// copies form
-// one stream over all its groups: the first slabs of the next group are in
-// flight while a group's last slabs are multiplied and its partial tiles
-// are added, so a workgroup with several groups does not refill its
-// pipeline from empty for each.  Every wait for memory is the one explicit
+// copies form one stream over all its groups: the first slabs of the next
+// group are in flight while a group's last slabs are multiplied and its
+// partial tiles are added, so a workgroup with several groups does not
+// refill its pipeline from empty for each.  Every wait for memory is the one explicit
 // wait per slab: no load writes a register, so the compiler has nothing of
 // its own to wait for.  Rows of A past M and of B past N lie past the copy
 // descriptor's num_records and are not fetched (their results are never
@@ -287,11 +286,13 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     // (rslot, rbuf).
     const int ppg = nslab > 0 ? nper * PS : 0;
     int ig = 0, ik = 0, islot = 0, ibuf = 0, rslot = 0, rbuf = 0;
-    // FIRST: the position issued starts a period (a compile-time fact: the
-    // loop below is unrolled by the PS positions of a period).
-    auto issue_next = [&](auto fc) {
+    // Issue the next position; `first` (a std::bool_constant) says whether it
+    // starts a period and so also copies that period's scale bytes, which is
+    // known at compile time: the loop below is unrolled by the PS positions
+    // of a period.
+    auto issue_next = [&](auto first) {
         issue(ig, ik, islot);
-        if constexpr (decltype(fc)::value) {
+        if constexpr (decltype(first)::value) {
             issue_scales(ig, ik / PS, ibuf);
             if (++ibuf == R) ibuf = 0;
         }
