@@ -207,6 +207,29 @@ def test_decode_plan_is_the_decode_kernel(fmt):
     _check(sub, BF16, first[:, torch.from_numpy(cols).cuda()], what="plan columns")
 
 
+@pytest.mark.parametrize("fa,fb", [(E4M3, E2M1), (E2M1, E2M1)], ids=["w4a8", "e2m1"])
+def test_decode_gateup_full_size(fa, fb):
+    """The 70B gate and up projections at batch 8 (8 x 57344 x 8192): 1792
+    column groups, 7 per workgroup, so every wave's copy stream runs through
+    seven groups.  The plan runs the decode kernel; the columns of the first,
+    second and last group of the first and last workgroup, and 200 spread
+    over the rest, match the oracle; a second call is bit-identical."""
+    import torch
+    M, N, K = 8, 57344, 8192
+    p = mxg.plan(fa, M, N, K)
+    assert p["variant"] == mxg.VARIANT_DECODE and p["workgroups"] == 256, p
+    case = _case(fa, fb, M, N, K, seed=1200 + fa)
+    d = _dev(case)
+    log("decode gate-up fa=%d fb=%d M=%d N=%d K=%d plan=%s" % (fa, fb, M, N, K, p))
+    first = _run(case, BF16, tile=None, d=d)
+    assert torch.equal(first, _run(case, BF16, tile=None, d=d))
+    groups = [0, 256, 1536, 255, 511, 1791]
+    cols = np.unique(np.r_[np.concatenate([np.arange(32 * g, 32 * g + 32) for g in groups]),
+                           np.linspace(0, N - 1, 200).astype(int)])
+    sub = dict(case, B=case["B"][cols], B_scale=case["B_scale"][cols], N=len(cols))
+    _check(sub, BF16, first[:, torch.from_numpy(cols).cuda()], what="gate-up columns")
+
+
 def test_decode_noalloc_entry_matches():
     """mx_gemm_noalloc on a decode-planned shape (no scratch needed) equals
     mx_gemm bit for bit, twice, the second call smaller."""
