@@ -459,7 +459,8 @@ extern "C" int mx_quantize(int fmt, int in_dtype, int64_t rows, int64_t K,
     const int rc = device_ready(&dev);
     if (rc != MX_OK) return rc;
     const int64_t nblocks = rows * (K / 32);
-    const int lpb = in_dtype == MX_IN_FP32 ? 8 : 4;            // lanes per block
+    const bool fp6 = fmt == MX_FMT_E2M3 || fmt == MX_FMT_E3M2;
+    const int lpb = fp6 ? 2 : in_dtype == MX_IN_FP32 ? 8 : 4;  // lanes per block
     const int64_t per_wg = 256 / lpb;                          // blocks per pass
     const unsigned grid = (unsigned)std::min<int64_t>(cdiv(nblocks, per_wg), 8 * kCUs);
     hipStream_t s = (hipStream_t)stream;
