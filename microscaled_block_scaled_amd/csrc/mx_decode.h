@@ -35,8 +35,11 @@ namespace mx {
 constexpr int kDecodeWaves = 4;      // waves per workgroup, one K-range each
 constexpr int kDecodeRows = 32;      // columns of C per workgroup, and the most rows of A
 constexpr int kDecodeLds = 163840;   // LDS per workgroup: all of a CU's 160 KB
-// LDS for adding the waves' partial tiles: a 32 x 32 FP32 tile per wave.
-constexpr int kDecodeRed = kDecodeWaves * kDecodeRows * kDecodeRows * 4;
+// A wave's 32 x 32 FP32 partial tile, added in a ring slot (see add_and_store).
+constexpr int kDecodeTileBytes = kDecodeRows * kDecodeRows * 4;
+// Beside the rings: the byte offset of each wave's slot holding its partial tile.
+constexpr int kDecodeOffs = kDecodeWaves * 4;
+constexpr int kDecodeMaxRing = 5;    // the deepest ring (slabs per wave)
 
 // Wait until at most N of this wave's memory loads are outstanding and all
 // of its LDS reads are done (the ring slot about to be refilled was read by
@@ -62,15 +65,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 
 // Slab geometry of the decode kernel for formats (FA, FB): the tile
 // kernel's slabs (128 K-values, 256 when both operands are E2M1), 32 rows
-// of A and 32 of B.  WA = 8 or 16 is for an E4M3 / E5M2 A with an E2M1 B
-// and M <= WA (8-bit activations, 4-bit weights): 256-K slabs, so that each
-// B row of a slab is one whole 128-byte line (with 128-K slabs it is half
-// of one, and the line's other half is fetched again), A rows of 256
-// bytes, and only WA A rows staged (2 or 4 copy instructions; 32 such rows
-// would leave room for fewer than 3 slabs).  (Staging 8 A rows in the
-// other geometries too, for a deeper ring, measured no faster on MI355X: at
-// M = 8, N = 8192, K = 28672 the same time within 1 %, and up to 18 %
-// slower for E2M1 with K <= 4096.)
+// of A and 32 of B.  WA = 8, 16 or 32 is for an E4M3 / E5M2 A with an E2M1
+// B and M <= WA (8-bit activations, 4-bit weights): 256-K slabs, so that
+// each B row of a slab is one whole 128-byte line (with 128-K slabs it is
+// half of one, and the line's other half is fetched again), A rows of 256
+// bytes, and only WA A rows staged (2, 4 or 8 copy instructions).
+// (Staging 8 A rows in the other geometries too, for a deeper ring,
+// measured no faster on MI355X: at M = 8, N = 8192, K = 28672 the same time
+// within 1 %, and up to 18 % slower for E2M1 with K <= 4096.)
 //
 // Scale bytes are staged once per 512-K period, beside the ring: a period's
 // 16 bytes of each of the 32 A and 32 B rows (1 KB, four 4-byte copy
@@ -78,12 +80,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // slab.  They are read into registers when that slab is multiplied, and the
 // buffer is refilled R periods later, which the ring's lead of S - 1 slabs
 // must not reach: R * PS > S - 1, with PS slabs per period.
+//
+// The ring is at most 5 slabs deep: 6 slabs of the 6 KB geometries fit, but
+// measured 4 % slower on MI355X with several column groups per workgroup
+// (8 x 57344 x 8192, an 8-bit A with an E2M1 B).
 template <int FA, int FB, int WA = 0>
 struct decode_geo {
     static constexpr bool WIDE = WA != 0;
     using SL = slab<FA, FB>;
     static_assert(!WIDE || (FB == FP4 && FA != FP4), "the wide slabs pair an 8-bit A with an E2M1 B");
-    static_assert(WA == 0 || WA == 8 || WA == 16, "8 or 16 staged A rows");
+    static_assert(WA == 0 || WA == 8 || WA == 16 || WA == 32, "8, 16 or 32 staged A rows");
     static constexpr int KS = WIDE ? 256 : SL::kvals;          // K-values per slab
     static constexpr int PS = 512 / KS;                        // slabs per scale period
     static constexpr int RA = WIDE ? 256 : SL::template row_bytes<FA>;   // slab row bytes
@@ -98,18 +104,21 @@ struct decode_geo {
     // copies, the most scale copies among them
     static constexpr int lead(int s) { return (s - 2) * NCOPY + NSC * ((s - 3 + PS) / PS); }
     static constexpr int wave_lds(int s) { return s * SLOT + bufs(s) * SCP; }
-    // ring depth: the most slabs that fit in the LDS beside the partial-tile
-    // area, with a wait count that fits the vmcnt field (at most 63)
+    // ring depth: the most slabs (up to kDecodeMaxRing) that fit in the LDS,
+    // with a wait count that fits the vmcnt field (at most 63)
     static constexpr int depth()
     {
         int s = 3;
-        while (kDecodeWaves * wave_lds(s + 1) + kDecodeRed <= kDecodeLds && lead(s + 1) <= 63) ++s;
+        while (s < kDecodeMaxRing && kDecodeWaves * wave_lds(s + 1) + kDecodeOffs <= kDecodeLds &&
+               lead(s + 1) <= 63)
+            ++s;
         return s;
     }
     static constexpr int S = depth();
     static constexpr int R = bufs(S);
     static constexpr int WAVE_LDS = wave_lds(S);
-    static constexpr int SMEM = kDecodeWaves * WAVE_LDS + kDecodeRed;
+    static constexpr int SMEM = kDecodeWaves * WAVE_LDS + kDecodeOffs;
+    static_assert(SLOT >= kDecodeTileBytes, "a ring slot holds a partial tile");
 };
 
 // LDS swizzle of a slab row of R bytes: the tile kernel's for 128- and
@@ -151,7 +160,7 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const int lr = lane & 31, g = lane >> 5;
     uint8_t *const ring = smem + wave * G::WAVE_LDS;
     uint8_t *const sring = ring + S * SLOT;          // the period buffers
-    float *const red = (float *)(smem + kDecodeWaves * G::WAVE_LDS);
+    int *const tile_at = (int *)(smem + kDecodeWaves * G::WAVE_LDS);
 
     // This workgroup's column groups: gi = 0 .. ng-1 is group
     // blockIdx.x + gi * gridDim.x, columns n0 .. n0+31 of it.
@@ -236,8 +245,8 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     };
 
     // Operands of step p of a slab for lane row lr, from NR staged rows of R
-    // bytes at `rows` (with NR = 8 or 16, the A rows of the wide slabs, lane
-    // row lr reads row lr % NR; only rows below M <= NR are stored): E4M3 / E5M2
+    // bytes at `rows` (with NR = 8 or 16 A rows of the wide slabs, lane row
+    // lr reads row lr % NR; only rows below M <= NR are stored): E4M3 / E5M2
     // chunks 4p+g and 4p+2+g, E2M1 chunk 2p+g.
     auto frag = [&](auto fc, auto rc, auto nc, const uint8_t *rows, int p, v8i &v) {
         constexpr int F = decltype(fc)::value, R = decltype(rc)::value, NR = decltype(nc)::value;
@@ -301,23 +310,32 @@ decode_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     };
 
     // Add the waves' partial tiles of group gi in wave order and store them.
+    // Each wave keeps its tile in the ring slot of the last slab it
+    // multiplied: the copies in flight fill the other S - 1 slots, and that
+    // one is refilled only by the next issue, after the second barrier below.
     // In the MFMA result lane (c, g) holds, in element e, row
-    // 8(e/4) + 4g + e%4 of column c; element e of lane l is kept at
-    // red[1024 w + 64 e + l].  The barriers order LDS only: the stream's
-    // copies into the rings stay in flight.
+    // 8(e/4) + 4g + e%4 of column c; element e of lane l is kept at float
+    // 64 e + l of the slot.  The barriers order LDS only: the stream's copies
+    // into the rings stay in flight.
     auto add_and_store = [&](int gi) {
         const int n0 = group_n0(gi), rows_b = min(kDecodeRows, N - n0);
+        const int at_slot = wave * G::WAVE_LDS + (rslot == 0 ? S - 1 : rslot - 1) * SLOT;
+        float *const mine = (float *)(smem + at_slot);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red[wave * 1024 + e * 64 + lane] = acc[e];
+        for (int e = 0; e < 16; ++e) mine[e * 64 + lane] = acc[e];
+        if (lane == 0) tile_at[wave] = at_slot;
         lds_barrier();
+        int from[kDecodeWaves];
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w) from[w] = tile_at[w];
 #pragma unroll
         for (int q = 0; q < kDecodeRows * kDecodeRows / (kDecodeWaves * 64); ++q) {
             const int m = q * 8 + (tid >> 5), c = tid & 31;
             if (m >= M || c >= rows_b) continue;
-            const int at = ((m >> 3) * 4 + (m & 3)) * 64 + c + 32 * ((m >> 2) & 1);
-            float v = red[at];
+            const int at = (((m >> 3) * 4 + (m & 3)) * 64 + c + 32 * ((m >> 2) & 1)) * 4;
+            float v = *(const float *)(smem + from[0] + at);
 #pragma unroll
-            for (int w = 1; w < kDecodeWaves; ++w) v += red[w * 1024 + at];
+            for (int w = 1; w < kDecodeWaves; ++w) v += *(const float *)(smem + from[w] + at);
             if constexpr (OUT == OF32) ((float *)C)[(int64_t)m * N + n0 + c] = v;
             else ((uint16_t *)C)[(int64_t)m * N + n0 + c] = f32_to_bf16(v);
         }

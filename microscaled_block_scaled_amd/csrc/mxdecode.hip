@@ -22,8 +22,8 @@ void go(int out_dtype, const void *A, const void *As, const void *B, const void 
     const uint8_t *a = (const uint8_t *)A, *as = (const uint8_t *)As;
     const uint8_t *b = (const uint8_t *)B, *bs = (const uint8_t *)Bs;
     const bool f32 = out_dtype == MX_OUT_FP32;
-    // An 8-bit A with an E2M1 B and at most 16 rows: the wide slabs, with
-    // 8 or 16 A rows staged
+    // An 8-bit A with an E2M1 B: the wide slabs, with 8, 16 or 32 A rows
+    // staged
     if constexpr (FB == mx::FP4 && FA != mx::FP4) {
         if (M <= 8) {
             if (f32)
@@ -43,13 +43,20 @@ void go(int out_dtype, const void *A, const void *As, const void *B, const void 
                                    a, as, b, bs, C, (int)M, (int)N, (int)K);
             return;
         }
+        if (f32)
+            hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OF32, 32>), grid, block, 0, s,
+                               a, as, b, bs, C, (int)M, (int)N, (int)K);
+        else
+            hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OBF16, 32>), grid, block, 0, s,
+                               a, as, b, bs, C, (int)M, (int)N, (int)K);
+    } else {
+        if (f32)
+            hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OF32, 0>), grid, block, 0, s, a,
+                               as, b, bs, C, (int)M, (int)N, (int)K);
+        else
+            hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OBF16, 0>), grid, block, 0, s, a,
+                               as, b, bs, C, (int)M, (int)N, (int)K);
     }
-    if (f32)
-        hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OF32, 0>), grid, block, 0, s, a, as,
-                           b, bs, C, (int)M, (int)N, (int)K);
-    else
-        hipLaunchKernelGGL((mx::decode_kernel<FA, FB, mx::OBF16, 0>), grid, block, 0, s, a,
-                           as, b, bs, C, (int)M, (int)N, (int)K);
 }
 
 int kernel_fmt(int fmt)

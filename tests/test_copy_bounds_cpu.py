@@ -161,28 +161,31 @@ def test_model_reports_unclamped_fp6_padding_lanes():
 # The decode kernel (csrc/mx_decode.h): a grid of at most 256 workgroups,
 # workgroup b taking column groups b, b + grid, ...; 4 waves per workgroup,
 # each a K-range of whole 512-K periods, a private ring of S slabs of the
-# staged A rows and 32 B rows, and R period buffers of those rows' scale
+# staged A rows and 32 B rows (a slot of which also holds the wave's
+# partial tile after each group), and R period buffers of those rows' scale
 # bytes; each wave's copies form one stream of slab positions over all its
 # groups, nper * PS positions per group (positions past a group's slabs, or
 # past its last group, copy with num_records 0), with four 4-byte scale
 # copies at each period's first position.
 DECODE_LDS, DECODE_ROWS, DECODE_WAVES, DECODE_CUS = 163840, 32, 4, 256
-DECODE_RED = DECODE_WAVES * DECODE_ROWS * DECODE_ROWS * 4
+DECODE_OFFS = DECODE_WAVES * 4       # the waves' partial-tile slot offsets
+DECODE_MAX_RING = 5
 
 
 def decode_wide(fa, fb, M):
     """The A rows the wide slabs stage (0: not wide): an 8-bit A with an
-    E2M1 B, 8 rows for M <= 8 and 16 for M <= 16."""
-    if fb != FP4 or fa == FP4 or M > 16:
+    E2M1 B, 8 rows for M <= 8, 16 for M <= 16, else 32."""
+    if fb != FP4 or fa == FP4:
         return 0
-    return 8 if M <= 8 else 16
+    return 8 if M <= 8 else 16 if M <= 16 else 32
 
 
 def decode_geo(fa, fb, wide=0):
     """(K-values per slab, A and B slab row bytes, rows of A staged, copies
     per slab, ring depth, period buffers) of the decode kernel: the deepest
-    ring whose slabs and period buffers fit beside the partial tiles, with
-    a wait count (the next S - 2 positions' loads) within 63."""
+    ring (at most 5 slabs) whose slabs and period buffers fit in the LDS,
+    with a wait count (the next S - 2 positions' loads) within 63; each
+    wave's partial tile is added in one of its ring slots."""
     kv = 256 if wide else kvals(fa, fb)
     RA, RB = slab_row_bytes(fa, kv), slab_row_bytes(fb, kv)
     MA = wide if wide else DECODE_ROWS
@@ -192,9 +195,11 @@ def decode_geo(fa, fb, wide=0):
     bufs = lambda s: (s - 1) // PS + 1
     lead = lambda s: (s - 2) * ncopy + 4 * ((s - 3 + PS) // PS)
     S = 3
-    while (DECODE_WAVES * ((S + 1) * slot + bufs(S + 1) * 1024) + DECODE_RED <= DECODE_LDS
+    while (S < DECODE_MAX_RING
+           and DECODE_WAVES * ((S + 1) * slot + bufs(S + 1) * 1024) + DECODE_OFFS <= DECODE_LDS
            and lead(S + 1) <= 63):
         S += 1
+    assert slot >= DECODE_ROWS * DECODE_ROWS * 4     # a slot holds a partial tile
     return kv, RA, RB, MA, ncopy, S, bufs(S)
 
 
@@ -242,7 +247,7 @@ def decode_check(fa, fb, M, N, K, scale_records_from_period=True, idle_records=T
     kv, RA, RB, MA, ncopy, S, R = decode_geo(fa, fb, decode_wide(fa, fb, M))
     PS = 512 // kv
     assert S >= 3 and (S - 2) * ncopy + 4 * ((S - 3 + PS) // PS) <= 63 and R * PS > S - 1
-    assert DECODE_WAVES * (S * (MA * RA + DECODE_ROWS * RB) + R * 1024) + DECODE_RED <= DECODE_LDS
+    assert DECODE_WAVES * (S * (MA * RA + DECODE_ROWS * RB) + R * 1024) + DECODE_OFFS <= DECODE_LDS
     rowba, rowbb = kbytes(fa, K), kbytes(fb, K)
     sps = K // 32
     per_w = -(-(K // 128) // (4 * DECODE_WAVES))
@@ -311,7 +316,8 @@ def test_decode_copies_stay_inside_their_operands(fa, fb):
     shapes = [(1, 1, 512), (8, 8192, 28672), (32, 203, 640), (5, 100, 1664), (17, 64, 3200),
               (32, 8161, 2048), (3, 40, 1152), (32, 96, 8192 + 384), (2, 33, 4096 + 128),
               (9, 40, 2560), (16, 70, 1152), (8, 28672, 4096), (4, 16417, 1664),
-              (32, 24607, 640), (12, 8200, 3200), (16, 16417, 4224)]
+              (32, 24607, 640), (12, 8200, 3200), (16, 16417, 4224), (24, 9000, 1664),
+              (32, 8192, 28672)]
     bad = []
     for M, N, K in shapes:
         bad += [((M, N, K), prob) for prob in decode_check(fa, fb, M, N, K)]

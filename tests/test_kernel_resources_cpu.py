@@ -69,9 +69,9 @@ def test_kernels_fit_their_register_budget(tmp_path):
     wide = [(k, v) for k, v in tiles.items()
             if v.get("max_flat_workgroup_size", 0) >= 512 and v.get("vgpr_count", 0) > 256]
     assert not wide, wide[:5]
-    # the decode kernels: the 9 pairs of E2M1 / E4M3 / E5M2 x 2 output types,
-    # and the wide slabs (8 and 16 A rows) of the two 8-bit x E2M1 pairs,
-    # none spilling at all
+    # the decode kernels: the 7 pairs of E2M1 / E4M3 / E5M2 other than an
+    # 8-bit A with an E2M1 B, and the wide slabs (8, 16 and 32 A rows) of
+    # those two pairs, x 2 output types, none spilling at all
     dec = {k: v for k, v in ks.items() if "decode_kernel" in k}
     assert len(dec) == 26, sorted(dec)
     assert not [(k, v) for k, v in dec.items() if v.get("vgpr_spill_count", 0) > 0]
@@ -80,8 +80,8 @@ def test_kernels_fit_their_register_budget(tmp_path):
 def test_decode_kernel_lds_matches_the_copy_model(tmp_path):
     """The decode kernels' LDS (from the code objects) is what the copy
     model's geometry implies: 4 waves x (S slabs + R period buffers of 1 KB)
-    plus the 16 KB partial-tile area, so the model checks the ring the
-    kernel really has."""
+    plus the 4 slot offsets of the partial tiles, so the model checks the
+    ring the kernel really has."""
     if not os.path.exists(LIB):
         pytest.skip("libmxgemm.so is not built")
     for tool in ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf"):
@@ -98,7 +98,7 @@ def test_decode_kernel_lds_matches_the_copy_model(tmp_path):
         fa, fb, wide = int(m.group(1)), int(m.group(2)), int(m.group(4))
         kv, RA, RB, MA, ncopy, S, R = cb.decode_geo(fa, fb, wide)
         want = (cb.DECODE_WAVES * (S * (MA * RA + cb.DECODE_ROWS * RB) + R * 1024)
-                + cb.DECODE_RED)
+                + cb.DECODE_OFFS)
         assert v.get("group_segment_fixed_size") == want, (name, v, want)
         seen += 1
     assert seen == 26
