@@ -230,6 +230,24 @@ def test_decode_gateup_full_size(fa, fb):
     _check(sub, BF16, first[:, torch.from_numpy(cols).cuda()], what="gate-up columns")
 
 
+@pytest.mark.parametrize("fa", [E4M3, E5M2], ids=["e4m3", "e5m2"])
+def test_decode_w4a8_plan_at_m32(fa):
+    """An 8-bit A with an E2M1 B at 32 rows and long K: the plan takes the
+    decode kernel's 32-row wide slabs (the M > 16 limit of the other pairs
+    does not apply), equal to the forced decode tile bit for bit, and
+    sampled columns match the oracle."""
+    import torch
+    M, N, K = 32, 8192, 28672
+    case = _case(fa, E2M1, M, N, K, seed=1300 + fa)
+    d = _dev(case)
+    log("decode w4a8 plan fa=%d M=%d N=%d K=%d" % (fa, M, N, K))
+    planned = _run(case, BF16, tile=None, d=d)
+    assert torch.equal(planned, _run(case, BF16, tile=DECODE, d=d))
+    cols = np.unique(np.r_[0:40, np.linspace(0, N - 1, 120).astype(int), N - 40:N])
+    sub = dict(case, B=case["B"][cols], B_scale=case["B_scale"][cols], N=len(cols))
+    _check(sub, BF16, planned[:, torch.from_numpy(cols).cuda()], what="w4a8 plan columns")
+
+
 def test_decode_noalloc_entry_matches():
     """mx_gemm_noalloc on a decode-planned shape (no scratch needed) equals
     mx_gemm bit for bit, twice, the second call smaller."""
